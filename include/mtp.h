@@ -1,0 +1,197 @@
+/*
+ * mtp.h -- C ABI of libmtp, the MI355X (gfx950) implementation of the MTP
+ * (multi-token-prediction) speculative-decoding round: the draft-head step, the
+ * pending-pair flush, speculative verification and draft-KV rollback.
+ *
+ * Conventions for every entry point
+ *  - Pointers named *_dev, and every tensor argument, are caller-owned DEVICE
+ *    pointers; structs passed by pointer (config, weights, kv descriptor,
+ *    sampling) are HOST memory read during the call only.
+ *  - The library never allocates device memory.  Scratch lives in a caller-owned
+ *    workspace sized by mtp_workspace_bytes / spec_verify_workspace_bytes; it
+ *    must be zeroed once before first use (mtp_workspace_init) and is left
+ *    zeroed-where-it-matters by every call (self-resetting counters).
+ *  - Every compute call is asynchronous on `stream` and does not synchronise.
+ *  - Host-checkable problems return a negative mtp_status BEFORE anything is
+ *    enqueued (fail closed).  Problems only the device can see (a device-side
+ *    count above its host bound, a KV append past capacity, a rollback past the
+ *    current length) set the sticky error word state[3] of the draft KV; every
+ *    later kernel on that KV is then a no-op.  Read state[] at the round's host
+ *    synchronisation.
+ *  - Not thread-safe per workspace or per KV; distinct (workspace, KV) pairs are
+ *    independent.  Calls that share a workspace must be ordered on one stream.
+ *  - Layouts are row-major; weight matrices are [out, in] (nn.Linear).  Norm
+ *    weights are the final multiplicative values (any +1.0 offset of a raw
+ *    checkpoint already applied).  Tokens are int32; logits and uniforms fp32.
+ *
+ * The pages describing the method: "Ollama qwen3_5 MTP loader and SelfDraft
+ * path" (Facts), "feat(inference): support the qwen3_5_mtp drafter for
+ * Qwen3.5/3.6/3.8 MTP speculative decoding" (sections "Where the MTP weights
+ * actually live", "Upstream contract to port", "Acceptance criteria"), and the
+ * Ollama x/mlxrunner commit log.
+ */
+#ifndef MTP_H_
+#define MTP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_E_INVALID_ARG = -1, /* null pointer, bad size, bad mode */
+  MTP_E_UNSUPPORTED = -2, /* shape or option outside what the kernels implement */
+  MTP_E_NOT_BOUND = -3,   /* embedding table or lm_head missing: the head borrows both */
+  MTP_E_CAPACITY = -4,    /* host-visible KV capacity or flush-size bound exceeded */
+  MTP_E_HIP = -5,         /* a HIP launch or runtime call failed */
+  MTP_E_DEVICE = -6,      /* reported by callers that read a non-zero state[3] */
+  MTP_E_WORKSPACE = -7    /* workspace smaller than the size function returns */
+} mtp_status;
+
+typedef enum { MTP_F32 = 0, MTP_BF16 = 1, MTP_I8G128 = 2 } mtp_dtype;
+
+/* Device error codes stored in mtp_kv.state[3]. */
+enum { MTP_DEV_OK = 0, MTP_DEV_CAPACITY = 1, MTP_DEV_ROLLBACK = 2, MTP_DEV_COUNT = 3 };
+
+/* Shape and storage of the draft head.  Source: "Upstream contract to port"
+ * (fc 2H->H, the two pre-fc RMSNorms, one full-attention layer with q/k norms,
+ * final norm; embedding and lm_head borrowed from the target).
+ * hidden, intermediate: multiples of 64; head_dim: 64, 128 or 256;
+ * n_q_heads / n_kv_heads in {1, 2, 3, 4, 6, 8}.
+ * weight_dtype (projections, norms, embedding): F32 or BF16.
+ * act_dtype (hidden states crossing the ABI): F32 or BF16.
+ * kv_dtype: F32 or BF16.  lm_head_dtype: F32, BF16 or I8G128 (int8 per row and
+ * 128-column group, fp16 scales [vocab, hidden/128], value = q * s). */
+typedef struct {
+  int32_t hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+  float rms_eps, rope_theta;
+  int32_t weight_dtype, act_dtype, kv_dtype, lm_head_dtype;
+} mtp_head_config;
+
+/* The 15 head tensors ("Where the MTP weights actually live") plus the borrowed
+ * embedding table [vocab, hidden] and lm_head [vocab, hidden].  Shapes:
+ * fc [H, 2H] (columns: embedding half first); q_proj [Hq*D, H]; k_proj, v_proj
+ * [Hkv*D, H]; o_proj [H, Hq*D]; gate_proj, up_proj [I, H]; down_proj [H, I];
+ * q_norm, k_norm [D]; the five other norms [H].  Must outlive the mtp_head. */
+typedef struct {
+  const void *embed, *lm_head, *lm_head_scales;
+  const void *pre_fc_norm_embedding, *pre_fc_norm_hidden, *fc, *input_layernorm;
+  const void *q_proj, *k_proj, *v_proj, *q_norm, *k_norm, *o_proj;
+  const void *post_attention_layernorm, *gate_proj, *up_proj, *down_proj, *norm;
+} mtp_head_weights;
+
+/* Opaque HOST object holding the validated config and weight pointers. */
+typedef struct mtp_head mtp_head;
+
+/* The head's own draft KV cache (separate from the target's; only the position
+ * offset is shared: "Upstream contract to port").  k, v: [n_kv_heads, capacity,
+ * head_dim] in kv_dtype.  state: device int32[4] = {len, round_base, reserved,
+ * err}; slot S holds the pair (token S+1, target hidden S) at RoPE position S. */
+typedef struct {
+  void *k, *v;
+  int32_t capacity;
+  int32_t *state;
+} mtp_kv;
+
+/* Sampler settings ("Ollama qwen3_5 MTP loader and SelfDraft path", Facts
+ * "Verification": temperature, penalty, top-k/top-p/min-p).  temperature 0 means
+ * greedy.  top_k 0 = off, top_p >= 1 = off, min_p 0 = off, repeat_penalty 1 = off.
+ * window: length of the history ring the penalty looks at (1..1024). */
+typedef struct {
+  float temperature, repeat_penalty, top_p, min_p;
+  int32_t top_k, window;
+} spec_sampling;
+
+enum { MTP_FLUSH_KV_ONLY = 0, MTP_FLUSH_LAST = 1, MTP_FLUSH_ALL = 2 };
+#define MTP_TO_ROUND_BASE (-1)
+#define MTP_MAX_FLUSH 256  /* pending-pair flush cap ("Facts": flush batches of up to 256) */
+#define MTP_MAX_DRAFT 16   /* drafts per verify */
+
+/* Human-readable name of a status code (static string). */
+const char *mtp_status_string(int status);
+
+/* Text of the last HIP error this thread's calls returned MTP_E_HIP for. */
+const char *mtp_last_error(void);
+
+/* Validate the config and weights and build the host-side head object.
+ * Returns MTP_E_NOT_BOUND if embed or lm_head is NULL (the head owns neither),
+ * MTP_E_INVALID_ARG for other NULL tensors or bad sizes, MTP_E_UNSUPPORTED for
+ * shapes outside the kernels.  *out is set only on success. */
+int mtp_head_create(const mtp_head_config *cfg, const mtp_head_weights *w, mtp_head **out);
+void mtp_head_destroy(mtp_head *head);
+
+/* Workspace bytes for calls with at most max_rows pairs (1..256) on a KV of at
+ * most max_capacity slots.  0 on invalid arguments. */
+size_t mtp_workspace_bytes(const mtp_head_config *cfg, int32_t max_rows, int32_t max_capacity);
+
+/* Zero a workspace (either kind) with a fill kernel on `stream`. */
+int mtp_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* One draft-head step ("Facts", MTP drafting: one head call per draft token) at
+ * slot S = state[0]: the pair (token_dev[0], hidden_in_dev) is appended to the
+ * draft KV at S and state[0] becomes S + 1.
+ * token_dev: int32[1]; hidden_in_dev: [hidden] act_dtype; hidden_out_dev:
+ * [hidden] act_dtype, the layer output before the final norm (the hidden a
+ * chained step feeds back); logits_dev (nullable): fp32 [vocab];
+ * argmax_dev (nullable): int32[1], lowest index among equal maxima.
+ * hidden_out_dev must not alias hidden_in_dev. */
+int mtp_draft_step(const mtp_head *head, const mtp_kv *kv, const int32_t *token_dev,
+                   const void *hidden_in_dev, void *hidden_out_dev, float *logits_dev,
+                   int32_t *argmax_dev, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Pending-pair flush ("Facts", MTP drafting: pending pairs flush in batches of
+ * up to 256): n complete pairs (tokens_dev[j], hiddens_dev[j]) are appended at
+ * slots state[0] + j, causal within the batch and over the whole prefix.
+ * n = n_max, or min(*n_dev, n_max) when n_dev is given (device count; a count
+ * above n_max or below 0 sets state[3] = MTP_DEV_COUNT).  n_max <= 256.
+ * out_mode KV_ONLY: only K/V.  LAST: hidden_out [hidden] (last row's g), logits
+ * and argmax of the last row.  ALL: hidden_out [n, hidden] for every row, logits
+ * and argmax of the last row.  set_round_base != 0 records state[1] = state[0]
+ * after the append (the first provisional slot of a round). */
+int mtp_flush_pairs(const mtp_head *head, const mtp_kv *kv, const int32_t *tokens_dev,
+                    const void *hiddens_dev, int32_t n_max, const int32_t *n_dev,
+                    int32_t out_mode, int32_t set_round_base, void *hidden_out_dev,
+                    float *logits_last_dev, int32_t *argmax_last_dev, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for spec_verify with n_draft drafts over vocab logits. */
+size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab);
+
+/* Verify n_draft (0..16) drafts against n_draft + 1 target rows ("Facts",
+ * Verification; the commit log's rejection sampling, greedy as its point-mass
+ * case).  target_logits_dev fp32 [n_draft+1, vocab]; draft_logits_dev fp32
+ * [n_draft, vocab] (must be NULL iff temperature == 0); draft_tokens_dev int32
+ * [n_draft]; history_dev int32 [window] ring with history_state_dev {head,
+ * count} (head = next write slot), updated with the committed tokens;
+ * uniforms_dev fp32 [n_draft+1] (u_i for the accept test of draft i, u_N for
+ * the residual or bonus draw; may be NULL when greedy).  Outputs:
+ * out_tokens_dev int32 [n_draft+1] (first k+1 valid), out_counts_dev int32[2] =
+ * {k accepted, k+1 committed}.  Accept d_i iff u_i * q_i(d_i) < p_i(d_i); at the
+ * first rejection draw from normalise(max(0, p - q)) (p if that is zero); if all
+ * are accepted draw the bonus from p_N.  Sampler order: penalty, temperature,
+ * top-k, softmax, top-p, min-p.  top_k must be 1..1024 when temperature > 0 and
+ * top_p < 1 (MTP_E_UNSUPPORTED otherwise). */
+int spec_verify(const spec_sampling *sp, int32_t n_draft, int32_t vocab,
+                const float *target_logits_dev, const float *draft_logits_dev,
+                const int32_t *draft_tokens_dev, int32_t *history_dev,
+                int32_t *history_state_dev, const float *uniforms_dev,
+                int32_t *out_tokens_dev, int32_t *out_counts_dev, void *ws,
+                size_t ws_bytes, hipStream_t stream);
+
+/* Draft-KV rollback (the #1174 comment: trim attention KV by the rejected
+ * count): state[0] := to_len (>= 0), or with MTP_TO_ROUND_BASE := state[1]
+ * (every chained entry provisional), or := state[1] + min(*n_accepted_dev,
+ * n_draft - 1) when n_accepted_dev is given (keep accepted chained entries).
+ * O(1): no K/V byte is touched.  A target above the current length sets
+ * state[3] = MTP_DEV_ROLLBACK.  to_len > capacity is rejected on the host. */
+int kv_rollback(const mtp_kv *kv, int32_t to_len, const int32_t *n_accepted_dev,
+                int32_t n_draft, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTP_H_ */

@@ -1,0 +1,256 @@
+"""Thin ctypes binding of libmtp (include/mtp.h): the same entry points, with
+argument marshalling only (torch tensors -> device pointers, the current HIP
+stream).  Every computation runs in the library's kernels.  Importing this
+module loads libmtp.so from the package directory and raises if it is missing:
+there is no fallback path.
+
+Small helpers own device memory for callers (torch allocations): ``Head`` keeps
+the weight tensors alive next to the native head handle, ``DraftKV`` holds the
+cache and its state words, ``Workspace`` a zero-initialised scratch buffer.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmtp.so")
+
+MTP_OK, MTP_E_INVALID_ARG, MTP_E_UNSUPPORTED, MTP_E_NOT_BOUND = 0, -1, -2, -3
+MTP_E_CAPACITY, MTP_E_HIP, MTP_E_DEVICE, MTP_E_WORKSPACE = -4, -5, -6, -7
+MTP_F32, MTP_BF16, MTP_I8G128 = 0, 1, 2
+KV_ONLY, LAST, ALL = 0, 1, 2
+TO_ROUND_BASE = -1
+DEV_OK, DEV_CAPACITY, DEV_ROLLBACK, DEV_COUNT = 0, 1, 2, 3
+
+WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
+                 "pre_fc_norm_hidden", "fc", "input_layernorm", "q_proj", "k_proj", "v_proj",
+                 "q_norm", "k_norm", "o_proj", "post_attention_layernorm", "gate_proj",
+                 "up_proj", "down_proj", "norm")
+
+EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_destroy", "mtp_workspace_bytes",
+           "mtp_workspace_init", "mtp_draft_step", "mtp_flush_pairs",
+           "spec_verify_workspace_bytes", "spec_verify", "kv_rollback")
+
+
+class mtp_head_config(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("intermediate", C.c_int32), ("vocab", C.c_int32),
+                ("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                ("weight_dtype", C.c_int32), ("act_dtype", C.c_int32), ("kv_dtype", C.c_int32),
+                ("lm_head_dtype", C.c_int32)]
+
+
+class mtp_head_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class mtp_kv(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_int32), ("state", C.c_void_p)]
+
+
+class spec_sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("repeat_penalty", C.c_float), ("top_p", C.c_float),
+                ("min_p", C.c_float), ("top_k", C.c_int32), ("window", C.c_int32)]
+
+
+def _load():
+    # torch ships its own HIP runtime under the same soname; loading torch first
+    # makes libmtp bind to that one copy, so both share one runtime and device.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmtp.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    lib.mtp_status_string.restype = C.c_char_p
+    lib.mtp_status_string.argtypes = [C.c_int]
+    lib.mtp_last_error.restype = C.c_char_p
+    lib.mtp_last_error.argtypes = []
+    lib.mtp_head_create.restype = C.c_int
+    lib.mtp_head_create.argtypes = [C.POINTER(mtp_head_config), C.POINTER(mtp_head_weights), C.POINTER(vp)]
+    lib.mtp_head_destroy.restype = None
+    lib.mtp_head_destroy.argtypes = [vp]
+    lib.mtp_workspace_bytes.restype = sz
+    lib.mtp_workspace_bytes.argtypes = [C.POINTER(mtp_head_config), i32, i32]
+    lib.mtp_workspace_init.restype = C.c_int
+    lib.mtp_workspace_init.argtypes = [vp, sz, vp]
+    lib.mtp_draft_step.restype = C.c_int
+    lib.mtp_draft_step.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mtp_flush_pairs.restype = C.c_int
+    lib.mtp_flush_pairs.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_workspace_bytes.restype = sz
+    lib.spec_verify_workspace_bytes.argtypes = [i32, i32]
+    lib.spec_verify.restype = C.c_int
+    lib.spec_verify.argtypes = [C.POINTER(spec_sampling), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kv_rollback.restype = C.c_int
+    lib.kv_rollback.argtypes = [C.POINTER(mtp_kv), i32, vp, i32, vp]
+    return lib
+
+
+lib = _load()
+
+
+class MtpError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = f"{where}: {lib.mtp_status_string(status).decode()} ({status})"
+        if status == MTP_E_HIP:
+            msg += f": {lib.mtp_last_error().decode()}"
+        super().__init__(msg)
+
+
+def _check(status, where):
+    if status != MTP_OK:
+        raise MtpError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+def mtp_status_string(status: int) -> str:
+    return lib.mtp_status_string(status).decode()
+
+
+def mtp_last_error() -> str:
+    return lib.mtp_last_error().decode()
+
+
+def mtp_head_create(cfg: mtp_head_config, weights: mtp_head_weights):
+    h = C.c_void_p()
+    st = lib.mtp_head_create(C.byref(cfg), C.byref(weights), C.byref(h))
+    _check(st, "mtp_head_create")
+    return h
+
+
+def mtp_head_destroy(handle):
+    lib.mtp_head_destroy(handle)
+
+
+def mtp_workspace_bytes(cfg: mtp_head_config, max_rows: int, max_capacity: int) -> int:
+    return lib.mtp_workspace_bytes(C.byref(cfg), max_rows, max_capacity)
+
+
+def mtp_workspace_init(ws, nbytes: int, stream=None):
+    _check(lib.mtp_workspace_init(_ptr(ws), nbytes, _stream(stream)), "mtp_workspace_init")
+
+
+def mtp_draft_step(head, kv, token, hidden_in, hidden_out, logits, argmax, ws, stream=None):
+    st = lib.mtp_draft_step(head.handle, C.byref(kv.desc), _ptr(token), _ptr(hidden_in),
+                            _ptr(hidden_out), _ptr(logits), _ptr(argmax), _ptr(ws), ws.nbytes,
+                            _stream(stream))
+    _check(st, "mtp_draft_step")
+
+
+def mtp_flush_pairs(head, kv, tokens, hiddens, n_max, n_dev, out_mode, set_round_base,
+                    hidden_out, logits_last, argmax_last, ws, stream=None):
+    st = lib.mtp_flush_pairs(head.handle, C.byref(kv.desc), _ptr(tokens), _ptr(hiddens), int(n_max),
+                             _ptr(n_dev), int(out_mode), int(set_round_base), _ptr(hidden_out),
+                             _ptr(logits_last), _ptr(argmax_last), _ptr(ws), ws.nbytes, _stream(stream))
+    _check(st, "mtp_flush_pairs")
+
+
+def spec_verify_workspace_bytes(n_draft: int, vocab: int) -> int:
+    return lib.spec_verify_workspace_bytes(n_draft, vocab)
+
+
+def spec_verify(sp: spec_sampling, n_draft, vocab, target_logits, draft_logits, draft_tokens,
+                history, history_state, uniforms, out_tokens, out_counts, ws, stream=None):
+    st = lib.spec_verify(C.byref(sp), int(n_draft), int(vocab), _ptr(target_logits), _ptr(draft_logits),
+                         _ptr(draft_tokens), _ptr(history), _ptr(history_state), _ptr(uniforms),
+                         _ptr(out_tokens), _ptr(out_counts), _ptr(ws), ws.nbytes, _stream(stream))
+    _check(st, "spec_verify")
+
+
+def kv_rollback(kv, to_len, n_accepted=None, n_draft=0, stream=None):
+    st = lib.kv_rollback(C.byref(kv.desc), int(to_len), _ptr(n_accepted), int(n_draft), _stream(stream))
+    _check(st, "kv_rollback")
+
+
+# ----------------------------------------------------------------------------
+# owners of device memory (torch allocations)
+# ----------------------------------------------------------------------------
+def to_device(arr: np.ndarray, device="cuda"):
+    """numpy storage -> torch device tensor (uint16 is bf16 bits, float16 stays)."""
+    import torch
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(arr).to(device)
+
+
+def config_of(shape) -> mtp_head_config:
+    code = {"f32": MTP_F32, "bf16": MTP_BF16, "i8g128": MTP_I8G128}
+    return mtp_head_config(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                           shape.intermediate, shape.vocab, shape.rms_eps, shape.rope_theta,
+                           code[shape.weight_dtype], code[shape.act_dtype], code[shape.kv_dtype],
+                           code[shape.lm_head_dtype])
+
+
+class Head:
+    """Weights on the device plus the native head handle."""
+
+    def __init__(self, shape, storage: dict, device="cuda"):
+        self.shape = shape
+        self.cfg = config_of(shape)
+        self.tensors = {k: to_device(v, device) for k, v in storage.items() if v is not None}
+        w = mtp_head_weights()
+        for name in WEIGHT_FIELDS:
+            t = self.tensors.get(name)
+            setattr(w, name, t.data_ptr() if t is not None else None)
+        self.weights = w
+        self.handle = mtp_head_create(self.cfg, w)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            mtp_head_destroy(h)
+            self.handle = None
+
+
+class DraftKV:
+    """K, V [n_kv_heads, capacity, head_dim] and the state words {len, base, -, err}."""
+
+    def __init__(self, shape, capacity: int, k=None, v=None, length: int = 0, device="cuda"):
+        import torch
+        dt = torch.bfloat16 if shape.kv_dtype == "bf16" else torch.float32
+        size = (shape.n_kv_heads, capacity, shape.head_dim)
+        self.k = to_device(k, device) if k is not None else torch.zeros(size, dtype=dt, device=device)
+        self.v = to_device(v, device) if v is not None else torch.zeros(size, dtype=dt, device=device)
+        assert tuple(self.k.shape) == size and self.k.dtype == dt
+        self.state = torch.tensor([length, length, 0, 0], dtype=torch.int32, device=device)
+        self.capacity = capacity
+        self.desc = mtp_kv(self.k.data_ptr(), self.v.data_ptr(), capacity, self.state.data_ptr())
+
+
+class Workspace:
+    def __init__(self, nbytes: int, device="cuda"):
+        import torch
+        if nbytes <= 0:
+            raise MtpError(MTP_E_INVALID_ARG, "Workspace")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.nbytes = nbytes
+        mtp_workspace_init(self.buf, nbytes)
+
+    def data_ptr(self):
+        return self.buf.data_ptr()
+
+
+def sampling(temperature=0.0, repeat_penalty=1.0, top_k=0, top_p=1.0, min_p=0.0, window=64):
+    return spec_sampling(temperature, repeat_penalty, top_p, min_p, top_k, window)

@@ -1,0 +1,409 @@
+// libmtp C ABI: host-side validation (fail closed before any enqueue), the
+// workspace layout, and the kernel sequences of the draft-head step, the
+// pending-pair flush, verification and rollback.
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "../../include/mtp.h"
+#include "kernels.h"
+
+using namespace mtp;
+
+namespace {
+thread_local hipError_t g_last_hip = hipSuccess;
+}  // namespace
+
+#define MTP_TRY(expr)                  \
+  do {                                 \
+    const hipError_t e_ = (expr);      \
+    if (e_ != hipSuccess) {            \
+      g_last_hip = e_;                 \
+      return MTP_E_HIP;                \
+    }                                  \
+  } while (0)
+
+struct mtp_head {
+  mtp_head_config cfg;
+  mtp_head_weights w;
+  int wt;   // weight type of projections / norms / embedding
+  int lmt;  // lm_head type
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kSyncBytes = 4096;  // counters and argmax slots, fixed at offset 0
+// sync area: u32 counters at byte 0, u64 slots at byte 1024
+constexpr int kCtrLm = 0, kCtrRope = 1, kCtrVerify = 2;
+constexpr int kSlotLm = 0;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int epc_of(int t) { return t == W_F32 ? 4 : (t == W_BF16 ? 8 : 16); }
+
+int lpr_for(int K, int t) {
+  const int nch = K / epc_of(t);
+  int l = 64;
+  while (l > 8 && nch % l) l >>= 1;
+  return (nch % l == 0 && nch >= l) ? l : 0;
+}
+
+int nr_for(int rows) {
+  int nr = 1;
+  while (nr < rows && nr < 16) nr <<= 1;
+  return nr;
+}
+
+int kp_for(int K, int t, int nr) {
+  const int budget = 16384 / nr;  // 64 KB of fp32 in LDS
+  if (K <= budget) return K;
+  const int q = lpr_for(K, t) * epc_of(t);
+  int kp = budget / q * q;
+  return kp > 0 ? kp : q;
+}
+
+int nchunk_for(const mtp_head_config& c, int capacity) {
+  const int min_chunks = (capacity + 479) / 480;
+  int target = (512 + c.n_kv_heads - 1) / c.n_kv_heads;
+  const int fine = (capacity + 15) / 16;
+  if (target > fine) target = fine;
+  return target > min_chunks ? target : min_chunks;
+}
+
+struct Layout {
+  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, total;
+  int nchunk;
+};
+
+Layout layout(const mtp_head_config& c, int rows, int capacity) {
+  Layout L{};
+  const size_t H = c.hidden, D = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, I = c.intermediate;
+  L.nchunk = nchunk_for(c, capacity);
+  size_t off = kSyncBytes;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.x = take(rows * H * 4);
+  L.qkv = take(rows * (hq + 2 * hkv) * D * 4);
+  L.qr = take(rows * hq * D * 4);
+  L.part_o = take(rows * hq * L.nchunk * D * 4);
+  L.part_ml = take(rows * hq * L.nchunk * 2 * 4);
+  L.o = take(rows * hq * D * 4);
+  L.x1 = take(rows * H * 4);
+  L.m = take(rows * I * 4);
+  L.g = take(rows * H * 4);
+  L.total = off;
+  return L;
+}
+
+bool dtype_ok(int t, bool allow_i8) { return t == MTP_F32 || t == MTP_BF16 || (allow_i8 && t == MTP_I8G128); }
+
+int validate_cfg(const mtp_head_config* c) {
+  if (!c) return MTP_E_INVALID_ARG;
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->intermediate <= 0 || c->vocab <= 0)
+    return MTP_E_INVALID_ARG;
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps) || !(c->rope_theta > 0.f) ||
+      !std::isfinite(c->rope_theta))
+    return MTP_E_INVALID_ARG;
+  if (!dtype_ok(c->weight_dtype, false) || !dtype_ok(c->act_dtype, false) ||
+      !dtype_ok(c->kv_dtype, false) || !dtype_ok(c->lm_head_dtype, true))
+    return MTP_E_INVALID_ARG;
+  if (c->hidden % 64 || c->intermediate % 64) return MTP_E_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return MTP_E_UNSUPPORTED;
+  if (c->n_q_heads % c->n_kv_heads) return MTP_E_UNSUPPORTED;
+  const int g = c->n_q_heads / c->n_kv_heads;
+  if (g != 1 && g != 2 && g != 3 && g != 4 && g != 6 && g != 8) return MTP_E_UNSUPPORTED;
+  if (c->lm_head_dtype == MTP_I8G128 && c->hidden % 128) return MTP_E_UNSUPPORTED;
+  if (static_cast<long long>(c->vocab) * c->hidden >= (1ll << 40)) return MTP_E_UNSUPPORTED;
+  return MTP_OK;
+}
+
+int validate_kv(const mtp_head* h, const mtp_kv* kv) {
+  if (!kv || !kv->k || !kv->v || !kv->state || kv->capacity <= 0) return MTP_E_INVALID_ARG;
+  (void)h;
+  return MTP_OK;
+}
+
+inline char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+inline unsigned int* ctr(void* ws, int i) { return reinterpret_cast<unsigned int*>(ws) + i; }
+inline unsigned long long* slot(void* ws, int i) {
+  return reinterpret_cast<unsigned long long*>(wsp(ws, 1024)) + i;
+}
+
+GemvArgs base_gemv(const mtp_head* h, const mtp_kv* kv) {
+  GemvArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.nw_bf16 = h->wt == W_BF16;
+  a.eps = h->cfg.rms_eps;
+  a.kv_state = kv->state;
+  return a;
+}
+
+hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t s) {
+  // ROWS_RANGE: blocks of up to 16 activation rows share one pass over the weights
+  a.row_sel = row_sel;
+  if (row_sel == ROW_LAST) {
+    a.row_base = 0;
+    a.kp = kp_for(a.K, wt, 1);
+    a.grid_stride = a.kp == a.K;
+    return launch_gemv(a, wt, 1, s);
+  }
+  const int nr = nr_for(rows_total);
+  a.kp = kp_for(a.K, wt, nr);
+  a.grid_stride = a.kp == a.K;
+  for (int b = 0; b < rows_total; b += nr) {
+    a.row_base = b;
+    hipError_t e = launch_gemv(a, wt, nr, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The head forward for n rows (n_max host bound, n_dev device count).
+// mode: KV_ONLY / LAST / ALL.  hidden_out: [1 or n, H] in act dtype (nullable).
+int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, const void* hiddens,
+                 int n_max, const int32_t* n_dev, int mode, int set_base, void* hidden_out,
+                 float* logits, int32_t* argmax, void* ws, hipStream_t s) {
+  const mtp_head_config& c = h->cfg;
+  const Layout L = layout(c, n_max, kv->capacity);
+  const int H = c.hidden, D = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, I = c.intermediate;
+  const int qkv_rows = (hq + 2 * hkv) * D;
+  float* x = reinterpret_cast<float*>(wsp(ws, L.x));
+  float* qkv = reinterpret_cast<float*>(wsp(ws, L.qkv));
+  float* qr = reinterpret_cast<float*>(wsp(ws, L.qr));
+  float* o = reinterpret_cast<float*>(wsp(ws, L.o));
+  float* x1 = reinterpret_cast<float*>(wsp(ws, L.x1));
+  float* m = reinterpret_cast<float*>(wsp(ws, L.m));
+  float* g = reinterpret_cast<float*>(wsp(ws, L.g));
+  // 1. x = W_fc [RMSNorm(E[t]) | RMSNorm(h)]
+  GemvArgs a = base_gemv(h, kv);
+  a.w[0] = h->w.fc; a.m[0] = H; a.M = H; a.K = 2 * H; a.lpr = lpr_for(2 * H, h->wt);
+  a.n_max = n_max; a.n_dev = n_dev;
+  a.in_mode = IN_EMBED; a.nw = h->w.pre_fc_norm_embedding; a.nw2 = h->w.pre_fc_norm_hidden;
+  a.tok = tokens; a.embed = h->w.embed; a.embed_bf16 = h->wt == W_BF16;
+  a.hid = hiddens; a.hid_bf16 = c.act_dtype == MTP_BF16; a.ld_hid = H;
+  a.out_mode = OUT_F32; a.y = x; a.ldy = H;
+  MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
+
+  // 2. q, k, v = W_{q,k,v} RMSNorm(x; w_in)
+  a = base_gemv(h, kv);
+  a.w[0] = h->w.q_proj; a.m[0] = hq * D;
+  a.w[1] = h->w.k_proj; a.m[1] = hkv * D;
+  a.w[2] = h->w.v_proj; a.m[2] = hkv * D;
+  a.M = qkv_rows; a.K = H; a.lpr = lpr_for(H, h->wt);
+  a.n_max = n_max; a.n_dev = n_dev;
+  a.in_mode = IN_RMS; a.x = x; a.ldx = H; a.nw = h->w.input_layernorm;
+  a.out_mode = OUT_F32; a.y = qkv; a.ldy = qkv_rows;
+  MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
+
+  // 3. q/k norm + RoPE, append K/V at slots len + j, advance len
+  RopeArgs r;
+  std::memset(&r, 0, sizeof(r));
+  r.qkv = qkv; r.ld_qkv = qkv_rows; r.q_out = qr;
+  r.q_norm = h->w.q_norm; r.k_norm = h->w.k_norm; r.nw_bf16 = h->wt == W_BF16;
+  r.eps = c.rms_eps; r.theta = c.rope_theta; r.hq = hq; r.hkv = hkv; r.d = D;
+  r.kc = kv->k; r.vc = kv->v; r.kv_bf16 = c.kv_dtype == MTP_BF16; r.capacity = kv->capacity;
+  r.state = kv->state; r.n_max = n_max; r.n_dev = n_dev; r.set_base = set_base;
+  r.counter = ctr(ws, kCtrRope);
+  MTP_TRY(launch_rope_append(r, s));
+  if (mode == MTP_FLUSH_KV_ONLY) return MTP_OK;
+
+  const int rsel = (mode == MTP_FLUSH_ALL) ? ROWS_RANGE : ROW_LAST;
+
+  // 4. attention over the draft KV
+  AttnArgs t;
+  std::memset(&t, 0, sizeof(t));
+  t.q = qr; t.kc = kv->k; t.vc = kv->v; t.kv_bf16 = c.kv_dtype == MTP_BF16; t.capacity = kv->capacity;
+  t.state = kv->state; t.hq = hq; t.hkv = hkv; t.d = D; t.n_max = n_max; t.n_dev = n_dev;
+  t.row_sel = rsel; t.nchunk = L.nchunk;
+  t.part_o = reinterpret_cast<float*>(wsp(ws, L.part_o));
+  t.part_ml = reinterpret_cast<float*>(wsp(ws, L.part_ml));
+  t.o = o;
+  MTP_TRY(launch_attention(t, s));
+
+  // 5. x1 = x + W_o o
+  a = base_gemv(h, kv);
+  a.w[0] = h->w.o_proj; a.m[0] = H; a.M = H; a.K = hq * D; a.lpr = lpr_for(hq * D, h->wt);
+  a.n_max = n_max; a.n_dev = n_dev;
+  a.in_mode = IN_F32; a.x = o; a.ldx = hq * D;
+  a.out_mode = OUT_RESID; a.res = x; a.ldres = H; a.y = x1; a.ldy = H;
+  MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+
+  // 6. m = silu(W_g b) * (W_u b), b = RMSNorm(x1; w_post)
+  a = base_gemv(h, kv);
+  a.w[0] = h->w.gate_proj; a.m[0] = I; a.w[1] = h->w.up_proj; a.m[1] = I;
+  a.M = I; a.K = H; a.lpr = lpr_for(H, h->wt);
+  a.n_max = n_max; a.n_dev = n_dev;
+  a.in_mode = IN_RMS; a.x = x1; a.ldx = H; a.nw = h->w.post_attention_layernorm;
+  a.out_mode = OUT_SWIGLU; a.y = m; a.ldy = I;
+  MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+
+  // 7. g = x1 + W_d m  (also written to hidden_out in the activation dtype)
+  a = base_gemv(h, kv);
+  a.w[0] = h->w.down_proj; a.m[0] = H; a.M = H; a.K = I; a.lpr = lpr_for(I, h->wt);
+  a.n_max = n_max; a.n_dev = n_dev;
+  a.in_mode = IN_F32; a.x = m; a.ldx = I;
+  a.out_mode = OUT_RESID; a.res = x1; a.ldres = H; a.y = g; a.ldy = H;
+  a.y2 = hidden_out; a.y2_bf16 = c.act_dtype == MTP_BF16; a.ldy2 = H;
+  MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+
+  // 8. logits = W_lm RMSNorm(g; w_norm) of the last row, with its argmax
+  a = base_gemv(h, kv);
+  a.w[0] = h->w.lm_head; a.m[0] = c.vocab; a.M = c.vocab; a.K = H; a.lpr = lpr_for(H, h->lmt);
+  a.scales = static_cast<const uint16_t*>(h->w.lm_head_scales);
+  a.n_max = n_max; a.n_dev = n_dev;
+  a.in_mode = IN_RMS; a.x = g; a.ldx = H; a.nw = h->w.norm;
+  a.out_mode = OUT_LOGITS; a.logits = logits; a.amax_slot = slot(ws, kSlotLm);
+  a.counter = ctr(ws, kCtrLm); a.amax_out = argmax;
+  MTP_TRY(run_gemv(a, h->lmt, 1, ROW_LAST, s));
+  return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mtp_last_error(void) { return hipGetErrorString(g_last_hip); }
+
+const char* mtp_status_string(int status) {
+  switch (status) {
+    case MTP_OK: return "MTP_OK";
+    case MTP_E_INVALID_ARG: return "MTP_E_INVALID_ARG";
+    case MTP_E_UNSUPPORTED: return "MTP_E_UNSUPPORTED";
+    case MTP_E_NOT_BOUND: return "MTP_E_NOT_BOUND";
+    case MTP_E_CAPACITY: return "MTP_E_CAPACITY";
+    case MTP_E_HIP: return "MTP_E_HIP";
+    case MTP_E_DEVICE: return "MTP_E_DEVICE";
+    case MTP_E_WORKSPACE: return "MTP_E_WORKSPACE";
+    default: return "MTP_E_UNKNOWN";
+  }
+}
+
+int mtp_head_create(const mtp_head_config* cfg, const mtp_head_weights* w, mtp_head** out) {
+  if (!out || !w) return MTP_E_INVALID_ARG;
+  int st = validate_cfg(cfg);
+  if (st != MTP_OK) return st;
+  if (!w->embed || !w->lm_head) return MTP_E_NOT_BOUND;
+  if (cfg->lm_head_dtype == MTP_I8G128 && !w->lm_head_scales) return MTP_E_INVALID_ARG;
+  const void* req[] = {w->pre_fc_norm_embedding, w->pre_fc_norm_hidden, w->fc, w->input_layernorm,
+                       w->q_proj, w->k_proj, w->v_proj, w->q_norm, w->k_norm, w->o_proj,
+                       w->post_attention_layernorm, w->gate_proj, w->up_proj, w->down_proj, w->norm};
+  for (const void* p : req)
+    if (!p) return MTP_E_INVALID_ARG;
+  mtp_head* h = new (std::nothrow) mtp_head;
+  if (!h) return MTP_E_INVALID_ARG;
+  h->cfg = *cfg;
+  h->w = *w;
+  h->wt = cfg->weight_dtype == MTP_BF16 ? W_BF16 : W_F32;
+  h->lmt = cfg->lm_head_dtype == MTP_I8G128 ? W_I8 : (cfg->lm_head_dtype == MTP_BF16 ? W_BF16 : W_F32);
+  // every GEMV shape must split into whole 16-byte chunks per lane
+  const int H = cfg->hidden;
+  if (!lpr_for(2 * H, h->wt) || !lpr_for(H, h->wt) || !lpr_for(cfg->intermediate, h->wt) ||
+      !lpr_for(cfg->n_q_heads * cfg->head_dim, h->wt) || !lpr_for(H, h->lmt)) {
+    delete h;
+    return MTP_E_UNSUPPORTED;
+  }
+  *out = h;
+  return MTP_OK;
+}
+
+void mtp_head_destroy(mtp_head* head) { delete head; }
+
+size_t mtp_workspace_bytes(const mtp_head_config* cfg, int32_t max_rows, int32_t max_capacity) {
+  if (validate_cfg(cfg) != MTP_OK || max_rows < 1 || max_rows > MTP_MAX_FLUSH || max_capacity < 1)
+    return 0;
+  return layout(*cfg, max_rows, max_capacity).total;
+}
+
+int mtp_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || ws_bytes == 0) return MTP_E_INVALID_ARG;
+  MTP_TRY(launch_fill_zero(ws, ws_bytes, stream));
+  return MTP_OK;
+}
+
+int mtp_draft_step(const mtp_head* head, const mtp_kv* kv, const int32_t* token_dev,
+                   const void* hidden_in_dev, void* hidden_out_dev, float* logits_dev,
+                   int32_t* argmax_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!head || !token_dev || !hidden_in_dev || !hidden_out_dev || !ws) return MTP_E_INVALID_ARG;
+  if (hidden_in_dev == hidden_out_dev) return MTP_E_INVALID_ARG;
+  int st = validate_kv(head, kv);
+  if (st != MTP_OK) return st;
+  if (ws_bytes < layout(head->cfg, 1, kv->capacity).total) return MTP_E_WORKSPACE;
+  return head_forward(head, kv, token_dev, hidden_in_dev, 1, nullptr, MTP_FLUSH_LAST, 0,
+                      hidden_out_dev, logits_dev, argmax_dev, ws, stream);
+}
+
+int mtp_flush_pairs(const mtp_head* head, const mtp_kv* kv, const int32_t* tokens_dev,
+                    const void* hiddens_dev, int32_t n_max, const int32_t* n_dev, int32_t out_mode,
+                    int32_t set_round_base, void* hidden_out_dev, float* logits_last_dev,
+                    int32_t* argmax_last_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!head || !tokens_dev || !hiddens_dev || !ws) return MTP_E_INVALID_ARG;
+  if (out_mode != MTP_FLUSH_KV_ONLY && out_mode != MTP_FLUSH_LAST && out_mode != MTP_FLUSH_ALL)
+    return MTP_E_INVALID_ARG;
+  if (n_max < 1) return MTP_E_INVALID_ARG;
+  if (n_max > MTP_MAX_FLUSH) return MTP_E_CAPACITY;
+  int st = validate_kv(head, kv);
+  if (st != MTP_OK) return st;
+  if (!n_dev && n_max > kv->capacity) return MTP_E_CAPACITY;
+  if (ws_bytes < layout(head->cfg, n_max, kv->capacity).total) return MTP_E_WORKSPACE;
+  if (hidden_out_dev && hidden_out_dev == hiddens_dev) return MTP_E_INVALID_ARG;
+  return head_forward(head, kv, tokens_dev, hiddens_dev, n_max, n_dev, out_mode,
+                      set_round_base ? 1 : 0, hidden_out_dev, logits_last_dev, argmax_last_dev, ws,
+                      stream);
+}
+
+size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab) {
+  if (n_draft < 0 || n_draft > MTP_MAX_DRAFT || vocab < 1) return 0;
+  return kSyncBytes + align_up(verify_sampled_scratch_bytes(n_draft, vocab, 4096));
+}
+
+int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
+                const float* target_logits_dev, const float* draft_logits_dev,
+                const int32_t* draft_tokens_dev, int32_t* history_dev, int32_t* history_state_dev,
+                const float* uniforms_dev, int32_t* out_tokens_dev, int32_t* out_counts_dev,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!sp || !target_logits_dev || !history_dev || !history_state_dev || !out_tokens_dev ||
+      !out_counts_dev || !ws)
+    return MTP_E_INVALID_ARG;
+  if (n_draft < 0 || n_draft > MTP_MAX_DRAFT || vocab < 1) return MTP_E_INVALID_ARG;
+  if (n_draft > 0 && !draft_tokens_dev) return MTP_E_INVALID_ARG;
+  if (sp->window < 1 || sp->window > 1024) return MTP_E_INVALID_ARG;
+  if (!(sp->temperature >= 0.f) || !std::isfinite(sp->temperature)) return MTP_E_INVALID_ARG;
+  if (!(sp->repeat_penalty > 0.f) || !std::isfinite(sp->repeat_penalty)) return MTP_E_INVALID_ARG;
+  if (!(sp->top_p > 0.f) || !(sp->min_p >= 0.f) || !(sp->min_p <= 1.f) || sp->top_k < 0)
+    return MTP_E_INVALID_ARG;
+  if (ws_bytes < spec_verify_workspace_bytes(n_draft, vocab)) return MTP_E_WORKSPACE;
+  const bool greedy = sp->temperature == 0.f;
+  if (greedy != (draft_logits_dev == nullptr) && n_draft > 0) return MTP_E_INVALID_ARG;
+  if (!greedy && !uniforms_dev) return MTP_E_INVALID_ARG;
+  if (!greedy && sp->top_p < 1.f && (sp->top_k < 1 || sp->top_k > 1024)) return MTP_E_UNSUPPORTED;
+  VerifyArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_draft = n_draft; a.vocab = vocab;
+  a.temperature = sp->temperature; a.penalty = sp->repeat_penalty; a.top_p = sp->top_p;
+  a.min_p = sp->min_p; a.top_k = sp->top_k; a.window = sp->window;
+  a.ln_min_p = sp->min_p > 0.f ? static_cast<float>(std::log(static_cast<double>(sp->min_p))) : -INFINITY;
+  a.target = target_logits_dev; a.draft = draft_logits_dev; a.drafts = draft_tokens_dev;
+  a.ring = history_dev; a.ring_state = history_state_dev; a.uniforms = uniforms_dev;
+  a.out_tokens = out_tokens_dev; a.out_counts = out_counts_dev;
+  a.slots = slot(ws, 0); a.counter = ctr(ws, kCtrVerify);
+  a.scratch = wsp(ws, kSyncBytes);
+  a.chunk = 4096;
+  const hipError_t e = greedy ? launch_verify_greedy(a, stream) : launch_verify_sampled(a, stream);
+  if (e == hipErrorNotSupported) return MTP_E_UNSUPPORTED;
+  MTP_TRY(e);
+  return MTP_OK;
+}
+
+int kv_rollback(const mtp_kv* kv, int32_t to_len, const int32_t* n_accepted_dev, int32_t n_draft,
+                hipStream_t stream) {
+  if (!kv || !kv->state || kv->capacity <= 0) return MTP_E_INVALID_ARG;
+  if (to_len < MTP_TO_ROUND_BASE) return MTP_E_INVALID_ARG;
+  if (to_len > kv->capacity) return MTP_E_CAPACITY;
+  if (n_draft < 0 || n_draft > MTP_MAX_DRAFT) return MTP_E_INVALID_ARG;
+  if (n_accepted_dev && to_len != MTP_TO_ROUND_BASE) return MTP_E_INVALID_ARG;
+  MTP_TRY(launch_rollback(kv->state, to_len, n_accepted_dev, n_draft, kv->capacity, stream));
+  return MTP_OK;
+}
+
+}  // extern "C"

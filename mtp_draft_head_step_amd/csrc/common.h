@@ -1,0 +1,85 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, wave64
+// reductions, orderable argmax keys, the grid-completion ticket.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+constexpr int kWave = 64;
+constexpr int MTP_MAX_DRAFT_DEV = 16;  // drafts per verify (host bound in the ABI)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Round to nearest, ties to even (NaN -> quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, kWave); }
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Monotone map float -> uint32 (larger float, larger key); -0 is folded into +0.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Argmax key: maximum value first, then the LOWEST index.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
+  return (static_cast<unsigned long long>(ord_key(v)) << 32) | (0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ int argmax_index(unsigned long long key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
+  uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
+  uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long w = shfl_xor_u64(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Grid-completion ticket: every workgroup calls this once after its last
+// global write; exactly one workgroup (the last to arrive) gets true, and the
+// counter is re-armed to zero by that workgroup.  Call from all threads.
+__device__ __forceinline__ bool last_block_ticket(unsigned int* counter, unsigned int nblocks) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned int prev = atomicAdd(counter, 1u);
+    s_last = (prev == nblocks - 1) ? 1 : 0;
+    if (s_last) {
+      __threadfence();
+      atomicExch(counter, 0u);
+    }
+  }
+  __syncthreads();
+  return s_last != 0;
+}
+
+__device__ __forceinline__ unsigned long long atomic_read_u64(unsigned long long* p) {
+  return atomicAdd(p, 0ull);
+}
+
+}  // namespace mtp

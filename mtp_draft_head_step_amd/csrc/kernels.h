@@ -1,0 +1,132 @@
+// Host-visible launch interfaces of the gfx950 kernels (C++ linkage, used by
+// the C ABI in api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+enum WType { W_F32 = 0, W_BF16 = 1, W_I8 = 2 };
+enum InMode { IN_F32 = 0, IN_RMS = 1, IN_EMBED = 2 };
+enum OutMode { OUT_F32 = 0, OUT_RESID = 1, OUT_SWIGLU = 2, OUT_LOGITS = 3 };
+enum RowSel { ROWS_RANGE = 0, ROW_LAST = 1 };
+
+// y[j, r] = sum_k W[r, k] * in(j)[k] for activation rows j, weight rows r.
+struct GemvArgs {
+  const void* w[3];        // up to three stacked matrices (rows concatenated)
+  int m[3];                // rows of each
+  int M;                   // output rows (SWIGLU: rows of one of the pair)
+  int K;                   // columns
+  const uint16_t* scales;  // W_I8: fp16 scales [M, K/128]
+  int lpr;                 // lanes per weight row (8..64, divides K/elements-per-16B)
+  int kp;                  // columns staged in LDS per phase
+  int grid_stride;         // single phase: workgroups loop over row blocks
+  // activation rows: j in [row_base, row_base + NR) and j < n, or j = n - 1
+  int row_sel;
+  int row_base;
+  int n_max;
+  const int32_t* n_dev;    // nullable device count
+  // input
+  int in_mode;
+  const float* x;
+  int ldx;
+  const void* nw;          // IN_RMS norm weight / IN_EMBED embedding-half norm
+  const void* nw2;         // IN_EMBED hidden-half norm
+  int nw_bf16;
+  float eps;
+  const int32_t* tok;      // IN_EMBED
+  const void* embed;
+  int embed_bf16;
+  const void* hid;
+  int hid_bf16;
+  int ld_hid;
+  // output
+  int out_mode;
+  float* y;
+  int ldy;
+  const float* res;
+  int ldres;
+  void* y2;                // optional copy in act dtype (ROW_LAST: written at row 0)
+  int y2_bf16;
+  int ldy2;
+  float* logits;           // OUT_LOGITS (nullable)
+  unsigned long long* amax_slot;
+  unsigned int* counter;
+  int32_t* amax_out;       // nullable
+  const int32_t* kv_state; // nullable: skip everything when state[3] != 0
+};
+
+hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s);
+
+// q/k RMSNorm + RoPE for rows j < n at positions state[0] + j, append k, v to
+// the cache, write roped q to `q_out`; the last workgroup advances state[0]
+// (and state[1] if set_base).
+struct RopeArgs {
+  const float* qkv;        // [rows, (Hq + 2 Hkv) * D]
+  int ld_qkv;
+  float* q_out;            // [rows, Hq * D]
+  const void* q_norm;
+  const void* k_norm;
+  int nw_bf16;
+  float eps;
+  float theta;
+  int hq, hkv, d;
+  void* kc;
+  void* vc;
+  int kv_bf16;
+  int capacity;
+  int32_t* state;
+  int n_max;
+  const int32_t* n_dev;
+  int set_base;
+  unsigned int* counter;
+};
+hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);
+
+// Split-K attention of query rows over the draft KV, then a merge.
+struct AttnArgs {
+  const float* q;          // [rows, Hq * D] roped
+  const void* kc;
+  const void* vc;
+  int kv_bf16;
+  int capacity;
+  const int32_t* state;
+  int hq, hkv, d;
+  int n_max;
+  const int32_t* n_dev;
+  int row_sel;             // ROWS_RANGE: rows 0..n-1; ROW_LAST: row n-1
+  int nchunk;              // chunks per (row, kv head)
+  float* part_o;           // [rows, Hq, nchunk, D]
+  float* part_ml;          // [rows, Hq, nchunk, 2]
+  float* o;                // [rows, Hq * D]
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// Greedy verification (argmax match) with repetition penalty.
+struct VerifyArgs {
+  int n_draft, vocab;
+  float temperature, penalty, top_p, min_p;
+  int top_k, window;
+  float ln_min_p;
+  const float* target;
+  const float* draft;
+  const int32_t* drafts;
+  int32_t* ring;
+  int32_t* ring_state;
+  const float* uniforms;
+  int32_t* out_tokens;
+  int32_t* out_counts;
+  unsigned long long* slots;   // [n_draft + 1]
+  unsigned int* counter;
+  void* scratch;               // sampled path candidates
+  int chunk;                   // elements per workgroup
+};
+hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s);
+size_t verify_sampled_scratch_bytes(int n_draft, int vocab, int chunk);
+
+hipError_t launch_rollback(int32_t* state, int to_len, const int32_t* n_acc, int n_draft,
+                           int capacity, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace mtp

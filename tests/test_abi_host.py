@@ -1,0 +1,126 @@
+"""The C ABI on the host: libmtp.so loads, exports every function include/mtp.h
+declares, and rejects bad arguments before anything is enqueued (these calls
+return before any HIP call, so they run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from mtp_draft_head_step_amd import abi
+from mtp_draft_head_step_amd import inputs as I
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mtp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(abi.EXPORTS), names
+    lib = C.CDLL(abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert abi.mtp_status_string(0) == "MTP_OK"
+    assert abi.mtp_status_string(-3) == "MTP_E_NOT_BOUND"
+    assert abi.mtp_status_string(-99) == "MTP_E_UNKNOWN"
+
+
+def fake_weights(shape, missing=()):
+    w = abi.mtp_head_weights()
+    for i, n in enumerate(abi.WEIGHT_FIELDS):
+        if n not in missing:
+            setattr(w, n, 0x10000 + 0x100 * i)      # never dereferenced on the host
+    return w
+
+
+def create(shape, w):
+    h = C.c_void_p()
+    st = abi.lib.mtp_head_create(C.byref(abi.config_of(shape)), C.byref(w), C.byref(h))
+    if st == 0:
+        abi.lib.mtp_head_destroy(h)
+    return st
+
+
+def test_create_validates():
+    s = I.TINY_F32
+    assert create(s, fake_weights(s, missing=("lm_head_scales",))) == abi.MTP_OK
+    assert create(s, fake_weights(s, missing=("embed",))) == abi.MTP_E_NOT_BOUND      # not bound
+    assert create(s, fake_weights(s, missing=("lm_head",))) == abi.MTP_E_NOT_BOUND
+    assert create(s, fake_weights(s, missing=("k_norm",))) == abi.MTP_E_INVALID_ARG
+    assert create(s.with_dtypes(head_dim=96), fake_weights(s)) == abi.MTP_E_UNSUPPORTED
+    assert create(s.with_dtypes(n_q_heads=5), fake_weights(s)) == abi.MTP_E_UNSUPPORTED
+    assert create(s.with_dtypes(n_q_heads=20, n_kv_heads=2), fake_weights(s)) == abi.MTP_E_UNSUPPORTED
+    assert create(s.with_dtypes(hidden=200), fake_weights(s)) == abi.MTP_E_UNSUPPORTED
+    assert create(s.with_dtypes(rms_eps=-1.0), fake_weights(s)) == abi.MTP_E_INVALID_ARG
+    q = s.with_dtypes(lm_head_dtype="i8g128")
+    assert create(q, fake_weights(q, missing=("lm_head_scales",))) == abi.MTP_E_INVALID_ARG
+    assert create(q, fake_weights(q)) == abi.MTP_OK
+    assert create(I.QWEN35_27B, fake_weights(I.QWEN35_27B)) == abi.MTP_OK
+
+
+def test_workspace_sizes():
+    cfg = abi.config_of(I.QWEN35_27B)
+    a = abi.mtp_workspace_bytes(cfg, 1, 4608)
+    b = abi.mtp_workspace_bytes(cfg, 3, 4608)
+    assert 0 < a < b
+    assert abi.mtp_workspace_bytes(cfg, 0, 4608) == 0
+    assert abi.mtp_workspace_bytes(cfg, 257, 4608) == 0
+    assert abi.spec_verify_workspace_bytes(4, 152064) > 0
+    assert abi.spec_verify_workspace_bytes(17, 152064) == 0
+
+
+def test_rollback_and_flush_fail_closed():
+    kv = abi.mtp_kv(0x1000, 0x2000, 128, 0x3000)
+    st = abi.lib.kv_rollback(C.byref(kv), 129, None, 2, None)
+    assert st == abi.MTP_E_CAPACITY
+    assert abi.lib.kv_rollback(C.byref(kv), -2, None, 2, None) == abi.MTP_E_INVALID_ARG
+    assert abi.lib.kv_rollback(C.byref(kv), 5, 0x4000, 2, None) == abi.MTP_E_INVALID_ARG
+    assert abi.lib.kv_rollback(C.byref(kv), -1, None, 17, None) == abi.MTP_E_INVALID_ARG
+    bad = abi.mtp_kv(0, 0x2000, 128, 0x3000)
+
+    s = I.TINY_F32
+    h = C.c_void_p()
+    assert abi.lib.mtp_head_create(C.byref(abi.config_of(s)), C.byref(fake_weights(s)), C.byref(h)) == 0
+    try:
+        ws = 1 << 40
+        f = abi.lib.mtp_flush_pairs
+        assert f(h, C.byref(kv), 0x10, 0x20, 257, None, 1, 0, 0x30, None, None, 0x40, ws, None) == abi.MTP_E_CAPACITY
+        assert f(h, C.byref(kv), 0x10, 0x20, 0, None, 1, 0, 0x30, None, None, 0x40, ws, None) == abi.MTP_E_INVALID_ARG
+        assert f(h, C.byref(kv), 0x10, 0x20, 4, None, 7, 0, 0x30, None, None, 0x40, ws, None) == abi.MTP_E_INVALID_ARG
+        assert f(h, C.byref(kv), 0x10, 0x20, 4, None, 1, 0, 0x30, None, None, 0x40, 16, None) == abi.MTP_E_WORKSPACE
+        assert f(h, C.byref(bad), 0x10, 0x20, 4, None, 1, 0, 0x30, None, None, 0x40, ws, None) == abi.MTP_E_INVALID_ARG
+        small = abi.mtp_kv(0x1000, 0x2000, 3, 0x3000)
+        assert f(h, C.byref(small), 0x10, 0x20, 4, None, 1, 0, 0x30, None, None, 0x40, ws, None) == abi.MTP_E_CAPACITY
+        d = abi.lib.mtp_draft_step
+        assert d(h, C.byref(kv), None, 0x20, 0x30, None, None, 0x40, ws, None) == abi.MTP_E_INVALID_ARG
+        assert d(h, C.byref(kv), 0x10, 0x20, 0x20, None, None, 0x40, ws, None) == abi.MTP_E_INVALID_ARG
+        assert d(h, C.byref(kv), 0x10, 0x20, 0x30, None, None, 0x40, 8, None) == abi.MTP_E_WORKSPACE
+    finally:
+        abi.lib.mtp_head_destroy(h)
+
+
+def test_verify_fails_closed():
+    v = abi.lib.spec_verify
+    ws = 1 << 30
+    greedy = abi.sampling()
+    sampled = abi.sampling(0.7, 1.1, 40, 0.9, 0.05, 64)
+    args = dict(t=0x10, d=0x20, dt=0x30, h=0x40, hs=0x50, u=0x60, ot=0x70, oc=0x80, ws=0x90)
+    def call(sp, n, vocab, draft=0x20, u=0x60, wsb=ws):
+        return v(C.byref(sp), n, vocab, 0x10, draft, 0x30, 0x40, 0x50, u, 0x70, 0x80, 0x90, wsb, None)
+    assert call(greedy, 17, 100, draft=None) == abi.MTP_E_INVALID_ARG
+    assert call(greedy, 2, 100, draft=0x20) == abi.MTP_E_INVALID_ARG     # greedy takes no draft rows
+    assert call(sampled, 2, 100, draft=None) == abi.MTP_E_INVALID_ARG    # sampled needs them
+    assert call(sampled, 2, 100, u=None) == abi.MTP_E_INVALID_ARG
+    assert call(greedy, 2, 100, draft=None, wsb=8) == abi.MTP_E_WORKSPACE
+    nucleus_all = abi.sampling(0.7, 1.0, 0, 0.9, 0.0, 64)
+    assert call(nucleus_all, 2, 100) == abi.MTP_E_UNSUPPORTED
+    bad_win = abi.sampling(window=0)
+    assert call(bad_win, 2, 100, draft=None) == abi.MTP_E_INVALID_ARG

@@ -1,0 +1,187 @@
+"""GPU parity of the draft-head step and the pending-pair flush against the
+oracle, through the C ABI (tiny fp32 head, tiny bf16 head)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mtp_draft_head_step_amd import inputs as I
+from oracle import head as OH
+from tests.gpu_util import argmax_ok, build, device_array, host, kv_pair, rel_err, tol_of
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {"tiny_f32": I.TINY_F32, "tiny_bf16": I.TINY_BF16}
+
+
+def act_dtype(shape):
+    return torch.bfloat16 if shape.act_dtype == I.BF16 else torch.float32
+
+
+def check_kv(gkv, okv, shape, lo, hi, tol):
+    k = host(gkv.k)[:, lo:hi]
+    v = host(gkv.v)[:, lo:hi]
+    assert rel_err(k, okv.K[:, lo:hi]) <= tol
+    assert rel_err(v, okv.V[:, lo:hi]) <= tol
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("prefix", [0, 1, 100, 1000])
+def test_step_parity(name, prefix):
+    from mtp_draft_head_step_amd import abi
+    shape = SHAPES[name]
+    tol = tol_of(shape)
+    wl = 40 + prefix
+    _, gh, oh = build(shape, wl)
+    cap = 1536
+    gkv, okv = kv_pair(shape, wl, prefix, cap)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, 1, cap))
+    tok = int(I.tokens_uniform(wl, 0, 1, shape.vocab)[0])
+    hid = I.target_hiddens(shape, wl, 0, 1)
+    t_tok = torch.tensor([tok], dtype=torch.int32, device="cuda")
+    t_hid = device_array(hid)
+    hout = torch.empty(shape.hidden, dtype=act_dtype(shape), device="cuda")
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    abi.mtp_draft_step(gh, gkv, t_tok, t_hid, hout, logits, amax, ws)
+    torch.cuda.synchronize()
+    ref = oh.step(okv, tok, I.decode(hid[0], shape.act_dtype))
+    lg = host(logits)
+    assert rel_err(lg, ref["logits"]) <= tol, rel_err(lg, ref["logits"])
+    assert rel_err(host(hout), ref["g"][0]) <= tol
+    ok, _ = argmax_ok(int(host(amax)[0]), ref["logits"], lg)
+    assert ok
+    assert int(host(amax)[0]) == int(np.argmax(lg))          # the fused argmax of its own logits
+    st = host(gkv.state)
+    assert st[0] == prefix + 1 and st[3] == 0
+    check_kv(gkv, okv, shape, 0, prefix + 1, tol)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_chained_steps(name):
+    """Three chained steps: each feeds its own argmax and hidden output (on the
+    device, no host round trip); the oracle runs the same chain from its values."""
+    from mtp_draft_head_step_amd import abi
+    shape = SHAPES[name]
+    tol = tol_of(shape)
+    wl = 60
+    _, gh, oh = build(shape, wl)
+    cap = 512
+    gkv, okv = kv_pair(shape, wl, 200, cap)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, 1, cap))
+    tok = torch.tensor([5], dtype=torch.int32, device="cuda")
+    hid = I.target_hiddens(shape, wl, 0, 1)
+    h_in = device_array(hid)[0]
+    toks = [torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(3)]
+    hs = [torch.empty(shape.hidden, dtype=act_dtype(shape), device="cuda") for _ in range(3)]
+    lgs = [torch.empty(shape.vocab, dtype=torch.float32, device="cuda") for _ in range(3)]
+    cur_t, cur_h = tok, h_in
+    for i in range(3):
+        abi.mtp_draft_step(gh, gkv, cur_t, cur_h, hs[i], lgs[i], toks[i], ws)
+        cur_t, cur_h = toks[i], hs[i]
+    torch.cuda.synchronize()
+    o_t, o_h = 5, I.decode(hid[0], shape.act_dtype)
+    for i in range(3):
+        ref = oh.step(okv, o_t, o_h)
+        lg = host(lgs[i])
+        assert rel_err(lg, ref["logits"]) <= tol * (i + 1)
+        ok, near = argmax_ok(int(host(toks[i])[0]), ref["logits"], lg)
+        assert ok
+        if near:
+            break                      # the chains legitimately diverge after a near tie
+        o_t, o_h = ref["argmax"], ref["g"][0]
+    assert host(gkv.state)[0] == 203
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("mode", [OH.KV_ONLY, OH.LAST, OH.ALL])
+@pytest.mark.parametrize("n, n_max, use_dev", [(5, 5, False), (3, 8, True), (37, 40, True), (1, 1, False)])
+def test_flush_parity(name, mode, n, n_max, use_dev):
+    """Flush of n pairs (device count n <= host bound n_max when use_dev) in each
+    output mode; more than 16 rows spans several row blocks of the GEMVs."""
+    from mtp_draft_head_step_amd import abi
+    shape = SHAPES[name]
+    tol = tol_of(shape)
+    wl = 70 + n
+    _, gh, oh = build(shape, wl)
+    cap = 1024
+    prefix = 300
+    gkv, okv = kv_pair(shape, wl, prefix, cap)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, n_max, cap))
+    toks = I.tokens_uniform(wl, 1, n_max, shape.vocab)
+    hids = I.target_hiddens(shape, wl, 1, n_max)
+    hout = torch.zeros((n_max if mode == OH.ALL else 1, shape.hidden), dtype=act_dtype(shape), device="cuda")
+    logits = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    n_dev = torch.tensor([n], dtype=torch.int32, device="cuda") if use_dev else None
+    abi.mtp_flush_pairs(gh, gkv, device_array(toks), device_array(hids), n_max if use_dev else n,
+                        n_dev, mode, 1, hout, logits, amax, ws)
+    torch.cuda.synchronize()
+    ref = oh.flush(okv, [int(t) for t in toks[:n]], [I.decode(h, shape.act_dtype) for h in hids[:n]],
+                   mode, set_round_base=True)
+    st = host(gkv.state)
+    assert st[0] == prefix + n and st[1] == prefix + n and st[3] == 0
+    check_kv(gkv, okv, shape, prefix, prefix + n, tol)
+    if mode == OH.KV_ONLY:
+        assert np.all(host(logits) == 0) and int(host(amax)[0]) == -1
+        return
+    lg = host(logits)
+    assert rel_err(lg, ref["logits"]) <= tol
+    assert argmax_ok(int(host(amax)[0]), ref["logits"], lg)[0]
+    g = host(hout)
+    if mode == OH.ALL:
+        for j in range(n):
+            assert rel_err(g[j], ref["g"][j]) <= tol
+        if n < n_max:
+            assert np.all(g[n:] == 0)                 # rows beyond the device count untouched
+    else:
+        assert rel_err(g[0], ref["g"][0]) <= tol
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_flush_equals_chain_on_gpu(name):
+    """Block = chain (the pages' chain-parity contract) on the GPU: a 4-pair flush
+    leaves the same K/V and last-row output as 4 steps, within the tolerance."""
+    from mtp_draft_head_step_amd import abi
+    shape = SHAPES[name]
+    tol = tol_of(shape)
+    _, gh, _ = build(shape, 80)
+    cap = 256
+    kv1, _ = kv_pair(shape, 80, 50, cap)
+    kv2, _ = kv_pair(shape, 80, 50, cap)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, 4, cap))
+    toks = device_array(I.tokens_uniform(80, 2, 4, shape.vocab))
+    hids = device_array(I.target_hiddens(shape, 80, 2, 4))
+    h1 = torch.empty((1, shape.hidden), dtype=act_dtype(shape), device="cuda")
+    l1 = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    abi.mtp_flush_pairs(gh, kv1, toks, hids, 4, None, OH.LAST, 0, h1, l1, None, ws)
+    h2 = torch.empty(shape.hidden, dtype=act_dtype(shape), device="cuda")
+    l2 = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    for j in range(4):
+        abi.mtp_draft_step(gh, kv2, toks[j:j + 1], hids[j], h2, l2, None, ws)
+    torch.cuda.synchronize()
+    assert rel_err(host(l1), host(l2)) <= tol
+    assert rel_err(host(kv1.k)[:, 50:54], host(kv2.k)[:, 50:54]) <= tol
+
+
+def test_capacity_and_count_errors_are_sticky():
+    from mtp_draft_head_step_amd import abi
+    shape = I.TINY_F32
+    _, gh, _ = build(shape, 81)
+    gkv, _ = kv_pair(shape, 81, 6, 8)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, 4, 8))
+    toks = device_array(I.tokens_uniform(81, 3, 4, shape.vocab))
+    hids = device_array(I.target_hiddens(shape, 81, 3, 4))
+    hout = torch.empty((1, shape.hidden), dtype=torch.float32, device="cuda")
+    n_bad = torch.tensor([5], dtype=torch.int32, device="cuda")          # above n_max = 4
+    abi.mtp_flush_pairs(gh, gkv, toks, hids, 4, n_bad, OH.LAST, 0, hout, None, None, ws)
+    torch.cuda.synchronize()
+    assert host(gkv.state).tolist() == [6, 6, 0, abi.DEV_COUNT]
+    gkv.state.copy_(torch.tensor([6, 6, 0, 0], dtype=torch.int32))
+    abi.mtp_flush_pairs(gh, gkv, toks, hids, 4, None, OH.LAST, 0, hout, None, None, ws)   # 6 + 4 > 8
+    torch.cuda.synchronize()
+    assert host(gkv.state).tolist() == [6, 6, 0, abi.DEV_CAPACITY]
+    abi.mtp_draft_step(gh, gkv, toks[:1], hids[0], hout[0], None, None, ws)           # no-op now
+    abi.kv_rollback(gkv, 2)
+    torch.cuda.synchronize()
+    assert host(gkv.state).tolist() == [6, 6, 0, abi.DEV_CAPACITY]
