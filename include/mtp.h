@@ -89,8 +89,9 @@ typedef struct mtp_head mtp_head;
 
 /* The head's own draft KV cache (separate from the target's; only the position
  * offset is shared: "Upstream contract to port").  k, v: [n_kv_heads, capacity,
- * head_dim] in kv_dtype.  state: device int32[4] = {len, round_base, reserved,
- * err}; slot S holds the pair (token S+1, target hidden S) at RoPE position S. */
+ * head_dim] in kv_dtype, capacity <= 2^20.  state: device int32[4] = {len,
+ * round_base, reserved, err}; slot S holds the pair (token S+1, target hidden S)
+ * at RoPE position S. */
 typedef struct {
   void *k, *v;
   int32_t capacity;
@@ -190,6 +191,18 @@ int spec_verify(const spec_sampling *sp, int32_t n_draft, int32_t vocab,
  * state[3] = MTP_DEV_ROLLBACK.  to_len > capacity is rejected on the host. */
 int kv_rollback(const mtp_kv *kv, int32_t to_len, const int32_t *n_accepted_dev,
                 int32_t n_draft, hipStream_t stream);
+
+/* Benchmark timing of the unembedding (lm_head GEMV) kernel: after
+ * mtp_timing_begin(n) the next n unembedding launches (any stream, eager or
+ * being captured into a graph) are each bracketed by a pair of HIP events
+ * recorded on their stream, in slots 0, 1, 2, ...  mtp_timing_elapsed waits for
+ * slots [first, first + count) and returns their summed kernel time (ms); a
+ * captured slot holds the timing of the graph's latest replay.  mtp_timing_end
+ * returns the sum over all used slots and their count, then releases the
+ * events.  Host-side state, process-wide. */
+int mtp_timing_begin(int32_t max_launches);
+int mtp_timing_elapsed(int32_t first, int32_t count, float *total_ms);
+int mtp_timing_end(float *total_ms, int32_t *launches);
 
 #ifdef __cplusplus
 }

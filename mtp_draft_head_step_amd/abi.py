@@ -32,7 +32,8 @@ WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
 
 EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_destroy", "mtp_workspace_bytes",
            "mtp_workspace_init", "mtp_draft_step", "mtp_flush_pairs",
-           "spec_verify_workspace_bytes", "spec_verify", "kv_rollback")
+           "spec_verify_workspace_bytes", "spec_verify", "kv_rollback", "mtp_timing_begin",
+           "mtp_timing_elapsed", "mtp_timing_end")
 
 
 class mtp_head_config(C.Structure):
@@ -86,6 +87,12 @@ def _load():
     lib.spec_verify.argtypes = [C.POINTER(spec_sampling), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kv_rollback.restype = C.c_int
     lib.kv_rollback.argtypes = [C.POINTER(mtp_kv), i32, vp, i32, vp]
+    lib.mtp_timing_begin.restype = C.c_int
+    lib.mtp_timing_begin.argtypes = [i32]
+    lib.mtp_timing_elapsed.restype = C.c_int
+    lib.mtp_timing_elapsed.argtypes = [i32, i32, C.POINTER(C.c_float)]
+    lib.mtp_timing_end.restype = C.c_int
+    lib.mtp_timing_end.argtypes = [C.POINTER(C.c_float), C.POINTER(i32)]
     return lib
 
 
@@ -181,6 +188,24 @@ def spec_verify(sp: spec_sampling, n_draft, vocab, target_logits, draft_logits, 
 def kv_rollback(kv, to_len, n_accepted=None, n_draft=0, stream=None):
     st = lib.kv_rollback(C.byref(kv.desc), int(to_len), _ptr(n_accepted), int(n_draft), _stream(stream))
     _check(st, "kv_rollback")
+
+
+def mtp_timing_begin(max_launches: int):
+    _check(lib.mtp_timing_begin(int(max_launches)), "mtp_timing_begin")
+
+
+def mtp_timing_elapsed(first: int, count: int) -> float:
+    ms = C.c_float()
+    _check(lib.mtp_timing_elapsed(int(first), int(count), C.byref(ms)), "mtp_timing_elapsed")
+    return ms.value
+
+
+def mtp_timing_end():
+    """-> (summed unembedding kernel milliseconds, launches timed)."""
+    ms = C.c_float()
+    n = C.c_int32()
+    _check(lib.mtp_timing_end(C.byref(ms), C.byref(n)), "mtp_timing_end")
+    return ms.value, n.value
 
 
 # ----------------------------------------------------------------------------

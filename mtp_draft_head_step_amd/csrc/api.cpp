@@ -3,7 +3,9 @@
 // pending-pair flush, verification and rollback.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/mtp.h"
 #include "kernels.h"
@@ -12,6 +14,26 @@ using namespace mtp;
 
 namespace {
 thread_local hipError_t g_last_hip = hipSuccess;
+
+// Event pairs bracketing unembedding launches while timing is on (benchmarks).
+struct UnembedTimer {
+  std::mutex mu;
+  std::vector<hipEvent_t> start, stop;
+  int used = 0;
+  bool on = false;
+} g_timer;
+
+void timer_mark(bool before, hipStream_t s, int& slot_index) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.on) { slot_index = -1; return; }
+  if (before) {
+    if (g_timer.used >= static_cast<int>(g_timer.start.size())) { slot_index = -1; return; }
+    slot_index = g_timer.used++;
+    hipEventRecord(g_timer.start[slot_index], s);
+  } else if (slot_index >= 0) {
+    hipEventRecord(g_timer.stop[slot_index], s);
+  }
+}
 }  // namespace
 
 #define MTP_TRY(expr)                  \
@@ -33,10 +55,8 @@ struct mtp_head {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kSyncBytes = 4096;  // counters and argmax slots, fixed at offset 0
-// sync area: u32 counters at byte 0, u64 slots at byte 1024
-constexpr int kCtrLm = 0, kCtrRope = 1, kCtrVerify = 2;
-constexpr int kSlotLm = 0;
+constexpr size_t kHeadBytes = 256;   // reserved at offset 0
+constexpr int kVerifyChunk = 4096;   // logits per verify workgroup
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -50,37 +70,40 @@ int lpr_for(int K, int t) {
 }
 
 int nr_for(int rows) {
-  int nr = 1;
-  while (nr < rows && nr < 16) nr <<= 1;
-  return nr;
+  if (rows <= 4) return rows < 1 ? 1 : rows;
+  return rows <= 8 ? 8 : 16;
 }
 
 int kp_for(int K, int t, int nr) {
-  const int budget = 16384 / nr;  // 64 KB of fp32 in LDS
+  const int budget = 32768 / nr;  // 128 KB of fp32 in LDS
   if (K <= budget) return K;
   const int q = lpr_for(K, t) * epc_of(t);
   int kp = budget / q * q;
   return kp > 0 ? kp : q;
 }
 
+// Key chunks per (row, kv head): about 256 attention workgroups per query row,
+// at least 32 keys per chunk.
 int nchunk_for(const mtp_head_config& c, int capacity) {
-  const int min_chunks = (capacity + 479) / 480;
-  int target = (512 + c.n_kv_heads - 1) / c.n_kv_heads;
-  const int fine = (capacity + 15) / 16;
+  int target = (256 + c.n_kv_heads - 1) / c.n_kv_heads;
+  const int fine = (capacity + 31) / 32;
   if (target > fine) target = fine;
-  return target > min_chunks ? target : min_chunks;
+  return target < 1 ? 1 : target;
 }
 
 struct Layout {
-  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, total;
+  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, total;
   int nchunk;
 };
+
+// upper bound on the unembedding GEMV's workgroup count (one argmax key each)
+size_t amax_parts(const mtp_head_config& c) { return static_cast<size_t>(c.vocab) / 4 + 2048; }
 
 Layout layout(const mtp_head_config& c, int rows, int capacity) {
   Layout L{};
   const size_t H = c.hidden, D = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, I = c.intermediate;
   L.nchunk = nchunk_for(c, capacity);
-  size_t off = kSyncBytes;
+  size_t off = kHeadBytes;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   L.x = take(rows * H * 4);
   L.qkv = take(rows * (hq + 2 * hkv) * D * 4);
@@ -91,6 +114,7 @@ Layout layout(const mtp_head_config& c, int rows, int capacity) {
   L.x1 = take(rows * H * 4);
   L.m = take(rows * I * 4);
   L.g = take(rows * H * 4);
+  L.amax = take(amax_parts(c) * 8);
   L.total = off;
   return L;
 }
@@ -120,15 +144,12 @@ int validate_cfg(const mtp_head_config* c) {
 
 int validate_kv(const mtp_head* h, const mtp_kv* kv) {
   if (!kv || !kv->k || !kv->v || !kv->state || kv->capacity <= 0) return MTP_E_INVALID_ARG;
+  if (kv->capacity > (1 << 20)) return MTP_E_UNSUPPORTED;
   (void)h;
   return MTP_OK;
 }
 
 inline char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
-inline unsigned int* ctr(void* ws, int i) { return reinterpret_cast<unsigned int*>(ws) + i; }
-inline unsigned long long* slot(void* ws, int i) {
-  return reinterpret_cast<unsigned long long*>(wsp(ws, 1024)) + i;
-}
 
 GemvArgs base_gemv(const mtp_head* h, const mtp_kv* kv) {
   GemvArgs a;
@@ -139,14 +160,15 @@ GemvArgs base_gemv(const mtp_head* h, const mtp_kv* kv) {
   return a;
 }
 
-hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t s) {
+hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t s,
+                    int* grid_out = nullptr) {
   // ROWS_RANGE: blocks of up to 16 activation rows share one pass over the weights
   a.row_sel = row_sel;
   if (row_sel == ROW_LAST) {
     a.row_base = 0;
     a.kp = kp_for(a.K, wt, 1);
     a.grid_stride = a.kp == a.K;
-    return launch_gemv(a, wt, 1, s);
+    return launch_gemv(a, wt, 1, s, grid_out);
   }
   const int nr = nr_for(rows_total);
   a.kp = kp_for(a.K, wt, nr);
@@ -203,10 +225,15 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   r.q_norm = h->w.q_norm; r.k_norm = h->w.k_norm; r.nw_bf16 = h->wt == W_BF16;
   r.eps = c.rms_eps; r.theta = c.rope_theta; r.hq = hq; r.hkv = hkv; r.d = D;
   r.kc = kv->k; r.vc = kv->v; r.kv_bf16 = c.kv_dtype == MTP_BF16; r.capacity = kv->capacity;
-  r.state = kv->state; r.n_max = n_max; r.n_dev = n_dev; r.set_base = set_base;
-  r.counter = ctr(ws, kCtrRope);
+  r.state = kv->state; r.n_max = n_max; r.n_dev = n_dev;
   MTP_TRY(launch_rope_append(r, s));
-  if (mode == MTP_FLUSH_KV_ONLY) return MTP_OK;
+  FinishArgs f;
+  std::memset(&f, 0, sizeof(f));
+  f.state = kv->state; f.n_max = n_max; f.n_dev = n_dev; f.set_base = set_base;
+  if (mode == MTP_FLUSH_KV_ONLY) {
+    MTP_TRY(launch_finish(f, s));
+    return MTP_OK;
+  }
 
   const int rsel = (mode == MTP_FLUSH_ALL) ? ROWS_RANGE : ROW_LAST;
 
@@ -253,9 +280,16 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.scales = static_cast<const uint16_t*>(h->w.lm_head_scales);
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_RMS; a.x = g; a.ldx = H; a.nw = h->w.norm;
-  a.out_mode = OUT_LOGITS; a.logits = logits; a.amax_slot = slot(ws, kSlotLm);
-  a.counter = ctr(ws, kCtrLm); a.amax_out = argmax;
-  MTP_TRY(run_gemv(a, h->lmt, 1, ROW_LAST, s));
+  a.out_mode = OUT_LOGITS; a.logits = logits;
+  a.amax_part = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax));
+  int tslot = -1, grid = 0;
+  timer_mark(true, s, tslot);
+  MTP_TRY(run_gemv(a, h->lmt, 1, ROW_LAST, s, &grid));
+  timer_mark(false, s, tslot);
+  if (static_cast<size_t>(grid) > amax_parts(c)) return MTP_E_UNSUPPORTED;   // cannot happen: sized above
+  // 9. argmax of the partial keys, commit the append (len, round base)
+  f.parts = a.amax_part; f.nparts = grid; f.amax_out = argmax;
+  MTP_TRY(launch_finish(f, s));
   return MTP_OK;
 }
 
@@ -354,7 +388,9 @@ int mtp_flush_pairs(const mtp_head* head, const mtp_kv* kv, const int32_t* token
 
 size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab) {
   if (n_draft < 0 || n_draft > MTP_MAX_DRAFT || vocab < 1) return 0;
-  return kSyncBytes + align_up(verify_sampled_scratch_bytes(n_draft, vocab, 4096));
+  const size_t nb = (static_cast<size_t>(vocab) + kVerifyChunk - 1) / kVerifyChunk;
+  return kHeadBytes + align_up((n_draft + 1) * nb * 8) +
+         align_up(verify_sampled_scratch_bytes(n_draft, vocab, kVerifyChunk));
 }
 
 int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
@@ -386,12 +422,69 @@ int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
   a.target = target_logits_dev; a.draft = draft_logits_dev; a.drafts = draft_tokens_dev;
   a.ring = history_dev; a.ring_state = history_state_dev; a.uniforms = uniforms_dev;
   a.out_tokens = out_tokens_dev; a.out_counts = out_counts_dev;
-  a.slots = slot(ws, 0); a.counter = ctr(ws, kCtrVerify);
-  a.scratch = wsp(ws, kSyncBytes);
-  a.chunk = 4096;
+  a.chunk = kVerifyChunk;
+  const size_t nb = (static_cast<size_t>(vocab) + kVerifyChunk - 1) / kVerifyChunk;
+  a.parts = reinterpret_cast<unsigned long long*>(wsp(ws, kHeadBytes));
+  a.scratch = wsp(ws, kHeadBytes + align_up((n_draft + 1) * nb * 8));
   const hipError_t e = greedy ? launch_verify_greedy(a, stream) : launch_verify_sampled(a, stream);
   if (e == hipErrorNotSupported) return MTP_E_UNSUPPORTED;
   MTP_TRY(e);
+  return MTP_OK;
+}
+
+int mtp_timing_begin(int32_t max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20)) return MTP_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  for (hipEvent_t e : g_timer.start) hipEventDestroy(e);
+  for (hipEvent_t e : g_timer.stop) hipEventDestroy(e);
+  g_timer.start.assign(max_launches, nullptr);
+  g_timer.stop.assign(max_launches, nullptr);
+  for (int i = 0; i < max_launches; ++i) {
+    if (hipEventCreate(&g_timer.start[i]) != hipSuccess || hipEventCreate(&g_timer.stop[i]) != hipSuccess) {
+      g_last_hip = hipErrorOutOfMemory;
+      g_timer.on = false;
+      return MTP_E_HIP;
+    }
+  }
+  g_timer.used = 0;
+  g_timer.on = true;
+  return MTP_OK;
+}
+
+int mtp_timing_elapsed(int32_t first, int32_t count, float* total_ms) {
+  if (!total_ms || first < 0 || count < 0) return MTP_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (first + count > g_timer.used) return MTP_E_INVALID_ARG;
+  float sum = 0.f;
+  for (int i = first; i < first + count; ++i) {
+    MTP_TRY(hipEventSynchronize(g_timer.stop[i]));
+    float ms = 0.f;
+    MTP_TRY(hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]));
+    sum += ms;
+  }
+  *total_ms = sum;
+  return MTP_OK;
+}
+
+int mtp_timing_end(float* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return MTP_E_INVALID_ARG;
+  float sum = 0.f;
+  int used = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    g_timer.on = false;
+    used = g_timer.used;
+  }
+  const int st = mtp_timing_elapsed(0, used, &sum);
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  for (hipEvent_t e : g_timer.start) hipEventDestroy(e);
+  for (hipEvent_t e : g_timer.stop) hipEventDestroy(e);
+  g_timer.start.clear();
+  g_timer.stop.clear();
+  g_timer.used = 0;
+  if (st != MTP_OK) return st;
+  *total_ms = sum;
+  *launches = used;
   return MTP_OK;
 }
 

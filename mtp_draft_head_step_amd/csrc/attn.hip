@@ -4,8 +4,8 @@
 // k_rope_append: per (row, head) wave: per-head RMSNorm of q or k over head_dim,
 //   rotate-half RoPE at position state[0] + row (angle computed in fp64), k and v
 //   appended to the cache in the KV dtype, roped q kept in fp32.  Capacity and
-//   count checks set the sticky error word; the last workgroup advances the
-//   length (and the round base when asked).
+//   count checks set the sticky error word.  The length itself is advanced by
+//   the finishing kernel, so every kernel of the step reads the same state[0].
 // k_attn: split-K attention.  Workgroup (chunk, kv head, row) covers a
 //   contiguous key range; lanes are laid along head_dim so each K/V row is read
 //   with coalesced 16-byte loads, and the GQA group's query heads share every
@@ -84,12 +84,6 @@ __global__ __launch_bounds__(64) void k_rope_append(RopeArgs a) {
       }
     }
   }
-  // all workgroups have read state[0]; the last one advances it
-  const bool last = last_block_ticket(a.counter, gridDim.x * gridDim.y);
-  if (last && threadIdx.x == 0) {
-    st[0] = len0 + n;
-    if (a.set_base) st[1] = len0 + n;
-  }
 }
 
 hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s) {
@@ -101,18 +95,38 @@ hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kMaxChunk = 512;
+constexpr int kMaxChunks = 4096;  // chunks per (row, head): capacity <= 2^20
 
+template <bool KVB>
+__device__ __forceinline__ void unpack16(const uint4& v, float (&f)[KVB ? 8 : 4]) {
+  if constexpr (KVB) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = __uint_as_float(w[q] << 16);
+      f[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+}
+
+// Split-K attention for one (key chunk, kv head, query row).  Lanes are laid
+// along head_dim (LPK lanes hold one 16-byte slice each of a K or V row), so a
+// wave covers KPI keys per load; each lane group keeps its own online-softmax
+// state (running max m, sum l, unnormalised o) over the keys it visits, KB keys
+// (2 KB loads) in flight per step.  Groups merge with xor shuffles, waves
+// through LDS; the chunk's (o, m, l) partial goes to the merge kernel.
 template <bool KVB, int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   constexpr int EPL = KVB ? 8 : 4;   // elements per lane (16 bytes)
   constexpr int LPK = D / EPL;       // lanes per key row
   constexpr int KPI = 64 / LPK;      // keys per wave instruction
-  __shared__ float qs[G][D];
-  __shared__ float sc[kMaxChunk][G];
-  __shared__ float red[kAttnWaves][G];
-  __shared__ float stat[2][G];
-  __shared__ float oacc[kAttnWaves][G][D];
+  constexpr int KB = 4;              // keys per lane group per step
+  constexpr float kNeg = -1e30f;
+  __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
+  __shared__ float s_o[kAttnWaves][G][D];
 
   const int32_t* st = a.state;
   if (st[3] != 0) return;
@@ -120,7 +134,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
   const int j = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.z);
   if (j < 0 || j >= n) return;
-  const int off = st[0] - n;        // the rows' K/V are already appended
+  const int off = st[0];            // pre-append length (committed by k_finish)
   const int L = off + j + 1;        // keys visible to row j
   const int h = blockIdx.y;
   const int c = blockIdx.x;
@@ -143,150 +157,137 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     return;
   }
 
-  const float scale = rsqrtf(static_cast<float>(D));
-  for (int idx = tid; idx < G * D; idx += kAttnThreads) {
-    const int g = idx / D, d = idx - g * D;
-    qs[g][d] = a.q[static_cast<size_t>(j) * a.hq * D + (h * G + g) * D + d] * scale;
-  }
-  __syncthreads();
-
   const int grp = lane / LPK;
   const int li = lane % LPK;
   const int d0 = li * EPL;
+  const float scale = rsqrtf(static_cast<float>(D));
   float qr[G][EPL];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g) {
+    const float* qp = a.q + (static_cast<size_t>(j) * a.hq + h * G + g) * D + d0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qr[g][e] = qs[g][d0 + e];
+    for (int e = 0; e < EPL; ++e) qr[g][e] = qp[e] * scale;
+  }
 
+  constexpr int ebytes = KVB ? 2 : 4;
   const size_t head_off = static_cast<size_t>(h) * a.capacity * D;
-  const char* kbase = static_cast<const char*>(a.kc) + head_off * (KVB ? 2 : 4);
-  const char* vbase = static_cast<const char*>(a.vc) + head_off * (KVB ? 2 : 4);
-  constexpr int row_bytes = D * (KVB ? 2 : 4);
+  const char* kbase = static_cast<const char*>(a.kc) + (head_off + d0) * ebytes;
+  const char* vbase = static_cast<const char*>(a.vc) + (head_off + d0) * ebytes;
+  constexpr int row_bytes = D * ebytes;
+  constexpr int kstride = KPI * kAttnWaves;   // keys between a group's consecutive keys
 
-  // scores
-  // wave-uniform trip count so every lane takes part in the group reductions
-  for (int base = k0 + wave * KPI; base < k1; base += KPI * kAttnWaves) {
-    const int kk = base + grp;
-    const bool ok = kk < k1;
-    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) kv = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(kk) * row_bytes + d0 * (KVB ? 2 : 4));
-    float kf[EPL];
-    if constexpr (KVB) {
-      const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+  float m[G], l[G], acc[G][EPL];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { kf[2 * q] = __uint_as_float(w[q] << 16); kf[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u); }
-    } else {
-      kf[0] = __uint_as_float(kv.x); kf[1] = __uint_as_float(kv.y); kf[2] = __uint_as_float(kv.z); kf[3] = __uint_as_float(kv.w);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) p += qr[g][e] * kf[e];
-      p = group_sum(p, LPK);
-      if (ok && li == 0) sc[kk - k0][g] = p;
-    }
-  }
-  __syncthreads();
-
-  // max and exp-sum per query head
-  const int cn = k1 - k0;
-  {
-    float m[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = -INFINITY;
-    for (int i = tid; i < cn; i += kAttnThreads)
-#pragma unroll
-      for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], sc[i][g]);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float v = wave_max(m[g]);
-      if (lane == 0) red[wave][g] = v;
-    }
-    __syncthreads();
-    if (tid < G) {
-      float v = red[0][tid];
-      for (int w = 1; w < kAttnWaves; ++w) v = fmaxf(v, red[w][tid]);
-      stat[0][tid] = v;
-    }
-    __syncthreads();
-    float l[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) l[g] = 0.f;
-    for (int i = tid; i < cn; i += kAttnThreads)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = __expf(sc[i][g] - stat[0][g]);
-        sc[i][g] = p;
-        l[g] += p;
-      }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float v = wave_sum(l[g]);
-      if (lane == 0) red[wave][g] = v;
-    }
-    __syncthreads();
-    if (tid < G) {
-      float v = 0.f;
-      for (int w = 0; w < kAttnWaves; ++w) v += red[w][tid];
-      stat[1][tid] = v;
-    }
-    __syncthreads();
-  }
-
-  // P . V
-  float acc[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNeg;
+    l[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  for (int kk = k0 + wave * KPI + grp; kk < k1; kk += KPI * kAttnWaves) {
-    const uint4 vv = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(kk) * row_bytes + d0 * (KVB ? 2 : 4));
-    float vf[EPL];
-    if constexpr (KVB) {
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  }
+
+  // wave-uniform trip count so every lane takes part in the group reductions
+  for (int base = k0 + wave * KPI; base < k1; base += KB * kstride) {
+    uint4 kv[KB], vv[KB];
+    bool ok[KB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { vf[2 * q] = __uint_as_float(w[q] << 16); vf[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u); }
-    } else {
-      vf[0] = __uint_as_float(vv.x); vf[1] = __uint_as_float(vv.y); vf[2] = __uint_as_float(vv.z); vf[3] = __uint_as_float(vv.w);
+    for (int b = 0; b < KB; ++b) {
+      const int kk = base + grp + b * kstride;
+      ok[b] = kk < k1;
+      const int kc = ok[b] ? kk : k0;           // a valid row; result masked below
+      kv[b] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(kc) * row_bytes);
+      vv[b] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(kc) * row_bytes);
+    }
+    float sc[KB][G];
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      float kf[EPL];
+      unpack16<KVB>(kv[b], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) p += qr[g][e] * kf[e];
+        p = group_sum(p, LPK);
+        sc[b][g] = ok[b] ? p : kNeg;
+      }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float p = sc[kk - k0][g];
+      float mb = sc[0][g];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += p * vf[e];
+      for (int b = 1; b < KB; ++b) mb = fmaxf(mb, sc[b][g]);
+      const float mnew = fmaxf(m[g], mb);
+      const float r = __expf(m[g] - mnew);
+      l[g] *= r;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= r;
+      m[g] = mnew;
+    }
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      float vf[EPL];
+      unpack16<KVB>(vv[b], vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = ok[b] ? __expf(sc[b][g] - m[g]) : 0.f;
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] += p * vf[e];
+      }
     }
   }
+
+  // merge the wave's lane groups (same head_dim slice, different keys)
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int o = LPK; o < 64; o <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float v = acc[g][e];
-      for (int o = LPK; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      acc[g][e] = v;
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(m[g], o, 64);
+      const float lo = __shfl_xor(l[g], o, 64);
+      const float mnew = fmaxf(m[g], mo);
+      const float ra = __expf(m[g] - mnew), rb = __expf(mo - mnew);
+      l[g] = l[g] * ra + lo * rb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * ra + __shfl_xor(acc[g][e], o, 64) * rb;
+      m[g] = mnew;
     }
+  }
   if (grp == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) oacc[wave][g][d0 + e] = acc[g][e];
+      for (int e = 0; e < EPL; ++e) s_o[wave][g][d0 + e] = acc[g][e];
+      if (li == 0) { s_m[wave][g] = m[g]; s_l[wave][g] = l[g]; }
+    }
   }
   __syncthreads();
+  // merge the waves
   for (int idx = tid; idx < G * D; idx += kAttnThreads) {
     const int g = idx / D, d = idx - g * D;
-    float v = 0.f;
+    float M = s_m[0][g];
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) v += oacc[w][g][d];
-    a.part_o[(pbase + static_cast<size_t>(g) * a.nchunk) * D + d] = v;
-  }
-  if (tid < G) {
-    a.part_ml[(pbase + static_cast<size_t>(tid) * a.nchunk) * 2] = stat[0][tid];
-    a.part_ml[(pbase + static_cast<size_t>(tid) * a.nchunk) * 2 + 1] = stat[1][tid];
+    for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float r = __expf(s_m[w][g] - M);
+      o += r * s_o[w][g][d];
+      lsum += r * s_l[w][g];
+    }
+    a.part_o[(pbase + static_cast<size_t>(g) * a.nchunk) * D + d] = o;
+    if (d == 0) {
+      a.part_ml[(pbase + static_cast<size_t>(g) * a.nchunk) * 2] = M;
+      a.part_ml[(pbase + static_cast<size_t>(g) * a.nchunk) * 2 + 1] = lsum;
+    }
   }
 }
 
+// One workgroup per (row, query head): chunk weights exp(m_c - M) in LDS, then
+// every thread sums its head_dim column over the chunks (independent loads).
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  __shared__ float wts[kMaxChunks];
+  __shared__ float red[4];
+  __shared__ float s_m, s_den;
   const int32_t* st = a.state;
   if (st[3] != 0) return;
   int n = a.n_max;
@@ -295,19 +296,43 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   if (j < 0 || j >= n) return;
   const int hq = blockIdx.x;
   const int D = a.d;
-  const size_t base = (static_cast<size_t>(j) * a.hq + hq) * a.nchunk;
-  float M = -INFINITY;
-  for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, a.part_ml[(base + c) * 2]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) {
-      const float mc = a.part_ml[(base + c) * 2];
-      if (mc == -INFINITY) continue;
-      const float w = __expf(mc - M);
-      num += w * a.part_o[(base + c) * D + d];
-      den += w * a.part_ml[(base + c) * 2 + 1];
+  const int nc = a.nchunk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t base = (static_cast<size_t>(j) * a.hq + hq) * nc;
+  float m = -INFINITY;
+  for (int c = tid; c < nc; c += 256) m = fmaxf(m, a.part_ml[(base + c) * 2]);
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (tid == 0) s_m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  const float M = s_m;
+  float den = 0.f;
+  for (int c = tid; c < nc; c += 256) {
+    const float mc = a.part_ml[(base + c) * 2];
+    const float w = (mc == -INFINITY) ? 0.f : __expf(mc - M);
+    wts[c] = w;
+    den += w * a.part_ml[(base + c) * 2 + 1];
+  }
+  den = wave_sum(den);
+  __syncthreads();
+  if (lane == 0) red[wave] = den;
+  __syncthreads();
+  if (tid == 0) s_den = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  const float inv = 1.0f / s_den;
+  const float* po = a.part_o + base * D;
+  for (int d = tid; d < D; d += 256) {
+    float num0 = 0.f, num1 = 0.f, num2 = 0.f, num3 = 0.f;
+    int c = 0;
+    for (; c + 4 <= nc; c += 4) {
+      num0 += wts[c] * po[static_cast<size_t>(c) * D + d];
+      num1 += wts[c + 1] * po[static_cast<size_t>(c + 1) * D + d];
+      num2 += wts[c + 2] * po[static_cast<size_t>(c + 2) * D + d];
+      num3 += wts[c + 3] * po[static_cast<size_t>(c + 3) * D + d];
     }
-    a.o[static_cast<size_t>(j) * a.hq * D + hq * D + d] = num / den;
+    for (; c < nc; ++c) num0 += wts[c] * po[static_cast<size_t>(c) * D + d];
+    a.o[static_cast<size_t>(j) * a.hq * D + hq * D + d] = ((num0 + num1) + (num2 + num3)) * inv;
   }
 }
 
@@ -348,7 +373,33 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_attn_merge, dim3(a.hq, rows), dim3(a.d < 256 ? a.d : 256), 0, s, a);
+  hipLaunchKernelGGL(k_attn_merge, dim3(a.hq, rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mtp
+
+namespace mtp {
+
+__global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
+  int32_t* st = a.state;
+  if (st[3] != 0) return;
+  int n = a.n_max;
+  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  if (a.parts) {
+    const unsigned long long b = block_max_u64(a.parts, a.nparts);
+    if (threadIdx.x == 0 && a.amax_out && n > 0) *a.amax_out = argmax_index(b);
+  }
+  if (threadIdx.x == 0) {
+    const int len = st[0] + n;
+    st[0] = len;
+    if (a.set_base) st[1] = len;
+  }
+}
+
+hipError_t launch_finish(const FinishArgs& a, hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_finish, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -34,6 +34,25 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// DPP move of v (lanes without a source read 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+
+// Sum over aligned groups of `width` lanes (8, 16, 32 or 64) with DPP row
+// operations; the group's total is valid in its LAST lane only.
+__device__ __forceinline__ float group_sum_last(float v, int width) {
+  v += dpp_mov<0xB1, 0xF>(v);                      // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E, 0xF>(v);                      // quad_perm [2,3,0,1]
+  v += dpp_mov<0x114, 0xF>(v);                     // row_shr:4
+  if (width >= 16) v += dpp_mov<0x118, 0xF>(v);    // row_shr:8
+  if (width >= 32) v += dpp_mov<0x142, 0xA>(v);    // row_bcast:15 into rows 1, 3
+  if (width >= 64) v += dpp_mov<0x143, 0xC>(v);    // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Monotone map float -> uint32 (larger float, larger key); -0 is folded into +0.
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);
@@ -59,27 +78,18 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
-// Grid-completion ticket: every workgroup calls this once after its last
-// global write; exactly one workgroup (the last to arrive) gets true, and the
-// counter is re-armed to zero by that workgroup.  Call from all threads.
-__device__ __forceinline__ bool last_block_ticket(unsigned int* counter, unsigned int nblocks) {
-  __shared__ int s_last;
-  __threadfence();
+// Largest key of n partial argmax keys, reduced by one workgroup (blockDim 256).
+__device__ __forceinline__ unsigned long long block_max_u64(const unsigned long long* parts, int n) {
+  __shared__ unsigned long long s_part[4];
+  unsigned long long b = 0ull;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) b = parts[i] > b ? parts[i] : b;
+  b = wave_max_u64(b);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = b;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned int prev = atomicAdd(counter, 1u);
-    s_last = (prev == nblocks - 1) ? 1 : 0;
-    if (s_last) {
-      __threadfence();
-      atomicExch(counter, 0u);
-    }
-  }
+  b = s_part[0];
+  for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) b = s_part[w] > b ? s_part[w] : b;
   __syncthreads();
-  return s_last != 0;
-}
-
-__device__ __forceinline__ unsigned long long atomic_read_u64(unsigned long long* p) {
-  return atomicAdd(p, 0ull);
+  return b;
 }
 
 }  // namespace mtp

@@ -11,9 +11,11 @@
 //  * lanes of a row are reduced with xor shuffles, in a fixed order (no float
 //    atomics: results are bit-identical run to run);
 //  * epilogues fuse the residual add, SwiGLU (gate and up rows of the same index
-//    are paired in one wave) and the logits argmax (packed 64-bit key, max value
-//    then lowest index, one atomicMax per workgroup, the last workgroup writes
-//    the int32 result and re-arms the slot).
+//    are paired in one wave) and the logits argmax (packed 64-bit key: max value
+//    then lowest index; one key per workgroup, merged by the finishing kernel).
+//  * no workgroup waits for or signals another: on gfx950 a device-scope fence
+//    writes back and invalidates the XCD's L2, which costs far more than the
+//    extra one-workgroup kernel that merges the partial keys.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,9 +23,9 @@ namespace mtp {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kRPW = 4;      // row slots per wave
 constexpr int kUnroll = 4;   // 16-byte loads per slot in flight
-constexpr int kLdsBytes = 64 * 1024;
+constexpr int kCUs = 256;
+constexpr int kMaxLds = 144 * 1024;   // dynamic LDS a GEMV may ask for
 
 template <int WT> struct WTraits;
 template <> struct WTraits<W_F32> { static constexpr int EPC = 4; };
@@ -63,7 +65,135 @@ __device__ __forceinline__ float dot_chunk(const uint4& w, const float* __restri
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <int WT, int NR>
+// 4 consecutive elements (bf16 or fp32) as fp32.
+__device__ __forceinline__ float4 load4(const void* p, size_t i, int bf16) {
+  if (bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+  }
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+}
+
+// Stage dst[k - k0] = src[off + k] * nw[noff + k] (nw may be null: factor 1)
+// for k in [kb, ke), 4 values per thread per step and up to 8 steps of loads in
+// flight, and add the sum of squares of the src values to ss.
+__device__ __forceinline__ void stage_range(float* dst, const void* src, long long off, int src_bf16,
+                                            const void* nw, long long noff, int nw_bf16, int kb, int ke,
+                                            int k0, float& ss) {
+  constexpr int kB = 8;
+  for (int base = kb + threadIdx.x * 4; base < ke; base += kB * kThreads * 4) {
+    float4 xv[kB], wv[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int k = base + u * kThreads * 4;
+      if (k < ke) {
+        xv[u] = load4(src, static_cast<size_t>(off + k), src_bf16);
+        wv[u] = nw ? load4(nw, static_cast<size_t>(noff + k), nw_bf16) : make_float4(1.f, 1.f, 1.f, 1.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int k = base + u * kThreads * 4;
+      if (k < ke) {
+        const float4 x = xv[u], w = wv[u];
+        ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+        *reinterpret_cast<float4*>(dst + (k - k0)) = make_float4(x.x * w.x, x.y * w.y, x.z * w.z, x.w * w.w);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float4 mul4(float4 a, float4 b, float s) {
+  return make_float4(a.x * b.x * s, a.y * b.y * s, a.z * b.z * s, a.w * b.w * s);
+}
+
+// U chunks of every row slot: all loads first (unconditional, wave-uniform
+// trip count), then the FMAs.  lane_row[s] points at this lane's first chunk of
+// row slot s; consecutive chunks of a lane are `stride` bytes apart.
+template <int RPW, int U>
+__device__ __forceinline__ void gemv_load(uint4 (&w)[RPW][U], const char* const (&lane_row)[RPW], int j,
+                                          int lpr) {
+  const size_t stride = static_cast<size_t>(lpr) * 16;
+#pragma unroll
+  for (int s = 0; s < RPW; ++s)
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      w[s][u] = *reinterpret_cast<const uint4*>(lane_row[s] + static_cast<size_t>(j + u) * stride);
+}
+
+template <int WT, int NR, int RPW, int U, bool TWO>
+__device__ __forceinline__ void gemv_fma(float (&acc)[RPW][NR], float (&acc2)[RPW][NR],
+                                         const uint4 (&w)[RPW][U], int j, int lpr,
+                                         const float* __restrict__ xl, int kp,
+                                         const uint16_t* const (&srow)[RPW], int g0, int split) {
+  constexpr int EPC = WTraits<WT>::EPC;
+  float scl[RPW][U];
+  if constexpr (WT == W_I8) {
+#pragma unroll
+    for (int s = 0; s < RPW; ++s)
+#pragma unroll
+      for (int u = 0; u < U; ++u) scl[s][u] = f16_to_f32(srow[s][(g0 + (j + u) * lpr) >> 3]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    // chunks at or past `split` (in chunk units of this lane's sequence) feed acc2
+    const bool second = TWO && g0 + (j + u) * lpr >= split;
+#pragma unroll
+    for (int s = 0; s < RPW; ++s)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float d = dot_chunk<WT>(w[s][u], xl + r * kp + (j + u) * lpr * EPC);
+        if constexpr (WT == W_I8) d *= scl[s][u];
+        if constexpr (TWO) {
+          if (second) acc2[s][r] += d; else acc[s][r] += d;
+        } else {
+          acc[s][r] += d;
+        }
+      }
+  }
+}
+
+template <int WT, int NR, int RPW, int U, bool TWO>
+__device__ __forceinline__ void gemv_body(float (&acc)[RPW][NR], float (&acc2)[RPW][NR],
+                                          const char* const (&lane_row)[RPW], int j, int lpr,
+                                          const float* __restrict__ xl, int kp,
+                                          const uint16_t* const (&srow)[RPW], int g0, int split) {
+  uint4 w[RPW][U];
+  gemv_load<RPW, U>(w, lane_row, j, lpr);
+  gemv_fma<WT, NR, RPW, U, TWO>(acc, acc2, w, j, lpr, xl, kp, srow, g0, split);
+}
+
+// Row slot s of row block blk: the weight row pointer (rows past the end read
+// row 0, a valid address, and are discarded), its index in its matrix, the
+// int8 scale row, and whether it is valid.
+template <int WT, int RPW>
+__device__ __forceinline__ void gemv_rows(const GemvArgs& a, int blk, int rows_per_wg, int wave, int rps,
+                                          int sub, bool swiglu, const char* (&rowp)[RPW],
+                                          const uint16_t* (&srow)[RPW], int (&rowid)[RPW],
+                                          bool (&valid)[RPW]) {
+  constexpr int WBYTES = WT == W_F32 ? 4 : (WT == W_BF16 ? 2 : 1);
+  const size_t row_bytes = static_cast<size_t>(a.K) * WBYTES;
+#pragma unroll
+  for (int s = 0; s < RPW; ++s) {
+    int r, mat = 0;
+    if (swiglu) {
+      r = blk * rows_per_wg + (wave * (RPW / 2) + s / 2) * rps + sub;
+      mat = s & 1;
+      valid[s] = r < a.M;
+    } else {
+      r = blk * rows_per_wg + (wave * RPW + s) * rps + sub;
+      valid[s] = r < a.M;
+      if (r >= a.m[0]) { r -= a.m[0]; mat = 1; if (r >= a.m[1]) { r -= a.m[1]; mat = 2; } }
+    }
+    if (!valid[s]) { r = 0; mat = 0; }
+    rowid[s] = r;
+    rowp[s] = static_cast<const char*>(a.w[mat]) + static_cast<size_t>(r) * row_bytes;
+    srow[s] = (WT == W_I8) ? a.scales + static_cast<size_t>(r) * (a.K >> 7) : nullptr;
+  }
+}
+
+template <int WT, int NR, int RPW, bool TWO>
 __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   extern __shared__ float xs[];  // [NR][kp]
   __shared__ float s_red[kWaves][2 * NR];
@@ -86,190 +216,132 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
     nrows = min(NR, n - a.row_base);
   }
   if (nrows <= 0) {
-    if (a.out_mode == OUT_LOGITS && last_block_ticket(a.counter, gridDim.x)) {
-      atomicExch(a.amax_slot, 0ull);
-    }
+    if (a.out_mode == OUT_LOGITS && threadIdx.x == 0) a.amax_part[blockIdx.x] = 0ull;
     return;
   }
   const int K = a.K;
-
-  // ---- per-row inverse RMS of the input (recomputed per workgroup from L2)
-  if (a.in_mode != IN_F32) {
-    const int half = (a.in_mode == IN_EMBED) ? K / 2 : K;
-    float ss[2 * NR];
-#pragma unroll
-    for (int i = 0; i < 2 * NR; ++i) ss[i] = 0.f;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (r < nrows) {
-        const int j = j0 + r;
-        if (a.in_mode == IN_RMS) {
-          const float* xr = a.x + static_cast<size_t>(j) * a.ldx;
-          for (int k = tid * 4; k < K; k += kThreads * 4) {
-            const float4 v = *reinterpret_cast<const float4*>(xr + k);
-            ss[2 * r] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-          }
-        } else {
-          const int t = a.tok[j];
-          for (int k = tid; k < half; k += kThreads) {
-            const float e = load_val(a.embed, static_cast<size_t>(t) * half + k, a.embed_bf16);
-            const float h = load_val(a.hid, j * a.ld_hid + k, a.hid_bf16);
-            ss[2 * r] += e * e;
-            ss[2 * r + 1] += h * h;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * NR; ++i) {
-      float v = wave_sum(ss[i]);
-      if (lane == 0) s_red[wave][i] = v;
-    }
-    __syncthreads();
-    if (tid < 2 * NR) {
-      float v = 0.f;
-      for (int w = 0; w < kWaves; ++w) v += s_red[w][tid];
-      s_inv[tid] = rsqrtf(v / static_cast<float>(half) + a.eps);
-    }
-    __syncthreads();
-  }
-
+  const int half = (a.in_mode == IN_EMBED) ? K / 2 : K;
   const int lpr = a.lpr;
   const int rps = kWave / lpr;          // rows per slot
   const int sub = lane / lpr;           // row within the slot
   const int li = lane % lpr;            // lane within the row
   const bool swiglu = (a.out_mode == OUT_SWIGLU);
-  const int rows_per_wg = kWaves * (swiglu ? kRPW / 2 : kRPW) * rps;
+  const int rows_per_wg = kWaves * (swiglu ? RPW / 2 : RPW) * rps;
   const int nblocks = (a.M + rows_per_wg - 1) / rows_per_wg;
   const int nphase = (K + a.kp - 1) / a.kp;
+
+  // Inputs are staged as x * w_norm; the scalar 1 / rms(x) of each activation
+  // row is applied to the finished dot products (it factors out), so the sum of
+  // squares is reduced after the weights have been streamed, not before.  The
+  // embedding-cat input has two halves with their own scales: chunks of the
+  // hidden half accumulate separately (acc2).
+  float ss[2 * NR];
+#pragma unroll
+  for (int i = 0; i < 2 * NR; ++i) ss[i] = 0.f;
+  const int split_chunk = TWO ? half / EPC : 0x7FFFFFFF;
+  bool have_inv = (a.in_mode == IN_F32);
+  if (have_inv && tid < 2 * NR) s_inv[tid] = (tid & 1) ? 0.f : 1.f;
 
   unsigned long long best = 0ull;
 
   for (int blk = blockIdx.x; blk < nblocks; blk += (a.grid_stride ? gridDim.x : nblocks)) {
-    // rows of the slots: plain mode slot s -> row; swiglu slot pair (2p, 2p+1) -> (gate r, up r)
-    const char* rowp[kRPW];
-    int rowid[kRPW];
-    bool valid[kRPW];
-#pragma unroll
-    for (int s = 0; s < kRPW; ++s) {
-      int r, mat;
-      if (swiglu) {
-        r = blk * rows_per_wg + (wave * (kRPW / 2) + s / 2) * rps + sub;
-        mat = s & 1;
-        valid[s] = r < a.M;
-      } else {
-        r = blk * rows_per_wg + (wave * kRPW + s) * rps + sub;
-        valid[s] = r < a.M;
-        mat = 0;
-        int rr = r;
-        if (rr >= a.m[0]) { rr -= a.m[0]; mat = 1; if (rr >= a.m[1]) { rr -= a.m[1]; mat = 2; } }
-        if (valid[s]) r = rr;
-      }
-      rowid[s] = r;
-      const size_t row_bytes = static_cast<size_t>(K) * (WT == W_F32 ? 4 : (WT == W_BF16 ? 2 : 1));
-      rowp[s] = valid[s] ? static_cast<const char*>(a.w[mat]) + static_cast<size_t>(r) * row_bytes
-                         : static_cast<const char*>(a.w[0]);
-    }
+    // row slots: plain mode slot s -> its row; swiglu slot pair (2p, 2p+1) -> (gate r, up r)
+    const char* rowp[RPW];
+    const uint16_t* srow[RPW];
+    int rowid[RPW];
+    bool valid[RPW];
+    gemv_rows<WT, RPW>(a, blk, rows_per_wg, wave, rps, sub, swiglu, rowp, srow, rowid, valid);
 
-    float acc[kRPW][NR];
+    float acc[RPW][NR], acc2[RPW][NR];   // acc2: hidden half of the embedding-cat input
 #pragma unroll
-    for (int s = 0; s < kRPW; ++s)
+    for (int s = 0; s < RPW; ++s)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) acc[s][r] = 0.f;
+      for (int r = 0; r < NR; ++r) acc[s][r] = acc2[s][r] = 0.f;
 
     for (int ph = 0; ph < nphase; ++ph) {
       const int k0 = ph * a.kp;
       const int klen = min(a.kp, K - k0);
-      // ---- stage the (normalised) inputs of this phase in LDS
-      // a single-phase grid-stride loop stages once; multi-phase restages per phase
-      const bool need_stage = (blk == static_cast<int>(blockIdx.x)) || nphase > 1;
-      if (need_stage) {
+      // ---- stage this phase's inputs in LDS; a single-phase grid-stride loop
+      // stages once, a multi-phase loop restages per phase
+      if (blk == static_cast<int>(blockIdx.x) || nphase > 1) {
         __syncthreads();
-        const int q4 = klen / 4;
-        for (int idx = tid; idx < NR * q4; idx += kThreads) {
-          const int r = idx / q4;
-          const int k = k0 + (idx - r * q4) * 4;
-          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (r < nrows) {
-            const int j = j0 + r;
-            if (a.in_mode == IN_F32) {
-              v = *reinterpret_cast<const float4*>(a.x + static_cast<size_t>(j) * a.ldx + k);
-            } else if (a.in_mode == IN_RMS) {
-              v = *reinterpret_cast<const float4*>(a.x + static_cast<size_t>(j) * a.ldx + k);
-              const float inv = s_inv[2 * r];
-              v.x *= inv * load_val(a.nw, k, a.nw_bf16);
-              v.y *= inv * load_val(a.nw, k + 1, a.nw_bf16);
-              v.z *= inv * load_val(a.nw, k + 2, a.nw_bf16);
-              v.w *= inv * load_val(a.nw, k + 3, a.nw_bf16);
-            } else {
-              const int half = K / 2;
-              float t[4];
-              for (int e = 0; e < 4; ++e) {
-                const int kk = k + e;
-                if (kk < half) {
-                  t[e] = load_val(a.embed, static_cast<size_t>(a.tok[j]) * half + kk, a.embed_bf16) * s_inv[2 * r] *
-                         load_val(a.nw, kk, a.nw_bf16);
-                } else {
-                  t[e] = load_val(a.hid, j * a.ld_hid + kk - half, a.hid_bf16) * s_inv[2 * r + 1] *
-                         load_val(a.nw2, kk - half, a.nw_bf16);
-                }
-              }
-              v = make_float4(t[0], t[1], t[2], t[3]);
-            }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          float* dst = xs + r * a.kp;
+          if (r >= nrows) {
+            for (int k = tid * 4; k < klen; k += kThreads * 4)
+              *reinterpret_cast<float4*>(dst + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+            continue;
           }
-          *reinterpret_cast<float4*>(xs + r * a.kp + (k - k0)) = v;
+          const int jr = j0 + r;
+          const void* nw = (a.in_mode == IN_RMS) ? a.nw : nullptr;
+          if (a.in_mode != IN_EMBED) {
+            stage_range(dst, a.x, static_cast<long long>(jr) * a.ldx, 0, nw, 0, a.nw_bf16, k0,
+                        k0 + klen, k0, ss[2 * r]);
+          } else {
+            const int ea = k0, eb = min(k0 + klen, half);
+            if (ea < eb)
+              stage_range(dst, a.embed, static_cast<long long>(a.tok[jr]) * half, a.embed_bf16, a.nw, 0,
+                          a.nw_bf16, ea, eb, k0, ss[2 * r]);
+            const int ha = max(k0, half), hb = k0 + klen;
+            if (ha < hb)
+              stage_range(dst, a.hid, static_cast<long long>(jr) * a.ld_hid - half, a.hid_bf16, a.nw2,
+                          -static_cast<long long>(half), a.nw_bf16, ha, hb, k0, ss[2 * r + 1]);
+          }
         }
         __syncthreads();
       }
 
-      // ---- stream the weights of this phase
-      const int nch = klen / EPC;
-      const int c_base = k0 / EPC;
-      for (int c = li; c < nch; c += lpr * kUnroll) {
-        uint4 wv[kRPW][kUnroll];
+      // ---- stream the weights of this phase: cpl chunks per lane (wave-uniform)
+      const int cpl = (klen / EPC) / lpr;
+      const char* lane_row[RPW];
 #pragma unroll
-        for (int s = 0; s < kRPW; ++s)
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const int cc = c + u * lpr;
-            if (valid[s] && cc < nch)
-              wv[s][u] = *reinterpret_cast<const uint4*>(rowp[s] + static_cast<size_t>(c_base + cc) * 16);
-            else
-              wv[s][u] = make_uint4(0u, 0u, 0u, 0u);
-          }
-#pragma unroll
-        for (int s = 0; s < kRPW; ++s)
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const int cc = c + u * lpr;
-            if (cc < nch) {
-              float scale = 1.f;
-              if constexpr (WT == W_I8) {
-                if (valid[s]) {
-                  const int grp = (k0 + cc * EPC) >> 7;
-                  scale = f16_to_f32(a.scales[static_cast<size_t>(rowid[s]) * (K >> 7) + grp]);
-                }
-              }
-#pragma unroll
-              for (int r = 0; r < NR; ++r) {
-                const float d = dot_chunk<WT>(wv[s][u], xs + r * a.kp + cc * EPC);
-                if constexpr (WT == W_I8) acc[s][r] += d * scale; else acc[s][r] += d;
-              }
-            }
-          }
-      }
+      for (int s = 0; s < RPW; ++s) lane_row[s] = rowp[s] + (static_cast<size_t>(k0 / EPC) + li) * 16;
+      const float* xl = xs + li * EPC;
+      const int g0 = (k0 / EPC) + li;   // chunk index of j = 0 (int8 scale groups)
+      int j = 0;
+      for (; j + kUnroll <= cpl; j += kUnroll)
+        gemv_body<WT, NR, RPW, kUnroll, TWO>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
+      for (; j + 2 <= cpl; j += 2)
+        gemv_body<WT, NR, RPW, 2, TWO>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
+      for (; j < cpl; ++j)
+        gemv_body<WT, NR, RPW, 1, TWO>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
     }
 
-    // ---- reduce each row over its lanes and run the epilogue
+    // ---- the inverse RMS of each activation row (once, after the first block)
+    if (!have_inv) {
 #pragma unroll
-    for (int s = 0; s < kRPW; ++s)
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[s][r] = group_sum(acc[s][r], lpr);
+      for (int i = 0; i < 2 * NR; ++i) {
+        const float v = wave_sum(ss[i]);
+        if (lane == 0) s_red[wave][i] = v;
+      }
+      __syncthreads();
+      if (tid < 2 * NR) {
+        float v = 0.f;
+        for (int w = 0; w < kWaves; ++w) v += s_red[w][tid];
+        // odd entries scale the hidden half, which only the embedding-cat input has
+        s_inv[tid] = ((tid & 1) && a.in_mode != IN_EMBED) ? 0.f
+                                                          : rsqrtf(v / static_cast<float>(half) + a.eps);
+      }
+      __syncthreads();
+      have_inv = true;
+    }
 
-    if (li == 0) {
+    // ---- reduce each row over its lanes (total in the row's last lane), apply
+    // 1/rms, run the epilogue
+#pragma unroll
+    for (int s = 0; s < RPW; ++s)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float v = group_sum_last(acc[s][r], lpr) * s_inv[2 * r];
+        if constexpr (TWO) v += group_sum_last(acc2[s][r], lpr) * s_inv[2 * r + 1];
+        acc[s][r] = v;
+      }
+
+    if (li == lpr - 1) {
       if (swiglu) {
 #pragma unroll
-        for (int s = 0; s < kRPW; s += 2) {
+        for (int s = 0; s < RPW; s += 2) {
           if (!valid[s]) continue;
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
@@ -280,9 +352,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < kRPW; ++s) {
+        for (int s = 0; s < RPW; ++s) {
           if (!valid[s]) continue;
-          const int row = blk * rows_per_wg + (wave * kRPW + s) * rps + sub;
+          const int row = blk * rows_per_wg + (wave * RPW + s) * rps + sub;
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             if (r >= nrows) continue;
@@ -314,45 +386,100 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
     if (tid == 0) {
       unsigned long long b = s_best[0];
       for (int w = 1; w < kWaves; ++w) b = s_best[w] > b ? s_best[w] : b;
-      atomicMax(a.amax_slot, b);
-    }
-    if (last_block_ticket(a.counter, gridDim.x) && tid == 0) {
-      const unsigned long long b = atomicExch(a.amax_slot, 0ull);
-      if (a.amax_out) *a.amax_out = argmax_index(b);
+      a.amax_part[blockIdx.x] = b;     // merged by the step's finishing kernel
     }
   }
 }
 
-template <int WT, int NR>
-static hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
+// Launch shape.  Single-phase launches are persistent: the grid is sized by
+// how many workgroups fit per CU (LDS bound) and balanced so every workgroup
+// gets the same number of row blocks (+-1); each stages its input once.
+struct GemvTuning {
+  // measured on MI355X (rows per slot, workgroups per CU) for the 27B-shaped head
+  int rpw_large = 2, wg_per_cu_large = 2;    // unembedding (>= large_rows rows)
+  int rpw_swiglu = 4, wg_per_cu_swiglu = 3;  // gate/up pairs
+  int rpw_small = 2, wg_per_cu_small = 6;    // 5K..8K-row projections
+  long large_rows = 65536;
+};
+GemvTuning g_gemv_tuning;
+
+template <int WT, int NR, int RPW, bool TWO>
+static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int max_per_cu) {
+  GemvArgs a = a0;
+  if (a.out_mode == OUT_SWIGLU && RPW < 2) return hipErrorInvalidValue;
   const int rps = kWave / a.lpr;
-  const int rows_per_wg = kWaves * ((a.out_mode == OUT_SWIGLU) ? kRPW / 2 : kRPW) * rps;
+  const int rows_per_wg = kWaves * ((a.out_mode == OUT_SWIGLU) ? RPW / 2 : RPW) * rps;
   const int nblocks = (a.M + rows_per_wg - 1) / rows_per_wg;
-  int grid = nblocks;
-  if (a.grid_stride) grid = nblocks < 2048 ? nblocks : 2048;
   const size_t lds = static_cast<size_t>(NR) * a.kp * sizeof(float);
+  int grid = nblocks;
+  if (a.grid_stride) {
+    int occ = static_cast<int>((160 * 1024) / (lds + 2048));
+    occ = occ < 1 ? 1 : (occ > max_per_cu ? max_per_cu : occ);
+    const int cap = kCUs * occ;
+    const int per = (nblocks + cap - 1) / cap;          // row blocks per workgroup
+    grid = (nblocks + per - 1) / per;
+  }
+  if (grid_out) *grid_out = grid;
+  if (lds > 64 * 1024) {   // gfx950 gives a workgroup up to 160 KB of LDS on request
+    static bool raised = false;
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
   (void)hipGetLastError();
-  hipLaunchKernelGGL((k_gemv<WT, NR>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((k_gemv<WT, NR, RPW, TWO>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-template <int WT>
-static hipError_t launch_w(const GemvArgs& a, int nr, hipStream_t s) {
-  switch (nr) {
-    case 1: return launch_t<WT, 1>(a, s);
-    case 2: return launch_t<WT, 2>(a, s);
-    case 4: return launch_t<WT, 4>(a, s);
-    case 8: return launch_t<WT, 8>(a, s);
-    case 16: return launch_t<WT, 16>(a, s);
-    default: return hipErrorInvalidValue;
+template <int WT, int NR>
+static hipError_t launch_r(const GemvArgs& a, hipStream_t s, int* g) {
+  const GemvTuning& t = g_gemv_tuning;
+  const bool swiglu = a.out_mode == OUT_SWIGLU;
+  int rpw, per_cu;
+  if (swiglu) { rpw = t.rpw_swiglu; per_cu = t.wg_per_cu_swiglu; }
+  else if (a.M >= t.large_rows) { rpw = t.rpw_large; per_cu = t.wg_per_cu_large; }
+  else { rpw = t.rpw_small; per_cu = t.wg_per_cu_small; }
+  if (swiglu && rpw < 2) rpw = 2;
+  if (a.in_mode == IN_EMBED) {
+    if constexpr (WT == W_I8) return hipErrorInvalidValue;
+    else return launch_t<WT, NR, 2, true>(a, s, g, per_cu);   // the fc projection
+  }
+  if constexpr (NR > 1) {
+    return launch_t<WT, NR, 2, false>(a, s, g, per_cu);   // few-row flushes: one shape
+  } else {
+    switch (rpw) {
+      case 1: return launch_t<WT, NR, 1, false>(a, s, g, per_cu);
+      case 2: return launch_t<WT, NR, 2, false>(a, s, g, per_cu);
+      default: return launch_t<WT, NR, 4, false>(a, s, g, per_cu);
+    }
   }
 }
 
-hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s) {
+template <int WT>
+static hipError_t launch_w(const GemvArgs& a, int nr, hipStream_t s, int* g) {
+  if constexpr (WT == W_I8) {
+    return nr == 1 ? launch_r<WT, 1>(a, s, g) : hipErrorInvalidValue;   // unembedding only
+  } else {
+    switch (nr) {
+      case 1: return launch_r<WT, 1>(a, s, g);
+      case 2: return launch_r<WT, 2>(a, s, g);
+      case 3: return launch_r<WT, 3>(a, s, g);
+      case 4: return launch_r<WT, 4>(a, s, g);
+      case 8: return launch_r<WT, 8>(a, s, g);
+      case 16: return launch_r<WT, 16>(a, s, g);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s, int* grid_out) {
   switch (wtype) {
-    case W_F32: return launch_w<W_F32>(a, nr, s);
-    case W_BF16: return launch_w<W_BF16>(a, nr, s);
-    case W_I8: return launch_w<W_I8>(a, nr, s);
+    case W_F32: return launch_w<W_F32>(a, nr, s, grid_out);
+    case W_BF16: return launch_w<W_BF16>(a, nr, s, grid_out);
+    case W_I8: return launch_w<W_I8>(a, nr, s, grid_out);
     default: return hipErrorInvalidValue;
   }
 }

@@ -50,17 +50,15 @@ struct GemvArgs {
   int y2_bf16;
   int ldy2;
   float* logits;           // OUT_LOGITS (nullable)
-  unsigned long long* amax_slot;
-  unsigned int* counter;
-  int32_t* amax_out;       // nullable
+  unsigned long long* amax_part;  // OUT_LOGITS: one argmax key per workgroup
   const int32_t* kv_state; // nullable: skip everything when state[3] != 0
 };
 
-hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s);
+// *grid_out (nullable) receives the number of workgroups launched.
+hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s, int* grid_out = nullptr);
 
 // q/k RMSNorm + RoPE for rows j < n at positions state[0] + j, append k, v to
-// the cache, write roped q to `q_out`; the last workgroup advances state[0]
-// (and state[1] if set_base).
+// the cache, write roped q to `q_out`.  state[0] is advanced later by k_finish.
 struct RopeArgs {
   const float* qkv;        // [rows, (Hq + 2 Hkv) * D]
   int ld_qkv;
@@ -78,8 +76,6 @@ struct RopeArgs {
   int32_t* state;
   int n_max;
   const int32_t* n_dev;
-  int set_base;
-  unsigned int* counter;
 };
 hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);
 
@@ -102,6 +98,20 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// End of a step or flush: merge the unembedding's per-workgroup argmax keys
+// (if any) into *amax_out and commit the append: state[0] += n (state[1] too
+// when set_base).  One workgroup.
+struct FinishArgs {
+  int32_t* state;
+  int n_max;
+  const int32_t* n_dev;
+  int set_base;
+  const unsigned long long* parts;  // nullable
+  int nparts;
+  int32_t* amax_out;                // nullable
+};
+hipError_t launch_finish(const FinishArgs& a, hipStream_t s);
+
 // Greedy verification (argmax match) with repetition penalty.
 struct VerifyArgs {
   int n_draft, vocab;
@@ -116,8 +126,7 @@ struct VerifyArgs {
   const float* uniforms;
   int32_t* out_tokens;
   int32_t* out_counts;
-  unsigned long long* slots;   // [n_draft + 1]
-  unsigned int* counter;
+  unsigned long long* parts;   // [n_draft + 1][blocks per row] argmax keys
   void* scratch;               // sampled path candidates
   int chunk;                   // elements per workgroup
 };

@@ -4,9 +4,9 @@
 // "draft i equals the argmax of target row i" (with the repetition penalty
 // applied to the row's window first).  Each row is split over many workgroups;
 // the window tokens that fall in a workgroup's id range are marked in an LDS
-// bitmap so the penalty costs one LDS read per logit.  Partial argmaxes meet in
-// one 64-bit atomicMax per (workgroup, row); the last workgroup resolves the
-// accepted count, writes the committed run and pushes it into the history ring.
+// bitmap so the penalty costs one LDS read per logit.  Every workgroup writes
+// its partial argmax key; a one-workgroup kernel merges them per row, resolves
+// the accepted count, writes the committed run and pushes it into the ring.
 #include "common.h"
 #include "kernels.h"
 
@@ -64,37 +64,42 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
   if (tid == 0) {
     unsigned long long b = s_best[0];
     for (int w = 1; w < kVThreads / 64; ++w) b = s_best[w] > b ? s_best[w] : b;
-    atomicMax(&a.slots[i], b);
+    a.parts[static_cast<size_t>(i) * gridDim.x + blockIdx.x] = b;
   }
-  if (last_block_ticket(a.counter, gridDim.x * gridDim.y) && tid == 0) {
-    const int n = a.n_draft;
-    int toks[MTP_MAX_DRAFT_DEV + 1];
-    int am[MTP_MAX_DRAFT_DEV + 1];
-    for (int r = 0; r <= n; ++r) am[r] = argmax_index(atomicExch(&a.slots[r], 0ull));
-    int k = n;
-    for (int r = 0; r < n; ++r) {
-      if (a.drafts[r] != am[r]) { k = r; break; }
-    }
-    for (int r = 0; r < k; ++r) toks[r] = a.drafts[r];
-    toks[k] = am[k];
-    for (int r = 0; r <= k; ++r) a.out_tokens[r] = toks[r];
-    a.out_counts[0] = k;
-    a.out_counts[1] = k + 1;
-    int h = head, c = count;
-    for (int r = 0; r <= k; ++r) {
-      a.ring[h] = toks[r];
-      h = (h + 1) % a.window;
-      c = c + 1 < a.window ? c + 1 : a.window;
-    }
-    a.ring_state[0] = h;
-    a.ring_state[1] = c;
+}
+
+__global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a, int nb) {
+  __shared__ int am[MTP_MAX_DRAFT_DEV + 1];
+  const int n = a.n_draft;
+  for (int r = 0; r <= n; ++r) {
+    const unsigned long long b = block_max_u64(a.parts + static_cast<size_t>(r) * nb, nb);
+    if (threadIdx.x == 0) am[r] = argmax_index(b);
   }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int k = n;
+  for (int r = 0; r < n; ++r) {
+    if (a.drafts[r] != am[r]) { k = r; break; }
+  }
+  int h = a.ring_state[0], c = a.ring_state[1];
+  for (int r = 0; r <= k; ++r) {
+    const int t = r < k ? a.drafts[r] : am[k];
+    a.out_tokens[r] = t;
+    a.ring[h] = t;
+    h = (h + 1) % a.window;
+    c = c + 1 < a.window ? c + 1 : a.window;
+  }
+  a.out_counts[0] = k;
+  a.out_counts[1] = k + 1;
+  a.ring_state[0] = h;
+  a.ring_state[1] = c;
 }
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
   const int nb = (a.vocab + a.chunk - 1) / a.chunk;
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_verify_greedy, dim3(nb, a.n_draft + 1), dim3(kVThreads), 0, s, a);
+  hipLaunchKernelGGL(k_verify_greedy_finish, dim3(1), dim3(kVThreads), 0, s, a, nb);
   return hipGetLastError();
 }
 

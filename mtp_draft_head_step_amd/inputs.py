@@ -281,7 +281,8 @@ def logits_rows(wl: int, stream: int, key, rows: int, vocab: int, std: float,
 
 def history_ring(wl: int, key, window: int, vocab: int):
     """A full ring of ``window`` uniform token ids (head 0, count window)."""
-    ring = tokens_uniform(wl, ("ring",) if key is None else key, window, vocab)
+    key = 0 if key is None else key
+    ring = tokens_uniform(wl, (77, key) if isinstance(key, int) else (77,) + tuple(key), window, vocab)
     return ring, np.array([0, window], dtype=np.int32)
 
 

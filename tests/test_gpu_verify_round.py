@@ -184,3 +184,82 @@ def test_rounds_match_oracle_and_classic(policy, n_draft, headkind):
     assert gpu_committed == R.classic_greedy(lambda tk, s: tgt.forward(tk, s), start, len(gpu_committed) - len(start))
     if headkind == "successor":
         assert max(ks) == N and min(ks) == 0
+
+
+def _round_session(shape, wl, n_draft, pool, cap):
+    from mtp_draft_head_step_amd import abi
+    st = I.head_weights(shape, wl)
+    gh = abi.Head(shape, st)
+    kp, vp = I.prefix_kv(shape, wl, 64, cap)
+    kv = abi.DraftKV(shape, cap, kp, vp, 64)
+    V, H, N = shape.vocab, shape.hidden, n_draft
+    dt = torch.bfloat16 if shape.act_dtype == I.BF16 else torch.float32
+    s = {
+        "gh": gh, "kv": kv,
+        "logits": device_array(np.stack([I.logits_rows(wl, 5, r, N + 1, V, 3.0)[0] for r in range(pool)])),
+        "hid": device_array(np.stack([I.target_hiddens(shape, wl, r, N + 1) for r in range(pool)])),
+        "io": torch.zeros(2 + N + 1, dtype=torch.int32, device="cuda"),
+        "d": torch.zeros(N, dtype=torch.int32, device="cuda"),
+        "g": torch.zeros((N, H), dtype=dt, device="cuda"),
+        "ring": torch.zeros(64, dtype=torch.int32, device="cuda"),
+        "ring_st": torch.zeros(2, dtype=torch.int32, device="cuda"),
+        "ws": abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, N + 1, cap)),
+        "vws": abi.Workspace(abi.spec_verify_workspace_bytes(N, V)),
+    }
+    s["io"][1] = 1
+    s["io"][2] = 5
+    return s
+
+
+def _enqueue(s, r, N, pool, stream):
+    from mtp_draft_head_step_amd import abi
+    io, d, g = s["io"], s["d"], s["g"]
+    abi.mtp_flush_pairs(s["gh"], s["kv"], io[2:], s["hid"][(r - 1) % pool], N + 1, io[1:2], abi.LAST, 1,
+                        g[0], None, d[0:1], s["ws"], stream)
+    for i in range(1, N):
+        abi.mtp_draft_step(s["gh"], s["kv"], d[i - 1:i], g[i - 1], g[i], None, d[i:i + 1], s["ws"], stream)
+    abi.spec_verify(abi.sampling(window=64), N, s["gh"].shape.vocab, s["logits"][r % pool], None, d,
+                    s["ring"], s["ring_st"], None, io[2:], io[0:2], s["vws"], stream)
+    abi.kv_rollback(s["kv"], abi.TO_ROUND_BASE, None, N, stream)
+
+
+@pytest.mark.parametrize("n_draft", [2, 3])
+def test_graph_replayed_rounds_equal_eager(n_draft):
+    """Rounds captured once into graphs and replayed many times (with eager work
+    and host syncs between replays) commit the same tokens and leave the same
+    draft KV as the same rounds launched eagerly."""
+    shape = I.TINY_BF16
+    pool, rounds, cap = 4, 12, 512
+    eager = _round_session(shape, 55, n_draft, pool, cap)
+    graph = _round_session(shape, 55, n_draft, pool, cap)
+    stream = torch.cuda.current_stream()
+    ref_tokens = []
+    for r in range(rounds):
+        _enqueue(eager, r, n_draft, pool, stream)
+        torch.cuda.synchronize()
+        io = host(eager["io"])
+        ref_tokens.append(io[2:2 + io[1]].tolist())
+    # capture one graph per pool slot, after one eager round on the graph session
+    _enqueue(graph, 0, n_draft, pool, stream)
+    torch.cuda.synchronize()
+    got = [host(graph["io"])[2:2 + host(graph["io"])[1]].tolist()]
+    cs = torch.cuda.Stream()
+    graphs = {}
+    for p in range(1, pool + 1):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cs):
+            _enqueue(graph, p, n_draft, pool, torch.cuda.current_stream())
+        graphs[p % pool] = gr
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 16, device="cuda")
+    for r in range(1, rounds):
+        graphs[r % pool].replay()
+        scratch.add_(1.0)                     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        io = host(graph["io"])
+        got.append(io[2:2 + io[1]].tolist())
+    assert got == ref_tokens
+    assert host(graph["kv"].state).tolist() == host(eager["kv"].state).tolist()
+    n = int(host(eager["kv"].state)[0])
+    assert torch.equal(graph["kv"].k[:, :n], eager["kv"].k[:, :n])
+    assert torch.equal(graph["kv"].v[:, :n], eager["kv"].v[:, :n])
