@@ -107,6 +107,9 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--cpu-rounds", type=int, default=1, help="oracle rounds for cpu_baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run three 1 GiB device-to-device copies (a plain copy kernel of known "
+                         "size, to scale HBM traffic counters)")
     ap.add_argument("--graph", action="store_true",
                     help="replay rounds from HIP graphs (no unembedding timing in this mode)")
     args = ap.parse_args()
@@ -225,6 +228,14 @@ def main():
     lm_ms, lm_n = (0.0, 0) if graphs is not None else abi.mtp_timing_end()
     log(f"timed {args.steps} rounds in {elapsed * 1e3:.1f} ms; unembedding {lm_n} launches")
     state = totals
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     rounds_s = args.steps / elapsed
     ms_step = elapsed / args.steps * 1e3

@@ -75,7 +75,8 @@ int nr_for(int rows) {
 }
 
 int kp_for(int K, int t, int nr) {
-  const int budget = 32768 / nr;  // 128 KB of fp32 in LDS
+  // 128 KB of staged inputs in LDS: fp32, or bf16 for few-row flushes with bf16 weights
+  const int budget = (nr > 1 && t == W_BF16 ? 65536 : 32768) / nr;
   if (K <= budget) return K;
   const int q = lpr_for(K, t) * epc_of(t);
   int kp = budget / q * q;

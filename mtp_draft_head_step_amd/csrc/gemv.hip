@@ -5,7 +5,8 @@
 //  * each weight row is split over `lpr` lanes; every lane issues 16-byte loads
 //    (8 bf16 / 4 fp32 / 16 int8) and a wave keeps RPW rows x UNROLL loads in
 //    flight before consuming them;
-//  * the activation rows (1..16) are staged once per workgroup in LDS as fp32,
+//  * the activation rows (1..16) are staged once per workgroup in LDS (fp32; bf16
+//    for few-row flushes with bf16 weights, which halves LDS and raises occupancy),
 //    with the producer's RMSNorm (or the embedding gather + twin RMSNorm of the
 //    pair) folded into the staging, so no separate norm kernel runs;
 //  * lanes of a row are reduced with xor shuffles, in a fixed order (no float
@@ -16,6 +17,8 @@
 //  * no workgroup waits for or signals another: on gfx950 a device-scope fence
 //    writes back and invalidates the XCD's L2, which costs far more than the
 //    extra one-workgroup kernel that merges the partial keys.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -63,6 +66,19 @@ __device__ __forceinline__ float dot_chunk(const uint4& w, const float* __restri
   return s;
 }
 
+// 16 bytes of bf16 weights times 8 bf16 inputs staged in LDS.
+__device__ __forceinline__ float dot_chunk_bb(const uint4& w, const uint16_t* __restrict__ xp) {
+  const uint4 x = *reinterpret_cast<const uint4*>(xp);
+  return __uint_as_float(w.x << 16) * __uint_as_float(x.x << 16) +
+         __uint_as_float(w.x & 0xFFFF0000u) * __uint_as_float(x.x & 0xFFFF0000u) +
+         __uint_as_float(w.y << 16) * __uint_as_float(x.y << 16) +
+         __uint_as_float(w.y & 0xFFFF0000u) * __uint_as_float(x.y & 0xFFFF0000u) +
+         __uint_as_float(w.z << 16) * __uint_as_float(x.z << 16) +
+         __uint_as_float(w.z & 0xFFFF0000u) * __uint_as_float(x.z & 0xFFFF0000u) +
+         __uint_as_float(w.w << 16) * __uint_as_float(x.w << 16) +
+         __uint_as_float(w.w & 0xFFFF0000u) * __uint_as_float(x.w & 0xFFFF0000u);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // 4 consecutive elements (bf16 or fp32) as fp32.
@@ -78,7 +94,8 @@ __device__ __forceinline__ float4 load4(const void* p, size_t i, int bf16) {
 // Stage dst[k - k0] = src[off + k] * nw[noff + k] (nw may be null: factor 1)
 // for k in [kb, ke), 4 values per thread per step and up to 8 steps of loads in
 // flight, and add the sum of squares of the src values to ss.
-__device__ __forceinline__ void stage_range(float* dst, const void* src, long long off, int src_bf16,
+template <bool XB>
+__device__ __forceinline__ void stage_range(void* dst, const void* src, long long off, int src_bf16,
                                             const void* nw, long long noff, int nw_bf16, int kb, int ke,
                                             int k0, float& ss) {
   constexpr int kB = 8;
@@ -98,7 +115,14 @@ __device__ __forceinline__ void stage_range(float* dst, const void* src, long lo
       if (k < ke) {
         const float4 x = xv[u], w = wv[u];
         ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-        *reinterpret_cast<float4*>(dst + (k - k0)) = make_float4(x.x * w.x, x.y * w.y, x.z * w.z, x.w * w.w);
+        if constexpr (XB) {
+          const uint32_t lo = f32_to_bf16(x.x * w.x) | (static_cast<uint32_t>(f32_to_bf16(x.y * w.y)) << 16);
+          const uint32_t hi = f32_to_bf16(x.z * w.z) | (static_cast<uint32_t>(f32_to_bf16(x.w * w.w)) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + (k - k0)) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(dst) + (k - k0)) =
+              make_float4(x.x * w.x, x.y * w.y, x.z * w.z, x.w * w.w);
+        }
       }
     }
   }
@@ -122,10 +146,10 @@ __device__ __forceinline__ void gemv_load(uint4 (&w)[RPW][U], const char* const 
       w[s][u] = *reinterpret_cast<const uint4*>(lane_row[s] + static_cast<size_t>(j + u) * stride);
 }
 
-template <int WT, int NR, int RPW, int U, bool TWO>
+template <int WT, int NR, int RPW, int U, bool TWO, bool XB>
 __device__ __forceinline__ void gemv_fma(float (&acc)[RPW][NR], float (&acc2)[RPW][NR],
                                          const uint4 (&w)[RPW][U], int j, int lpr,
-                                         const float* __restrict__ xl, int kp,
+                                         const void* __restrict__ xl, int kp,
                                          const uint16_t* const (&srow)[RPW], int g0, int split) {
   constexpr int EPC = WTraits<WT>::EPC;
   float scl[RPW][U];
@@ -143,10 +167,15 @@ __device__ __forceinline__ void gemv_fma(float (&acc)[RPW][NR], float (&acc2)[RP
     for (int s = 0; s < RPW; ++s)
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        float d = dot_chunk<WT>(w[s][u], xl + r * kp + (j + u) * lpr * EPC);
+        float d;
+        if constexpr (XB)
+          d = dot_chunk_bb(w[s][u], static_cast<const uint16_t*>(xl) + r * kp + (j + u) * lpr * EPC);
+        else
+          d = dot_chunk<WT>(w[s][u], static_cast<const float*>(xl) + r * kp + (j + u) * lpr * EPC);
         if constexpr (WT == W_I8) d *= scl[s][u];
-        if constexpr (TWO) {
-          if (second) acc2[s][r] += d; else acc[s][r] += d;
+        if constexpr (TWO) {          // value selects: both arrays stay in registers
+          acc[s][r] += second ? 0.f : d;
+          acc2[s][r] += second ? d : 0.f;
         } else {
           acc[s][r] += d;
         }
@@ -154,14 +183,14 @@ __device__ __forceinline__ void gemv_fma(float (&acc)[RPW][NR], float (&acc2)[RP
   }
 }
 
-template <int WT, int NR, int RPW, int U, bool TWO>
+template <int WT, int NR, int RPW, int U, bool TWO, bool XB>
 __device__ __forceinline__ void gemv_body(float (&acc)[RPW][NR], float (&acc2)[RPW][NR],
                                           const char* const (&lane_row)[RPW], int j, int lpr,
-                                          const float* __restrict__ xl, int kp,
+                                          const void* __restrict__ xl, int kp,
                                           const uint16_t* const (&srow)[RPW], int g0, int split) {
   uint4 w[RPW][U];
   gemv_load<RPW, U>(w, lane_row, j, lpr);
-  gemv_fma<WT, NR, RPW, U, TWO>(acc, acc2, w, j, lpr, xl, kp, srow, g0, split);
+  gemv_fma<WT, NR, RPW, U, TWO, XB>(acc, acc2, w, j, lpr, xl, kp, srow, g0, split);
 }
 
 // Row slot s of row block blk: the weight row pointer (rows past the end read
@@ -193,9 +222,12 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int blk, int rows_p
   }
 }
 
-template <int WT, int NR, int RPW, bool TWO>
+template <int WT, int NR, int RPW, bool TWO, bool XB>
 __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
-  extern __shared__ float xs[];  // [NR][kp]
+  // staged inputs [NR][kp]: fp32, or bf16 when XB (few-row flushes with bf16 weights)
+  extern __shared__ float xs_f[];
+  using XT = typename std::conditional<XB, uint16_t, float>::type;
+  XT* xs = reinterpret_cast<XT*>(xs_f);
   __shared__ float s_red[kWaves][2 * NR];
   __shared__ float s_inv[2 * NR];
   __shared__ unsigned long long s_best[kWaves];
@@ -267,27 +299,28 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          float* dst = xs + r * a.kp;
-          if (r >= nrows) {
-            for (int k = tid * 4; k < klen; k += kThreads * 4)
-              *reinterpret_cast<float4*>(dst + k) = make_float4(0.f, 0.f, 0.f, 0.f);
-            continue;
-          }
-          const int jr = j0 + r;
-          const void* nw = (a.in_mode == IN_RMS) ? a.nw : nullptr;
-          if (a.in_mode != IN_EMBED) {
-            stage_range(dst, a.x, static_cast<long long>(jr) * a.ldx, 0, nw, 0, a.nw_bf16, k0,
-                        k0 + klen, k0, ss[2 * r]);
+          XT* dst = xs + r * a.kp;
+          float se = 0.f, sh = 0.f;   // sums of squares: whole input / hidden half
+          if (r < nrows) {
+            const int jr = j0 + r;
+            if (a.in_mode != IN_EMBED) {
+              stage_range<XB>(dst, a.x, static_cast<long long>(jr) * a.ldx, 0,
+                          (a.in_mode == IN_RMS) ? a.nw : nullptr, 0, a.nw_bf16, k0, k0 + klen, k0, se);
+            } else {
+              const int ea = k0, eb = min(k0 + klen, half);
+              if (ea < eb)
+                stage_range<XB>(dst, a.embed, static_cast<long long>(a.tok[jr]) * half, a.embed_bf16, a.nw, 0,
+                            a.nw_bf16, ea, eb, k0, se);
+              const int ha = max(k0, half), hb = k0 + klen;
+              if (ha < hb)
+                stage_range<XB>(dst, a.hid, static_cast<long long>(jr) * a.ld_hid - half, a.hid_bf16, a.nw2,
+                            -static_cast<long long>(half), a.nw_bf16, ha, hb, k0, sh);
+            }
           } else {
-            const int ea = k0, eb = min(k0 + klen, half);
-            if (ea < eb)
-              stage_range(dst, a.embed, static_cast<long long>(a.tok[jr]) * half, a.embed_bf16, a.nw, 0,
-                          a.nw_bf16, ea, eb, k0, ss[2 * r]);
-            const int ha = max(k0, half), hb = k0 + klen;
-            if (ha < hb)
-              stage_range(dst, a.hid, static_cast<long long>(jr) * a.ld_hid - half, a.hid_bf16, a.nw2,
-                          -static_cast<long long>(half), a.nw_bf16, ha, hb, k0, ss[2 * r + 1]);
+            for (int k = tid; k < klen; k += kThreads) dst[k] = XT(0);
           }
+          ss[2 * r] += se;
+          ss[2 * r + 1] += sh;
         }
         __syncthreads();
       }
@@ -297,15 +330,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       const char* lane_row[RPW];
 #pragma unroll
       for (int s = 0; s < RPW; ++s) lane_row[s] = rowp[s] + (static_cast<size_t>(k0 / EPC) + li) * 16;
-      const float* xl = xs + li * EPC;
+      const XT* xl = xs + li * EPC;
       const int g0 = (k0 / EPC) + li;   // chunk index of j = 0 (int8 scale groups)
       int j = 0;
       for (; j + kUnroll <= cpl; j += kUnroll)
-        gemv_body<WT, NR, RPW, kUnroll, TWO>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
+        gemv_body<WT, NR, RPW, kUnroll, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
       for (; j + 2 <= cpl; j += 2)
-        gemv_body<WT, NR, RPW, 2, TWO>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
+        gemv_body<WT, NR, RPW, 2, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
       for (; j < cpl; ++j)
-        gemv_body<WT, NR, RPW, 1, TWO>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
+        gemv_body<WT, NR, RPW, 1, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
     }
 
     // ---- the inverse RMS of each activation row (once, after the first block)
@@ -405,12 +438,13 @@ GemvTuning g_gemv_tuning;
 
 template <int WT, int NR, int RPW, bool TWO>
 static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int max_per_cu) {
+  constexpr bool XB = NR > 1 && WT == W_BF16;
   GemvArgs a = a0;
   if (a.out_mode == OUT_SWIGLU && RPW < 2) return hipErrorInvalidValue;
   const int rps = kWave / a.lpr;
   const int rows_per_wg = kWaves * ((a.out_mode == OUT_SWIGLU) ? RPW / 2 : RPW) * rps;
   const int nblocks = (a.M + rows_per_wg - 1) / rows_per_wg;
-  const size_t lds = static_cast<size_t>(NR) * a.kp * sizeof(float);
+  const size_t lds = static_cast<size_t>(NR) * a.kp * (XB ? 2 : 4);
   int grid = nblocks;
   if (a.grid_stride) {
     int occ = static_cast<int>((160 * 1024) / (lds + 2048));
@@ -423,14 +457,14 @@ static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int
   if (lds > 64 * 1024) {   // gfx950 gives a workgroup up to 160 KB of LDS on request
     static bool raised = false;
     if (!raised) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO>),
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO, XB>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
   (void)hipGetLastError();
-  hipLaunchKernelGGL((k_gemv<WT, NR, RPW, TWO>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((k_gemv<WT, NR, RPW, TWO, XB>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
