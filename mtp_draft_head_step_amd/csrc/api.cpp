@@ -413,7 +413,7 @@ int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
   const bool greedy = sp->temperature == 0.f;
   if (greedy != (draft_logits_dev == nullptr) && n_draft > 0) return MTP_E_INVALID_ARG;
   if (!greedy && !uniforms_dev) return MTP_E_INVALID_ARG;
-  if (!greedy && sp->top_p < 1.f && (sp->top_k < 1 || sp->top_k > 1024)) return MTP_E_UNSUPPORTED;
+  if (!greedy && !verify_sampled_supported(sp->top_k, vocab)) return MTP_E_UNSUPPORTED;
   VerifyArgs a;
   std::memset(&a, 0, sizeof(a));
   a.n_draft = n_draft; a.vocab = vocab;

@@ -103,14 +103,281 @@ hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Sampled verification (temperature > 0): Leviathan/Chen rejection sampling
+// over transformed rows.  Rows 0..N are the target rows, N+1..2N the draft rows.
+//  A. k_sample_chunk  (chunks x rows): a chunk's logits are penalised (window of
+//     its row), divided by the temperature, turned into 64-bit keys (value desc,
+//     id asc) and bitonic-sorted in LDS; the chunk's best kk keys are kept.
+//  B. k_sample_row    (rows): the row's candidates are merged (bitonic sort in
+//     LDS), the top-k is exact; softmax over it, top-p prefix, min-p cut,
+//     renormalise; the support is written sorted by token id.
+//  C. k_sample_decide (1 thread): accept d_i iff u_i q_i(d_i) < p_i(d_i); at the
+//     first rejection draw from normalise(max(0, p - q)) (p if that is zero) with
+//     u_N by inverse CDF in ascending id; else the bonus from p_N; ring push.
+constexpr int kSChunk = 4096;      // logits per phase-A workgroup
+constexpr int kSMaxCand = 8192;    // phase-B merge capacity (keys)
+constexpr int kSMaxTopK = 256;     // largest supported top_k
+
+struct SampledScratch {
+  unsigned long long* cand;  // [rows][nb * kk]
+  int* cnt;                  // [rows]
+  int* ids;                  // [rows][kSMaxTopK]
+  float* probs;              // [rows][kSMaxTopK]
+};
+
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+__host__ __device__ inline SampledScratch sampled_scratch(void* base, int n_draft, int vocab) {
+  const int rows = 2 * n_draft + 1;
+  const int nb = (vocab + kSChunk - 1) / kSChunk;
+  char* p = static_cast<char*>(base);
+  SampledScratch s;
+  s.cand = reinterpret_cast<unsigned long long*>(p);
+  p += align256(static_cast<size_t>(rows) * nb * kSMaxTopK * 8);
+  s.cnt = reinterpret_cast<int*>(p);
+  p += align256(static_cast<size_t>(rows) * 4);
+  s.ids = reinterpret_cast<int*>(p);
+  p += align256(static_cast<size_t>(rows) * kSMaxTopK * 4);
+  s.probs = reinterpret_cast<float*>(p);
+  return s;
+}
+
 size_t verify_sampled_scratch_bytes(int n_draft, int vocab, int chunk) {
-  (void)n_draft; (void)vocab; (void)chunk;
-  return 0;
+  (void)chunk;
+  const int rows = 2 * n_draft + 1;
+  const size_t nb = (static_cast<size_t>(vocab) + kSChunk - 1) / kSChunk;
+  return align256(rows * nb * kSMaxTopK * 8) + align256(rows * 4ull) + 2 * align256(rows * kSMaxTopK * 4ull) + 256;
+}
+
+// Descending bitonic sort of n (a power of two) keys in LDS by the workgroup.
+__device__ void bitonic_desc(unsigned long long* s, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < (n >> 1); t += blockDim.x) {
+        const int i = 2 * t - (t & (stride - 1));
+        const int j = i + stride;
+        const bool desc = (i & size) == 0;
+        const unsigned long long x = s[i], y = s[j];
+        if ((x < y) == desc) { s[i] = y; s[j] = x; }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ float key_value(unsigned long long key) {
+  const uint32_t k = static_cast<uint32_t>(key >> 32);
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+__global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, SampledScratch sc, int nb, int kk) {
+  __shared__ unsigned long long keys[kSChunk];
+  __shared__ uint32_t bits[kSChunk / 32];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int n = a.n_draft;
+  const bool draft = row > n;
+  const int i = draft ? row - (n + 1) : row;            // window index of the row
+  const float* src = (draft ? a.draft : a.target) + static_cast<size_t>(i) * a.vocab;
+  const int lo = blockIdx.x * kSChunk;
+  const int hi = min(a.vocab, lo + kSChunk);
+  const bool pen = a.penalty != 1.0f;
+  if (pen) {
+    const int head = a.ring_state[0], count = a.ring_state[1];
+    for (int w = tid; w < kSChunk / 32; w += kVThreads) bits[w] = 0u;
+    __syncthreads();
+    const int total = count + i;
+    const int start = total > a.window ? total - a.window : 0;
+    for (int t = start + tid; t < total; t += kVThreads) {
+      const int tok = window_token(a.ring, head, count, a.window, a.drafts, t);
+      if (tok >= lo && tok < hi) atomicOr(&bits[(tok - lo) >> 5], 1u << ((tok - lo) & 31));
+    }
+    __syncthreads();
+  }
+  for (int t = tid; t < kSChunk; t += kVThreads) {
+    const int k = lo + t;
+    unsigned long long key = 0ull;                      // below every real key
+    if (k < hi) {
+      float v = src[k];
+      if (pen && ((bits[t >> 5] >> (t & 31)) & 1u)) v = penalise(v, a.penalty);
+      key = argmax_key(v / a.temperature, static_cast<uint32_t>(k));
+    }
+    keys[t] = key;
+  }
+  __syncthreads();
+  bitonic_desc(keys, kSChunk);
+  unsigned long long* out = sc.cand + (static_cast<size_t>(row) * nb + blockIdx.x) * kk;
+  for (int t = tid; t < kk; t += kVThreads) out[t] = keys[t];
+}
+
+__global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledScratch sc, int nb, int kk,
+                                                         int n2, int topk) {
+  extern __shared__ unsigned long long s[];             // n2 keys
+  __shared__ float sp[kSMaxTopK];
+  __shared__ int s_keep;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int ncand = nb * kk;
+  const unsigned long long* cand = sc.cand + static_cast<size_t>(row) * ncand;
+  for (int t = tid; t < n2; t += kVThreads) s[t] = t < ncand ? cand[t] : 0ull;
+  __syncthreads();
+  bitonic_desc(s, n2);
+  if (tid == 0) {
+    int nv = 0;
+    while (nv < topk && nv < n2 && s[nv] != 0ull) ++nv;  // exact top-k (fewer if the row is shorter)
+    const float y0 = key_value(s[0]);
+    float total = 0.f;
+    for (int j = 0; j < nv; ++j) {
+      sp[j] = expf(key_value(s[j]) - y0);
+      total += sp[j];
+    }
+    int keep = nv;
+    if (a.top_p < 1.0f) {
+      const float target = a.top_p * total;
+      float c = 0.f;
+      for (int j = 0; j < nv; ++j) {
+        c += sp[j];
+        if (c >= target) { keep = j + 1; break; }
+      }
+    }
+    if (a.min_p > 0.0f) {
+      int m = 0;
+      while (m < keep && (key_value(s[m]) - y0) >= a.ln_min_p) ++m;
+      keep = m < keep ? m : keep;
+    }
+    float z = 0.f;
+    for (int j = 0; j < keep; ++j) z += sp[j];
+    const float inv = 1.0f / z;
+    for (int j = 0; j < keep; ++j) sp[j] *= inv;
+    s_keep = keep;
+  }
+  __syncthreads();
+  const int keep = s_keep;
+  // re-key the kept entries by token id (ascending) with their probability bits
+  int k2 = 1;
+  while (k2 < keep) k2 <<= 1;
+  unsigned long long mine[kSMaxTopK / kVThreads + 1];
+  int c = 0;
+  for (int j = tid; j < k2; j += kVThreads) {
+    unsigned long long v = ~0ull;                       // sorts after every real entry
+    if (j < keep) {
+      const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s[j]);
+      v = (static_cast<unsigned long long>(id) << 32) | __float_as_uint(sp[j]);
+    }
+    mine[c++] = v;
+  }
+  __syncthreads();
+  c = 0;
+  for (int j = tid; j < k2; j += kVThreads) s[j] = ~mine[c++];   // descending of ~v = ascending of v
+  __syncthreads();
+  bitonic_desc(s, k2);
+  for (int j = tid; j < keep; j += kVThreads) {
+    const unsigned long long v = ~s[j];
+    sc.ids[static_cast<size_t>(row) * kSMaxTopK + j] = static_cast<int>(v >> 32);
+    sc.probs[static_cast<size_t>(row) * kSMaxTopK + j] = __uint_as_float(static_cast<uint32_t>(v));
+  }
+  if (tid == 0) sc.cnt[row] = keep;
+}
+
+__device__ float prob_in(const SampledScratch& sc, int row, int tok) {
+  const int* ids = sc.ids + static_cast<size_t>(row) * kSMaxTopK;
+  int lo = 0, hi = sc.cnt[row];
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ids[mid] < tok) lo = mid + 1; else hi = mid;
+  }
+  return (lo < sc.cnt[row] && ids[lo] == tok) ? sc.probs[static_cast<size_t>(row) * kSMaxTopK + lo] : 0.f;
+}
+
+// Inverse CDF over the ascending-id union of rows ra and rb with weight
+// max(0, p_a - p_b) (rb < 0: weight p_a): first id whose running sum exceeds
+// u * total; the last positive-weight id if none does.  Returns -1 if total is 0.
+__device__ int draw(const SampledScratch& sc, int ra, int rb, float u) {
+  const int* ia = sc.ids + static_cast<size_t>(ra) * kSMaxTopK;
+  const float* pa = sc.probs + static_cast<size_t>(ra) * kSMaxTopK;
+  const int na = sc.cnt[ra];
+  const int* ib = rb >= 0 ? sc.ids + static_cast<size_t>(rb) * kSMaxTopK : nullptr;
+  const float* pb = rb >= 0 ? sc.probs + static_cast<size_t>(rb) * kSMaxTopK : nullptr;
+  const int nbb = rb >= 0 ? sc.cnt[rb] : 0;
+  // tokens only in row b have weight max(0, 0 - q) = 0: walk row a's ids only
+  float total = 0.f;
+  for (int x = 0, y = 0; x < na; ++x) {
+    while (y < nbb && ib[y] < ia[x]) ++y;
+    const float q = (y < nbb && ib[y] == ia[x]) ? pb[y] : 0.f;
+    total += fmaxf(pa[x] - q, 0.f);
+  }
+  if (!(total > 0.f)) return -1;
+  const float t = u * total;
+  float cum = 0.f;
+  int last = -1;
+  for (int x = 0, y = 0; x < na; ++x) {
+    while (y < nbb && ib[y] < ia[x]) ++y;
+    const float q = (y < nbb && ib[y] == ia[x]) ? pb[y] : 0.f;
+    const float w = fmaxf(pa[x] - q, 0.f);
+    cum += w;
+    if (w > 0.f) last = ia[x];
+    if (t < cum) return ia[x];
+  }
+  return last;
+}
+
+__global__ void k_sample_decide(VerifyArgs a, SampledScratch sc) {
+  if (threadIdx.x != 0) return;
+  const int n = a.n_draft;
+  int k = n, tok = -1;
+  for (int i = 0; i < n; ++i) {
+    const int d = a.drafts[i];
+    const float p = prob_in(sc, i, d);
+    const float q = prob_in(sc, n + 1 + i, d);
+    if (a.uniforms[i] * q < p) continue;
+    k = i;
+    tok = draw(sc, i, n + 1 + i, a.uniforms[n]);
+    if (tok < 0) tok = draw(sc, i, -1, a.uniforms[n]);
+    break;
+  }
+  if (k == n) tok = draw(sc, n, -1, a.uniforms[n]);
+  int h = a.ring_state[0], c = a.ring_state[1];
+  for (int r = 0; r <= k; ++r) {
+    const int t = r < k ? a.drafts[r] : tok;
+    a.out_tokens[r] = t;
+    a.ring[h] = t;
+    h = (h + 1) % a.window;
+    c = c + 1 < a.window ? c + 1 : a.window;
+  }
+  a.out_counts[0] = k;
+  a.out_counts[1] = k + 1;
+  a.ring_state[0] = h;
+  a.ring_state[1] = c;
+}
+
+bool verify_sampled_supported(int top_k, int vocab) {
+  const int nb = (vocab + kSChunk - 1) / kSChunk;
+  return top_k >= 1 && top_k <= kSMaxTopK && static_cast<long>(nb) * (top_k < kSChunk ? top_k : kSChunk) <= kSMaxCand;
 }
 
 hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
-  (void)a; (void)s;
-  return hipErrorNotSupported;
+  if (!verify_sampled_supported(a.top_k, a.vocab)) return hipErrorNotSupported;
+  const int rows = 2 * a.n_draft + 1;
+  const int nb = (a.vocab + kSChunk - 1) / kSChunk;
+  const int kk = a.top_k < kSChunk ? a.top_k : kSChunk;
+  int n2 = 1;
+  while (n2 < nb * kk) n2 <<= 1;
+  const SampledScratch sc = sampled_scratch(a.scratch, a.n_draft, a.vocab);
+  static bool raised = false;   // the merge stage may use 64 KB of keys plus its own LDS
+  if (!raised) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sample_row),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_sample_chunk, dim3(nb, rows), dim3(kVThreads), 0, s, a, sc, nb, kk);
+  hipLaunchKernelGGL(k_sample_row, dim3(rows), dim3(kVThreads), static_cast<size_t>(n2) * 8, s, a, sc, nb, kk,
+                     n2, a.top_k);
+  hipLaunchKernelGGL(k_sample_decide, dim3(1), dim3(64), 0, s, a, sc);
+  return hipGetLastError();
 }
 
 }  // namespace mtp

@@ -81,8 +81,10 @@ def ring_push(ring, state, tokens):
 
 
 def window_for_row(history, drafts, i, window):
+    """The last ``window`` tokens of history ++ d_0..d_{i-1} (all of them when
+    there are fewer)."""
     seq = list(history) + [int(t) for t in drafts[:i]]
-    return seq[len(seq) - window:] if window > 0 else []
+    return seq[max(0, len(seq) - window):] if window > 0 else []
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,125 @@
+"""GPU parity of sampled verification (temperature > 0) against the oracle.
+
+Given identical inputs, k and the committed tokens must be equal; the oracle
+reports the smallest decision margin on the path it took (top-p crossing,
+accept test, inverse-CDF step), and rounds whose margin is below 1e-4 are fp32
+vs fp64 boundary cases where either outcome is correct: there the GPU result
+must still be a valid outcome (its tokens in the right supports)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mtp_draft_head_step_amd import inputs as I
+from oracle import verify as OV
+from tests.gpu_util import device_array, host
+
+pytestmark = pytest.mark.gpu
+MARGIN = 1e-4
+
+
+def gpu_verify(sp, rows, drows, drafts, ring, ring_state, u, ws=None):
+    from mtp_draft_head_step_amd import abi
+    n = len(drafts)
+    v = rows.shape[1]
+    ws = ws or abi.Workspace(abi.spec_verify_workspace_bytes(n, v))
+    t_ring = device_array(ring.astype(np.int32))
+    t_st = device_array(ring_state.astype(np.int32))
+    out_t = torch.full((n + 1,), -1, dtype=torch.int32, device="cuda")
+    out_c = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    abi.spec_verify(sp, n, v, device_array(rows.astype(np.float32)), device_array(drows.astype(np.float32))
+                    if n else None, device_array(np.asarray(drafts, np.int32)) if n else None, t_ring, t_st,
+                    device_array(np.asarray(u, np.float32)), out_t, out_c, ws)
+    torch.cuda.synchronize()
+    k = int(host(out_c)[0])
+    return {"k": k, "count": int(host(out_c)[1]), "tokens": host(out_t)[: k + 1].tolist(),
+            "ring": host(t_ring), "state": host(t_st)}
+
+
+def draft_tokens(sp_o, drows, ring, st, key, vocab):
+    """d_i drawn from q_i (the draft row's transform, window history ++ d_<i)."""
+    r = np.random.default_rng(key)
+    d = []
+    for i in range(drows.shape[0]):
+        d.append(OV.sample(sp_o, drows[i], ring, st, r.random(), prefix=d))
+    return d
+
+
+def check(sp_o, sp_g, rows, drows, d, ring, st, u):
+    ref = OV.verify(sp_o, rows, drows, d, ring, st, u)
+    got = gpu_verify(sp_g, rows, drows, d, ring, st, u)
+    if ref["margin"] < MARGIN:
+        return ref, got, True
+    assert got["k"] == ref["k"], (got, ref["k"], ref["tokens"])
+    assert got["tokens"] == ref["tokens"]
+    assert np.array_equal(got["ring"], ref["ring"]) and np.array_equal(got["state"], ref["state"])
+    return ref, got, False
+
+
+@pytest.mark.parametrize("coverage", [False, True])
+def test_verify_workload_parity(coverage):
+    """The verification workload: N = 4, V = 152064, target rows N(0,4) with 3
+    spikes of +12, draft rows N(0,4) (coverage: sharing the target's spikes),
+    T 0.7, penalty 1.1 over a 64-token ring, top-k 40, top-p 0.9, min-p 0.05."""
+    from mtp_draft_head_step_amd import abi
+    wl, n, v = I.WL_VERIFY, 4, 152064
+    sp_o = OV.Sampling(temperature=0.7, repeat_penalty=1.1, top_k=40, top_p=0.9, min_p=0.05, window=64)
+    sp_g = abi.sampling(0.7, 1.1, 40, 0.9, 0.05, 64)
+    flagged, ks = 0, []
+    for rnd in range(12):
+        rows, pos = I.logits_rows(wl, 5, rnd, n + 1, v, 4.0, spikes=3, spike=12.0)
+        drows, _ = I.logits_rows(wl, 6, rnd, n, v, 4.0, spikes=3 if coverage else 0, spike=12.0,
+                                 spike_positions=pos[:n] if coverage else None)
+        ring, st = I.history_ring(wl, rnd, 64, v)
+        d = draft_tokens(sp_o, drows, ring, st, [wl, 10, rnd], v)
+        u = I.uniforms(wl, rnd, n + 1)
+        ref, got, near = check(sp_o, sp_g, rows, drows, d, ring, st, u)
+        flagged += near
+        ks.append(ref["k"])
+    assert flagged <= 1
+    if coverage:
+        assert max(ks) >= 1          # the accept paths ran
+
+
+@pytest.mark.parametrize("vocab", [7, 300, 4097, 20000])
+@pytest.mark.parametrize("params", [
+    dict(temperature=1.0, repeat_penalty=1.0, top_k=3, top_p=1.0, min_p=0.0),
+    dict(temperature=0.5, repeat_penalty=1.3, top_k=1, top_p=1.0, min_p=0.0),
+    dict(temperature=1.5, repeat_penalty=1.0, top_k=256, top_p=0.5, min_p=0.0),
+    dict(temperature=0.8, repeat_penalty=0.8, top_k=40, top_p=0.95, min_p=0.3),
+    dict(temperature=1.0, repeat_penalty=1.2, top_k=16, top_p=0.9, min_p=0.05),
+])
+@pytest.mark.parametrize("n", [0, 1, 3])
+def test_sampled_parity_sweep(vocab, params, n):
+    from mtp_draft_head_step_amd import abi
+    if vocab < params["top_k"] and vocab > 7:
+        pytest.skip("top_k larger than the vocabulary is covered at vocab 7")
+    sp_o = OV.Sampling(window=16, **params)
+    sp_g = abi.sampling(params["temperature"], params["repeat_penalty"], params["top_k"], params["top_p"],
+                        params["min_p"], 16)
+    rng = np.random.default_rng([vocab, n, params["top_k"]])
+    flagged = 0
+    for rnd in range(6):
+        base = rng.standard_normal((n + 1, vocab)).astype(np.float32) * 2
+        drows = (base[:n] + 0.7 * rng.standard_normal((n, vocab))).astype(np.float32)
+        ring = rng.integers(0, vocab, 16).astype(np.int32)
+        st = np.array([int(rng.integers(0, 16)), int(rng.integers(0, 17))], np.int32)
+        d = draft_tokens(sp_o, drows, ring, st, [vocab, n, rnd], vocab) if n else []
+        u = rng.random(n + 1).astype(np.float32)
+        _, _, near = check(sp_o, sp_g, base, drows if n else np.zeros((0, vocab), np.float32), d, ring, st, u)
+        flagged += near
+    assert flagged <= 1
+
+
+def test_identical_rows_always_accept():
+    """q = p: every draft is accepted (u q < p iff u < 1) and the bonus comes from p_N."""
+    from mtp_draft_head_step_amd import abi
+    rng = np.random.default_rng(3)
+    v, n = 5000, 3
+    rows = (rng.standard_normal((n + 1, v)) * 2).astype(np.float32)
+    sp_o = OV.Sampling(temperature=0.9, top_k=20, window=8)
+    ring, st = np.zeros(8, np.int32), np.array([0, 0], np.int32)
+    d = draft_tokens(sp_o, rows[:n], ring, st, [5], v)
+    got = gpu_verify(abi.sampling(0.9, 1.0, 20, 1.0, 0.0, 8), rows, rows[:n], d, ring, st,
+                     rng.random(n + 1).astype(np.float32))
+    assert got["k"] == n and got["tokens"][:n] == d
