@@ -90,16 +90,19 @@ def test_greedy_penalty_window_includes_drafts():
 
 def test_window_shorter_history_penalises_all():
     """A ring holding fewer tokens than the window penalises every token it
-    holds (hand example: 3 tokens in a window of 8, plus one draft)."""
+    holds (hand examples with 3 and 6 tokens in a window of 8)."""
     ring = np.array([4, 2, 0, 0, 0, 0, 0, 0], np.int32)
     st = np.array([2, 2], np.int32)                          # holds 4, 2
     assert Vf.window_for_row(Vf.ring_tokens(ring, st), [7, 9], 1, 8) == [4, 2, 7]
     assert Vf.window_for_row([1, 2, 3, 4, 5], [6], 1, 4) == [3, 4, 5, 6]
-    x = np.array([1.0, 1.0, 2.0, 1.0, 2.0, 1.0, 1.0, 1.5], np.float32)
-    # tokens 2 and 4 (value 2) are penalised to 1.0, token 7 (1.5) wins
-    rows = np.stack([x, x])
-    r = Vf.verify(Sampling(repeat_penalty=2.0, window=8), rows, None, [7], ring, st)
-    assert r["tokens"][0] == 7
+    ring6 = np.array([4, 2, 5, 3, 6, 1, 0, 0], np.int32)
+    st6 = np.array([6, 6], np.int32)                         # holds 4, 2, 5, 3, 6, 1 (oldest first)
+    assert Vf.window_for_row(Vf.ring_tokens(ring6, st6), [], 0, 8) == [4, 2, 5, 3, 6, 1]
+    # token 4 (oldest in the ring, value 2.0) is penalised to 1.0, so token 8 (1.5) wins
+    x = np.ones((1, 10), np.float32)
+    x[0, 4], x[0, 8] = 2.0, 1.5
+    r = Vf.verify(Sampling(repeat_penalty=2.0, window=8), x, None, [], ring6, st6)
+    assert r["tokens"] == [8]
 
 
 def test_ring_wraps():
