@@ -2,7 +2,7 @@
 
 Given identical inputs, k and the committed tokens must be equal; the oracle
 reports the smallest decision margin on the path it took (top-p crossing,
-accept test, inverse-CDF step), and rounds whose margin is below 1e-4 are fp32
+accept test, inverse-CDF step), and rounds whose margin is below 2e-5 are fp32
 vs fp64 boundary cases where either outcome is correct: there the GPU result
 must still be a valid outcome (its tokens in the right supports)."""
 import numpy as np
@@ -15,7 +15,7 @@ from oracle import verify as OV
 from tests.gpu_util import device_array, host
 
 pytestmark = pytest.mark.gpu
-MARGIN = 1e-4
+MARGIN = 2e-5
 
 
 def gpu_verify(sp, rows, drows, drafts, ring, ring_state, u, ws=None):
@@ -49,6 +49,9 @@ def check(sp_o, sp_g, rows, drows, d, ring, st, u):
     ref = OV.verify(sp_o, rows, drows, d, ring, st, u)
     got = gpu_verify(sp_g, rows, drows, d, ring, st, u)
     if ref["margin"] < MARGIN:
+        # a boundary case: either outcome is correct, but it must be a well-formed one
+        k = got["k"]
+        assert 0 <= k <= len(d) and got["count"] == k + 1 and got["tokens"][:k] == list(d[:k])
         return ref, got, True
     assert got["k"] == ref["k"], (got, ref["k"], ref["tokens"])
     assert got["tokens"] == ref["tokens"]
@@ -59,8 +62,10 @@ def check(sp_o, sp_g, rows, drows, d, ring, st, u):
 @pytest.mark.parametrize("coverage", [False, True])
 def test_verify_workload_parity(coverage):
     """The verification workload: N = 4, V = 152064, target rows N(0,4) with 3
-    spikes of +12, draft rows N(0,4) (coverage: sharing the target's spikes),
-    T 0.7, penalty 1.1 over a 64-token ring, top-k 40, top-p 0.9, min-p 0.05."""
+    spikes of +12, draft rows N(0,4), T 0.7, penalty 1.1 over a 64-token ring,
+    top-k 40, top-p 0.9, min-p 0.05.  With independent draft rows acceptance is
+    essentially nil, so the coverage variant's draft row i is target row i plus
+    N(0, 0.5) noise, which exercises the accept, residual and bonus paths."""
     from mtp_draft_head_step_amd import abi
     wl, n, v = I.WL_VERIFY, 4, 152064
     sp_o = OV.Sampling(temperature=0.7, repeat_penalty=1.1, top_k=40, top_p=0.9, min_p=0.05, window=64)
@@ -68,17 +73,18 @@ def test_verify_workload_parity(coverage):
     flagged, ks = 0, []
     for rnd in range(12):
         rows, pos = I.logits_rows(wl, 5, rnd, n + 1, v, 4.0, spikes=3, spike=12.0)
-        drows, _ = I.logits_rows(wl, 6, rnd, n, v, 4.0, spikes=3 if coverage else 0, spike=12.0,
-                                 spike_positions=pos[:n] if coverage else None)
+        drows, _ = I.logits_rows(wl, 6, rnd, n, v, 0.5 if coverage else 4.0)
+        if coverage:
+            drows = (rows[:n] + drows).astype(np.float32)
         ring, st = I.history_ring(wl, rnd, 64, v)
         d = draft_tokens(sp_o, drows, ring, st, [wl, 10, rnd], v)
         u = I.uniforms(wl, rnd, n + 1)
         ref, got, near = check(sp_o, sp_g, rows, drows, d, ring, st, u)
         flagged += near
         ks.append(ref["k"])
-    assert flagged <= 1
+    assert flagged <= 4
     if coverage:
-        assert max(ks) >= 1          # the accept paths ran
+        assert max(ks) >= 2          # the accept paths ran
 
 
 @pytest.mark.parametrize("vocab", [7, 300, 4097, 20000])
@@ -108,7 +114,7 @@ def test_sampled_parity_sweep(vocab, params, n):
         u = rng.random(n + 1).astype(np.float32)
         _, _, near = check(sp_o, sp_g, base, drows if n else np.zeros((0, vocab), np.float32), d, ring, st, u)
         flagged += near
-    assert flagged <= 1
+    assert flagged <= 3
 
 
 def test_identical_rows_always_accept():
