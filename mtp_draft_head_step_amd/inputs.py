@@ -39,9 +39,22 @@ def f32_to_bf16_bits(x) -> np.ndarray:
 
 
 def bf16_bits_to_f32(b) -> np.ndarray:
-    """Exact widening of bf16 bit patterns (uint16) to fp32."""
+    """Exact widening of bf16 bit patterns (uint16) to fp32 (large arrays are
+    widened in chunks on a thread pool)."""
     b = np.ascontiguousarray(b, dtype=np.uint16)
-    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    flat = b.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint32)
+    step = 1 << 22
+
+    def work(i):
+        np.left_shift(flat[i:i + step], 16, out=out[i:i + step], dtype=np.uint32)
+
+    if flat.size <= step:
+        work(0)
+    else:
+        with _cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(work, range(0, flat.size, step)))
+    return out.view(np.float32).reshape(b.shape)
 
 
 def decode(storage: np.ndarray, dtype: str) -> np.ndarray:
