@@ -1,30 +1,41 @@
 #!/usr/bin/env python3
 """MTP round throughput on one MI355X.
 
-Workload: the Qwen3.5-27B-shaped MTP head (H=5120, 24/4 heads, head_dim 256,
-SwiGLU 17408, vocab 152064 borrowed lm_head), bf16 weights and activations with
-fp32 accumulation, batch 1, draft KV context 4096, 2 drafts per round
-(block_size 3), temperature 0, weights N(0, 0.02) seeded (synthetic: no
-checkpoint).  One bench step is one MTP round, the whole hot path:
+Default workload (``--workload qwen35_27b_round``): the Qwen3.5-27B-shaped MTP
+head (H=5120, 24/4 heads, head_dim 256, SwiGLU 17408, vocab 152064 borrowed
+lm_head), bf16 weights and activations with fp32 accumulation, batch 1, draft
+KV context 4096, 2 drafts per round (block_size 3), temperature 0, weights
+N(0, 0.02) seeded (synthetic: no checkpoint).  One bench step is one MTP round,
+the whole hot path:
   flush of the completed pairs (LAST) -> 1 chained draft step -> greedy verify of
   the 3 target rows -> draft-KV rollback (policy A) -> one host sync reading the
   accepted count, committed tokens and the KV state.
 Target logits rows (N(0, 3)) and target hiddens (N(0, 1)) are synthetic inputs
-drawn per round from a pool of 8 resident rounds.
+drawn per round from a pool of 8 resident rounds.  Every pointer and count of a
+round is device-resident, so the host enqueues round r + 1 before it waits for
+round r: the round's host synchronisation overlaps the next round's GPU work.
+--graph replays each round from a HIP graph instead.
 
-Every pointer and count of a round is device-resident, so the host enqueues
-round r + 1 before it waits for round r: the round's host synchronisation
-(reading k, the committed tokens and the KV error word) overlaps the next
-round's GPU work.  --graph replays each round from a HIP graph instead.
+Other workloads (one JSON line each, same keys):
+  tiny_round            the tiny fp32 head (H 256), prefix 128, 2 drafts, 64 rounds
+  flush256_prefix8192   the 256-pair flush (tiny head in bf16) after an 8192-slot
+                        prefix, ALL mode, the KV rolled back after each flush
+  verify_sampled        sampled verification: N=4, V=152064, T 0.7, penalty 1.1
+                        over a 64-token ring, top-k 40, top-p 0.9, min-p 0.05
+  depth_ctx32768        rounds of the tiny bf16 head over a 32768-slot prefix at
+                        depth --depth (1..8), lm_head bf16 or int8-g128 (--lm),
+                        planted acceptance p_i = 0.8 * 0.85^i, policy A or B,
+                        --sessions independent sessions rotated (cold KV)
 
-Prints ONE JSON line.  value = draft tokens/s (2 per round); rounds/s is given
-beside it.  roofline = the unembedding GEMV (the dominant kernel), timed with HIP
-events around each of its launches inside the timed region.  cpu_baseline = the
-fp64 numpy oracle running one round of the same workload on the host.
+Each line carries ``roofline`` for the workload's dominant kernel (algorithmic
+bytes or flops per launch / its average duration from HIP events recorded
+around each launch inside the timed region) and ``cpu_baseline`` (the fp64 numpy
+oracle timed on a bounded sample of the same workload on the host).
 """
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import json
 import os
@@ -35,9 +46,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+METRIC = "MTP draft tokens/sec + verify rounds/sec at batch 1 (GB/s vs HBM peak)"
 HBM_PEAK_GBS = 8000.0
-N_DRAFT = 2
-CTX = 4096
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+VALU_FP32_PEAK_TFLOPS = 157.3
 POOL = 8
 
 
@@ -45,16 +57,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------------------
+# algorithmic bytes and flops
+# ---------------------------------------------------------------------------
+def _bytes_of(dtype):
+    return {"bf16": 2, "f32": 4, "i8g128": 1}[dtype]
+
+
 def step_bytes(shape, ctx_len, with_logits=False):
     """Algorithmic HBM bytes of one draft-head step at KV length ctx_len (the new
     slot included): every weight once, one embedding row, the KV read and the new
     K/V row written, the hidden in/out, plus logits if they are written."""
     H, D, hkv, V = shape.hidden, shape.head_dim, shape.n_kv_heads, shape.vocab
-    wb = 2 if shape.weight_dtype == "bf16" else 4
-    kvb = 2 if shape.kv_dtype == "bf16" else 4
-    ab = 2 if shape.act_dtype == "bf16" else 4
+    wb, kvb, ab = _bytes_of(shape.weight_dtype), _bytes_of(shape.kv_dtype), _bytes_of(shape.act_dtype)
     head = shape.head_param_count() * wb
-    lm = V * H * (1 if shape.lm_head_dtype == "i8g128" else wb)
+    lm = V * H * _bytes_of(shape.lm_head_dtype)
     if shape.lm_head_dtype == "i8g128":
         lm += V * (H // 128) * 2
     kv = 2 * hkv * D * kvb * ctx_len
@@ -62,32 +79,63 @@ def step_bytes(shape, ctx_len, with_logits=False):
 
 
 def unembed_bytes(shape):
-    """Algorithmic bytes of one unembedding launch: the lm_head, the fp32 input
-    vector, the final-norm weight (logits are not written in the timed rounds)."""
+    """Algorithmic bytes of one unembedding launch: the lm_head (plus its scales),
+    the fp32 input vector, the final-norm weight (logits are not written in the
+    timed rounds)."""
     H, V = shape.hidden, shape.vocab
-    wb = 2 if shape.lm_head_dtype == "bf16" else (1 if shape.lm_head_dtype == "i8g128" else 4)
     extra = V * (H // 128) * 2 if shape.lm_head_dtype == "i8g128" else 0
-    return V * H * wb + extra + H * 4 + H * 2
+    return V * H * _bytes_of(shape.lm_head_dtype) + extra + H * 4 + H * _bytes_of(shape.weight_dtype)
 
 
-def gemv_source_digest():
+def attention_bytes(shape, keys, rows=1):
+    """Algorithmic bytes of one attention launch: the K and V of ``keys`` slots
+    (read once per kv head), the fp32 roped q read and the fp32 o written per row."""
+    kvb = _bytes_of(shape.kv_dtype)
+    return 2 * shape.n_kv_heads * shape.head_dim * kvb * keys + rows * 2 * shape.n_q_heads * shape.head_dim * 4
+
+
+def flush_attention_flops(shape, prefix, n):
+    """Causal attention flops of an n-row flush after `prefix` slots: row j
+    attends over prefix + j + 1 keys, 4 D flops per key per query head (q.k and
+    p.v)."""
+    keys = n * (prefix + 1) + n * (n - 1) // 2
+    return 4 * shape.head_dim * shape.n_q_heads * keys
+
+
+def flush_projection_flops(shape, n, rows_out):
+    """Projection flops of a flush: fc and q/k/v for every row; o, gate/up, down
+    for the rows whose output is requested; the unembedding of the last row."""
+    H, D, I = shape.hidden, shape.head_dim, shape.intermediate
+    qkv = (shape.n_q_heads + 2 * shape.n_kv_heads) * D * H
+    per_out = shape.n_q_heads * D * H + 3 * H * I
+    return 2 * (n * (2 * H * H + qkv) + rows_out * per_out + shape.vocab * H)
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (rocprofv3 PMC summaries committed under profiles/)
+# ---------------------------------------------------------------------------
+def source_digest(files):
     h = hashlib.sha256()
-    for f in ("gemv.hip", "common.h", "kernels.h"):
+    for f in files:
         with open(os.path.join(ROOT, "mtp_draft_head_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per unembedding launch from the committed rocprofv3 PMC summary,
-    or None if there is none or the kernel source changed since it was taken."""
-    p = os.path.join(ROOT, "profiles", "unembed_qwen35_27b_traffic.json")
+def gemv_source_digest():
+    return source_digest(("gemv.hip", "common.h", "kernels.h"))
+
+
+def measured_traffic(name, files):
+    """HBM bytes per launch from a committed PMC summary profiles/<name>.json, or
+    None if there is none or the kernel's sources changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", name + ".json")
     try:
         with open(p) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
-    if d.get("gemv_source_digest") != gemv_source_digest():
+    if d.get("source_digest", d.get("gemv_source_digest")) != source_digest(files):
         return None
     return d.get("bytes_per_launch")
 
@@ -101,53 +149,87 @@ def cpu_threads():
         return 1
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--cpu-rounds", type=int, default=1, help="oracle rounds for cpu_baseline (0 = skip)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run three 1 GiB device-to-device copies (a plain copy kernel of known "
-                         "size, to scale HBM traffic counters)")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay rounds from HIP graphs (no unembedding timing in this mode)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: the MTP round is a batch-1 path on a single MI355X; "
-              "run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def single_thread_blas():
+    """Context limiting BLAS to one thread (the small oracle products)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except Exception:
+        return contextlib.nullcontext()
 
+
+def timed_sample(unit_fn, seconds, max_units):
+    """Run oracle units until `seconds` of CPU time have passed (at least one,
+    at most max_units); returns (units, elapsed seconds)."""
+    t = time.perf_counter()
+    n = 0
+    while n < max_units:
+        unit_fn(n)
+        n += 1
+        if time.perf_counter() - t >= seconds:
+            break
+    return n, time.perf_counter() - t
+
+
+def roofline(bound, achieved, peak, unit, traffic, **extra):
+    if achieved is None:
+        return None
+    d = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    d.update(extra)
+    return d
+
+
+def base_line(args, value, unit, ms_step, dtype, data, config):
+    return {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": data, "config": config}
+
+
+def calibrate_copy(args):
+    """Three 1 GiB device-to-device copies: a plain copy kernel of known size,
+    for scaling HBM traffic counters."""
+    if not args.calibrate_copy:
+        return
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# greedy rounds (the 27B-shaped head; the tiny fp32 head)
+# ---------------------------------------------------------------------------
+def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
     import numpy as np
     import torch
 
     from mtp_draft_head_step_amd import abi
     from mtp_draft_head_step_amd import inputs as I
 
-    shape, wl, N = I.QWEN35_27B, I.WL_QWEN, N_DRAFT
     V, H = shape.vocab, shape.hidden
     t0 = time.time()
     storage = I.head_weights(shape, wl)
     log(f"weights generated in {time.time() - t0:.1f}s")
     head = abi.Head(shape, storage)
-    cap = CTX + 1 + (args.warmup + args.steps + 4) * (N + 1) + 64
-    kp, vp = I.prefix_kv(shape, wl, CTX, cap)
-    kv = abi.DraftKV(shape, cap, kp, vp, CTX)
+    cap = ctx + 1 + (args.warmup + args.steps + 4) * (N + 1) + 64
+    kp, vp = I.prefix_kv(shape, wl, ctx, cap)
+    kv = abi.DraftKV(shape, cap, kp, vp, ctx)
     pool_logits = np.stack([I.logits_rows(wl, 5, r, N + 1, V, 3.0)[0] for r in range(POOL)])
     pool_hid = np.stack([I.target_hiddens(shape, wl, r, N + 1) for r in range(POOL)])
     first_tok = I.tokens_uniform(wl, 0, N + 1, V)
     first_hid = I.target_hiddens(shape, wl, 1000, N + 1)
     ring0, ring_st0 = I.history_ring(wl, None, 64, V)
-    dev = "cuda"
+    act = torch.bfloat16 if shape.act_dtype == I.BF16 else torch.float32
     t_logits = abi.to_device(pool_logits)
     t_hid = abi.to_device(pool_hid)
-    t_tok0 = abi.to_device(first_tok)
-    t_hid0 = abi.to_device(first_hid)
     ring = abi.to_device(ring0)
     ring_st = abi.to_device(ring_st0)
-    io = torch.zeros(2 + N + 1, dtype=torch.int32, device=dev)      # {k, k+1, tokens...}
-    d_buf = torch.zeros(N, dtype=torch.int32, device=dev)
-    g_buf = torch.zeros((N, H), dtype=torch.bfloat16, device=dev)
+    io = torch.zeros(2 + N + 1, dtype=torch.int32, device="cuda")      # {k, k+1, tokens...}
+    d_buf = torch.zeros(N, dtype=torch.int32, device="cuda")
+    g_buf = torch.zeros((N, H), dtype=act, device="cuda")
     ws = abi.Workspace(abi.mtp_workspace_bytes(head.cfg, N + 1, cap))
     vws = abi.Workspace(abi.spec_verify_workspace_bytes(N, V))
     sp = abi.sampling(window=64)
@@ -159,8 +241,8 @@ def main():
     # tokens = io[2:] (written by the previous verify), count = io[1], hiddens =
     # the previous round's target hiddens.  Round 0 starts from one pending pair.
     io[1] = 1
-    io[2:] = t_tok0
-    t_hid[POOL - 1].copy_(t_hid0)
+    io[2:] = abi.to_device(first_tok)
+    t_hid[POOL - 1].copy_(abi.to_device(first_hid))
     width = 2 + N + 1 + 4
     host = torch.zeros((POOL, width), dtype=torch.int32).pin_memory()
     totals = {"committed": 0, "accepted": 0}
@@ -192,8 +274,8 @@ def main():
 
     graphs = None
     if args.graph:
-        # one graph per pool slot (the unembedding timing is not available for
-        # captured launches, so the roofline is left null in this mode)
+        # one graph per pool slot (kernel timing is not available for captured
+        # launches, so the roofline is left null in this mode)
         cap_stream = torch.cuda.Stream()
         graphs = {}
         for p_ in range(POOL):
@@ -205,7 +287,7 @@ def main():
         torch.cuda.synchronize()
         log("captured %d round graphs" % POOL)
     else:
-        abi.mtp_timing_begin(args.steps * N + 4)
+        abi.mtp_timing_begin(abi.TIME_UNEMBED, args.steps * N + 4)
 
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -227,93 +309,559 @@ def main():
     elapsed = time.perf_counter() - t_start
     lm_ms, lm_n = (0.0, 0) if graphs is not None else abi.mtp_timing_end()
     log(f"timed {args.steps} rounds in {elapsed * 1e3:.1f} ms; unembedding {lm_n} launches")
-    state = totals
-
-    if args.calibrate_copy:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibrate_copy(args)
 
     rounds_s = args.steps / elapsed
-    ms_step = elapsed / args.steps * 1e3
     lm_avg_s = lm_ms / lm_n / 1e3 if lm_n else None
     ub = unembed_bytes(shape)
-    achieved = ub / lm_avg_s / 1e9 if lm_avg_s else None
-    round_bytes = N * step_bytes(shape, CTX + 2) + (N + 1) * V * 4
-    traffic = measured_traffic()
+    round_bytes = N * step_bytes(shape, ctx + 2) + (N + 1) * V * 4
+    traffic = measured_traffic("unembed_qwen35_27b_traffic", ("gemv.hip", "common.h", "kernels.h")) \
+        if workload == "qwen35_27b_mtp_head_round" else None
 
     cpu = None
-    if args.cpu_rounds > 0:
-        cpu = cpu_baseline(shape, storage, kp, vp, cap, pool_logits, pool_hid, first_tok, first_hid,
-                           ring0, ring_st0, args.cpu_rounds)
+    if args.cpu_seconds > 0:
+        cpu = cpu_rounds(shape, storage, kp, vp, cap, ctx, N, pool_logits, pool_hid, first_tok, first_hid,
+                         ring0, ring_st0, args.cpu_seconds, args.steps + args.warmup, single=shape.hidden < 1024)
 
-    out = {
-        "metric": "MTP draft tokens/sec + verify rounds/sec at batch 1 (GB/s vs HBM peak)",
-        "value": round(N * rounds_s, 2),
-        "unit": "draft tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights of the Qwen3.5-27B MTP head shape; N(0,3) target logits, N(0,1) target hiddens)",
-        "config": {"workload": "qwen35_27b_mtp_head_round", "hidden": H, "heads": "24q/4kv",
-                   "head_dim": 256, "intermediate": shape.intermediate, "vocab": V,
-                   "draft_kv_context": CTX, "drafts_per_round": N, "block_size": N + 1,
-                   "temperature": 0.0, "batch": 1, "policy": "A"},
+    dtype = "bf16" if shape.weight_dtype == I.BF16 else "f32"
+    out = base_line(args, round(N * rounds_s, 2), "draft tokens/s", elapsed / args.steps * 1e3, dtype, data,
+                    {"workload": workload, "hidden": H, "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv",
+                     "head_dim": shape.head_dim, "intermediate": shape.intermediate, "vocab": V,
+                     "draft_kv_context": ctx, "drafts_per_round": N, "block_size": N + 1,
+                     "temperature": 0.0, "batch": 1, "policy": "A"})
+    out.update({
         "rounds_per_s": round(rounds_s, 2),
         "round_gbs": round(round_bytes / (elapsed / args.steps) / 1e9, 1),
         "round_hbm_frac": round(round_bytes / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
-        "committed_per_round": round(state["committed"] / (args.warmup + args.steps), 4),
+        "committed_per_round": round(totals["committed"] / (args.warmup + args.steps), 4),
         "launch": ("hip graph per round" if args.graph else "eager") +
                   ", host sync per round overlapped with the next round",
-        "roofline": None if achieved is None else {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "unembedding GEMV (lm_head 152064x5120 bf16)",
-            "bytes_per_launch": ub, "avg_us": round(lm_avg_s * 1e6, 2), "launches": lm_n},
+        "roofline": roofline("hbm", ub / lm_avg_s / 1e9 if lm_avg_s else None, HBM_PEAK_GBS, "GB/s", traffic,
+                             kernel=f"unembedding GEMV (lm_head {V}x{H} {shape.lm_head_dtype})",
+                             bytes_per_launch=ub, avg_us=round(lm_avg_s * 1e6, 2) if lm_avg_s else None,
+                             launches=lm_n),
         "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+    })
+    return out
 
 
-def cpu_baseline(shape, storage, kp, vp, cap, pool_logits, pool_hid, first_tok, first_hid, ring0,
-                 ring_st0, rounds):
+def cpu_rounds(shape, storage, kp, vp, cap, ctx, N, pool_logits, pool_hid, first_tok, first_hid, ring0,
+               ring_st0, seconds, max_rounds, single):
     """The oracle as it stands, on the host: `rounds` rounds of the same workload."""
+    from mtp_draft_head_step_amd import inputs as I
+    from oracle import head as OH
+    from oracle import rounds as OR
+    from oracle.kvcache import DraftKV
+    t0 = time.time()
+    oh = OH.Head(shape, I.weight_values(shape, storage))
+    okv = DraftKV(shape.n_kv_heads, cap, shape.head_dim, I.decode(kp, shape.kv_dtype),
+                  I.decode(vp, shape.kv_dtype), ctx)
+    pending = [(int(first_tok[0]), I.decode(first_hid[0], shape.act_dtype))]
+    st = OR.RoundState(oh, okv, pending, [0] * (ctx + 2), ring0, ring_st0, window=64)
+    log(f"oracle inputs decoded in {time.time() - t0:.1f}s")
+
+    def target_fn(toks, start):
+        r = target_fn.r
+        return pool_logits[r % POOL], I.decode(pool_hid[r % POOL], shape.act_dtype)
+
+    def unit(r):
+        target_fn.r = r
+        OR.run_round(st, N, target_fn, policy="A")
+    with (single_thread_blas() if single else contextlib.nullcontext()):
+        cores = 1 if single else cpu_threads()
+        rounds, el = timed_sample(unit, seconds, max_rounds)
+    log(f"oracle {rounds} round(s) in {el:.1f}s")
+    return {"value": round(N * rounds / el, 4), "unit": "draft tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rounds} round(s) of the same workload (flush + {N - 1} chained step(s) + greedy verify "
+                      f"+ rollback at draft KV context {ctx}), numpy fp64"}
+
+
+# ---------------------------------------------------------------------------
+# the 256-pair flush
+# ---------------------------------------------------------------------------
+def run_flush(args):
+    import torch
+
+    from mtp_draft_head_step_amd import abi
+    from mtp_draft_head_step_amd import inputs as I
+
+    shape, wl = I.TINY_BF16, I.WL_FLUSH
+    prefix, n = 8192, 256
+    cap = prefix + n
+    storage = I.head_weights(shape, wl)
+    head = abi.Head(shape, storage)
+    kp, vp = I.prefix_kv(shape, wl, prefix, cap)
+    kv = abi.DraftKV(shape, cap, kp, vp, prefix)
+    toks_np = I.tokens_uniform(wl, 0, n, shape.vocab)
+    hids_np = I.target_hiddens(shape, wl, 0, n)
+    toks, hids = abi.to_device(toks_np), abi.to_device(hids_np)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(head.cfg, n, cap))
+    hout = torch.zeros((n, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def flush(mode):
+        abi.mtp_flush_pairs(head, kv, toks, hids, n, None, mode, 1, hout if mode == abi.ALL else hout[:1],
+                            logits, amax, ws, stream)
+        abi.kv_rollback(kv, prefix, None, 0, stream)
+
+    def timed(mode, steps, kind=None):
+        for _ in range(args.warmup):
+            flush(mode)
+        torch.cuda.synchronize()
+        if kind is not None:
+            abi.mtp_timing_begin(kind, 64 * steps + 4)
+        t = time.perf_counter()
+        for _ in range(steps):
+            flush(mode)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t
+        k = abi.mtp_timing_end() if kind is not None else None
+        if int(kv.state[3].item()) != 0:
+            raise RuntimeError("device error word set")
+        return el / steps, k
+
+    side = max(args.steps // 4, 5)
+    t_all, (att_ms, att_n) = timed(abi.ALL, args.steps, abi.TIME_ATTENTION)
+    _, (proj_ms, proj_n) = timed(abi.ALL, side, abi.TIME_PROJECTION)
+    t_last, _ = timed(abi.LAST, side)
+    t_kv, _ = timed(abi.KV_ONLY, side)
+    calibrate_copy(args)
+    att_flops = flush_attention_flops(shape, prefix, n)
+    proj_flops = flush_projection_flops(shape, n, n)
+    total_flops = att_flops + proj_flops
+    att_avg = att_ms / att_n / 1e3
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_flush(shape, storage, kp, vp, cap, prefix, toks_np, hids_np, args.cpu_seconds, args.steps)
+    out = base_line(args, round(n / t_all, 1), "flushed pairs/s", t_all * 1e3, "bf16",
+                    "synthetic (seeded N(0,0.02) weights of the tiny head in bf16; 256 uniform tokens, "
+                    "N(0,1) bf16 hiddens; N(0,1) bf16 prefix K/V)",
+                    {"workload": "flush256_prefix8192", "hidden": shape.hidden, "heads": "4q/2kv", "head_dim": 64,
+                     "intermediate": shape.intermediate, "vocab": shape.vocab, "pairs": n,
+                     "prefix": prefix, "mode": "ALL (every row's g; last row's logits and argmax)"})
+    out.update({
+        "flush_us": {"all": round(t_all * 1e6, 2), "last": round(t_last * 1e6, 2), "kv_only": round(t_kv * 1e6, 2)},
+        "flush_tflops": round(total_flops / t_all / 1e12, 3),
+        "flush_mfma_frac": round(total_flops / t_all / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+        "algorithmic_gflop": {"attention": round(att_flops / 1e9, 4), "projections": round(proj_flops / 1e9, 4)},
+        "projection_us_per_flush": round(proj_ms / side * 1e3, 2),
+        "projection_launches_per_flush": proj_n // side,
+        "roofline": roofline("alu", att_flops / att_avg / 1e12, VALU_FP32_PEAK_TFLOPS, "TFLOP/s", None,
+                             kernel="causal flush attention (256 rows x 4 q heads over 8193..8448 keys; "
+                                    "fp32 VALU dot products)",
+                             flops_per_launch=att_flops, avg_us=round(att_avg * 1e6, 2), launches=att_n),
+        "cpu_baseline": cpu,
+    })
+    return out
+
+
+def cpu_flush(shape, storage, kp, vp, cap, prefix, toks, hids, seconds, max_flushes):
+    from mtp_draft_head_step_amd import inputs as I
+    from oracle import head as OH
+    from oracle.kvcache import DraftKV
+    oh = OH.Head(shape, I.weight_values(shape, storage))
+    tk = [int(t) for t in toks]
+    hv = [I.decode(h, shape.act_dtype) for h in hids]
+    K, V = I.decode(kp, shape.kv_dtype), I.decode(vp, shape.kv_dtype)
+    def unit(_):
+        okv = DraftKV(shape.n_kv_heads, cap, shape.head_dim, K, V, prefix)
+        oh.flush(okv, tk, hv, OH.ALL, set_round_base=True)
+    with single_thread_blas():
+        flushes, el = timed_sample(unit, seconds, max_flushes)
+    return {"value": round(len(tk) * flushes / el, 2), "unit": "flushed pairs/s", "cores": 1, "kind": "oracle",
+            "sample": f"{flushes} flushes of the same 256 pairs in ALL mode, numpy fp64, one BLAS thread"}
+
+
+# ---------------------------------------------------------------------------
+# sampled verification
+# ---------------------------------------------------------------------------
+VERIFY_POOL = 64
+
+
+def run_verify(args):
+    import numpy as np
+    import torch
+
+    from mtp_draft_head_step_amd import abi
+    from mtp_draft_head_step_amd import inputs as I
+
+    wl, N, V = I.WL_VERIFY, 4, 152064
+    steps = args.steps
+    sp = abi.sampling(0.7, 1.1, 40, 0.9, 0.05, 64)
+    t0 = time.time()
+    rows = np.stack([I.logits_rows(wl, 5, r, N + 1, V, 4.0, spikes=3, spike=12.0)[0] for r in range(VERIFY_POOL)])
+    drows = np.stack([I.logits_rows(wl, 6, r, N, V, 4.0)[0] for r in range(VERIFY_POOL)])
+    t_rows, t_drows = abi.to_device(rows), abi.to_device(drows)
+    ring0, st0 = I.history_ring(wl, None, 64, V)
+    ring, ring_st = abi.to_device(ring0), abi.to_device(st0)
+    # draft tokens: d_i drawn from q_i (history ++ d_<i) by the library's own
+    # sampler (a verification of no drafts over the draft row) on a ring copy
+    vws0 = abi.Workspace(abi.spec_verify_workspace_bytes(0, V))
+    drafts = torch.zeros((VERIFY_POOL, N), dtype=torch.int32, device="cuda")
+    du = abi.to_device(np.stack([I.uniforms(wl, r, N, stream=10) for r in range(VERIFY_POOL)]))
+    tmp_c = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for r in range(VERIFY_POOL):
+        rc, sc = ring.clone(), ring_st.clone()
+        for i in range(N):
+            abi.spec_verify(sp, 0, V, t_drows[r, i], None, None, rc, sc, du[r, i:i + 1], drafts[r, i:i + 1],
+                            tmp_c, vws0)
+    total = args.warmup + steps
+    uni = abi.to_device(np.stack([I.uniforms(wl, (1, r), N + 1) for r in range(total)]))
+    out_t = torch.zeros((total, N + 1), dtype=torch.int32, device="cuda")
+    out_c = torch.zeros((total, 2), dtype=torch.int32, device="cuda")
+    vws = abi.Workspace(abi.spec_verify_workspace_bytes(N, V))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"verify inputs resident ({time.time() - t0:.1f}s): {VERIFY_POOL} rounds of logits, "
+        f"{(rows.nbytes + drows.nbytes) >> 20} MiB")
+
+    def one(r):
+        p = r % VERIFY_POOL
+        abi.spec_verify(sp, N, V, t_rows[p], t_drows[p], drafts[p], ring, ring_st, uni[r], out_t[r], out_c[r],
+                        vws, stream)
+
+    for r in range(args.warmup):
+        one(r)
+    torch.cuda.synchronize()
+    abi.mtp_timing_begin(abi.TIME_VERIFY, steps + 4)
+    t = time.perf_counter()
+    for r in range(args.warmup, total):
+        one(r)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t
+    ms, nl = abi.mtp_timing_end()
+    calibrate_copy(args)
+    counts = out_c[args.warmup:].cpu().numpy()
+    if counts.min() < 0 or np.any(counts[:, 1] != counts[:, 0] + 1):
+        raise RuntimeError("verification returned malformed counts")
+    chunk_bytes = (2 * N + 1) * V * 4 + 64 * 4
+    avg = ms / nl / 1e3
+    cpu = cpu_verify(rows, drows, ring0, st0, wl, N, args.cpu_seconds, total) if args.cpu_seconds > 0 else None
+    out = base_line(args, round(steps / el, 1), "verify rounds/s", el / steps * 1e3, "f32",
+                    "synthetic (seeded N(0,4) fp32 target rows with 3 spikes of +12, N(0,4) draft rows, "
+                    "64 resident rounds cycled, fresh uniforms per round)",
+                    {"workload": "verify_sampled_n4_v152064", "n_draft": N, "vocab": V, "temperature": 0.7,
+                     "repeat_penalty": 1.1, "window": 64, "top_k": 40, "top_p": 0.9, "min_p": 0.05})
+    out.update({
+        "us_per_round": round(el / steps * 1e6, 2),
+        "round_gbs": round(chunk_bytes / (el / steps) / 1e9, 1),
+        "mean_accepted": round(float(counts[:, 0].mean()), 4),
+        "roofline": roofline("hbm", chunk_bytes / avg / 1e9, HBM_PEAK_GBS, "GB/s", None,
+                             kernel="per-chunk top-k pass over the 9 rows (penalty, temperature, bitonic sort)",
+                             bytes_per_launch=chunk_bytes, avg_us=round(avg * 1e6, 2), launches=nl),
+        "cpu_baseline": cpu,
+    })
+    return out
+
+
+def cpu_verify(rows, drows, ring0, st0, wl, N, seconds, max_rounds):
+    import numpy as np
+
+    from mtp_draft_head_step_amd import inputs as I
+    from oracle import verify as OV
+    sp = OV.Sampling(temperature=0.7, repeat_penalty=1.1, top_k=40, top_p=0.9, min_p=0.05, window=64)
+    state = {"ring": np.array(ring0), "st": np.array(st0)}
+
+    def unit(r):
+        # the oracle draws its own drafts from q_i with the same seeded uniforms
+        p = r % VERIFY_POOL
+        ring, st = state["ring"], state["st"]
+        du = I.uniforms(wl, p, N, stream=10)
+        d = []
+        for i in range(N):
+            d.append(OV.sample(sp, drows[p, i], ring, st, float(du[i]), prefix=d))
+        res = OV.verify(sp, rows[p], drows[p], d, ring, st, I.uniforms(wl, (1, r), N + 1))
+        state["ring"], state["st"] = res["ring"], res["state"]
+    n_rounds, el = timed_sample(unit, seconds, max_rounds)
+    return {"value": round(n_rounds / el, 3), "unit": "verify rounds/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_rounds} rounds (draft draws + verification), numpy fp64 sort-based transforms"}
+
+
+# ---------------------------------------------------------------------------
+# depth sweep over a 32768-slot prefix
+# ---------------------------------------------------------------------------
+def run_depth(args, N, lm):
+    import numpy as np
+    import torch
+
+    from mtp_draft_head_step_amd import abi
+    from mtp_draft_head_step_amd import inputs as I
+
+    ctx, S, policy = 32768, args.sessions, args.policy
+    shape = I.TINY_BF16.with_dtypes(lm_head_dtype=I.I8G128 if lm == "i8g128" else I.BF16)
+    wl, V, H = I.WL_DEPTH, shape.vocab, shape.hidden
+    R = args.warmup + args.steps
+    per_session = (R + S - 1) // S
+    cap = ctx + per_session * (N + 1) + 64
+    t0 = time.time()
+    storage = I.head_weights(shape, wl)
+    head = abi.Head(shape, storage)
+    kp, vp = I.prefix_kv(shape, wl, ctx, cap)
+    pool_hid = abi.to_device(np.stack([I.target_hiddens(shape, wl, r, N + 1) for r in range(POOL)]))
+    first_tok = int(I.tokens_uniform(wl, 1, ctx + 2, V)[-1])
+    first_hid = abi.to_device(I.target_hiddens(shape, wl, 1000, 1)[0])
+    first_rows = torch.zeros((N + 1, H), dtype=torch.bfloat16, device="cuda")
+    first_rows[0].copy_(first_hid)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(head.cfg, N + 1, cap))
+    vws = abi.Workspace(abi.spec_verify_workspace_bytes(N, V))
+    sp = abi.sampling(window=64)
+    sessions = []
+    for _ in range(S):
+        sessions.append({
+            "kv": abi.DraftKV(shape, cap, kp, vp, ctx),
+            "io": torch.zeros(2 + N + 1, dtype=torch.int32, device="cuda"),   # {k, k+1, tokens}
+            "n_dev": torch.zeros(1, dtype=torch.int32, device="cuda"),
+            "d": torch.zeros(N, dtype=torch.int32, device="cuda"),
+            "g": torch.zeros((N, H), dtype=torch.bfloat16, device="cuda"),
+            "ring": torch.zeros(64, dtype=torch.int32, device="cuda"),
+            "ring_st": torch.zeros(2, dtype=torch.int32, device="cuda"),
+        })
+    step_out = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
+    step_tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log(f"{S} sessions of a {ctx}-slot KV resident ({time.time() - t0:.1f}s)")
+
+    def reset():
+        for s in sessions:
+            s["kv"].state.copy_(torch.tensor([ctx, ctx, 0, 0], dtype=torch.int32))
+            s["ring"].zero_()
+            s["ring_st"].zero_()
+            s["io"].zero_()
+            s["io"][1] = 1
+            s["io"][2] = first_tok
+        torch.cuda.synchronize()
+
+    base_rows = [I.logits_rows(wl, 5, r, N + 1, V, 3.0)[0] for r in range(POOL)]
+    planted = torch.zeros((R, N + 1, V), dtype=torch.float32, device="cuda")
+    k_of = [I.acceptance_draws(wl, r, N) for r in range(R)]
+    prev_round = {}                                    # session -> its previous round
+
+    def j0_of(k):
+        return 0 if policy == "A" else min(k, N - 1)
+
+    def pending_of(s):
+        """The session's pending pairs: tokens out_tokens[j0..k] of its previous
+        verify (io[2 + j0:]), hiddens rows j0..k of that round's target hiddens,
+        count k + 1 - j0 (io[1] when j0 = 0).  j0 > 0 only under policy B, with k
+        known from the recording pass."""
+        ss = sessions[s]
+        pr = prev_round.get(s)
+        if pr is None:
+            return ss["io"][2:], first_rows, ss["io"][1:2]
+        j0 = j0_of(k_of[pr])
+        return ss["io"][2 + j0:], pool_hid[pr % POOL][j0:], (ss["io"][1:2] if j0 == 0 else ss["n_dev"])
+
+    def draft(s, st):
+        ss = sessions[s]
+        toks, hid, cnt = pending_of(s)
+        abi.mtp_flush_pairs(head, ss["kv"], toks, hid, N + 1, cnt, abi.LAST, 1, ss["g"][0], None, ss["d"][0:1],
+                            ws, st)
+        for i in range(1, N):
+            abi.mtp_draft_step(head, ss["kv"], ss["d"][i - 1:i], ss["g"][i - 1], ss["g"][i], None,
+                               ss["d"][i:i + 1], ws, st)
+
+    def verify_and_rollback(s, r, st):
+        ss = sessions[s]
+        abi.spec_verify(sp, N, V, planted[r], None, ss["d"], ss["ring"], ss["ring_st"], None, ss["io"][2:],
+                        ss["io"][0:2], vws, st)
+        abi.kv_rollback(ss["kv"], abi.TO_ROUND_BASE, ss["io"][0:1] if policy == "B" else None, N, st)
+        if j0_of(k_of[r]) > 0:
+            ss["n_dev"].fill_(k_of[r] + 1 - j0_of(k_of[r]))
+        prev_round[s] = r
+
+    # recording pass: the drafts decide where the acceptance is planted
+    stream = torch.cuda.current_stream()
+    reset()
+    t0 = time.time()
+    lens, committed = [], []
+    for r in range(R):
+        s = r % S
+        before = int(sessions[s]["kv"].state[0].item())
+        pr = prev_round.get(s)
+        n_pend = 1 if pr is None else k_of[pr] + 1 - j0_of(k_of[pr])
+        draft(s, stream)
+        d = sessions[s]["d"].cpu().numpy()
+        rows = base_rows[r % POOL].copy()
+        I.plant_acceptance(rows, d.astype(np.int64), k_of[r])
+        planted[r].copy_(torch.from_numpy(rows))
+        verify_and_rollback(s, r, stream)
+        k = int(sessions[s]["io"][0].item())
+        if k != k_of[r]:
+            raise RuntimeError(f"planted acceptance {k_of[r]} but verification accepted {k} in round {r}")
+        lens.append((before, n_pend))
+        committed.append(sessions[s]["io"][2:2 + k + 1].cpu().tolist())
+    log(f"recording pass: {R} rounds in {time.time() - t0:.1f}s")
+
+    # timed replay: the same device work, host sync per round overlapped
+    reset()
+    prev_round.clear()
+    host = torch.zeros((POOL, 2 + N + 1 + 4), dtype=torch.int32).pin_memory()
+    got = [None] * R
+
+    def enqueue(r):
+        s = r % S
+        draft(s, stream)
+        verify_and_rollback(s, r, stream)
+        host[r % POOL, : 2 + N + 1].copy_(sessions[s]["io"], non_blocking=True)
+        host[r % POOL, 2 + N + 1:].copy_(sessions[s]["kv"].state, non_blocking=True)
+
+    def consume(r):
+        row = host[r % POOL]
+        if int(row[2 + N + 1 + 3]) != 0:
+            raise RuntimeError(f"device error word in round {r}")
+        got[r] = row[2: 2 + int(row[1])].tolist()
+
+    for r in range(args.warmup):
+        enqueue(r)
+        stream.synchronize()
+        consume(r)
+    abi.mtp_timing_begin(abi.TIME_ATTENTION, args.steps * N + 4)
+    torch.cuda.synchronize()
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    t = time.perf_counter()
+    prev = None
+    for r in range(args.warmup, R):
+        enqueue(r)
+        done[r % 2].record(stream)
+        if prev is not None:
+            done[prev % 2].synchronize()
+            consume(prev)
+        prev = r
+    done[prev % 2].synchronize()
+    consume(prev)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t
+    att_ms, att_n = abi.mtp_timing_end()
+    if got != committed:
+        raise RuntimeError("the timed replay committed a different stream than the recording pass")
+
+    # chained draft steps alone, rotating sessions (their KV lengths restored after)
+    n_steps = 8 * S
+    st_before = [s["kv"].state.clone() for s in sessions]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n_steps):
+        ss = sessions[i % S]
+        abi.mtp_draft_step(head, ss["kv"], ss["d"][0:1], ss["g"][0], step_out, None, step_tok, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / n_steps
+    for s, stb in zip(sessions, st_before):
+        s["kv"].state.copy_(stb)
+    calibrate_copy(args)
+
+    att_bytes = 0
+    for r in range(args.warmup, R):
+        before, n_pend = lens[r]
+        att_bytes += sum(attention_bytes(shape, before + n_pend + i) for i in range(N))
+    att_avg = att_ms / att_n / 1e3
+    ks = np.array(k_of[args.warmup:])
+    expected = 1.0 + sum(float(np.prod([0.8 * 0.85 ** i for i in range(j)])) for j in range(1, N + 1))
+    committed_tok = int(sum(int(k) + 1 for k in ks))
+    cpu = cpu_depth(shape, storage, kp, vp, cap, ctx, N, policy, base_rows, args.cpu_seconds / len(
+        str(args.depth).split(",")), R) if args.cpu_seconds > 0 else None
+    out = base_line(args, round(N * args.steps / el, 2), "draft tokens/s", el / args.steps * 1e3, "bf16",
+                    "synthetic (seeded N(0,0.02) tiny-head weights in bf16, N(0,1) bf16 prefix K/V, N(0,3) "
+                    "target rows with planted greedy acceptance p_i = 0.8*0.85^i)",
+                    {"workload": "depth_ctx32768", "hidden": H, "heads": "4q/2kv", "head_dim": 64,
+                     "intermediate": shape.intermediate, "vocab": V, "draft_kv_context": ctx, "depth": N,
+                     "lm_head": lm, "policy": policy, "sessions": S, "batch": 1, "temperature": 0.0})
+    out.update({
+        "rounds_per_s": round(args.steps / el, 2),
+        "us_per_round": round(el / args.steps * 1e6, 2),
+        "us_per_draft_step": round(step_us, 2),
+        "committed_per_round": round(committed_tok / args.steps, 4),
+        "committed_per_round_closed_form": round(expected, 4),
+        "committed_tokens_per_s": round(committed_tok / el, 1),
+        "roofline": roofline("hbm", att_bytes / (att_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s", None,
+                             kernel="split-K attention over the 32768+ slot draft KV (2 kv heads, D 64, bf16)",
+                             bytes_per_launch=round(att_bytes / att_n), avg_us=round(att_avg * 1e6, 2),
+                             launches=att_n),
+        "cpu_baseline": cpu,
+    })
+    return out
+
+
+def cpu_depth(shape, storage, kp, vp, cap, ctx, N, policy, base_rows, seconds, max_rounds):
     import numpy as np
 
     from mtp_draft_head_step_amd import inputs as I
     from oracle import head as OH
     from oracle import rounds as OR
     from oracle.kvcache import DraftKV
-    t0 = time.time()
-    vals = I.weight_values(shape, storage)
-    oh = OH.Head(shape, vals)
-    okv = DraftKV(shape.n_kv_heads, cap, shape.head_dim, I.decode(kp, "bf16"), I.decode(vp, "bf16"), CTX)
-    pending = [(int(first_tok[0]), I.decode(first_hid[0], "bf16"))]
-    committed = [0] * (CTX + 2)
-    st = OR.RoundState(oh, okv, pending, committed, ring0, ring_st0, window=64)
-    log(f"oracle inputs decoded in {time.time() - t0:.1f}s")
+    wl = I.WL_DEPTH
+    oh = OH.Head(shape, I.weight_values(shape, storage))
+    okv = DraftKV(shape.n_kv_heads, cap, shape.head_dim, I.decode(kp, shape.kv_dtype), I.decode(vp, shape.kv_dtype),
+                  ctx)
+    committed = [int(t) for t in I.tokens_uniform(wl, 1, ctx + 2, shape.vocab)]
+    hid0 = I.decode(I.target_hiddens(shape, wl, 1000, 1)[0], shape.act_dtype)
+    st = OR.RoundState(oh, okv, [(committed[-1], hid0)], committed, window=64)
+    def unit(r):
+        k_r = I.acceptance_draws(wl, r, N)
+        hid = I.decode(I.target_hiddens(shape, wl, r % POOL, N + 1), shape.act_dtype)
 
-    def target_fn(toks, start):
-        r = target_fn.r
-        return pool_logits[r % POOL], I.decode(pool_hid[r % POOL], "bf16")
-    t1 = time.perf_counter()
-    for r in range(rounds):
-        target_fn.r = r
-        OR.run_round(st, N_DRAFT, target_fn, policy="A")
-    el = time.perf_counter() - t1
-    log(f"oracle {rounds} round(s) in {el:.1f}s")
-    return {"value": round(N_DRAFT * rounds / el, 4), "unit": "draft tokens/s", "cores": cpu_threads(),
-            "kind": "oracle",
-            "sample": f"{rounds} round(s) of the same workload (flush + 1 chained step + greedy verify + "
-                      f"rollback at draft KV context {CTX}), numpy fp64"}
+        def fn(tokens, start):
+            rows = base_rows[r % POOL].copy()
+            I.plant_acceptance(rows, np.asarray(tokens[1:], np.int64), k_r)
+            return rows, hid
+        OR.run_round(st, N, fn, policy=policy)
+    with single_thread_blas():
+        n_rounds, el = timed_sample(unit, seconds, max_rounds)
+    return {"value": round(N * n_rounds / el, 3), "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_rounds} rounds of one session at depth {N} (flush + chained steps + greedy "
+                      f"verification + rollback over the 32768-slot prefix), numpy fp64, one BLAS thread"}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (rounds, flushes or verify rounds)")
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="qwen35_27b_round",
+                    choices=["qwen35_27b_round", "tiny_round", "flush256_prefix8192", "verify_sampled",
+                             "depth_ctx32768"])
+    ap.add_argument("--depth", default="4", help="depth_ctx32768: drafts per round (comma list: one line each)")
+    ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"], help="depth_ctx32768: lm_head storage")
+    ap.add_argument("--policy", default="B", choices=["A", "B"], help="depth_ctx32768: KV policy")
+    ap.add_argument("--sessions", type=int, default=32, help="depth_ctx32768: sessions rotated (1 = warm)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle sample for cpu_baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run three 1 GiB device-to-device copies (a plain copy kernel of known "
+                         "size, to scale HBM traffic counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="greedy rounds: replay rounds from HIP graphs (no kernel timing in this mode)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the MTP round is a batch-1 path on a single MI355X; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    default_steps = {"qwen35_27b_round": 40, "tiny_round": 64, "flush256_prefix8192": 50,
+                     "verify_sampled": 10000, "depth_ctx32768": 256}
+    if args.steps is None:
+        args.steps = default_steps[args.workload]
+
+    import torch  # noqa: F401  (the HIP runtime comes up before libmtp loads)
+
+    from mtp_draft_head_step_amd import inputs as I
+    if args.workload == "qwen35_27b_round":
+        lines = [run_greedy_rounds(args, I.QWEN35_27B, I.WL_QWEN, 4096, 2, "qwen35_27b_mtp_head_round",
+                                   "synthetic (seeded N(0,0.02) weights of the Qwen3.5-27B MTP head shape; "
+                                   "N(0,3) target logits, N(0,1) target hiddens)")]
+    elif args.workload == "tiny_round":
+        lines = [run_greedy_rounds(args, I.TINY_F32, I.WL_TINY, 128, 2, "tiny_f32_head_round",
+                                   "synthetic (seeded N(0,0.02) tiny-head weights in fp32; N(0,3) target "
+                                   "logits, N(0,1) target hiddens)")]
+    elif args.workload == "flush256_prefix8192":
+        lines = [run_flush(args)]
+    elif args.workload == "verify_sampled":
+        lines = [run_verify(args)]
+    else:
+        lines = [run_depth(args, int(d), args.lm) for d in str(args.depth).split(",")]
+    for line in lines:
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -54,8 +54,11 @@ typedef enum {
 
 typedef enum { MTP_F32 = 0, MTP_BF16 = 1, MTP_I8G128 = 2 } mtp_dtype;
 
-/* Device error codes stored in mtp_kv.state[3]. */
-enum { MTP_DEV_OK = 0, MTP_DEV_CAPACITY = 1, MTP_DEV_ROLLBACK = 2, MTP_DEV_COUNT = 3 };
+/* Device error codes stored in mtp_kv.state[3]: the append would pass the
+ * capacity; a rollback target above the length; a device pair count outside
+ * [0, n_max]; a pair's token outside [0, vocab).  Once set, every later kernel on
+ * that cache is a no-op until the caller clears the word. */
+enum { MTP_DEV_OK = 0, MTP_DEV_CAPACITY = 1, MTP_DEV_ROLLBACK = 2, MTP_DEV_COUNT = 3, MTP_DEV_TOKEN = 4 };
 
 /* Shape and storage of the draft head.  Source: "Upstream contract to port"
  * (fc 2H->H, the two pre-fc RMSNorms, one full-attention layer with q/k norms,
@@ -192,15 +195,22 @@ int spec_verify(const spec_sampling *sp, int32_t n_draft, int32_t vocab,
 int kv_rollback(const mtp_kv *kv, int32_t to_len, const int32_t *n_accepted_dev,
                 int32_t n_draft, hipStream_t stream);
 
-/* Benchmark timing of the unembedding (lm_head GEMV) kernel: after
- * mtp_timing_begin(n) the next n unembedding launches (any stream, eager or
- * being captured into a graph) are each bracketed by a pair of HIP events
- * recorded on their stream, in slots 0, 1, 2, ...  mtp_timing_elapsed waits for
- * slots [first, first + count) and returns their summed kernel time (ms); a
- * captured slot holds the timing of the graph's latest replay.  mtp_timing_end
- * returns the sum over all used slots and their count, then releases the
- * events.  Host-side state, process-wide. */
-int mtp_timing_begin(int32_t max_launches);
+/* Benchmark timing of one kernel class.  After mtp_timing_begin(kind, n) the
+ * next n launches of that class (any stream, eager or being captured into a
+ * graph) are each bracketed by a pair of HIP events recorded on their stream,
+ * in slots 0, 1, 2, ...  mtp_timing_elapsed waits for slots [first, first +
+ * count) and returns their summed kernel time (ms); a captured slot holds the
+ * timing of the graph's latest replay.  mtp_timing_end returns the sum over all
+ * used slots and their count, then releases the events.  Host-side state,
+ * process-wide; one class at a time.  Classes:
+ *   MTP_TIME_UNEMBED     the unembedding GEMV (lm_head, fused argmax partials)
+ *   MTP_TIME_ATTENTION   the attention kernel over the draft KV (not its merge)
+ *   MTP_TIME_VERIFY      the verification kernel that reads every logit (the
+ *                        per-chunk top-k pass, or the greedy argmax pass)
+ *   MTP_TIME_PROJECTION  every projection launch of the head other than the
+ *                        unembedding (fc, q/k/v, o, gate/up, down) */
+enum { MTP_TIME_UNEMBED = 0, MTP_TIME_ATTENTION = 1, MTP_TIME_VERIFY = 2, MTP_TIME_PROJECTION = 3 };
+int mtp_timing_begin(int32_t kind, int32_t max_launches);
 int mtp_timing_elapsed(int32_t first, int32_t count, float *total_ms);
 int mtp_timing_end(float *total_ms, int32_t *launches);
 

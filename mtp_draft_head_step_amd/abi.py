@@ -23,7 +23,7 @@ MTP_E_CAPACITY, MTP_E_HIP, MTP_E_DEVICE, MTP_E_WORKSPACE = -4, -5, -6, -7
 MTP_F32, MTP_BF16, MTP_I8G128 = 0, 1, 2
 KV_ONLY, LAST, ALL = 0, 1, 2
 TO_ROUND_BASE = -1
-DEV_OK, DEV_CAPACITY, DEV_ROLLBACK, DEV_COUNT = 0, 1, 2, 3
+DEV_OK, DEV_CAPACITY, DEV_ROLLBACK, DEV_COUNT, DEV_TOKEN = 0, 1, 2, 3, 4
 
 WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
                  "pre_fc_norm_hidden", "fc", "input_layernorm", "q_proj", "k_proj", "v_proj",
@@ -88,7 +88,7 @@ def _load():
     lib.kv_rollback.restype = C.c_int
     lib.kv_rollback.argtypes = [C.POINTER(mtp_kv), i32, vp, i32, vp]
     lib.mtp_timing_begin.restype = C.c_int
-    lib.mtp_timing_begin.argtypes = [i32]
+    lib.mtp_timing_begin.argtypes = [i32, i32]
     lib.mtp_timing_elapsed.restype = C.c_int
     lib.mtp_timing_elapsed.argtypes = [i32, i32, C.POINTER(C.c_float)]
     lib.mtp_timing_end.restype = C.c_int
@@ -190,8 +190,12 @@ def kv_rollback(kv, to_len, n_accepted=None, n_draft=0, stream=None):
     _check(st, "kv_rollback")
 
 
-def mtp_timing_begin(max_launches: int):
-    _check(lib.mtp_timing_begin(int(max_launches)), "mtp_timing_begin")
+TIME_UNEMBED, TIME_ATTENTION, TIME_VERIFY, TIME_PROJECTION = 0, 1, 2, 3
+
+
+def mtp_timing_begin(kind: int, max_launches: int):
+    """Time the next ``max_launches`` launches of kernel class ``kind``."""
+    _check(lib.mtp_timing_begin(int(kind), int(max_launches)), "mtp_timing_begin")
 
 
 def mtp_timing_elapsed(first: int, count: int) -> float:
@@ -201,7 +205,7 @@ def mtp_timing_elapsed(first: int, count: int) -> float:
 
 
 def mtp_timing_end():
-    """-> (summed unembedding kernel milliseconds, launches timed)."""
+    """-> (summed kernel milliseconds of the timed class, launches timed)."""
     ms = C.c_float()
     n = C.c_int32()
     _check(lib.mtp_timing_end(C.byref(ms), C.byref(n)), "mtp_timing_end")

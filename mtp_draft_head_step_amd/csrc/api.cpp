@@ -15,25 +15,30 @@ using namespace mtp;
 namespace {
 thread_local hipError_t g_last_hip = hipSuccess;
 
-// Event pairs bracketing unembedding launches while timing is on (benchmarks).
-struct UnembedTimer {
+// Event pairs bracketing the launches of one kernel class while timing is on
+// (benchmarks).
+struct KernelTimer {
   std::mutex mu;
   std::vector<hipEvent_t> start, stop;
   int used = 0;
+  int kind = -1;
   bool on = false;
 } g_timer;
+}  // namespace
 
-void timer_mark(bool before, hipStream_t s, int& slot_index) {
+void mtp::time_mark(int kind, bool before, hipStream_t s, int* slot) {
   std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (!g_timer.on) { slot_index = -1; return; }
+  if (!g_timer.on || g_timer.kind != kind) { *slot = -1; return; }
   if (before) {
-    if (g_timer.used >= static_cast<int>(g_timer.start.size())) { slot_index = -1; return; }
-    slot_index = g_timer.used++;
-    hipEventRecord(g_timer.start[slot_index], s);
-  } else if (slot_index >= 0) {
-    hipEventRecord(g_timer.stop[slot_index], s);
+    if (g_timer.used >= static_cast<int>(g_timer.start.size())) { *slot = -1; return; }
+    *slot = g_timer.used++;
+    hipEventRecord(g_timer.start[*slot], s);
+  } else if (*slot >= 0) {
+    hipEventRecord(g_timer.stop[*slot], s);
   }
 }
+
+namespace {
 }  // namespace
 
 #define MTP_TRY(expr)                  \
@@ -161,22 +166,31 @@ GemvArgs base_gemv(const mtp_head* h, const mtp_kv* kv) {
   return a;
 }
 
+// One GEMV launch, bracketed for the benchmark timer when `kind` >= 0.
+hipError_t timed_gemv(const GemvArgs& a, int wt, int nr, hipStream_t s, int* grid_out, int kind) {
+  int slot = -1;
+  if (kind >= 0) time_mark(kind, true, s, &slot);
+  const hipError_t e = launch_gemv(a, wt, nr, s, grid_out);
+  if (kind >= 0) time_mark(kind, false, s, &slot);
+  return e;
+}
+
 hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t s,
-                    int* grid_out = nullptr) {
+                    int* grid_out = nullptr, int kind = TIME_PROJECTION) {
   // ROWS_RANGE: blocks of up to 16 activation rows share one pass over the weights
   a.row_sel = row_sel;
   if (row_sel == ROW_LAST) {
     a.row_base = 0;
     a.kp = kp_for(a.K, wt, 1);
     a.grid_stride = a.kp == a.K;
-    return launch_gemv(a, wt, 1, s, grid_out);
+    return timed_gemv(a, wt, 1, s, grid_out, kind);
   }
   const int nr = nr_for(rows_total);
   a.kp = kp_for(a.K, wt, nr);
   a.grid_stride = a.kp == a.K;
   for (int b = 0; b < rows_total; b += nr) {
     a.row_base = b;
-    hipError_t e = launch_gemv(a, wt, nr, s);
+    hipError_t e = timed_gemv(a, wt, nr, s, nullptr, kind);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -203,7 +217,8 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.w[0] = h->w.fc; a.m[0] = H; a.M = H; a.K = 2 * H; a.lpr = lpr_for(2 * H, h->wt);
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_EMBED; a.nw = h->w.pre_fc_norm_embedding; a.nw2 = h->w.pre_fc_norm_hidden;
-  a.tok = tokens; a.embed = h->w.embed; a.embed_bf16 = h->wt == W_BF16;
+  a.tok = tokens; a.vocab_tok = c.vocab; a.err = kv->state + 3;
+  a.embed = h->w.embed; a.embed_bf16 = h->wt == W_BF16;
   a.hid = hiddens; a.hid_bf16 = c.act_dtype == MTP_BF16; a.ld_hid = H;
   a.out_mode = OUT_F32; a.y = x; a.ldy = H;
   MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
@@ -284,9 +299,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.out_mode = OUT_LOGITS; a.logits = logits;
   a.amax_part = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax));
   int tslot = -1, grid = 0;
-  timer_mark(true, s, tslot);
-  MTP_TRY(run_gemv(a, h->lmt, 1, ROW_LAST, s, &grid));
-  timer_mark(false, s, tslot);
+  time_mark(TIME_UNEMBED, true, s, &tslot);
+  MTP_TRY(run_gemv(a, h->lmt, 1, ROW_LAST, s, &grid, -1));
+  time_mark(TIME_UNEMBED, false, s, &tslot);
   if (static_cast<size_t>(grid) > amax_parts(c)) return MTP_E_UNSUPPORTED;   // cannot happen: sized above
   // 9. argmax of the partial keys, commit the append (len, round base)
   f.parts = a.amax_part; f.nparts = grid; f.amax_out = argmax;
@@ -433,8 +448,9 @@ int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
   return MTP_OK;
 }
 
-int mtp_timing_begin(int32_t max_launches) {
+int mtp_timing_begin(int32_t kind, int32_t max_launches) {
   if (max_launches < 1 || max_launches > (1 << 20)) return MTP_E_INVALID_ARG;
+  if (kind < MTP_TIME_UNEMBED || kind > MTP_TIME_PROJECTION) return MTP_E_INVALID_ARG;
   std::lock_guard<std::mutex> lk(g_timer.mu);
   for (hipEvent_t e : g_timer.start) hipEventDestroy(e);
   for (hipEvent_t e : g_timer.stop) hipEventDestroy(e);
@@ -448,6 +464,7 @@ int mtp_timing_begin(int32_t max_launches) {
     }
   }
   g_timer.used = 0;
+  g_timer.kind = kind;
   g_timer.on = true;
   return MTP_OK;
 }

@@ -356,6 +356,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int rows = (a.row_sel == ROW_LAST) ? 1 : a.n_max;
   const dim3 grid(a.nchunk, a.hkv, rows);
   hipError_t e;
+  int slot = -1;
+  time_mark(TIME_ATTENTION, true, s, &slot);
   if (a.kv_bf16) {
     switch (a.d) {
       case 64: e = attn_d<true, 64>(a, grid, s); break;
@@ -371,6 +373,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   }
+  time_mark(TIME_ATTENTION, false, s, &slot);
   if (e != hipSuccess) return e;
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_attn_merge, dim3(a.hq, rows), dim3(256), 0, s, a);

@@ -308,9 +308,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
                           (a.in_mode == IN_RMS) ? a.nw : nullptr, 0, a.nw_bf16, k0, k0 + klen, k0, se);
             } else {
               const int ea = k0, eb = min(k0 + klen, half);
-              if (ea < eb)
-                stage_range<XB>(dst, a.embed, static_cast<long long>(a.tok[jr]) * half, a.embed_bf16, a.nw, 0,
-                            a.nw_bf16, ea, eb, k0, se);
+              const int tk = a.tok[jr];
+              if (tk >= 0 && tk < a.vocab_tok) {
+                if (ea < eb)
+                  stage_range<XB>(dst, a.embed, static_cast<long long>(tk) * half, a.embed_bf16, a.nw, 0,
+                              a.nw_bf16, ea, eb, k0, se);
+              } else {
+                // a token outside the vocabulary: its embedding half stays zero and
+                // the KV error word is set (every later kernel is then a no-op)
+                for (int k = ea + tid; k < eb; k += kThreads) dst[k - k0] = XT(0);
+                if (a.err && blockIdx.x == 0 && tid == 0) *a.err = 4;
+              }
               const int ha = max(k0, half), hb = k0 + klen;
               if (ha < hb)
                 stage_range<XB>(dst, a.hid, static_cast<long long>(jr) * a.ld_hid - half, a.hid_bf16, a.nw2,

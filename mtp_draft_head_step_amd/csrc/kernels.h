@@ -6,6 +6,12 @@
 
 namespace mtp {
 
+// Benchmark timing hook (defined with the C ABI): brackets one launch of kernel
+// class `kind` with events on `s` when that class is being timed.  *slot
+// carries the event slot from the `before` call to the `after` call.
+void time_mark(int kind, bool before, hipStream_t s, int* slot);
+enum TimeKind { TIME_UNEMBED = 0, TIME_ATTENTION = 1, TIME_VERIFY = 2, TIME_PROJECTION = 3 };
+
 enum WType { W_F32 = 0, W_BF16 = 1, W_I8 = 2 };
 enum InMode { IN_F32 = 0, IN_RMS = 1, IN_EMBED = 2 };
 enum OutMode { OUT_F32 = 0, OUT_RESID = 1, OUT_SWIGLU = 2, OUT_LOGITS = 3 };
@@ -34,7 +40,9 @@ struct GemvArgs {
   const void* nw2;         // IN_EMBED hidden-half norm
   int nw_bf16;
   float eps;
-  const int32_t* tok;      // IN_EMBED
+  const int32_t* tok;      // IN_EMBED: token ids, valid in [0, vocab_tok)
+  int vocab_tok;
+  int32_t* err;            // IN_EMBED: state[3], set to 4 on a token out of range
   const void* embed;
   int embed_bf16;
   const void* hid;

@@ -27,6 +27,14 @@ __device__ __forceinline__ int window_token(const int32_t* ring, int head, int c
   return drafts[idx - count];
 }
 
+// The ring's state words as stored by the caller, brought into range: head in
+// [0, window), count in [0, window].
+__device__ __forceinline__ int ring_head(const VerifyArgs& a) {
+  const int h = a.ring_state[0] % a.window;
+  return h < 0 ? h + a.window : h;
+}
+__device__ __forceinline__ int ring_count(const VerifyArgs& a) { return min(max(a.ring_state[1], 0), a.window); }
+
 __device__ __forceinline__ float penalise(float v, float pen) { return v > 0.f ? v / pen : v * pen; }
 
 __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
@@ -37,8 +45,8 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
   const int lo = blockIdx.x * a.chunk;
   const int hi = min(a.vocab, lo + a.chunk);
   const bool pen = a.penalty != 1.0f;
-  const int head = a.ring_state[0];
-  const int count = a.ring_state[1];
+  const int head = ring_head(a);
+  const int count = ring_count(a);
   if (pen) {
     for (int w = tid; w < kVMaxChunk / 32; w += kVThreads) bits[w] = 0u;
     __syncthreads();
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a
   for (int r = 0; r < n; ++r) {
     if (a.drafts[r] != am[r]) { k = r; break; }
   }
-  int h = a.ring_state[0], c = a.ring_state[1];
+  int h = ring_head(a), c = ring_count(a);
   for (int r = 0; r <= k; ++r) {
     const int t = r < k ? a.drafts[r] : am[k];
     a.out_tokens[r] = t;
@@ -98,7 +106,10 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
   const int nb = (a.vocab + a.chunk - 1) / a.chunk;
   (void)hipGetLastError();
+  int slot = -1;
+  time_mark(TIME_VERIFY, true, s, &slot);
   hipLaunchKernelGGL(k_verify_greedy, dim3(nb, a.n_draft + 1), dim3(kVThreads), 0, s, a);
+  time_mark(TIME_VERIFY, false, s, &slot);
   hipLaunchKernelGGL(k_verify_greedy_finish, dim3(1), dim3(kVThreads), 0, s, a, nb);
   return hipGetLastError();
 }
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
   const int hi = min(a.vocab, lo + kSChunk);
   const bool pen = a.penalty != 1.0f;
   if (pen) {
-    const int head = a.ring_state[0], count = a.ring_state[1];
+    const int head = ring_head(a), count = ring_count(a);
     for (int w = tid; w < kSChunk / 32; w += kVThreads) bits[w] = 0u;
     __syncthreads();
     const int total = count + i;
@@ -338,7 +349,7 @@ __global__ void k_sample_decide(VerifyArgs a, SampledScratch sc) {
     break;
   }
   if (k == n) tok = draw(sc, n, -1, a.uniforms[n]);
-  int h = a.ring_state[0], c = a.ring_state[1];
+  int h = ring_head(a), c = ring_count(a);
   for (int r = 0; r <= k; ++r) {
     const int t = r < k ? a.drafts[r] : tok;
     a.out_tokens[r] = t;
@@ -373,7 +384,10 @@ hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
     raised = true;
   }
   (void)hipGetLastError();
+  int slot = -1;
+  time_mark(TIME_VERIFY, true, s, &slot);
   hipLaunchKernelGGL(k_sample_chunk, dim3(nb, rows), dim3(kVThreads), 0, s, a, sc, nb, kk);
+  time_mark(TIME_VERIFY, false, s, &slot);
   hipLaunchKernelGGL(k_sample_row, dim3(rows), dim3(kVThreads), static_cast<size_t>(n2) * 8, s, a, sc, nb, kk,
                      n2, a.top_k);
   hipLaunchKernelGGL(k_sample_decide, dim3(1), dim3(64), 0, s, a, sc);

@@ -51,20 +51,29 @@ class RoundState:
 
 
 def run_round(st: RoundState, n_draft: int, target_fn, sp: Sampling = GREEDY,
-              policy: str = "A", uniforms=None, draft_rows_fn=None):
+              policy: str = "A", uniforms=None, draft_rows_fn=None, forced_drafts=None):
     """Run one round in place.  ``target_fn(tokens_in, start_pos)`` returns
     (logits [N + 1, V] fp32, hiddens [N + 1, H]) for tokens_in = [current] + drafts
-    processed at positions start_pos + j.  Returns a dict with the drafts, k and
-    the committed tokens."""
+    processed at positions start_pos + j.  Returns a dict with the drafts, k, the
+    committed tokens and each draft step's logits.
+
+    ``forced_drafts`` (comparisons only) replaces each step's argmax by the given
+    token when the chain continues, so a run can follow another implementation
+    through a near tie; the returned logits are still this oracle's own."""
     head, kv = st.head, st.kv
     toks = [t for t, _ in st.pending]
     hids = [h for _, h in st.pending]
     out = head.flush(kv, toks, hids, LAST, set_round_base=True)
-    drafts = [out["argmax"]]
+
+    def pick(i, o):
+        return int(forced_drafts[i]) if forced_drafts is not None else o["argmax"]
+    drafts = [pick(0, out)]
+    draft_logits = [out["logits"]]
     g = out["g"][-1]
-    for _ in range(1, n_draft):
+    for i in range(1, n_draft):
         o = head.step(kv, drafts[-1], g)
-        drafts.append(o["argmax"])
+        drafts.append(pick(i, o))
+        draft_logits.append(o["logits"])
         g = o["g"][-1]
     c = len(st.committed) - 1                    # position of the current token
     rows, hid_rows = target_fn([st.committed[-1]] + drafts, c)
@@ -82,7 +91,7 @@ def run_round(st: RoundState, n_draft: int, target_fn, sp: Sampling = GREEDY,
         raise ValueError(policy)
     st.pending = [(committed[j], hid_rows[j]) for j in range(j0, k + 1)]
     st.committed.extend(committed)
-    return {"drafts": drafts, "k": k, "tokens": committed}
+    return {"drafts": drafts, "k": k, "tokens": committed, "draft_logits": draft_logits}
 
 
 def classic_greedy(target_fn, committed, n_new: int, sp: Sampling = GREEDY, ring=None, ring_state=None):

@@ -246,8 +246,7 @@ def test_depth_rounds_parity(lm, policy, n_draft):
     pend_h[0] = device_array(hid0[0])
     n_dev = torch.tensor([1], dtype=torch.int32, device="cuda")
     gpu_committed = list(committed)
-    diverged = False
-    n_diverged = 0
+    near_ties = 0
     for rnd in range(12):
         base = int(host(gkv.state)[0])
         abi.mtp_flush_pairs(gh, gkv, pend_t, pend_h, N + 1, n_dev, abi.LAST, 1, g_buf[0], None, d_buf[0:1], ws)
@@ -270,17 +269,20 @@ def test_depth_rounds_parity(lm, policy, n_draft):
         pend_h[: k + 1 - j0] = device_array(hid_st[j0:k + 1])
         n_dev.fill_(k + 1 - j0)
         gpu_committed += toks
-        out = R.run_round(ost, N, fn, policy=policy)
-        diverged = diverged or out["drafts"] != drafts          # a draft near tie: both valid
-        n_diverged += out["drafts"] != drafts
-        assert out["k"] == k_r
+        # the oracle round follows the GPU's drafts; where they differ from the
+        # oracle's argmax the oracle's top-two margin must be within the logits
+        # tolerance (a near tie, where either token is correct)
+        out = R.run_round(ost, N, fn, policy=policy, forced_drafts=drafts)
+        for i, lg in enumerate(out["draft_logits"]):
+            ref_tok = int(np.argmax(lg))
+            if ref_tok != drafts[i]:
+                near_ties += 1
+                assert lg[ref_tok] - lg[drafts[i]] <= 2 * tol * np.max(np.abs(lg)), (rnd, i)
+        assert out["k"] == k_r and out["tokens"] == toks
         st_now = host(gkv.state)
         assert st_now[3] == 0
-        if not diverged:
-            assert out["tokens"] == toks
-            assert st_now[0] == ost.kv.len and st_now[1] == ost.kv.base
-            # every entry the round appended (flushed pairs and chained drafts)
-            _check_slots(gkv, ost.kv, base, appended, tol)
-    if not diverged:
-        assert gpu_committed == ost.committed
-    assert n_diverged == 0      # these seeds have no draft near tie
+        assert st_now[0] == ost.kv.len and st_now[1] == ost.kv.base
+        # every entry the round appended (flushed pairs and chained drafts)
+        _check_slots(gkv, ost.kv, base, appended, tol)
+    assert gpu_committed == ost.committed
+    assert near_ties <= 2

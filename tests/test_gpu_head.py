@@ -185,3 +185,21 @@ def test_capacity_and_count_errors_are_sticky():
     abi.kv_rollback(gkv, 2)
     torch.cuda.synchronize()
     assert host(gkv.state).tolist() == [6, 6, 0, abi.DEV_CAPACITY]
+
+
+@pytest.mark.parametrize("bad", [-1, 1024, 1 << 30])
+def test_token_out_of_range_sets_error(bad):
+    """A pair whose token is outside [0, vocab) is not read from the embedding
+    table: the KV error word becomes MTP_DEV_TOKEN and nothing is appended."""
+    from mtp_draft_head_step_amd import abi
+    shape = I.TINY_F32
+    _, gh, _ = build(shape, 82)
+    gkv, _ = kv_pair(shape, 82, 6, 64)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, 4, 64))
+    toks = I.tokens_uniform(82, 3, 4, shape.vocab)
+    toks[2] = bad
+    hids = device_array(I.target_hiddens(shape, 82, 3, 4))
+    hout = torch.empty((1, shape.hidden), dtype=torch.float32, device="cuda")
+    abi.mtp_flush_pairs(gh, gkv, device_array(toks), hids, 4, None, OH.LAST, 1, hout, None, None, ws)
+    torch.cuda.synchronize()
+    assert host(gkv.state).tolist() == [6, 6, 0, abi.DEV_TOKEN]
