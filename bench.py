@@ -448,9 +448,9 @@ def run_flush(args):
         "algorithmic_gflop": {"attention": round(att_flops / 1e9, 4), "projections": round(proj_flops / 1e9, 4)},
         "projection_us_per_flush": round(proj_ms / side * 1e3, 2),
         "projection_launches_per_flush": proj_n // side,
-        "roofline": roofline("alu", att_flops / att_avg / 1e12, VALU_FP32_PEAK_TFLOPS, "TFLOP/s", None,
-                             kernel="causal flush attention (256 rows x 4 q heads over 8193..8448 keys; "
-                                    "fp32 VALU dot products)",
+        "roofline": roofline("mfma", att_flops / att_avg / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None,
+                             kernel="causal flush attention on bf16 MFMA (256 rows x 4 q heads over "
+                                    "8193..8448 keys; 16 key chunks, split-K partials)",
                              flops_per_launch=att_flops, avg_us=round(att_avg * 1e6, 2), launches=att_n),
         "cpu_baseline": cpu,
     })

@@ -98,9 +98,12 @@ int nchunk_for(const mtp_head_config& c, int capacity) {
 }
 
 struct Layout {
-  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, total;
+  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, xa, total;
   int nchunk;
 };
+
+// Flushes of more rows than one GEMV pass covers go through the MFMA tiles.
+constexpr int kGemvMaxRows = 16;
 
 // upper bound on the unembedding GEMV's workgroup count (one argmax key each)
 size_t amax_parts(const mtp_head_config& c) { return static_cast<size_t>(c.vocab) / 4 + 2048; }
@@ -121,6 +124,7 @@ Layout layout(const mtp_head_config& c, int rows, int capacity) {
   L.m = take(rows * I * 4);
   L.g = take(rows * H * 4);
   L.amax = take(amax_parts(c) * 8);
+  L.xa = rows > kGemvMaxRows ? take(rows * 2 * H * 2) : off;   // bf16 normalised rows
   L.total = off;
   return L;
 }
@@ -196,6 +200,35 @@ hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t
   return hipSuccess;
 }
 
+hipError_t timed_gemm(const GemmArgs& g, hipStream_t s) {
+  int slot = -1;
+  time_mark(TIME_PROJECTION, true, s, &slot);
+  const hipError_t e = launch_gemm(g, s);
+  time_mark(TIME_PROJECTION, false, s, &slot);
+  return e;
+}
+
+GemmArgs base_gemm(const mtp_kv* kv, int n_max, const int32_t* n_dev) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.n_max = n_max;
+  g.n_dev = n_dev;
+  g.kv_state = kv->state;
+  return g;
+}
+
+PrepArgs base_prep(const mtp_head* h, const mtp_kv* kv, int n_max, const int32_t* n_dev, uint16_t* out) {
+  PrepArgs p;
+  std::memset(&p, 0, sizeof(p));
+  p.n_max = n_max;
+  p.n_dev = n_dev;
+  p.kv_state = kv->state;
+  p.nw_bf16 = h->wt == W_BF16;
+  p.eps = h->cfg.rms_eps;
+  p.out = out;
+  return p;
+}
+
 // The head forward for n rows (n_max host bound, n_dev device count).
 // mode: KV_ONLY / LAST / ALL.  hidden_out: [1 or n, H] in act dtype (nullable).
 int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, const void* hiddens,
@@ -212,7 +245,31 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   float* x1 = reinterpret_cast<float*>(wsp(ws, L.x1));
   float* m = reinterpret_cast<float*>(wsp(ws, L.m));
   float* g = reinterpret_cast<float*>(wsp(ws, L.g));
+  uint16_t* xa = reinterpret_cast<uint16_t*>(wsp(ws, L.xa));
+  // many rows with bf16 weights: normalised rows + MFMA tiles instead of GEMV passes
+  const bool mfma = h->wt == W_BF16 && n_max > kGemvMaxRows;
+  if (mfma) {
+    const int mq[3] = {hq * D, hkv * D, hkv * D};
+    const int mh[1] = {H};
+    const int mi[1] = {I};
+    if (!gemm_supported(H, 2 * H, mh, 1) || !gemm_supported(qkv_rows, H, mq, 3) ||
+        !gemm_supported(H, hq * D, mh, 1) || !gemm_supported(I, H, mi, 1) || !gemm_supported(H, I, mh, 1))
+      return MTP_E_UNSUPPORTED;
+  }
   // 1. x = W_fc [RMSNorm(E[t]) | RMSNorm(h)]
+  if (mfma) {
+    PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+    p.in_mode = IN_EMBED; p.K = 2 * H; p.ld_out = 2 * H;
+    p.nw = h->w.pre_fc_norm_embedding; p.nw2 = h->w.pre_fc_norm_hidden;
+    p.tok = tokens; p.vocab_tok = c.vocab; p.err = kv->state + 3;
+    p.embed = h->w.embed; p.embed_bf16 = 1;
+    p.hid = hiddens; p.hid_bf16 = c.act_dtype == MTP_BF16; p.ld_hid = H;
+    MTP_TRY(launch_rows_prep(p, s));
+    GemmArgs m1 = base_gemm(kv, n_max, n_dev);
+    m1.w[0] = static_cast<const uint16_t*>(h->w.fc); m1.m[0] = H; m1.M = H; m1.K = 2 * H;
+    m1.a = xa; m1.lda = 2 * H; m1.out_mode = OUT_F32; m1.y = x; m1.ldy = H;
+    MTP_TRY(timed_gemm(m1, s));
+  }
   GemvArgs a = base_gemv(h, kv);
   a.w[0] = h->w.fc; a.m[0] = H; a.M = H; a.K = 2 * H; a.lpr = lpr_for(2 * H, h->wt);
   a.n_max = n_max; a.n_dev = n_dev;
@@ -221,9 +278,20 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.embed = h->w.embed; a.embed_bf16 = h->wt == W_BF16;
   a.hid = hiddens; a.hid_bf16 = c.act_dtype == MTP_BF16; a.ld_hid = H;
   a.out_mode = OUT_F32; a.y = x; a.ldy = H;
-  MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
+  if (!mfma) MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
 
   // 2. q, k, v = W_{q,k,v} RMSNorm(x; w_in)
+  if (mfma) {
+    PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+    p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x; p.ldx = H; p.nw = h->w.input_layernorm;
+    MTP_TRY(launch_rows_prep(p, s));
+    GemmArgs m2 = base_gemm(kv, n_max, n_dev);
+    m2.w[0] = static_cast<const uint16_t*>(h->w.q_proj); m2.m[0] = hq * D;
+    m2.w[1] = static_cast<const uint16_t*>(h->w.k_proj); m2.m[1] = hkv * D;
+    m2.w[2] = static_cast<const uint16_t*>(h->w.v_proj); m2.m[2] = hkv * D;
+    m2.M = qkv_rows; m2.K = H; m2.a = xa; m2.lda = H; m2.out_mode = OUT_F32; m2.y = qkv; m2.ldy = qkv_rows;
+    MTP_TRY(timed_gemm(m2, s));
+  }
   a = base_gemv(h, kv);
   a.w[0] = h->w.q_proj; a.m[0] = hq * D;
   a.w[1] = h->w.k_proj; a.m[1] = hkv * D;
@@ -232,7 +300,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_RMS; a.x = x; a.ldx = H; a.nw = h->w.input_layernorm;
   a.out_mode = OUT_F32; a.y = qkv; a.ldy = qkv_rows;
-  MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
+  if (!mfma) MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
 
   // 3. q/k norm + RoPE, append K/V at slots len + j, advance len
   RopeArgs r;
@@ -252,6 +320,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   }
 
   const int rsel = (mode == MTP_FLUSH_ALL) ? ROWS_RANGE : ROW_LAST;
+  const bool mfma_out = mfma && rsel == ROWS_RANGE;   // o, MLP over every row
 
   // 4. attention over the draft KV
   AttnArgs t;
@@ -259,6 +328,13 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   t.q = qr; t.kc = kv->k; t.vc = kv->v; t.kv_bf16 = c.kv_dtype == MTP_BF16; t.capacity = kv->capacity;
   t.state = kv->state; t.hq = hq; t.hkv = hkv; t.d = D; t.n_max = n_max; t.n_dev = n_dev;
   t.row_sel = rsel; t.nchunk = L.nchunk;
+  if (mfma_out && c.kv_dtype == MTP_BF16) {
+    // matrix-core flush attention: about 256 workgroups of 64 query vectors
+    const int qblocks = (n_max * (hq / hkv) + 63) / 64;
+    int ns = (256 + qblocks * hkv - 1) / (qblocks * hkv);
+    t.mfma = 1;
+    t.nchunk = ns < 1 ? 1 : (ns > L.nchunk ? L.nchunk : ns);
+  }
   t.part_o = reinterpret_cast<float*>(wsp(ws, L.part_o));
   t.part_ml = reinterpret_cast<float*>(wsp(ws, L.part_ml));
   t.o = o;
@@ -270,7 +346,15 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_F32; a.x = o; a.ldx = hq * D;
   a.out_mode = OUT_RESID; a.res = x; a.ldres = H; a.y = x1; a.ldy = H;
-  MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+  if (mfma_out) {
+    GemmArgs m5 = base_gemm(kv, n_max, n_dev);
+    m5.w[0] = static_cast<const uint16_t*>(h->w.o_proj); m5.m[0] = H; m5.M = H; m5.K = hq * D;
+    m5.a = o; m5.a_f32 = 1; m5.lda = hq * D;
+    m5.out_mode = OUT_RESID; m5.res = x; m5.ldres = H; m5.y = x1; m5.ldy = H;
+    MTP_TRY(timed_gemm(m5, s));
+  } else {
+    MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+  }
 
   // 6. m = silu(W_g b) * (W_u b), b = RMSNorm(x1; w_post)
   a = base_gemv(h, kv);
@@ -279,7 +363,18 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_RMS; a.x = x1; a.ldx = H; a.nw = h->w.post_attention_layernorm;
   a.out_mode = OUT_SWIGLU; a.y = m; a.ldy = I;
-  MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+  if (mfma_out) {
+    PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+    p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x1; p.ldx = H; p.nw = h->w.post_attention_layernorm;
+    MTP_TRY(launch_rows_prep(p, s));
+    GemmArgs m6 = base_gemm(kv, n_max, n_dev);
+    m6.w[0] = static_cast<const uint16_t*>(h->w.gate_proj); m6.m[0] = I;
+    m6.w[1] = static_cast<const uint16_t*>(h->w.up_proj); m6.m[1] = I;
+    m6.M = I; m6.K = H; m6.a = xa; m6.lda = H; m6.out_mode = OUT_SWIGLU; m6.y = m; m6.ldy = I;
+    MTP_TRY(timed_gemm(m6, s));
+  } else {
+    MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+  }
 
   // 7. g = x1 + W_d m  (also written to hidden_out in the activation dtype)
   a = base_gemv(h, kv);
@@ -288,7 +383,16 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.in_mode = IN_F32; a.x = m; a.ldx = I;
   a.out_mode = OUT_RESID; a.res = x1; a.ldres = H; a.y = g; a.ldy = H;
   a.y2 = hidden_out; a.y2_bf16 = c.act_dtype == MTP_BF16; a.ldy2 = H;
-  MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+  if (mfma_out) {
+    GemmArgs m7 = base_gemm(kv, n_max, n_dev);
+    m7.w[0] = static_cast<const uint16_t*>(h->w.down_proj); m7.m[0] = H; m7.M = H; m7.K = I;
+    m7.a = m; m7.a_f32 = 1; m7.lda = I;
+    m7.out_mode = OUT_RESID; m7.res = x1; m7.ldres = H; m7.y = g; m7.ldy = H;
+    m7.y2 = hidden_out; m7.y2_bf16 = c.act_dtype == MTP_BF16; m7.ldy2 = H;
+    MTP_TRY(timed_gemm(m7, s));
+  } else {
+    MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+  }
 
   // 8. logits = W_lm RMSNorm(g; w_norm) of the last row, with its argmax
   a = base_gemv(h, kv);

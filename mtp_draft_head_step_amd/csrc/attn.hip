@@ -358,7 +358,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipError_t e;
   int slot = -1;
   time_mark(TIME_ATTENTION, true, s, &slot);
-  if (a.kv_bf16) {
+  if (a.mfma && a.kv_bf16 && a.row_sel == ROWS_RANGE) {
+    e = launch_attention_flush(a, s);
+  } else if (a.kv_bf16) {
     switch (a.d) {
       case 64: e = attn_d<true, 64>(a, grid, s); break;
       case 128: e = attn_d<true, 128>(a, grid, s); break;

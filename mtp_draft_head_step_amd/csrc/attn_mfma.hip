@@ -1,0 +1,201 @@
+// Causal attention of the many-row pending-pair flush on the gfx950 matrix
+// cores (bf16 draft KV).
+//
+// Flush row j (slot off + j) attends over keys [0, off + j] of its kv head
+// (the head's own draft cache; "feat(inference): support the qwen3_5_mtp
+// drafter ...", section "Upstream contract to port": one full-attention layer).
+// The query vectors of a kv head are the (row, grouped head) pairs, taken 64 at
+// a time by a workgroup (16 per wave) over one key chunk; chunks are merged by
+// the log-sum-exp merge of the split-K decode path, so the partial (o, m, l)
+// layout is the same.
+//
+// Per 64-key block a wave computes its 16 x 64 scores transposed, S^T = K Q^T,
+// with v_mfma_f32_16x16x32_bf16 (K rows straight from LDS as the A operand, the
+// wave's bf16 queries held in registers as B), runs the online softmax per
+// query (a query's 64 scores sit in the four lanes that share lane % 16), and
+// accumulates O^T += V^T P^T: the probabilities never leave registers, because
+// the B operand of that product takes each lane's own score values (keys
+// 32s + 4 (lane/16) + {0..3} and 32s + 16 + 4 (lane/16) + {0..3}) and the A
+// operand reads V^T (staged transposed in LDS) at the same keys.
+#include "common.h"
+#include "kernels.h"
+
+namespace mtp {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8v;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
+
+constexpr int kFKeys = 64;     // keys per block
+constexpr int kFQ = 64;        // query vectors per workgroup (16 per wave)
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_flush(AttnArgs a) {
+  constexpr int KLD = D + 8;          // bf16 per LDS K row
+  constexpr int VLD = kFKeys + 8;     // bf16 per LDS V^T row
+  constexpr int DK = D / 32;          // 32-wide head_dim steps of S^T
+  constexpr int DT = D / 16;          // 16-row head_dim tiles of O^T
+  constexpr float kNeg = -INFINITY;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kFKeys * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VLD];
+
+  const int32_t* st = a.state;
+  if (st[3] != 0) return;
+  int n = a.n_max;
+  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  const int G = a.hq / a.hkv;
+  const int nq = n * G;
+  const int qb = blockIdx.y * kFQ;
+  if (qb >= nq) return;
+  const int kvh = blockIdx.z;
+  const int c = blockIdx.x;
+  const int off = st[0];                    // pre-append length (committed by k_finish)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // the key chunk, and the keys this workgroup's rows can see
+  int ck = (off + n + a.nchunk - 1) / a.nchunk;
+  ck = (ck + kFKeys - 1) / kFKeys * kFKeys;
+  const int jmax = min(n, (qb + kFQ - 1) / G + 1) - 1;      // last row in this workgroup
+  const int k0 = c * ck;
+  const int k1 = min(k0 + ck, off + jmax + 1);
+
+  // this lane's query vector (column lane % 16 of the wave's S^T tiles)
+  const int qv = qb + wave * 16 + (lane & 15);
+  const bool qok = qv < nq;
+  const int jq = qok ? qv / G : 0;
+  const int head = kvh * G + (qok ? qv % G : 0);
+  const int kmax = off + jq;                                 // last key row jq sees
+  const float scale = rsqrtf(static_cast<float>(D));
+  bf16x8v qf[DK];
+  {
+    const float* qp = a.q + (static_cast<size_t>(jq) * a.hq + head) * D + (lane >> 4) * 8;
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = qok ? qp[dk * 32 + 2 * i] * scale : 0.f;
+        const float x1 = qok ? qp[dk * 32 + 2 * i + 1] * scale : 0.f;
+        w[i] = f32_to_bf16(x0) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
+      }
+      qf[dk] = __builtin_bit_cast(bf16x8v, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  }
+
+  f32x4v acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  float m = kNeg, l = 0.f;
+
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + static_cast<size_t>(kvh) * a.capacity * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + static_cast<size_t>(kvh) * a.capacity * D;
+  constexpr int kChunks = kFKeys * D / 8;                    // 16-byte pieces per block
+
+  for (int kb = k0; kb < k1; kb += kFKeys) {
+    __syncthreads();
+    // stage K rows and V^T of keys [kb, kb + 64) (rows past k1 as zeros)
+    for (int e = tid; e < kChunks; e += 256) {
+      const int key = e / (D / 8), d8 = (e % (D / 8)) * 8;
+      uint4 kv4 = make_uint4(0u, 0u, 0u, 0u), vv4 = make_uint4(0u, 0u, 0u, 0u);
+      if (kb + key < k1) {
+        kv4 = *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(kb + key) * D + d8);
+        vv4 = *reinterpret_cast<const uint4*>(vc + static_cast<size_t>(kb + key) * D + d8);
+      }
+      *reinterpret_cast<uint4*>(Ks + key * KLD + d8) = kv4;
+      const uint32_t vw[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Vt[(d8 + 2 * i) * VLD + key] = static_cast<uint16_t>(vw[i] & 0xFFFFu);
+        Vt[(d8 + 2 * i + 1) * VLD + key] = static_cast<uint16_t>(vw[i] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // S^T for four 16-key tiles
+    f32x4v s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) {
+        const bf16x8v kf = __builtin_bit_cast(bf16x8v,
+            *reinterpret_cast<const uint4*>(Ks + (kt * 16 + (lane & 15)) * KLD + dk * 32 + (lane >> 4) * 8));
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[dk], s[kt], 0, 0, 0);
+      }
+    }
+    // causal mask and the online softmax of query lane % 16
+    float bmax = kNeg;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + kt * 16 + (lane >> 4) * 4 + i;
+        if (!qok || key >= k1 || key > kmax) s[kt][i] = kNeg;
+        bmax = fmaxf(bmax, s[kt][i]);
+      }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const float mnew = fmaxf(m, bmax);
+    const float r = (mnew == kNeg) ? 1.f : __expf(m - mnew);
+    m = mnew;
+    l *= r;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] *= r;
+    uint32_t pw[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (s[kt][i] == kNeg) ? 0.f : __expf(s[kt][i] - mnew);
+        l += p[i];
+      }
+      pw[kt][0] = f32_to_bf16(p[0]) | (static_cast<uint32_t>(f32_to_bf16(p[1])) << 16);
+      pw[kt][1] = f32_to_bf16(p[2]) | (static_cast<uint32_t>(f32_to_bf16(p[3])) << 16);
+    }
+    // O^T += V^T P^T over two 32-key steps
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8v pf = __builtin_bit_cast(bf16x8v,
+          make_uint4(pw[2 * ks][0], pw[2 * ks][1], pw[2 * ks + 1][0], pw[2 * ks + 1][1]));
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const uint16_t* vrow = Vt + (t * 16 + (lane & 15)) * VLD + ks * 32 + (lane >> 4) * 4;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const bf16x8v vf = __builtin_bit_cast(bf16x8v, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // the chunk's partial: o (unnormalised), m, l for each query vector
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!qok) return;
+  const size_t pidx = (static_cast<size_t>(jq) * a.hq + head) * a.nchunk + c;
+  float* po = a.part_o + pidx * D;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const int d = t * 16 + (lane >> 4) * 4;
+    *reinterpret_cast<float4*>(po + d) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+  }
+  if ((lane >> 4) == 0) {
+    a.part_ml[pidx * 2] = m;
+    a.part_ml[pidx * 2 + 1] = l;
+  }
+}
+
+hipError_t launch_attention_flush(const AttnArgs& a, hipStream_t s) {
+  const int G = a.hq / a.hkv;
+  const dim3 grid(a.nchunk, (a.n_max * G + kFQ - 1) / kFQ, a.hkv);
+  (void)hipGetLastError();
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL(k_attn_flush<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(k_attn_flush<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(k_attn_flush<256>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mtp

@@ -65,6 +65,61 @@ struct GemvArgs {
 // *grid_out (nullable) receives the number of workgroups launched.
 hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s, int* grid_out = nullptr);
 
+// Normalised bf16 input rows for the matrix-core projections: RMSNorm(x; nw)
+// (IN_RMS) or [RMSNorm(E[tok]; nw) | RMSNorm(hid; nw2)] (IN_EMBED, K = 2H), one
+// row per activation row j < n.
+struct PrepArgs {
+  int in_mode;
+  int K;
+  int n_max;
+  const int32_t* n_dev;
+  const int32_t* kv_state;   // skip everything when state[3] != 0
+  const float* x;
+  int ldx;
+  const void* nw;
+  const void* nw2;
+  int nw_bf16;
+  float eps;
+  const int32_t* tok;
+  int vocab_tok;
+  int32_t* err;              // state[3], set to 4 on a token out of range
+  const void* embed;
+  int embed_bf16;
+  const void* hid;
+  int hid_bf16;
+  int ld_hid;
+  uint16_t* out;             // [n_max, ld_out] bf16
+  int ld_out;
+};
+hipError_t launch_rows_prep(const PrepArgs& a, hipStream_t s);
+
+// Y[j, c] = sum_k A[j, k] W[c, k] over activation rows j < n on bf16 MFMA tiles
+// (64 rows x 64 columns per workgroup).  W: up to three stacked bf16 matrices
+// (OUT_SWIGLU: w[0] gate and w[1] up, M rows each).  A: bf16 rows, or fp32 rows
+// rounded to bf16 on load (a_f32).  Requires M, K and every m[i] multiples of 64.
+struct GemmArgs {
+  const uint16_t* w[3];
+  int m[3];
+  int M;
+  int K;
+  int n_max;
+  const int32_t* n_dev;
+  const int32_t* kv_state;
+  const void* a;
+  int a_f32;
+  int lda;
+  int out_mode;              // OUT_F32, OUT_RESID or OUT_SWIGLU
+  float* y;
+  int ldy;
+  const float* res;
+  int ldres;
+  void* y2;                  // optional copy of y in the activation dtype
+  int y2_bf16;
+  int ldy2;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+bool gemm_supported(int M, int K, const int* m, int nmat);
+
 // q/k RMSNorm + RoPE for rows j < n at positions state[0] + j, append k, v to
 // the cache, write roped q to `q_out`.  state[0] is advanced later by k_finish.
 struct RopeArgs {
@@ -100,11 +155,13 @@ struct AttnArgs {
   const int32_t* n_dev;
   int row_sel;             // ROWS_RANGE: rows 0..n-1; ROW_LAST: row n-1
   int nchunk;              // chunks per (row, kv head)
+  int mfma;                // ROWS_RANGE over bf16 K/V: the matrix-core flush kernel
   float* part_o;           // [rows, Hq, nchunk, D]
   float* part_ml;          // [rows, Hq, nchunk, 2]
   float* o;                // [rows, Hq * D]
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_flush(const AttnArgs& a, hipStream_t s);   // the mfma path's first kernel
 
 // End of a step or flush: merge the unembedding's per-workgroup argmax keys
 // (if any) into *amax_out and commit the append: state[0] += n (state[1] too

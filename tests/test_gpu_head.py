@@ -203,3 +203,50 @@ def test_token_out_of_range_sets_error(bad):
     abi.mtp_flush_pairs(gh, gkv, device_array(toks), hids, 4, None, OH.LAST, 1, hout, None, None, ws)
     torch.cuda.synchronize()
     assert host(gkv.state).tolist() == [6, 6, 0, abi.DEV_TOKEN]
+
+
+# head_dim 128 and 256 with grouped heads 4 and 6: the matrix-core flush kernels
+# at their other tile shapes (bf16 weights, activations and KV)
+MID_SHAPES = {
+    "d128_g4": I.HeadShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
+                           vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
+                                                   lm_head_dtype=I.BF16),
+    "d256_g6": I.HeadShape(hidden=512, n_q_heads=6, n_kv_heads=1, head_dim=256, intermediate=1536,
+                           vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
+                                                   lm_head_dtype=I.BF16),
+}
+
+
+@pytest.mark.parametrize("name", list(MID_SHAPES))
+@pytest.mark.parametrize("n, n_max", [(17, 17), (70, 100), (130, 130)])
+def test_flush_many_rows_parity(name, n, n_max):
+    """ALL-mode flushes past 16 rows (the matrix-core projections and attention)
+    at head_dim 128/256, every row's g, the last logits and the appended K/V."""
+    from mtp_draft_head_step_amd import abi
+    shape = MID_SHAPES[name]
+    tol = tol_of(shape)
+    wl = 90 + n
+    _, gh, oh = build(shape, wl)
+    cap, prefix = 1024, 333
+    gkv, okv = kv_pair(shape, wl, prefix, cap)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, n_max, cap))
+    toks = I.tokens_uniform(wl, 1, n_max, shape.vocab)
+    hids = I.target_hiddens(shape, wl, 1, n_max)
+    hout = torch.zeros((n_max, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    n_dev = torch.tensor([n], dtype=torch.int32, device="cuda")
+    abi.mtp_flush_pairs(gh, gkv, device_array(toks), device_array(hids), n_max, n_dev, OH.ALL, 1,
+                        hout, logits, amax, ws)
+    torch.cuda.synchronize()
+    ref = oh.flush(okv, [int(t) for t in toks[:n]], [I.decode(h, shape.act_dtype) for h in hids[:n]],
+                   OH.ALL, set_round_base=True)
+    assert host(gkv.state).tolist() == [prefix + n, prefix + n, 0, 0]
+    check_kv(gkv, okv, shape, prefix, prefix + n, tol)
+    lg = host(logits)
+    assert rel_err(lg, ref["logits"]) <= tol
+    assert argmax_ok(int(host(amax)[0]), ref["logits"], lg)[0]
+    g = host(hout)
+    for j in range(n):
+        assert rel_err(g[j], ref["g"][j]) <= tol, j
+    assert np.all(g[n:] == 0)
