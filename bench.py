@@ -216,7 +216,10 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
     head = abi.Head(shape, storage)
     cap = ctx + 1 + (args.warmup + args.steps + 4) * (N + 1) + 64
     kp, vp = I.prefix_kv(shape, wl, ctx, cap)
-    kv = abi.DraftKV(shape, cap, kp, vp, ctx)
+    # one device buffer {KV state words | k, k+1, committed tokens}: the round's
+    # results reach the host in one copy
+    iost = torch.zeros(4 + 2 + N + 1, dtype=torch.int32, device="cuda")
+    kv = abi.DraftKV(shape, cap, kp, vp, ctx, state=iost[0:4])
     pool_logits = np.stack([I.logits_rows(wl, 5, r, N + 1, V, 3.0)[0] for r in range(POOL)])
     pool_hid = np.stack([I.target_hiddens(shape, wl, r, N + 1) for r in range(POOL)])
     first_tok = I.tokens_uniform(wl, 0, N + 1, V)
@@ -227,7 +230,7 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
     t_hid = abi.to_device(pool_hid)
     ring = abi.to_device(ring0)
     ring_st = abi.to_device(ring_st0)
-    io = torch.zeros(2 + N + 1, dtype=torch.int32, device="cuda")      # {k, k+1, tokens...}
+    io = iost[4:]                                                      # {k, k+1, tokens...}
     d_buf = torch.zeros(N, dtype=torch.int32, device="cuda")
     g_buf = torch.zeros((N, H), dtype=act, device="cuda")
     ws = abi.Workspace(abi.mtp_workspace_bytes(head.cfg, N + 1, cap))
@@ -243,8 +246,7 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
     io[1] = 1
     io[2:] = abi.to_device(first_tok)
     t_hid[POOL - 1].copy_(abi.to_device(first_hid))
-    width = 2 + N + 1 + 4
-    host = torch.zeros((POOL, width), dtype=torch.int32).pin_memory()
+    host = torch.zeros((POOL, iost.numel()), dtype=torch.int32).pin_memory()
     totals = {"committed": 0, "accepted": 0}
 
     def enqueue_round(r, st):
@@ -255,16 +257,15 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
             abi.mtp_draft_step(head, kv, d_buf[i - 1:i], g_buf[i - 1], g_buf[i], None, d_buf[i:i + 1], ws, st)
         abi.spec_verify(sp, N, V, t_logits[r % POOL], None, d_buf, ring, ring_st, None, io[2:], io[0:2], vws, st)
         abi.kv_rollback(kv, abi.TO_ROUND_BASE, None, N, st)
-        # the round's results for the host: k, k+1, tokens and the KV state words
-        host[r % POOL, : 2 + N + 1].copy_(io, non_blocking=True)
-        host[r % POOL, 2 + N + 1:].copy_(kv.state, non_blocking=True)
+        # the round's results for the host: the KV state words, k, k+1, tokens
+        host[r % POOL].copy_(iost, non_blocking=True)
 
     def consume(r):
         row = host[r % POOL]
-        if int(row[2 + N + 1 + 3]) != 0:
-            raise RuntimeError(f"device error word {int(row[2 + N + 1 + 3])} in round {r}")
-        totals["committed"] += int(row[1])
-        totals["accepted"] += int(row[0])
+        if int(row[3]) != 0:
+            raise RuntimeError(f"device error word {int(row[3])} in round {r}")
+        totals["committed"] += int(row[5])
+        totals["accepted"] += int(row[4])
 
     for r in range(args.warmup):                       # eager rounds
         enqueue_round(r, stream)
@@ -609,9 +610,11 @@ def run_depth(args, N, lm):
     sp = abi.sampling(window=64)
     sessions = []
     for _ in range(S):
+        iost = torch.zeros(4 + 2 + N + 1, dtype=torch.int32, device="cuda")  # {state | k, k+1, tokens}
         sessions.append({
-            "kv": abi.DraftKV(shape, cap, kp, vp, ctx),
-            "io": torch.zeros(2 + N + 1, dtype=torch.int32, device="cuda"),   # {k, k+1, tokens}
+            "iost": iost,
+            "kv": abi.DraftKV(shape, cap, kp, vp, ctx, state=iost[0:4]),
+            "io": iost[4:],
             "n_dev": torch.zeros(1, dtype=torch.int32, device="cuda"),
             "d": torch.zeros(N, dtype=torch.int32, device="cuda"),
             "g": torch.zeros((N, H), dtype=torch.bfloat16, device="cuda"),
@@ -696,21 +699,20 @@ def run_depth(args, N, lm):
     # timed replay: the same device work, host sync per round overlapped
     reset()
     prev_round.clear()
-    host = torch.zeros((POOL, 2 + N + 1 + 4), dtype=torch.int32).pin_memory()
+    host = torch.zeros((POOL, 4 + 2 + N + 1), dtype=torch.int32).pin_memory()
     got = [None] * R
 
     def enqueue(r):
         s = r % S
         draft(s, stream)
         verify_and_rollback(s, r, stream)
-        host[r % POOL, : 2 + N + 1].copy_(sessions[s]["io"], non_blocking=True)
-        host[r % POOL, 2 + N + 1:].copy_(sessions[s]["kv"].state, non_blocking=True)
+        host[r % POOL].copy_(sessions[s]["iost"], non_blocking=True)   # one copy per round
 
     def consume(r):
         row = host[r % POOL]
-        if int(row[2 + N + 1 + 3]) != 0:
+        if int(row[3]) != 0:
             raise RuntimeError(f"device error word in round {r}")
-        got[r] = row[2: 2 + int(row[1])].tolist()
+        got[r] = row[6: 6 + int(row[5])].tolist()
 
     for r in range(args.warmup):
         enqueue(r)

@@ -256,14 +256,22 @@ class Head:
 class DraftKV:
     """K, V [n_kv_heads, capacity, head_dim] and the state words {len, base, -, err}."""
 
-    def __init__(self, shape, capacity: int, k=None, v=None, length: int = 0, device="cuda"):
+    def __init__(self, shape, capacity: int, k=None, v=None, length: int = 0, device="cuda", state=None):
+        """``state`` (optional): an int32 device tensor of 4 elements to hold the
+        state words (for instance a slice of a buffer the caller copies back
+        with other per-round results); it is initialised here."""
         import torch
         dt = torch.bfloat16 if shape.kv_dtype == "bf16" else torch.float32
         size = (shape.n_kv_heads, capacity, shape.head_dim)
         self.k = to_device(k, device) if k is not None else torch.zeros(size, dtype=dt, device=device)
         self.v = to_device(v, device) if v is not None else torch.zeros(size, dtype=dt, device=device)
         assert tuple(self.k.shape) == size and self.k.dtype == dt
-        self.state = torch.tensor([length, length, 0, 0], dtype=torch.int32, device=device)
+        if state is None:
+            self.state = torch.tensor([length, length, 0, 0], dtype=torch.int32, device=device)
+        else:
+            assert state.dtype == torch.int32 and state.numel() == 4 and state.is_contiguous()
+            state.copy_(torch.tensor([length, length, 0, 0], dtype=torch.int32))
+            self.state = state
         self.capacity = capacity
         self.desc = mtp_kv(self.k.data_ptr(), self.v.data_ptr(), capacity, self.state.data_ptr())
 

@@ -189,6 +189,15 @@ hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t
     a.grid_stride = a.kp == a.K;
     return timed_gemv(a, wt, 1, s, grid_out, kind);
   }
+  if (wt == W_BF16 && rows_total >= 2 && skinny_supported(a, rows_total)) {
+    // few rows, bf16 weights: one weight pass on the matrix cores
+    a.row_base = 0;
+    int slot = -1;
+    if (kind >= 0) time_mark(kind, true, s, &slot);
+    const hipError_t e = launch_skinny(a, rows_total, s);
+    if (kind >= 0) time_mark(kind, false, s, &slot);
+    return e;
+  }
   const int nr = nr_for(rows_total);
   a.kp = kp_for(a.K, wt, nr);
   a.grid_stride = a.kp == a.K;
@@ -310,7 +319,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   r.eps = c.rms_eps; r.theta = c.rope_theta; r.hq = hq; r.hkv = hkv; r.d = D;
   r.kc = kv->k; r.vc = kv->v; r.kv_bf16 = c.kv_dtype == MTP_BF16; r.capacity = kv->capacity;
   r.state = kv->state; r.n_max = n_max; r.n_dev = n_dev;
-  MTP_TRY(launch_rope_append(r, s));
+  // LAST mode: the norm/RoPE/append runs inside the attention kernel
+  const bool fuse_rope = mode == MTP_FLUSH_LAST;
+  if (!fuse_rope) MTP_TRY(launch_rope_append(r, s));
   FinishArgs f;
   std::memset(&f, 0, sizeof(f));
   f.state = kv->state; f.n_max = n_max; f.n_dev = n_dev; f.set_base = set_base;
@@ -328,6 +339,10 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   t.q = qr; t.kc = kv->k; t.vc = kv->v; t.kv_bf16 = c.kv_dtype == MTP_BF16; t.capacity = kv->capacity;
   t.state = kv->state; t.hq = hq; t.hkv = hkv; t.d = D; t.n_max = n_max; t.n_dev = n_dev;
   t.row_sel = rsel; t.nchunk = L.nchunk;
+  if (fuse_rope) {
+    t.fuse_rope = 1; t.qkv = qkv; t.ld_qkv = qkv_rows; t.q_norm = h->w.q_norm; t.k_norm = h->w.k_norm;
+    t.nw_bf16 = h->wt == W_BF16; t.eps = c.rms_eps; t.theta = c.rope_theta;
+  }
   if (mfma_out && c.kv_dtype == MTP_BF16) {
     // matrix-core flush attention: about 256 workgroups of 64 query vectors
     const int qblocks = (n_max * (hq / hkv) + 63) / 64;

@@ -2,7 +2,7 @@
 // batch-1 step and small in-round flushes).
 //
 // k_rope_append: per (row, head) wave: per-head RMSNorm of q or k over head_dim,
-//   rotate-half RoPE at position state[0] + row (angle computed in fp64), k and v
+//   rotate-half RoPE at position state[0] + row (angle reduced in fp64), k and v
 //   appended to the cache in the KV dtype, roped q kept in fp32.  Capacity and
 //   count checks set the sticky error word.  The length itself is advanced by
 //   the finishing kernel, so every kernel of the step reads the same state[0].
@@ -52,11 +52,10 @@ __global__ __launch_bounds__(64) void k_rope_append(RopeArgs a) {
       sv[d] = src[d] * inv * w;
     }
     __syncthreads();
+    const double l2t = log2(static_cast<double>(a.theta));
     for (int i = lane; i < half; i += 64) {
-      const double invf = pow(static_cast<double>(a.theta), -2.0 * i / D);
-      const double ang = static_cast<double>(pos) * invf;
-      const float c = static_cast<float>(cos(ang));
-      const float s = static_cast<float>(sin(ang));
+      float c, s;
+      rope_cs(pos, i, D, l2t, c, s);
       const float x1 = sv[i], x2 = sv[i + half];
       const float o1 = x1 * c - x2 * s;
       const float o2 = x1 * s + x2 * c;
@@ -118,7 +117,29 @@ __device__ __forceinline__ void unpack16(const uint4& v, float (&f)[KVB ? 8 : 4]
 // state (running max m, sum l, unnormalised o) over the keys it visits, KB keys
 // (2 KB loads) in flight per step.  Groups merge with xor shuffles, waves
 // through LDS; the chunk's (o, m, l) partial goes to the merge kernel.
-template <bool KVB, int D, int G>
+// RMSNorm over head_dim of one head (src, D fp32 values) times the norm weight,
+// then rotate-half RoPE at `pos` (one wave): put(d, value) for every d < D, each
+// value by the lane that computed it.
+template <int D, typename Put>
+__device__ __forceinline__ void norm_rope_head(const float* src, const void* nw, int nw_bf16, float eps,
+                                               int pos, double l2t, int lane, Put put) {
+  float ss = 0.f;
+  for (int d = lane; d < D; d += 64) ss += src[d] * src[d];
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / static_cast<float>(D) + eps);
+  for (int i = lane; i < D / 2; i += 64) {
+    const float w1 = nw_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(nw)[i]) : static_cast<const float*>(nw)[i];
+    const float w2 = nw_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(nw)[i + D / 2])
+                             : static_cast<const float*>(nw)[i + D / 2];
+    const float x1 = src[i] * inv * w1, x2 = src[i + D / 2] * inv * w2;
+    float c, s;
+    rope_cs(pos, i, D, l2t, c, s);
+    put(i, x1 * c - x2 * s);
+    put(i + D / 2, x1 * s + x2 * c);
+  }
+}
+
+template <bool KVB, int D, int G, bool FUSE>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   constexpr int EPL = KVB ? 8 : 4;   // elements per lane (16 bytes)
   constexpr int LPK = D / EPL;       // lanes per key row
@@ -127,11 +148,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   constexpr float kNeg = -1e30f;
   __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
   __shared__ float s_o[kAttnWaves][G][D];
+  __shared__ float s_q[FUSE ? G : 1][FUSE ? D : 1];
 
-  const int32_t* st = a.state;
+  int32_t* st = a.state;
   if (st[3] != 0) return;
   int n = a.n_max;
-  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  if constexpr (FUSE) {
+    // the append's checks (once per launch, by the first workgroup)
+    const int ndev = a.n_dev ? *a.n_dev : a.n_max;
+    const bool bad_count = ndev < 0 || ndev > a.n_max;
+    if (bad_count || st[0] + ndev > a.capacity) {
+      if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) st[3] = bad_count ? 3 : 1;
+      return;
+    }
+    n = ndev;
+  } else if (a.n_dev) {
+    n = min(max(*a.n_dev, 0), a.n_max);
+  }
   const int j = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.z);
   if (j < 0 || j >= n) return;
   const int off = st[0];            // pre-append length (committed by k_finish)
@@ -162,11 +195,42 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   const int d0 = li * EPL;
   const float scale = rsqrtf(static_cast<float>(D));
   float qr[G][EPL];
+  if constexpr (FUSE) {
+    const double l2t = log2(static_cast<double>(a.theta));
+    // new slots in this chunk: k normed and roped, k and v appended (a wave per slot)
+    const int s0 = max(off, k0), s1 = min(off + n, k1);
+    for (int sl = s0 + wave; sl < s1; sl += kAttnWaves) {
+      const float* row = a.qkv + static_cast<size_t>(sl - off) * a.ld_qkv;
+      const size_t o = (static_cast<size_t>(h) * a.capacity + sl) * D;
+      norm_rope_head<D>(row + (a.hq + h) * D, a.k_norm, a.nw_bf16, a.eps, sl, l2t, lane, [&](int d, float v) {
+        if constexpr (KVB) static_cast<uint16_t*>(a.kc)[o + d] = f32_to_bf16(v);
+        else static_cast<float*>(a.kc)[o + d] = v;
+      });
+      const float* vsrc = row + (a.hq + a.hkv + h) * D;
+      for (int d = lane; d < D; d += 64) {
+        if constexpr (KVB) static_cast<uint16_t*>(a.vc)[o + d] = f32_to_bf16(vsrc[d]);
+        else static_cast<float*>(a.vc)[o + d] = vsrc[d];
+      }
+    }
+    // the query heads of this kv head, row j, normed and roped
+    const float* qrow = a.qkv + static_cast<size_t>(j) * a.ld_qkv;
+    for (int g = wave; g < G; g += kAttnWaves) {
+      float* qd = s_q[g];
+      norm_rope_head<D>(qrow + (h * G + g) * D, a.q_norm, a.nw_bf16, a.eps, off + j, l2t, lane,
+                        [&](int d, float v) { qd[d] = v; });
+    }
+    __syncthreads();   // the appended rows and the queries are visible to the whole workgroup
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float* qp = a.q + (static_cast<size_t>(j) * a.hq + h * G + g) * D + d0;
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qr[g][e] = qp[e] * scale;
+      for (int e = 0; e < EPL; ++e) qr[g][e] = s_q[g][d0 + e] * scale;
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float* qp = a.q + (static_cast<size_t>(j) * a.hq + h * G + g) * D + d0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qr[g][e] = qp[e] * scale;
+    }
   }
 
   constexpr int ebytes = KVB ? 2 : 4;
@@ -336,20 +400,26 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   }
 }
 
-template <bool KVB, int D>
-static hipError_t attn_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
+template <bool KVB, int D, bool FUSE>
+static hipError_t attn_dg(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int g = a.hq / a.hkv;
   (void)hipGetLastError();
   switch (g) {
-    case 1: hipLaunchKernelGGL((k_attn<KVB, D, 1>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attn<KVB, D, 2>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_attn<KVB, D, 3>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attn<KVB, D, 4>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_attn<KVB, D, 6>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_attn<KVB, D, 8>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_attn<KVB, D, 1, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attn<KVB, D, 2, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_attn<KVB, D, 3, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attn<KVB, D, 4, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_attn<KVB, D, 6, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_attn<KVB, D, 8, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <bool KVB, int D>
+static hipError_t attn_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  return (a.fuse_rope && a.row_sel == ROW_LAST) ? attn_dg<KVB, D, true>(a, grid, s)
+                                                : attn_dg<KVB, D, false>(a, grid, s);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {

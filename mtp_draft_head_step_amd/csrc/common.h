@@ -53,6 +53,25 @@ __device__ __forceinline__ float group_sum_last(float v, int width) {
   return v;
 }
 
+// 16-byte streaming load: a non-temporal hint for data read once (weights), so
+// it does not displace reusable lines from the caches.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// cos and sin of the RoPE angle pos * theta^(-2i/D): the angle is formed and
+// reduced to [-pi, pi] in fp64 (positions reach 2^20), then fp32 sincos.
+// l2t = log2(theta) in fp64.
+__device__ __forceinline__ void rope_cs(int pos, int i, int D, double l2t, float& c, float& s) {
+  const double inv_freq = exp2(-2.0 * static_cast<double>(i) / static_cast<double>(D) * l2t);
+  const double ang = static_cast<double>(pos) * inv_freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double r = fma(-rint(ang * (1.0 / two_pi)), two_pi, ang);
+  sincosf(static_cast<float>(r), &s, &c);
+}
+
 // Monotone map float -> uint32 (larger float, larger key); -0 is folded into +0.
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);

@@ -143,7 +143,7 @@ __device__ __forceinline__ void gemv_load(uint4 (&w)[RPW][U], const char* const 
   for (int s = 0; s < RPW; ++s)
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      w[s][u] = *reinterpret_cast<const uint4*>(lane_row[s] + static_cast<size_t>(j + u) * stride);
+      w[s][u] = load_stream16(lane_row[s] + static_cast<size_t>(j + u) * stride);
 }
 
 template <int WT, int NR, int RPW, int U, bool TWO, bool XB>
@@ -222,7 +222,11 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int blk, int rows_p
   }
 }
 
-template <int WT, int NR, int RPW, bool TWO, bool XB>
+// WSK: the four waves of a workgroup share its rows and split each row's
+// chunks between them (partial dot products summed through LDS in wave
+// order), so a workgroup's row block is RPW rows and a persistent grid divides
+// the rows evenly over the CUs.
+template <int WT, int NR, int RPW, bool TWO, bool XB, bool WSK>
 __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   // staged inputs [NR][kp]: fp32, or bf16 when XB (few-row flushes with bf16 weights)
   extern __shared__ float xs_f[];
@@ -231,6 +235,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   __shared__ float s_red[kWaves][2 * NR];
   __shared__ float s_inv[2 * NR];
   __shared__ unsigned long long s_best[kWaves];
+  __shared__ float s_wsk[WSK ? kWaves : 1][WSK ? RPW * 8 * NR : 1][2];
   constexpr int EPC = WTraits<WT>::EPC;
 
   if (a.kv_state && a.kv_state[3] != 0) return;
@@ -258,9 +263,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   const int sub = lane / lpr;           // row within the slot
   const int li = lane % lpr;            // lane within the row
   const bool swiglu = (a.out_mode == OUT_SWIGLU);
-  const int rows_per_wg = kWaves * (swiglu ? RPW / 2 : RPW) * rps;
+  const int rows_per_wg = (WSK ? 1 : kWaves) * (swiglu ? RPW / 2 : RPW) * rps;
   const int nblocks = (a.M + rows_per_wg - 1) / rows_per_wg;
   const int nphase = (K + a.kp - 1) / a.kp;
+  const int wrow = WSK ? 0 : wave;      // the wave's place in the row block
 
   // Inputs are staged as x * w_norm; the scalar 1 / rms(x) of each activation
   // row is applied to the finished dot products (it factors out), so the sum of
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
     const uint16_t* srow[RPW];
     int rowid[RPW];
     bool valid[RPW];
-    gemv_rows<WT, RPW>(a, blk, rows_per_wg, wave, rps, sub, swiglu, rowp, srow, rowid, valid);
+    gemv_rows<WT, RPW>(a, blk, rows_per_wg, wrow, rps, sub, swiglu, rowp, srow, rowid, valid);
 
     float acc[RPW][NR], acc2[RPW][NR];   // acc2: hidden half of the embedding-cat input
 #pragma unroll
@@ -340,12 +346,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       for (int s = 0; s < RPW; ++s) lane_row[s] = rowp[s] + (static_cast<size_t>(k0 / EPC) + li) * 16;
       const XT* xl = xs + li * EPC;
       const int g0 = (k0 / EPC) + li;   // chunk index of j = 0 (int8 scale groups)
-      int j = 0;
-      for (; j + kUnroll <= cpl; j += kUnroll)
+      int j = WSK ? wave * cpl / kWaves : 0;
+      const int je = WSK ? (wave + 1) * cpl / kWaves : cpl;
+      for (; j + kUnroll <= je; j += kUnroll)
         gemv_body<WT, NR, RPW, kUnroll, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
-      for (; j + 2 <= cpl; j += 2)
+      for (; j + 2 <= je; j += 2)
         gemv_body<WT, NR, RPW, 2, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
-      for (; j < cpl; ++j)
+      for (; j < je; ++j)
         gemv_body<WT, NR, RPW, 1, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
     }
 
@@ -374,12 +381,47 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
     for (int s = 0; s < RPW; ++s)
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        float v = group_sum_last(acc[s][r], lpr) * s_inv[2 * r];
-        if constexpr (TWO) v += group_sum_last(acc2[s][r], lpr) * s_inv[2 * r + 1];
+        acc[s][r] = group_sum_last(acc[s][r], lpr);
+        if constexpr (TWO) acc2[s][r] = group_sum_last(acc2[s][r], lpr);
+      }
+    if constexpr (WSK) {
+      // the waves' partial sums of each row, added in wave order
+      if (li == lpr - 1) {
+#pragma unroll
+        for (int s = 0; s < RPW; ++s)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            s_wsk[wave][(s * 8 + sub) * NR + r][0] = acc[s][r];
+            if constexpr (TWO) s_wsk[wave][(s * 8 + sub) * NR + r][1] = acc2[s][r];
+          }
+      }
+      __syncthreads();
+      if (wave == 0 && li == lpr - 1) {
+#pragma unroll
+        for (int s = 0; s < RPW; ++s)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            float v = 0.f, v2 = 0.f;
+            for (int w = 0; w < kWaves; ++w) {
+              v += s_wsk[w][(s * 8 + sub) * NR + r][0];
+              if constexpr (TWO) v2 += s_wsk[w][(s * 8 + sub) * NR + r][1];
+            }
+            acc[s][r] = v;
+            if constexpr (TWO) acc2[s][r] = v2;
+          }
+      }
+      __syncthreads();   // s_wsk is rewritten by the next row block
+    }
+#pragma unroll
+    for (int s = 0; s < RPW; ++s)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float v = acc[s][r] * s_inv[2 * r];
+        if constexpr (TWO) v += acc2[s][r] * s_inv[2 * r + 1];
         acc[s][r] = v;
       }
 
-    if (li == lpr - 1) {
+    if (li == lpr - 1 && (!WSK || wave == 0)) {
       if (swiglu) {
 #pragma unroll
         for (int s = 0; s < RPW; s += 2) {
@@ -395,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 #pragma unroll
         for (int s = 0; s < RPW; ++s) {
           if (!valid[s]) continue;
-          const int row = blk * rows_per_wg + (wave * RPW + s) * rps + sub;
+          const int row = blk * rows_per_wg + (wrow * RPW + s) * rps + sub;
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             if (r >= nrows) continue;
@@ -436,21 +478,26 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 // how many workgroups fit per CU (LDS bound) and balanced so every workgroup
 // gets the same number of row blocks (+-1); each stages its input once.
 struct GemvTuning {
-  // measured on MI355X (rows per slot, workgroups per CU) for the 27B-shaped head
-  int rpw_large = 2, wg_per_cu_large = 2;    // unembedding (>= large_rows rows)
-  int rpw_swiglu = 4, wg_per_cu_swiglu = 3;  // gate/up pairs
-  int rpw_small = 2, wg_per_cu_small = 6;    // 5K..8K-row projections
+  // measured on MI355X (rows per slot, workgroups per CU, waves splitting each
+  // row) for the 27B-shaped head
+  int rpw_large = 2, wg_per_cu_large = 2, wsk_large = 0;    // unembedding (>= large_rows rows)
+  int rpw_swiglu = 4, wg_per_cu_swiglu = 2, wsk_swiglu = 0; // gate/up pairs
+  int rpw_small = 4, wg_per_cu_small = 2, wsk_small = 0;    // 5K..8K-row projections
+  int rpw_long = 4, wg_per_cu_long = 2, wsk_long = 1;       // the same with rows of >= long_k columns
+  int rpw_embed = 2, wg_per_cu_embed = 6, wsk_embed = 0;    // the fc projection
+  int wg_per_cu_rows = 6;                                    // few-row (NR > 1) flush passes
   long large_rows = 65536;
+  int long_k = 12288;
 };
 GemvTuning g_gemv_tuning;
 
-template <int WT, int NR, int RPW, bool TWO>
+template <int WT, int NR, int RPW, bool TWO, bool WSK = false>
 static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int max_per_cu) {
   constexpr bool XB = NR > 1 && WT == W_BF16;
   GemvArgs a = a0;
   if (a.out_mode == OUT_SWIGLU && RPW < 2) return hipErrorInvalidValue;
   const int rps = kWave / a.lpr;
-  const int rows_per_wg = kWaves * ((a.out_mode == OUT_SWIGLU) ? RPW / 2 : RPW) * rps;
+  const int rows_per_wg = (WSK ? 1 : kWaves) * ((a.out_mode == OUT_SWIGLU) ? RPW / 2 : RPW) * rps;
   const int nblocks = (a.M + rows_per_wg - 1) / rows_per_wg;
   const size_t lds = static_cast<size_t>(NR) * a.kp * (XB ? 2 : 4);
   int grid = nblocks;
@@ -465,14 +512,14 @@ static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int
   if (lds > 64 * 1024) {   // gfx950 gives a workgroup up to 160 KB of LDS on request
     static bool raised = false;
     if (!raised) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO, XB>),
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO, XB, WSK>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
   (void)hipGetLastError();
-  hipLaunchKernelGGL((k_gemv<WT, NR, RPW, TWO, XB>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((k_gemv<WT, NR, RPW, TWO, XB, WSK>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -480,18 +527,34 @@ template <int WT, int NR>
 static hipError_t launch_r(const GemvArgs& a, hipStream_t s, int* g) {
   const GemvTuning& t = g_gemv_tuning;
   const bool swiglu = a.out_mode == OUT_SWIGLU;
-  int rpw, per_cu;
-  if (swiglu) { rpw = t.rpw_swiglu; per_cu = t.wg_per_cu_swiglu; }
-  else if (a.M >= t.large_rows) { rpw = t.rpw_large; per_cu = t.wg_per_cu_large; }
-  else { rpw = t.rpw_small; per_cu = t.wg_per_cu_small; }
+  int rpw, per_cu, wsk;
+  if (a.in_mode == IN_EMBED) { rpw = t.rpw_embed; per_cu = t.wg_per_cu_embed; wsk = t.wsk_embed; }
+  else if (swiglu) { rpw = t.rpw_swiglu; per_cu = t.wg_per_cu_swiglu; wsk = t.wsk_swiglu; }
+  else if (a.M >= t.large_rows) { rpw = t.rpw_large; per_cu = t.wg_per_cu_large; wsk = t.wsk_large; }
+  else if (a.K >= t.long_k) { rpw = t.rpw_long; per_cu = t.wg_per_cu_long; wsk = t.wsk_long; }
+  else { rpw = t.rpw_small; per_cu = t.wg_per_cu_small; wsk = t.wsk_small; }
   if (swiglu && rpw < 2) rpw = 2;
+  // the wave-split rows: one-row launches of bf16 weights
+  constexpr bool kWsk = NR == 1 && WT == W_BF16;
   if (a.in_mode == IN_EMBED) {
     if constexpr (WT == W_I8) return hipErrorInvalidValue;
-    else return launch_t<WT, NR, 2, true>(a, s, g, per_cu);   // the fc projection
+    else if constexpr (kWsk) {
+      if (wsk) return launch_t<WT, NR, 2, true, true>(a, s, g, per_cu);
+    }
+    if constexpr (WT != W_I8) return launch_t<WT, NR, 2, true>(a, s, g, per_cu);   // the fc projection
   }
   if constexpr (NR > 1) {
-    return launch_t<WT, NR, 2, false>(a, s, g, per_cu);   // few-row flushes: one shape
+    return launch_t<WT, NR, 2, false>(a, s, g, t.wg_per_cu_rows);   // few-row flushes: one shape
   } else {
+    if constexpr (kWsk) {
+      if (wsk) {
+        switch (rpw) {
+          case 1: return launch_t<WT, NR, 1, false, true>(a, s, g, per_cu);
+          case 2: return launch_t<WT, NR, 2, false, true>(a, s, g, per_cu);
+          default: return launch_t<WT, NR, 4, false, true>(a, s, g, per_cu);
+        }
+      }
+    }
     switch (rpw) {
       case 1: return launch_t<WT, NR, 1, false>(a, s, g, per_cu);
       case 2: return launch_t<WT, NR, 2, false>(a, s, g, per_cu);

@@ -65,6 +65,13 @@ struct GemvArgs {
 // *grid_out (nullable) receives the number of workgroups launched.
 hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s, int* grid_out = nullptr);
 
+// The same product for 2..16 activation rows j in [row_base, row_base + nr) with
+// bf16 weights on 16x16x32 MFMA tiles (ROWS_RANGE; OUT_F32, OUT_RESID or
+// OUT_SWIGLU).  skinny_supported: M and every m[i] multiples of 16, K of 64,
+// the nr staged bf16 rows within 128 KB of LDS.
+bool skinny_supported(const GemvArgs& a, int nr);
+hipError_t launch_skinny(const GemvArgs& a, int nr, hipStream_t s);
+
 // Normalised bf16 input rows for the matrix-core projections: RMSNorm(x; nw)
 // (IN_RMS) or [RMSNorm(E[tok]; nw) | RMSNorm(hid; nw2)] (IN_EMBED, K = 2H), one
 // row per activation row j < n.
@@ -145,11 +152,11 @@ hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);
 // Split-K attention of query rows over the draft KV, then a merge.
 struct AttnArgs {
   const float* q;          // [rows, Hq * D] roped
-  const void* kc;
-  const void* vc;
+  void* kc;
+  void* vc;
   int kv_bf16;
   int capacity;
-  const int32_t* state;
+  int32_t* state;
   int hq, hkv, d;
   int n_max;
   const int32_t* n_dev;
@@ -159,6 +166,17 @@ struct AttnArgs {
   float* part_o;           // [rows, Hq, nchunk, D]
   float* part_ml;          // [rows, Hq, nchunk, 2]
   float* o;                // [rows, Hq * D]
+  // ROW_LAST with fuse_rope: the q/k RMSNorm + RoPE and the K/V append of the
+  // rows j < n run inside the attention kernel (no separate append launch); the
+  // q/k/v projections of the rows are read from qkv.
+  int fuse_rope;
+  const float* qkv;        // [rows, (Hq + 2 Hkv) * D]
+  int ld_qkv;
+  const void* q_norm;
+  const void* k_norm;
+  int nw_bf16;
+  float eps;
+  float theta;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_flush(const AttnArgs& a, hipStream_t s);   // the mfma path's first kernel

@@ -14,6 +14,7 @@ namespace mtp {
 
 constexpr int kVThreads = 256;
 constexpr int kVMaxChunk = 8192;
+constexpr int kVGreedyChunk = 4096;   // logits per greedy workgroup (the host's chunk)
 
 // Token at position idx of (ring oldest-first ++ drafts).
 __device__ __forceinline__ int window_token(const int32_t* ring, int head, int count, int window,
@@ -47,6 +48,15 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
   const bool pen = a.penalty != 1.0f;
   const int head = ring_head(a);
   const int count = ring_count(a);
+  // the chunk's logits first (all loads in flight at once), then the window
+  const float* row = a.target + static_cast<size_t>(i) * a.vocab;
+  constexpr int kPer = kVGreedyChunk / kVThreads;
+  float v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int k = lo + tid + u * kVThreads;
+    v[u] = k < hi ? row[k] : 0.f;
+  }
   if (pen) {
     for (int w = tid; w < kVMaxChunk / 32; w += kVThreads) bits[w] = 0u;
     __syncthreads();
@@ -58,12 +68,14 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
     }
     __syncthreads();
   }
-  const float* row = a.target + static_cast<size_t>(i) * a.vocab;
   unsigned long long best = 0ull;
-  for (int k = lo + tid; k < hi; k += kVThreads) {
-    float v = row[k];
-    if (pen && ((bits[(k - lo) >> 5] >> ((k - lo) & 31)) & 1u)) v = penalise(v, a.penalty);
-    const unsigned long long key = argmax_key(v, static_cast<uint32_t>(k));
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int k = lo + tid + u * kVThreads;
+    if (k >= hi) continue;
+    float x = v[u];
+    if (pen && ((bits[(k - lo) >> 5] >> ((k - lo) & 31)) & 1u)) x = penalise(x, a.penalty);
+    const unsigned long long key = argmax_key(x, static_cast<uint32_t>(k));
     best = key > best ? key : best;
   }
   best = wave_max_u64(best);
@@ -104,6 +116,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a
 }
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
+  if (a.chunk != kVGreedyChunk) return hipErrorInvalidValue;
   const int nb = (a.vocab + a.chunk - 1) / a.chunk;
   (void)hipGetLastError();
   int slot = -1;
