@@ -51,6 +51,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 VALU_FP32_PEAK_TFLOPS = 157.3
 POOL = 8
+TIME_EVERY = 8     # rounds between the ones whose dominant kernel carries timing events
 
 
 def log(msg):
@@ -298,7 +299,10 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
         if graphs is not None:
             graphs[r % POOL].replay()
         else:
+            if r % TIME_EVERY == 0 or r == args.warmup:
+                abi.mtp_timing_pause(False)
             enqueue_round(r, stream)
+            abi.mtp_timing_pause(True)
         done[r % 2].record(stream)
         if prev is not None:                          # the one host sync per round,
             done[prev % 2].synchronize()              # overlapped with the next round
@@ -414,7 +418,9 @@ def run_flush(args):
         if kind is not None:
             abi.mtp_timing_begin(kind, 64 * steps + 4)
         t = time.perf_counter()
-        for _ in range(steps):
+        for i in range(steps):
+            if kind is not None:
+                abi.mtp_timing_pause(i % TIME_EVERY != 0)
             flush(mode)
         torch.cuda.synchronize()
         el = time.perf_counter() - t
@@ -424,6 +430,7 @@ def run_flush(args):
         return el / steps, k
 
     side = max(args.steps // 4, 5)
+    timed_side = (side + TIME_EVERY - 1) // TIME_EVERY      # flushes carrying timing events
     t_all, (att_ms, att_n) = timed(abi.ALL, args.steps, abi.TIME_ATTENTION)
     _, (proj_ms, proj_n) = timed(abi.ALL, side, abi.TIME_PROJECTION)
     t_last, _ = timed(abi.LAST, side)
@@ -447,8 +454,8 @@ def run_flush(args):
         "flush_tflops": round(total_flops / t_all / 1e12, 3),
         "flush_mfma_frac": round(total_flops / t_all / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
         "algorithmic_gflop": {"attention": round(att_flops / 1e9, 4), "projections": round(proj_flops / 1e9, 4)},
-        "projection_us_per_flush": round(proj_ms / side * 1e3, 2),
-        "projection_launches_per_flush": proj_n // side,
+        "projection_us_per_flush": round(proj_ms / timed_side * 1e3, 2),
+        "projection_launches_per_flush": proj_n // timed_side,
         "roofline": roofline("mfma", att_flops / att_avg / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None,
                              kernel="causal flush attention on bf16 MFMA (256 rows x 4 q heads over "
                                     "8193..8448 keys; 16 key chunks, split-K partials)",
@@ -529,6 +536,7 @@ def run_verify(args):
     abi.mtp_timing_begin(abi.TIME_VERIFY, steps + 4)
     t = time.perf_counter()
     for r in range(args.warmup, total):
+        abi.mtp_timing_pause(r % TIME_EVERY != 0)
         one(r)
     torch.cuda.synchronize()
     el = time.perf_counter() - t
@@ -724,6 +732,7 @@ def run_depth(args, N, lm):
     t = time.perf_counter()
     prev = None
     for r in range(args.warmup, R):
+        abi.mtp_timing_pause(not (r % TIME_EVERY == 0 or r == args.warmup))
         enqueue(r)
         done[r % 2].record(stream)
         if prev is not None:
@@ -753,10 +762,11 @@ def run_depth(args, N, lm):
         s["kv"].state.copy_(stb)
     calibrate_copy(args)
 
-    att_bytes = 0
+    att_bytes = 0                       # over the rounds whose attention launches were timed
     for r in range(args.warmup, R):
-        before, n_pend = lens[r]
-        att_bytes += sum(attention_bytes(shape, before + n_pend + i) for i in range(N))
+        if r % TIME_EVERY == 0 or r == args.warmup:
+            before, n_pend = lens[r]
+            att_bytes += sum(attention_bytes(shape, before + n_pend + i) for i in range(N))
     att_avg = att_ms / att_n / 1e3
     ks = np.array(k_of[args.warmup:])
     expected = 1.0 + sum(float(np.prod([0.8 * 0.85 ** i for i in range(j)])) for j in range(1, N + 1))

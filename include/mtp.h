@@ -211,6 +211,10 @@ int kv_rollback(const mtp_kv *kv, int32_t to_len, const int32_t *n_accepted_dev,
  *                        unembedding (fc, q/k/v, o, gate/up, down) */
 enum { MTP_TIME_UNEMBED = 0, MTP_TIME_ATTENTION = 1, MTP_TIME_VERIFY = 2, MTP_TIME_PROJECTION = 3 };
 int mtp_timing_begin(int32_t kind, int32_t max_launches);
+/* Suspend (paused != 0) or resume bracketing new launches without releasing
+ * the slots, so that only a sample of launches carries the events (each event
+ * pair holds the stream for a few microseconds). */
+int mtp_timing_pause(int32_t paused);
 int mtp_timing_elapsed(int32_t first, int32_t count, float *total_ms);
 int mtp_timing_end(float *total_ms, int32_t *launches);
 

@@ -33,7 +33,7 @@ WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
 EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_destroy", "mtp_workspace_bytes",
            "mtp_workspace_init", "mtp_draft_step", "mtp_flush_pairs",
            "spec_verify_workspace_bytes", "spec_verify", "kv_rollback", "mtp_timing_begin",
-           "mtp_timing_elapsed", "mtp_timing_end")
+           "mtp_timing_pause", "mtp_timing_elapsed", "mtp_timing_end")
 
 
 class mtp_head_config(C.Structure):
@@ -89,6 +89,8 @@ def _load():
     lib.kv_rollback.argtypes = [C.POINTER(mtp_kv), i32, vp, i32, vp]
     lib.mtp_timing_begin.restype = C.c_int
     lib.mtp_timing_begin.argtypes = [i32, i32]
+    lib.mtp_timing_pause.restype = C.c_int
+    lib.mtp_timing_pause.argtypes = [i32]
     lib.mtp_timing_elapsed.restype = C.c_int
     lib.mtp_timing_elapsed.argtypes = [i32, i32, C.POINTER(C.c_float)]
     lib.mtp_timing_end.restype = C.c_int
@@ -196,6 +198,11 @@ TIME_UNEMBED, TIME_ATTENTION, TIME_VERIFY, TIME_PROJECTION = 0, 1, 2, 3
 def mtp_timing_begin(kind: int, max_launches: int):
     """Time the next ``max_launches`` launches of kernel class ``kind``."""
     _check(lib.mtp_timing_begin(int(kind), int(max_launches)), "mtp_timing_begin")
+
+
+def mtp_timing_pause(paused: bool):
+    """Suspend or resume bracketing launches (the slots are kept)."""
+    _check(lib.mtp_timing_pause(1 if paused else 0), "mtp_timing_pause")
 
 
 def mtp_timing_elapsed(first: int, count: int) -> float:

@@ -23,6 +23,7 @@ struct KernelTimer {
   int used = 0;
   int kind = -1;
   bool on = false;
+  bool paused = false;
 } g_timer;
 }  // namespace
 
@@ -30,6 +31,7 @@ void mtp::time_mark(int kind, bool before, hipStream_t s, int* slot) {
   std::lock_guard<std::mutex> lk(g_timer.mu);
   if (!g_timer.on || g_timer.kind != kind) { *slot = -1; return; }
   if (before) {
+    if (g_timer.paused) { *slot = -1; return; }
     if (g_timer.used >= static_cast<int>(g_timer.start.size())) { *slot = -1; return; }
     *slot = g_timer.used++;
     hipEventRecord(g_timer.start[*slot], s);
@@ -124,7 +126,7 @@ Layout layout(const mtp_head_config& c, int rows, int capacity) {
   L.m = take(rows * I * 4);
   L.g = take(rows * H * 4);
   L.amax = take(amax_parts(c) * 8);
-  L.xa = rows > kGemvMaxRows ? take(rows * 2 * H * 2) : off;   // bf16 normalised rows
+  L.xa = rows > kGemvMaxRows ? take(rows * 2 * H * 2) : off;   // bf16 normalised rows (MFMA path)
   L.total = off;
   return L;
 }
@@ -188,15 +190,6 @@ hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t
     a.kp = kp_for(a.K, wt, 1);
     a.grid_stride = a.kp == a.K;
     return timed_gemv(a, wt, 1, s, grid_out, kind);
-  }
-  if (wt == W_BF16 && rows_total >= 2 && skinny_supported(a, rows_total)) {
-    // few rows, bf16 weights: one weight pass on the matrix cores
-    a.row_base = 0;
-    int slot = -1;
-    if (kind >= 0) time_mark(kind, true, s, &slot);
-    const hipError_t e = launch_skinny(a, rows_total, s);
-    if (kind >= 0) time_mark(kind, false, s, &slot);
-    return e;
   }
   const int nr = nr_for(rows_total);
   a.kp = kp_for(a.K, wt, nr);
@@ -585,6 +578,13 @@ int mtp_timing_begin(int32_t kind, int32_t max_launches) {
   g_timer.used = 0;
   g_timer.kind = kind;
   g_timer.on = true;
+  g_timer.paused = false;
+  return MTP_OK;
+}
+
+int mtp_timing_pause(int32_t paused) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  g_timer.paused = paused != 0;
   return MTP_OK;
 }
 

@@ -7,8 +7,9 @@
 //
 //   k_rows_prep  one workgroup per activation row: the normalised input row in
 //                bf16, RMSNorm(x; w) or [RMSNorm(E[t]; w_pe) | RMSNorm(h; w_ph)]
-//                (the fused input of the head's fc), fp32 arithmetic, one
-//                rounding to bf16 per element.
+//                (the fused input of the head's fc), or plain x (IN_F32), fp32
+//                arithmetic, one rounding to bf16 per element; 16-byte loads,
+//                four per thread in flight.
 //   k_gemm       Y[j, c] = sum_k A[j, k] W[c, k] for a 64 x 64 tile of (row j,
 //                output c) per workgroup; four waves each own a 32 x 32 block
 //                computed with v_mfma_f32_32x32x16_bf16 from 64-column slices
@@ -31,8 +32,22 @@ constexpr int kLdsRow = kTK + 8;   // bf16 per LDS row (16 B pad against bank co
 // ---------------------------------------------------------------------------
 // row preparation
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float load1(const void* p, long long i, int bf16) {
-  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+// 8 consecutive elements (bf16 or fp32) as fp32.
+__device__ __forceinline__ void load8f(const void* p, long long i, int bf16, float (&v)[8]) {
+  if (bf16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  }
 }
 
 __device__ float block_sum(float v, float* red) {
@@ -46,6 +61,27 @@ __device__ float block_sum(float v, float* red) {
   return t;
 }
 
+// One row: source segment(s) of 8-element jobs.  IN_EMBED: jobs k < half read
+// the embedding row, the rest the hidden row.
+struct PrepRow {
+  const void* src0;  long long off0;  int bf0;   // embedding row / x row
+  const void* src1;  long long off1;  int bf1;   // hidden row (IN_EMBED)
+  int half;
+};
+
+constexpr int kPrepU = 4;   // jobs in flight per thread
+
+__device__ __forceinline__ void prep_load(const PrepRow& r, int k, float (&v)[8]) {
+  if (k < r.half) {
+    if (r.src0) load8f(r.src0, r.off0 + k, r.bf0, v);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  } else {
+    load8f(r.src1, r.off1 + (k - r.half), r.bf1, v);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_rows_prep(PrepArgs a) {
   __shared__ float red[4];
   if (a.kv_state && a.kv_state[3] != 0) return;
@@ -54,36 +90,76 @@ __global__ __launch_bounds__(256) void k_rows_prep(PrepArgs a) {
   const int j = blockIdx.x;
   if (j >= n) return;
   uint16_t* out = a.out + static_cast<long long>(j) * a.ld_out;
-  if (a.in_mode == IN_RMS) {
-    const float* x = a.x + static_cast<long long>(j) * a.ldx;
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < a.K; k += blockDim.x) ss += x[k] * x[k];
-    const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(a.K) + a.eps);
-    for (int k = threadIdx.x; k < a.K; k += blockDim.x)
-      out[k] = f32_to_bf16(x[k] * load1(a.nw, k, a.nw_bf16) * inv);
-    return;
+  const int K = a.K;
+  PrepRow r;
+  if (a.in_mode == IN_EMBED) {
+    const int tk = a.tok[j];
+    const bool ok = tk >= 0 && tk < a.vocab_tok;
+    if (!ok && a.err && threadIdx.x == 0) *a.err = 4;   // token outside the vocabulary
+    r.half = K / 2;
+    r.src0 = ok ? a.embed : nullptr; r.off0 = static_cast<long long>(ok ? tk : 0) * r.half; r.bf0 = a.embed_bf16;
+    r.src1 = a.hid; r.off1 = static_cast<long long>(j) * a.ld_hid; r.bf1 = a.hid_bf16;
+  } else {
+    r.half = K;
+    r.src0 = a.x; r.off0 = static_cast<long long>(j) * a.ldx; r.bf0 = 0;
+    r.src1 = nullptr; r.off1 = 0; r.bf1 = 0;
   }
-  // IN_EMBED: [RMSNorm(E[tok]; nw) | RMSNorm(hid; nw2)], each half `half` wide
-  const int half = a.K / 2;
-  const int tk = a.tok[j];
-  const bool ok = tk >= 0 && tk < a.vocab_tok;
-  if (!ok && a.err && threadIdx.x == 0) *a.err = 4;   // token outside the vocabulary
-  const long long eoff = static_cast<long long>(ok ? tk : 0) * half;
-  const long long hoff = static_cast<long long>(j) * a.ld_hid;
+  const int njobs = K / 8;
+  // pass 1: sums of squares (first part / second part)
   float se = 0.f, sh = 0.f;
-  for (int k = threadIdx.x; k < half; k += blockDim.x) {
-    const float e = ok ? load1(a.embed, eoff + k, a.embed_bf16) : 0.f;
-    const float h = load1(a.hid, hoff + k, a.hid_bf16);
-    se += e * e;
-    sh += h * h;
+  if (a.in_mode != IN_F32) {
+    for (int f0 = threadIdx.x; f0 < njobs; f0 += 256 * kPrepU) {
+      float v[kPrepU][8];
+#pragma unroll
+      for (int u = 0; u < kPrepU; ++u)
+        if (f0 + u * 256 < njobs) prep_load(r, (f0 + u * 256) * 8, v[u]);
+#pragma unroll
+      for (int u = 0; u < kPrepU; ++u) {
+        const int k = (f0 + u * 256) * 8;
+        if (k >= K) continue;
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += v[u][e] * v[u][e];
+        if (k < r.half) se += t; else sh += t;
+      }
+    }
   }
-  const float inv_e = 1.0f / sqrtf(block_sum(se, red) / static_cast<float>(half) + a.eps);
-  const float inv_h = 1.0f / sqrtf(block_sum(sh, red) / static_cast<float>(half) + a.eps);
-  for (int k = threadIdx.x; k < half; k += blockDim.x) {
-    const float e = ok ? load1(a.embed, eoff + k, a.embed_bf16) : 0.f;
-    const float h = load1(a.hid, hoff + k, a.hid_bf16);
-    out[k] = f32_to_bf16(e * load1(a.nw, k, a.nw_bf16) * inv_e);
-    out[half + k] = f32_to_bf16(h * load1(a.nw2, k, a.nw_bf16) * inv_h);
+  float inv0 = 1.f, inv1 = 1.f;
+  if (a.in_mode == IN_RMS) {
+    inv0 = 1.0f / sqrtf(block_sum(se, red) / static_cast<float>(K) + a.eps);
+  } else if (a.in_mode == IN_EMBED) {
+    inv0 = 1.0f / sqrtf(block_sum(se, red) / static_cast<float>(r.half) + a.eps);
+    inv1 = 1.0f / sqrtf(block_sum(sh, red) / static_cast<float>(r.half) + a.eps);
+  }
+  // pass 2: bf16(x * w * inv) (IN_F32: bf16(x))
+  for (int f0 = threadIdx.x; f0 < njobs; f0 += 256 * kPrepU) {
+    float v[kPrepU][8], w[kPrepU][8];
+#pragma unroll
+    for (int u = 0; u < kPrepU; ++u) {
+      const int k = (f0 + u * 256) * 8;
+      if (k >= K) continue;
+      prep_load(r, k, v[u]);
+      if (a.in_mode == IN_F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[u][e] = 1.f;
+      } else if (k < r.half) {
+        load8f(a.nw, k, a.nw_bf16, w[u]);
+      } else {
+        load8f(a.nw2, k - r.half, a.nw_bf16, w[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepU; ++u) {
+      const int k = (f0 + u * 256) * 8;
+      if (k >= K) continue;
+      const float inv = k < r.half ? inv0 : inv1;
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = f32_to_bf16(v[u][2 * q] * w[u][2 * q] * inv) |
+               (static_cast<uint32_t>(f32_to_bf16(v[u][2 * q + 1] * w[u][2 * q + 1] * inv)) << 16);
+      *reinterpret_cast<uint4*>(out + k) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
 }
 

@@ -66,17 +66,18 @@ __device__ __forceinline__ float dot_chunk(const uint4& w, const float* __restri
   return s;
 }
 
-// 16 bytes of bf16 weights times 8 bf16 inputs staged in LDS.
+// 16 bytes of bf16 weights times 8 bf16 inputs staged in LDS: four packed
+// bf16 dot products (v_dot2_f32_bf16, fp32 accumulation).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
 __device__ __forceinline__ float dot_chunk_bb(const uint4& w, const uint16_t* __restrict__ xp) {
   const uint4 x = *reinterpret_cast<const uint4*>(xp);
-  return __uint_as_float(w.x << 16) * __uint_as_float(x.x << 16) +
-         __uint_as_float(w.x & 0xFFFF0000u) * __uint_as_float(x.x & 0xFFFF0000u) +
-         __uint_as_float(w.y << 16) * __uint_as_float(x.y << 16) +
-         __uint_as_float(w.y & 0xFFFF0000u) * __uint_as_float(x.y & 0xFFFF0000u) +
-         __uint_as_float(w.z << 16) * __uint_as_float(x.z << 16) +
-         __uint_as_float(w.z & 0xFFFF0000u) * __uint_as_float(x.z & 0xFFFF0000u) +
-         __uint_as_float(w.w << 16) * __uint_as_float(x.w << 16) +
-         __uint_as_float(w.w & 0xFFFF0000u) * __uint_as_float(x.w & 0xFFFF0000u);
+  float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x),
+                                            0.f, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), d, false);
+  return d;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -348,8 +349,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       const int g0 = (k0 / EPC) + li;   // chunk index of j = 0 (int8 scale groups)
       int j = WSK ? wave * cpl / kWaves : 0;
       const int je = WSK ? (wave + 1) * cpl / kWaves : cpl;
-      for (; j + kUnroll <= je; j += kUnroll)
-        gemv_body<WT, NR, RPW, kUnroll, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
+      // few-row passes keep twice the loads in flight (their staged rows cap
+      // the workgroups per CU)
+      constexpr int kU = NR > 1 ? 2 * kUnroll : kUnroll;
+      for (; j + kU <= je; j += kU)
+        gemv_body<WT, NR, RPW, kU, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
+      if constexpr (kU > kUnroll)
+        for (; j + kUnroll <= je; j += kUnroll)
+          gemv_body<WT, NR, RPW, kUnroll, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
       for (; j + 2 <= je; j += 2)
         gemv_body<WT, NR, RPW, 2, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
       for (; j < je; ++j)
@@ -480,13 +487,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 struct GemvTuning {
   // measured on MI355X (rows per slot, workgroups per CU, waves splitting each
   // row) for the 27B-shaped head
-  int rpw_large = 2, wg_per_cu_large = 2, wsk_large = 0;    // unembedding (>= large_rows rows)
-  int rpw_swiglu = 4, wg_per_cu_swiglu = 2, wsk_swiglu = 0; // gate/up pairs
-  int rpw_small = 4, wg_per_cu_small = 2, wsk_small = 0;    // 5K..8K-row projections
+  int rpw_large = 4, wg_per_cu_large = 2, wsk_large = 0;    // unembedding (>= large_rows rows)
+  int rpw_swiglu = 2, wg_per_cu_swiglu = 2, wsk_swiglu = 0; // gate/up pairs
+  int rpw_small = 4, wg_per_cu_small = 3, wsk_small = 0;    // 6K..64K-row projections
+  int rpw_few = 2, wg_per_cu_few = 8, wsk_few = 0;          // projections of < few_rows rows
   int rpw_long = 4, wg_per_cu_long = 2, wsk_long = 1;       // the same with rows of >= long_k columns
   int rpw_embed = 2, wg_per_cu_embed = 6, wsk_embed = 0;    // the fc projection
-  int wg_per_cu_rows = 6;                                    // few-row (NR > 1) flush passes
+  int wg_per_cu_rows = 6, wsk_rows = 0, rpw_rows = 2;       // few-row (NR > 1) flush passes
   long large_rows = 65536;
+  int few_rows = 6144;
   int long_k = 12288;
 };
 GemvTuning g_gemv_tuning;
@@ -502,7 +511,18 @@ static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int
   const size_t lds = static_cast<size_t>(NR) * a.kp * (XB ? 2 : 4);
   int grid = nblocks;
   if (a.grid_stride) {
-    int occ = static_cast<int>((160 * 1024) / (lds + 2048));
+    // workgroups per CU: the kernel's real occupancy (registers and LDS) at this
+    // LDS size, capped by the tuning
+    static int occ_lds = -1, occ_val = 1;
+    if (occ_lds != static_cast<int>(lds)) {
+      int o = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_gemv<WT, NR, RPW, TWO, XB, WSK>, kThreads, lds) !=
+              hipSuccess || o < 1)
+        o = static_cast<int>((160 * 1024) / (lds + 2048));
+      occ_lds = static_cast<int>(lds);
+      occ_val = o;
+    }
+    int occ = occ_val;
     occ = occ < 1 ? 1 : (occ > max_per_cu ? max_per_cu : occ);
     const int cap = kCUs * occ;
     const int per = (nblocks + cap - 1) / cap;          // row blocks per workgroup
@@ -532,19 +552,28 @@ static hipError_t launch_r(const GemvArgs& a, hipStream_t s, int* g) {
   else if (swiglu) { rpw = t.rpw_swiglu; per_cu = t.wg_per_cu_swiglu; wsk = t.wsk_swiglu; }
   else if (a.M >= t.large_rows) { rpw = t.rpw_large; per_cu = t.wg_per_cu_large; wsk = t.wsk_large; }
   else if (a.K >= t.long_k) { rpw = t.rpw_long; per_cu = t.wg_per_cu_long; wsk = t.wsk_long; }
+  else if (a.M < t.few_rows) { rpw = t.rpw_few; per_cu = t.wg_per_cu_few; wsk = t.wsk_few; }
   else { rpw = t.rpw_small; per_cu = t.wg_per_cu_small; wsk = t.wsk_small; }
   if (swiglu && rpw < 2) rpw = 2;
-  // the wave-split rows: one-row launches of bf16 weights
-  constexpr bool kWsk = NR == 1 && WT == W_BF16;
+  // the wave-split rows: launches of bf16 weights
+  constexpr bool kWsk = WT == W_BF16;
+  if (NR > 1) { per_cu = t.wg_per_cu_rows; wsk = t.wsk_rows; }
   if (a.in_mode == IN_EMBED) {
     if constexpr (WT == W_I8) return hipErrorInvalidValue;
     else if constexpr (kWsk) {
       if (wsk) return launch_t<WT, NR, 2, true, true>(a, s, g, per_cu);
     }
-    if constexpr (WT != W_I8) return launch_t<WT, NR, 2, true>(a, s, g, per_cu);   // the fc projection
+    if constexpr (WT != W_I8) {   // the fc projection
+      if (NR > 1 && t.rpw_rows == 1) return launch_t<WT, NR, 1, true>(a, s, g, per_cu);
+      return launch_t<WT, NR, 2, true>(a, s, g, per_cu);
+    }
   }
   if constexpr (NR > 1) {
-    return launch_t<WT, NR, 2, false>(a, s, g, t.wg_per_cu_rows);   // few-row flushes: one shape
+    if constexpr (kWsk) {
+      if (wsk) return launch_t<WT, NR, 2, false, true>(a, s, g, per_cu);
+    }
+    if (t.rpw_rows == 1) return launch_t<WT, NR, 1, false>(a, s, g, per_cu);
+    return launch_t<WT, NR, 2, false>(a, s, g, per_cu);   // few-row flushes
   } else {
     if constexpr (kWsk) {
       if (wsk) {

@@ -65,13 +65,6 @@ struct GemvArgs {
 // *grid_out (nullable) receives the number of workgroups launched.
 hipError_t launch_gemv(const GemvArgs& a, int wtype, int nr, hipStream_t s, int* grid_out = nullptr);
 
-// The same product for 2..16 activation rows j in [row_base, row_base + nr) with
-// bf16 weights on 16x16x32 MFMA tiles (ROWS_RANGE; OUT_F32, OUT_RESID or
-// OUT_SWIGLU).  skinny_supported: M and every m[i] multiples of 16, K of 64,
-// the nr staged bf16 rows within 128 KB of LDS.
-bool skinny_supported(const GemvArgs& a, int nr);
-hipError_t launch_skinny(const GemvArgs& a, int nr, hipStream_t s);
-
 // Normalised bf16 input rows for the matrix-core projections: RMSNorm(x; nw)
 // (IN_RMS) or [RMSNorm(E[tok]; nw) | RMSNorm(hid; nw2)] (IN_EMBED, K = 2H), one
 // row per activation row j < n.
