@@ -558,7 +558,7 @@ def run_verify(args):
         "round_gbs": round(chunk_bytes / (el / steps) / 1e9, 1),
         "mean_accepted": round(float(counts[:, 0].mean()), 4),
         "roofline": roofline("hbm", chunk_bytes / avg / 1e9, HBM_PEAK_GBS, "GB/s", None,
-                             kernel="per-chunk top-k pass over the 9 rows (penalty, temperature, bitonic sort)",
+                             kernel="per-chunk top-k pass over the 9 rows (penalty, temperature, radix select)",
                              bytes_per_launch=chunk_bytes, avg_us=round(avg * 1e6, 2), launches=nl),
         "cpu_baseline": cpu,
     })

@@ -131,10 +131,11 @@ hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
 // Sampled verification (temperature > 0): Leviathan/Chen rejection sampling
 // over transformed rows.  Rows 0..N are the target rows, N+1..2N the draft rows.
 //  A. k_sample_chunk  (chunks x rows): a chunk's logits are penalised (window of
-//     its row), divided by the temperature, turned into 64-bit keys (value desc,
-//     id asc) and bitonic-sorted in LDS; the chunk's best kk keys are kept.
-//  B. k_sample_row    (rows): the row's candidates are merged (bitonic sort in
-//     LDS), the top-k is exact; softmax over it, top-p prefix, min-p cut,
+//     its row), divided by the temperature and turned into 64-bit keys (value
+//     desc, id asc); a radix select finds the chunk's kk-th key and the kk keys
+//     at or above it are kept.
+//  B. k_sample_row    (rows): a radix select over the row's candidates gives the
+//     exact top-k, sorted in LDS; softmax over it, top-p prefix, min-p cut,
 //     renormalise; the support is written sorted by token id.
 //  C. k_sample_decide (1 thread): accept d_i iff u_i q_i(d_i) < p_i(d_i); at the
 //     first rejection draw from normalise(max(0, p - q)) (p if that is zero) with
@@ -174,9 +175,68 @@ size_t verify_sampled_scratch_bytes(int n_draft, int vocab, int chunk) {
   return align256(rows * nb * kSMaxTopK * 8) + align256(rows * 4ull) + 2 * align256(rows * kSMaxTopK * 4ull) + 256;
 }
 
-// Descending bitonic sort of n (a power of two) keys in LDS by the workgroup.
-__device__ void bitonic_desc(unsigned long long* s, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
+__device__ __forceinline__ float key_value(unsigned long long key) {
+  const uint32_t k = static_cast<uint32_t>(key >> 32);
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Radix select over the workgroup's 64-bit keys (N per thread, 0 = empty; real
+// keys are distinct): returns the kk-th largest key T, so the top kk are
+// exactly the keys >= T (kk <= number of real keys).  Eight-bit digits from the
+// top; the low 32 bits are only examined when keys share T's high half beyond
+// what is needed (equal scores).  Per digit: a 256-bin histogram of the keys
+// still matching the prefix (LDS integer atomics), then one wave finds the bin
+// holding the kk-th key with a suffix scan.
+template <int N>
+__device__ unsigned long long kth_largest(const unsigned long long (&key)[N], int kk, int* hist, int* sh) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  unsigned long long prefix = 0ull, mask = 0ull;
+  int need = kk;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int b = tid; b < 256; b += blockDim.x) hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      if (key[u] != 0ull && (key[u] & mask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255], 1);
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins 4l..4l+3; inclusive suffix sums over lanes (bins from the top)
+      const int b0 = hist[4 * lane], b1 = hist[4 * lane + 1], b2 = hist[4 * lane + 2], b3 = hist[4 * lane + 3];
+      int suf = b0 + b1 + b2 + b3;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += v;
+      }
+      const int above = suf - (b0 + b1 + b2 + b3);    // keys in bins of higher lanes
+      if (above < need && suf >= need) {               // the need-th key is in this lane's bins
+        int acc = above, d = 4 * lane + 3;
+        const int bins[4] = {b0, b1, b2, b3};
+        for (int q = 3; q >= 0; --q) {
+          d = 4 * lane + q;
+          if (acc + bins[q] >= need) break;
+          acc += bins[q];
+        }
+        sh[0] = d;
+        sh[1] = acc;                                    // keys above the chosen bin
+        sh[2] = bins[d - 4 * lane];                     // keys in the chosen bin
+      }
+    }
+    __syncthreads();
+    const int d = sh[0];
+    need -= sh[1];
+    prefix |= static_cast<unsigned long long>(d) << shift;
+    mask |= 255ull << shift;
+    const bool done = sh[2] == need;                    // every key with this prefix is taken
+    __syncthreads();
+    if (done) return prefix;                            // the smallest key with this prefix is >= prefix
+  }
+  return prefix;
+}
+
+// Descending bitonic sort of n (a power of two, <= 2 * blockDim) keys in LDS.
+__device__ void bitonic_small(unsigned long long* s, int n) {
+  for (int size = 2; size <= n; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int t = threadIdx.x; t < (n >> 1); t += blockDim.x) {
         const int i = 2 * t - (t & (stride - 1));
@@ -187,18 +247,15 @@ __device__ void bitonic_desc(unsigned long long* s, int n) {
       }
       __syncthreads();
     }
-  }
 }
 
-__device__ __forceinline__ float key_value(unsigned long long key) {
-  const uint32_t k = static_cast<uint32_t>(key >> 32);
-  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-  return __uint_as_float(u);
-}
+constexpr int kSPer = kSChunk / kVThreads;   // chunk keys per thread
 
 __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, SampledScratch sc, int nb, int kk) {
-  __shared__ unsigned long long keys[kSChunk];
   __shared__ uint32_t bits[kSChunk / 32];
+  __shared__ int hist[256];
+  __shared__ int sh[4];
+  __shared__ int s_cnt;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int n = a.n_draft;
@@ -207,6 +264,13 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
   const float* src = (draft ? a.draft : a.target) + static_cast<size_t>(i) * a.vocab;
   const int lo = blockIdx.x * kSChunk;
   const int hi = min(a.vocab, lo + kSChunk);
+  // the chunk's logits first (all loads in flight), then the window
+  float v[kSPer];
+#pragma unroll
+  for (int u = 0; u < kSPer; ++u) {
+    const int k = lo + tid + u * kVThreads;
+    v[u] = k < hi ? src[k] : 0.f;
+  }
   const bool pen = a.penalty != 1.0f;
   if (pen) {
     const int head = ring_head(a), count = ring_count(a);
@@ -220,46 +284,85 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
     }
     __syncthreads();
   }
-  for (int t = tid; t < kSChunk; t += kVThreads) {
+  unsigned long long key[kSPer];
+#pragma unroll
+  for (int u = 0; u < kSPer; ++u) {
+    const int t = tid + u * kVThreads;
     const int k = lo + t;
-    unsigned long long key = 0ull;                      // below every real key
+    key[u] = 0ull;                                       // below every real key
     if (k < hi) {
-      float v = src[k];
-      if (pen && ((bits[t >> 5] >> (t & 31)) & 1u)) v = penalise(v, a.penalty);
-      key = argmax_key(v / a.temperature, static_cast<uint32_t>(k));
+      float x = v[u];
+      if (pen && ((bits[t >> 5] >> (t & 31)) & 1u)) x = penalise(x, a.penalty);
+      key[u] = argmax_key(x / a.temperature, static_cast<uint32_t>(k));
     }
-    keys[t] = key;
   }
+  const int take = min(kk, hi - lo);
+  const unsigned long long thr = kth_largest<kSPer>(key, take, hist, sh);
+  if (tid == 0) s_cnt = 0;
   __syncthreads();
-  bitonic_desc(keys, kSChunk);
   unsigned long long* out = sc.cand + (static_cast<size_t>(row) * nb + blockIdx.x) * kk;
-  for (int t = tid; t < kk; t += kVThreads) out[t] = keys[t];
+#pragma unroll
+  for (int u = 0; u < kSPer; ++u)
+    if (key[u] != 0ull && key[u] >= thr) {                // exactly `take` keys
+      const int pos = atomicAdd(&s_cnt, 1);
+      if (pos < kk) out[pos] = key[u];
+    }
+  for (int t = take + tid; t < kk; t += kVThreads) out[t] = 0ull;
 }
 
+constexpr int kSRowPer = kSMaxCand / kVThreads;   // merge keys per thread
+
 __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledScratch sc, int nb, int kk,
-                                                         int n2, int topk) {
-  extern __shared__ unsigned long long s[];             // n2 keys
+                                                         int topk) {
+  __shared__ unsigned long long s[kSMaxTopK];
   __shared__ float sp[kSMaxTopK];
-  __shared__ int s_keep;
+  __shared__ int hist[256];
+  __shared__ int sh[4];
+  __shared__ int s_keep, s_cnt;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int ncand = nb * kk;
   const unsigned long long* cand = sc.cand + static_cast<size_t>(row) * ncand;
-  for (int t = tid; t < n2; t += kVThreads) s[t] = t < ncand ? cand[t] : 0ull;
+  unsigned long long key[kSRowPer];
+  int nreal = 0;
+#pragma unroll
+  for (int u = 0; u < kSRowPer; ++u) {
+    const int t = tid + u * kVThreads;
+    key[u] = t < ncand ? cand[t] : 0ull;
+    nreal += key[u] != 0ull;
+  }
+  // real candidates in the row (<= vocab); the exact top-k of them
+  nreal = wave_sum(static_cast<float>(nreal)) + 0.5f;   // small integers: exact in fp32
+  if ((tid & 63) == 0) hist[tid >> 6] = nreal;
   __syncthreads();
-  bitonic_desc(s, n2);
+  int total = 0;
+  for (int w = 0; w < kVThreads / 64; ++w) total += hist[w];
+  __syncthreads();
+  const int nv = min(topk, total);
+  const unsigned long long thr = kth_largest<kSRowPer>(key, nv, hist, sh);
+  int k2 = 1;
+  while (k2 < nv) k2 <<= 1;
+  for (int t = tid; t < k2; t += kVThreads) s[t] = 0ull;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kSRowPer; ++u)
+    if (key[u] != 0ull && key[u] >= thr) {                // exactly nv keys
+      const int pos = atomicAdd(&s_cnt, 1);
+      if (pos < k2) s[pos] = key[u];
+    }
+  __syncthreads();
+  bitonic_small(s, k2);                                  // the top-k by (value desc, id asc)
   if (tid == 0) {
-    int nv = 0;
-    while (nv < topk && nv < n2 && s[nv] != 0ull) ++nv;  // exact top-k (fewer if the row is shorter)
     const float y0 = key_value(s[0]);
-    float total = 0.f;
+    float tot = 0.f;
     for (int j = 0; j < nv; ++j) {
       sp[j] = expf(key_value(s[j]) - y0);
-      total += sp[j];
+      tot += sp[j];
     }
     int keep = nv;
     if (a.top_p < 1.0f) {
-      const float target = a.top_p * total;
+      const float target = a.top_p * tot;
       float c = 0.f;
       for (int j = 0; j < nv; ++j) {
         c += sp[j];
@@ -280,27 +383,21 @@ __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledS
   __syncthreads();
   const int keep = s_keep;
   // re-key the kept entries by token id (ascending) with their probability bits
-  int k2 = 1;
-  while (k2 < keep) k2 <<= 1;
-  unsigned long long mine[kSMaxTopK / kVThreads + 1];
-  int c = 0;
-  for (int j = tid; j < k2; j += kVThreads) {
-    unsigned long long v = ~0ull;                       // sorts after every real entry
-    if (j < keep) {
-      const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s[j]);
-      v = (static_cast<unsigned long long>(id) << 32) | __float_as_uint(sp[j]);
-    }
-    mine[c++] = v;
+  int k3 = 1;
+  while (k3 < keep) k3 <<= 1;
+  unsigned long long mine = ~0ull;                       // sorts after every real entry
+  if (tid < k3 && tid < keep) {
+    const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s[tid]);
+    mine = (static_cast<unsigned long long>(id) << 32) | __float_as_uint(sp[tid]);
   }
   __syncthreads();
-  c = 0;
-  for (int j = tid; j < k2; j += kVThreads) s[j] = ~mine[c++];   // descending of ~v = ascending of v
+  if (tid < k3) s[tid] = ~mine;                          // descending of ~v = ascending of v
   __syncthreads();
-  bitonic_desc(s, k2);
+  bitonic_small(s, k3);
   for (int j = tid; j < keep; j += kVThreads) {
-    const unsigned long long v = ~s[j];
-    sc.ids[static_cast<size_t>(row) * kSMaxTopK + j] = static_cast<int>(v >> 32);
-    sc.probs[static_cast<size_t>(row) * kSMaxTopK + j] = __uint_as_float(static_cast<uint32_t>(v));
+    const unsigned long long vv = ~s[j];
+    sc.ids[static_cast<size_t>(row) * kSMaxTopK + j] = static_cast<int>(vv >> 32);
+    sc.probs[static_cast<size_t>(row) * kSMaxTopK + j] = __uint_as_float(static_cast<uint32_t>(vv));
   }
   if (tid == 0) sc.cnt[row] = keep;
 }
@@ -386,23 +483,13 @@ hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
   const int rows = 2 * a.n_draft + 1;
   const int nb = (a.vocab + kSChunk - 1) / kSChunk;
   const int kk = a.top_k < kSChunk ? a.top_k : kSChunk;
-  int n2 = 1;
-  while (n2 < nb * kk) n2 <<= 1;
   const SampledScratch sc = sampled_scratch(a.scratch, a.n_draft, a.vocab);
-  static bool raised = false;   // the merge stage may use 64 KB of keys plus its own LDS
-  if (!raised) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sample_row),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    if (e != hipSuccess) return e;
-    raised = true;
-  }
   (void)hipGetLastError();
   int slot = -1;
   time_mark(TIME_VERIFY, true, s, &slot);
   hipLaunchKernelGGL(k_sample_chunk, dim3(nb, rows), dim3(kVThreads), 0, s, a, sc, nb, kk);
   time_mark(TIME_VERIFY, false, s, &slot);
-  hipLaunchKernelGGL(k_sample_row, dim3(rows), dim3(kVThreads), static_cast<size_t>(n2) * 8, s, a, sc, nb, kk,
-                     n2, a.top_k);
+  hipLaunchKernelGGL(k_sample_row, dim3(rows), dim3(kVThreads), 0, s, a, sc, nb, kk, a.top_k);
   hipLaunchKernelGGL(k_sample_decide, dim3(1), dim3(64), 0, s, a, sc);
   return hipGetLastError();
 }
