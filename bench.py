@@ -20,6 +20,8 @@ Other workloads (one JSON line each, same keys):
   tiny_round            the tiny fp32 head (H 256), prefix 128, 2 drafts, 64 rounds
   flush256_prefix8192   the 256-pair flush (tiny head in bf16) after an 8192-slot
                         prefix, ALL mode, the KV rolled back after each flush
+  flush256_qwen35_27b   the same flush at the 27B shape after 4096 slots (the
+                        pages' 2.5 MiB flush cap; MFMA GEMM roofline)
   verify_sampled        sampled verification: N=4, V=152064, T 0.7, penalty 1.1
                         over a 64-token ring, top-k 40, top-p 0.9, min-p 0.05
   depth_ctx32768        rounds of the tiny bf16 head over a 32768-slot prefix at
@@ -252,10 +254,8 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
 
     def enqueue_round(r, st):
         prev = (r - 1) % POOL
-        abi.mtp_flush_pairs(head, kv, io[2:], t_hid[prev], N + 1, io[1:2], abi.LAST, 1,
-                            g_buf[0], None, d_buf[0:1], ws, st)
-        for i in range(1, N):
-            abi.mtp_draft_step(head, kv, d_buf[i - 1:i], g_buf[i - 1], g_buf[i], None, d_buf[i:i + 1], ws, st)
+        # flush of the pending pairs + N - 1 chained steps, one call
+        abi.mtp_draft_chain(head, kv, io[2:], t_hid[prev], N + 1, io[1:2], N, d_buf, g_buf, None, ws, st)
         abi.spec_verify(sp, N, V, t_logits[r % POOL], None, d_buf, ring, ring_st, None, io[2:], io[0:2], vws, st)
         abi.kv_rollback(kv, abi.TO_ROUND_BASE, None, N, st)
         # the round's results for the host: the KV state words, k, k+1, tokens
@@ -384,14 +384,21 @@ def cpu_rounds(shape, storage, kp, vp, cap, ctx, N, pool_logits, pool_hid, first
 # ---------------------------------------------------------------------------
 # the 256-pair flush
 # ---------------------------------------------------------------------------
-def run_flush(args):
+def run_flush(args, big=False):
+    """The 256-pair flush in ALL mode: the tiny head in bf16 after 8192 slots, or
+    (big) the 27B-shaped head after 4096 slots (256 x 5120 bf16 pending hiddens,
+    the pages' 2.5 MiB flush cap).  Timed with a rollback to the prefix after
+    each flush."""
     import torch
 
     from mtp_draft_head_step_amd import abi
     from mtp_draft_head_step_amd import inputs as I
 
-    shape, wl = I.TINY_BF16, I.WL_FLUSH
-    prefix, n = 8192, 256
+    if big:
+        shape, wl, prefix = I.QWEN35_27B, I.WL_QWEN, 4096
+    else:
+        shape, wl, prefix = I.TINY_BF16, I.WL_FLUSH, 8192
+    n = 256
     cap = prefix + n
     storage = I.head_weights(shape, wl)
     head = abi.Head(shape, storage)
@@ -438,48 +445,68 @@ def run_flush(args):
     calibrate_copy(args)
     att_flops = flush_attention_flops(shape, prefix, n)
     proj_flops = flush_projection_flops(shape, n, n)
+    gemm_flops = proj_flops - 2 * shape.vocab * shape.hidden      # the last row's unembedding is a GEMV
     total_flops = att_flops + proj_flops
     att_avg = att_ms / att_n / 1e3
+    proj_s = proj_ms / timed_side / 1e3                             # the GEMMs of one flush
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_flush(shape, storage, kp, vp, cap, prefix, toks_np, hids_np, args.cpu_seconds, args.steps)
+        cpu = cpu_flush(shape, storage, kp, vp, cap, prefix, toks_np, hids_np, args.cpu_seconds, args.steps,
+                        cache_fp64=big)
+    heads = f"{shape.n_q_heads}q/{shape.n_kv_heads}kv"
+    name = "flush256_qwen35_27b_prefix4096" if big else "flush256_prefix8192"
     out = base_line(args, round(n / t_all, 1), "flushed pairs/s", t_all * 1e3, "bf16",
-                    "synthetic (seeded N(0,0.02) weights of the tiny head in bf16; 256 uniform tokens, "
-                    "N(0,1) bf16 hiddens; N(0,1) bf16 prefix K/V)",
-                    {"workload": "flush256_prefix8192", "hidden": shape.hidden, "heads": "4q/2kv", "head_dim": 64,
+                    f"synthetic (seeded N(0,0.02) weights of the {'Qwen3.5-27B-shaped' if big else 'tiny'} head "
+                    "in bf16; 256 uniform tokens, N(0,1) bf16 hiddens; N(0,1) bf16 prefix K/V)",
+                    {"workload": name, "hidden": shape.hidden, "heads": heads, "head_dim": shape.head_dim,
                      "intermediate": shape.intermediate, "vocab": shape.vocab, "pairs": n,
                      "prefix": prefix, "mode": "ALL (every row's g; last row's logits and argmax)"})
+    if big:   # the projections dominate: the roofline is the MFMA GEMMs of one flush
+        line = roofline("mfma", gemm_flops / proj_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None,
+                        kernel="the flush's five MFMA GEMMs (fc, qkv, o, gate/up, down; 256 rows, 64x64 tiles)",
+                        flops_per_launch=round(gemm_flops / max(1, proj_n // timed_side)),
+                        avg_us=round(proj_s * 1e6 / max(1, proj_n // timed_side), 2), launches=proj_n)
+    else:     # the attention dominates
+        line = roofline("mfma", att_flops / att_avg / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None,
+                        kernel="causal flush attention on bf16 MFMA (256 rows x 4 q heads over "
+                               "8193..8448 keys; split-K partials)",
+                        flops_per_launch=att_flops, avg_us=round(att_avg * 1e6, 2), launches=att_n)
     out.update({
         "flush_us": {"all": round(t_all * 1e6, 2), "last": round(t_last * 1e6, 2), "kv_only": round(t_kv * 1e6, 2)},
         "flush_tflops": round(total_flops / t_all / 1e12, 3),
         "flush_mfma_frac": round(total_flops / t_all / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
         "algorithmic_gflop": {"attention": round(att_flops / 1e9, 4), "projections": round(proj_flops / 1e9, 4)},
-        "projection_us_per_flush": round(proj_ms / timed_side * 1e3, 2),
+        "attention_us": round(att_avg * 1e6, 2),
+        "attention_tflops": round(att_flops / att_avg / 1e12, 2),
+        "projection_us_per_flush": round(proj_s * 1e6, 2),
+        "projection_tflops": round(gemm_flops / proj_s / 1e12, 2),
         "projection_launches_per_flush": proj_n // timed_side,
-        "roofline": roofline("mfma", att_flops / att_avg / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None,
-                             kernel="causal flush attention on bf16 MFMA (256 rows x 4 q heads over "
-                                    "8193..8448 keys; 16 key chunks, split-K partials)",
-                             flops_per_launch=att_flops, avg_us=round(att_avg * 1e6, 2), launches=att_n),
+        "roofline": line,
         "cpu_baseline": cpu,
     })
     return out
 
 
-def cpu_flush(shape, storage, kp, vp, cap, prefix, toks, hids, seconds, max_flushes):
+def cpu_flush(shape, storage, kp, vp, cap, prefix, toks, hids, seconds, max_flushes, cache_fp64=False):
     from mtp_draft_head_step_amd import inputs as I
     from oracle import head as OH
     from oracle.kvcache import DraftKV
-    oh = OH.Head(shape, I.weight_values(shape, storage))
+    oh = OH.Head(shape, I.weight_values(shape, storage), cache_fp64=cache_fp64)
     tk = [int(t) for t in toks]
     hv = [I.decode(h, shape.act_dtype) for h in hids]
     K, V = I.decode(kp, shape.kv_dtype), I.decode(vp, shape.kv_dtype)
     def unit(_):
         okv = DraftKV(shape.n_kv_heads, cap, shape.head_dim, K, V, prefix)
         oh.flush(okv, tk, hv, OH.ALL, set_round_base=True)
-    with single_thread_blas():
-        flushes, el = timed_sample(unit, seconds, max_flushes)
-    return {"value": round(len(tk) * flushes / el, 2), "unit": "flushed pairs/s", "cores": 1, "kind": "oracle",
-            "sample": f"{flushes} flushes of the same 256 pairs in ALL mode, numpy fp64, one BLAS thread"}
+    if cache_fp64:   # the large head: BLAS on every host thread, one flush
+        flushes, el = timed_sample(unit, 0, 1)
+        cores = cpu_threads()
+    else:
+        with single_thread_blas():
+            flushes, el = timed_sample(unit, seconds, max_flushes)
+        cores = 1
+    return {"value": round(len(tk) * flushes / el, 4), "unit": "flushed pairs/s", "cores": cores, "kind": "oracle",
+            "sample": f"{flushes} flush(es) of the same 256 pairs in ALL mode, numpy fp64"}
 
 
 # ---------------------------------------------------------------------------
@@ -623,6 +650,8 @@ def run_depth(args, N, lm):
             "iost": iost,
             "kv": abi.DraftKV(shape, cap, kp, vp, ctx, state=iost[0:4]),
             "io": iost[4:],
+            "pend_t": torch.zeros(N + 1, dtype=torch.int32, device="cuda"),
+            "pend_h": torch.zeros((N + 1, H), dtype=torch.bfloat16, device="cuda"),
             "n_dev": torch.zeros(1, dtype=torch.int32, device="cuda"),
             "d": torch.zeros(N, dtype=torch.int32, device="cuda"),
             "g": torch.zeros((N, H), dtype=torch.bfloat16, device="cuda"),
@@ -652,33 +681,31 @@ def run_depth(args, N, lm):
         return 0 if policy == "A" else min(k, N - 1)
 
     def pending_of(s):
-        """The session's pending pairs: tokens out_tokens[j0..k] of its previous
-        verify (io[2 + j0:]), hiddens rows j0..k of that round's target hiddens,
-        count k + 1 - j0 (io[1] when j0 = 0).  j0 > 0 only under policy B, with k
-        known from the recording pass."""
+        """The session's pending pairs.  Policy A: the previous verify's tokens
+        (io[2:]), that round's target hiddens and the count io[1], as they stand.
+        Policy B: pend_t / pend_h / n_dev, rebuilt on the device by
+        mtp_repair_pending.  Round 0: the one initial pair."""
         ss = sessions[s]
         pr = prev_round.get(s)
         if pr is None:
             return ss["io"][2:], first_rows, ss["io"][1:2]
-        j0 = j0_of(k_of[pr])
-        return ss["io"][2 + j0:], pool_hid[pr % POOL][j0:], (ss["io"][1:2] if j0 == 0 else ss["n_dev"])
+        if policy == "A":
+            return ss["io"][2:], pool_hid[pr % POOL], ss["io"][1:2]
+        return ss["pend_t"], ss["pend_h"], ss["n_dev"]
 
     def draft(s, st):
         ss = sessions[s]
         toks, hid, cnt = pending_of(s)
-        abi.mtp_flush_pairs(head, ss["kv"], toks, hid, N + 1, cnt, abi.LAST, 1, ss["g"][0], None, ss["d"][0:1],
-                            ws, st)
-        for i in range(1, N):
-            abi.mtp_draft_step(head, ss["kv"], ss["d"][i - 1:i], ss["g"][i - 1], ss["g"][i], None,
-                               ss["d"][i:i + 1], ws, st)
+        abi.mtp_draft_chain(head, ss["kv"], toks, hid, N + 1, cnt, N, ss["d"], ss["g"], None, ws, st)
 
     def verify_and_rollback(s, r, st):
         ss = sessions[s]
         abi.spec_verify(sp, N, V, planted[r], None, ss["d"], ss["ring"], ss["ring_st"], None, ss["io"][2:],
                         ss["io"][0:2], vws, st)
         abi.kv_rollback(ss["kv"], abi.TO_ROUND_BASE, ss["io"][0:1] if policy == "B" else None, N, st)
-        if j0_of(k_of[r]) > 0:
-            ss["n_dev"].fill_(k_of[r] + 1 - j0_of(k_of[r]))
+        if policy == "B":
+            abi.mtp_repair_pending(ss["io"][2:], ss["io"][0:2], pool_hid[r % POOL], H, abi.MTP_BF16, N,
+                                   ss["pend_t"], ss["pend_h"], ss["n_dev"], st)
         prev_round[s] = r
 
     # recording pass: the drafts decide where the acceptance is planted
@@ -832,8 +859,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (rounds, flushes or verify rounds)")
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="qwen35_27b_round",
-                    choices=["qwen35_27b_round", "tiny_round", "flush256_prefix8192", "verify_sampled",
-                             "depth_ctx32768"])
+                    choices=["qwen35_27b_round", "tiny_round", "flush256_prefix8192", "flush256_qwen35_27b",
+                             "verify_sampled", "depth_ctx32768"])
     ap.add_argument("--depth", default="4", help="depth_ctx32768: drafts per round (comma list: one line each)")
     ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"], help="depth_ctx32768: lm_head storage")
     ap.add_argument("--policy", default="B", choices=["A", "B"], help="depth_ctx32768: KV policy")
@@ -850,7 +877,7 @@ def main():
         print("bench.py measures one GPU: the MTP round is a batch-1 path on a single MI355X; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    default_steps = {"qwen35_27b_round": 40, "tiny_round": 64, "flush256_prefix8192": 50,
+    default_steps = {"qwen35_27b_round": 40, "tiny_round": 64, "flush256_prefix8192": 50, "flush256_qwen35_27b": 16,
                      "verify_sampled": 10000, "depth_ctx32768": 256}
     if args.steps is None:
         args.steps = default_steps[args.workload]
@@ -868,6 +895,8 @@ def main():
                                    "logits, N(0,1) target hiddens)")]
     elif args.workload == "flush256_prefix8192":
         lines = [run_flush(args)]
+    elif args.workload == "flush256_qwen35_27b":
+        lines = [run_flush(args, big=True)]
     elif args.workload == "verify_sampled":
         lines = [run_verify(args)]
     else:

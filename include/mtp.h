@@ -162,6 +162,34 @@ int mtp_flush_pairs(const mtp_head *head, const mtp_kv *kv, const int32_t *token
                     float *logits_last_dev, int32_t *argmax_last_dev, void *ws,
                     size_t ws_bytes, hipStream_t stream);
 
+/* A round's drafting in one call ("Facts", MTP drafting: the pending pairs are
+ * flushed, then one head call per draft token): mtp_flush_pairs(pending, LAST,
+ * set_round_base = 1) followed by n_draft - 1 chained mtp_draft_step calls,
+ * step i taking (d_{i-1}, g_{i-1}).  pend_tokens_dev / pend_hiddens_dev /
+ * n_max / n_dev as for mtp_flush_pairs; drafts_dev int32[n_draft] receives
+ * d_0..d_{n-1}; hiddens_out_dev [n_draft, hidden] (act dtype, must not overlap
+ * the pending hiddens) the g of every draft; draft_logits_dev (nullable) fp32
+ * [n_draft, vocab] the draft rows (sampled verification needs them).  The
+ * workspace must hold n_max rows.  1 <= n_draft <= MTP_MAX_DRAFT. */
+int mtp_draft_chain(const mtp_head *head, const mtp_kv *kv, const int32_t *pend_tokens_dev,
+                    const void *pend_hiddens_dev, int32_t n_max, const int32_t *n_dev, int32_t n_draft,
+                    int32_t *drafts_dev, void *hiddens_out_dev, float *draft_logits_dev, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* Re-pairing under the keep-accepted rollback policy (the #1174 comment: only
+ * the rejected suffix is trimmed), on the device: with k = out_counts_dev[0]
+ * from spec_verify and j0 = min(k, n_draft - 1), the next round's pending pairs
+ * j = 0..k - j0 are (out_tokens_dev[j0 + j], target hidden row j0 + j) and
+ * *pend_count_dev = k + 1 - j0 (1 pair if k < n_draft, 2 if all were
+ * accepted).  target_hiddens_dev: [n_draft + 1, hidden] in act_dtype (MTP_F32 or
+ * MTP_BF16); pend_hiddens_dev must not overlap it.  Under the roll-back-to-base
+ * policy no call is needed: the pending pairs are out_tokens_dev, the target
+ * hidden rows and out_counts_dev[1] as they stand. */
+int mtp_repair_pending(const int32_t *out_tokens_dev, const int32_t *out_counts_dev,
+                       const void *target_hiddens_dev, int32_t hidden, int32_t act_dtype, int32_t n_draft,
+                       int32_t *pend_tokens_dev, void *pend_hiddens_dev, int32_t *pend_count_dev,
+                       hipStream_t stream);
+
 /* Workspace bytes for spec_verify with n_draft drafts over vocab logits. */
 size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab);
 

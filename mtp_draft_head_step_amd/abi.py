@@ -31,7 +31,7 @@ WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
                  "up_proj", "down_proj", "norm")
 
 EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_destroy", "mtp_workspace_bytes",
-           "mtp_workspace_init", "mtp_draft_step", "mtp_flush_pairs",
+           "mtp_workspace_init", "mtp_draft_step", "mtp_flush_pairs", "mtp_draft_chain", "mtp_repair_pending",
            "spec_verify_workspace_bytes", "spec_verify", "kv_rollback", "mtp_timing_begin",
            "mtp_timing_pause", "mtp_timing_elapsed", "mtp_timing_end")
 
@@ -81,6 +81,10 @@ def _load():
     lib.mtp_draft_step.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mtp_flush_pairs.restype = C.c_int
     lib.mtp_flush_pairs.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.mtp_draft_chain.restype = C.c_int
+    lib.mtp_draft_chain.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, i32, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.mtp_repair_pending.restype = C.c_int
+    lib.mtp_repair_pending.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     lib.spec_verify_workspace_bytes.restype = sz
     lib.spec_verify_workspace_bytes.argtypes = [i32, i32]
     lib.spec_verify.restype = C.c_int
@@ -173,6 +177,22 @@ def mtp_flush_pairs(head, kv, tokens, hiddens, n_max, n_dev, out_mode, set_round
                              _ptr(n_dev), int(out_mode), int(set_round_base), _ptr(hidden_out),
                              _ptr(logits_last), _ptr(argmax_last), _ptr(ws), ws.nbytes, _stream(stream))
     _check(st, "mtp_flush_pairs")
+
+
+def mtp_draft_chain(head, kv, pend_tokens, pend_hiddens, n_max, n_dev, n_draft, drafts, hiddens_out,
+                    draft_logits, ws, stream=None):
+    st = lib.mtp_draft_chain(head.handle, C.byref(kv.desc), _ptr(pend_tokens), _ptr(pend_hiddens), int(n_max),
+                             _ptr(n_dev), int(n_draft), _ptr(drafts), _ptr(hiddens_out), _ptr(draft_logits),
+                             _ptr(ws), ws.nbytes, _stream(stream))
+    _check(st, "mtp_draft_chain")
+
+
+def mtp_repair_pending(out_tokens, out_counts, target_hiddens, hidden, act_dtype, n_draft, pend_tokens,
+                       pend_hiddens, pend_count, stream=None):
+    st = lib.mtp_repair_pending(_ptr(out_tokens), _ptr(out_counts), _ptr(target_hiddens), int(hidden),
+                                int(act_dtype), int(n_draft), _ptr(pend_tokens), _ptr(pend_hiddens),
+                                _ptr(pend_count), _stream(stream))
+    _check(st, "mtp_repair_pending")
 
 
 def spec_verify_workspace_bytes(n_draft: int, vocab: int) -> int:

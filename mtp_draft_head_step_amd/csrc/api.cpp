@@ -514,6 +514,56 @@ int mtp_flush_pairs(const mtp_head* head, const mtp_kv* kv, const int32_t* token
                       stream);
 }
 
+int mtp_draft_chain(const mtp_head* head, const mtp_kv* kv, const int32_t* pend_tokens_dev,
+                    const void* pend_hiddens_dev, int32_t n_max, const int32_t* n_dev, int32_t n_draft,
+                    int32_t* drafts_dev, void* hiddens_out_dev, float* draft_logits_dev, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  if (!head || !pend_tokens_dev || !pend_hiddens_dev || !drafts_dev || !hiddens_out_dev || !ws)
+    return MTP_E_INVALID_ARG;
+  if (n_draft < 1 || n_draft > MTP_MAX_DRAFT || n_max < 1) return MTP_E_INVALID_ARG;
+  if (n_max > MTP_MAX_FLUSH) return MTP_E_CAPACITY;
+  int st = validate_kv(head, kv);
+  if (st != MTP_OK) return st;
+  if (ws_bytes < layout(head->cfg, n_max, kv->capacity).total) return MTP_E_WORKSPACE;
+  if (hiddens_out_dev == pend_hiddens_dev) return MTP_E_INVALID_ARG;
+  const mtp_head_config& c = head->cfg;
+  const size_t row_bytes = static_cast<size_t>(c.hidden) * (c.act_dtype == MTP_BF16 ? 2 : 4);
+  char* hout = static_cast<char*>(hiddens_out_dev);
+  // the flush of the pending pairs gives d_0 and g_0
+  st = head_forward(head, kv, pend_tokens_dev, pend_hiddens_dev, n_max, n_dev, MTP_FLUSH_LAST, 1, hout,
+                    draft_logits_dev, drafts_dev, ws, stream);
+  if (st != MTP_OK) return st;
+  // chained steps: (d_{i-1}, g_{i-1}) -> d_i, g_i
+  for (int i = 1; i < n_draft; ++i) {
+    st = head_forward(head, kv, drafts_dev + (i - 1), hout + (i - 1) * row_bytes, 1, nullptr, MTP_FLUSH_LAST, 0,
+                      hout + i * row_bytes, draft_logits_dev ? draft_logits_dev + static_cast<size_t>(i) * c.vocab
+                                                             : nullptr,
+                      drafts_dev + i, ws, stream);
+    if (st != MTP_OK) return st;
+  }
+  return MTP_OK;
+}
+
+int mtp_repair_pending(const int32_t* out_tokens_dev, const int32_t* out_counts_dev,
+                       const void* target_hiddens_dev, int32_t hidden, int32_t act_dtype, int32_t n_draft,
+                       int32_t* pend_tokens_dev, void* pend_hiddens_dev, int32_t* pend_count_dev,
+                       hipStream_t stream) {
+  if (!out_tokens_dev || !out_counts_dev || !target_hiddens_dev || !pend_tokens_dev || !pend_hiddens_dev ||
+      !pend_count_dev)
+    return MTP_E_INVALID_ARG;
+  if (hidden < 1 || n_draft < 1 || n_draft > MTP_MAX_DRAFT) return MTP_E_INVALID_ARG;
+  if (act_dtype != MTP_F32 && act_dtype != MTP_BF16) return MTP_E_INVALID_ARG;
+  const size_t row_bytes = static_cast<size_t>(hidden) * (act_dtype == MTP_BF16 ? 2 : 4);
+  // the pending rows must not overlap the rows they are copied from
+  const char* hs = static_cast<const char*>(target_hiddens_dev);
+  const char* hd = static_cast<const char*>(pend_hiddens_dev);
+  const size_t span = (n_draft + 1) * row_bytes;
+  if (hd < hs + span && hs < hd + span) return MTP_E_INVALID_ARG;
+  MTP_TRY(launch_repair(out_tokens_dev, out_counts_dev, target_hiddens_dev, static_cast<int>(row_bytes / 2),
+                        n_draft, pend_tokens_dev, pend_hiddens_dev, pend_count_dev, stream));
+  return MTP_OK;
+}
+
 size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab) {
   if (n_draft < 0 || n_draft > MTP_MAX_DRAFT || vocab < 1) return 0;
   const size_t nb = (static_cast<size_t>(vocab) + kVerifyChunk - 1) / kVerifyChunk;

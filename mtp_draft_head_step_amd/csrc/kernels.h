@@ -215,5 +215,7 @@ bool verify_sampled_supported(int top_k, int vocab);
 hipError_t launch_rollback(int32_t* state, int to_len, const int32_t* n_acc, int n_draft,
                            int capacity, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_repair(const int32_t* out_tokens, const int32_t* out_counts, const void* hid, int elems16,
+                         int n_draft, int32_t* pend_tokens, void* pend_hid, int32_t* pend_count, hipStream_t s);
 
 }  // namespace mtp

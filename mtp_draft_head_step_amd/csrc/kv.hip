@@ -33,6 +33,33 @@ hipError_t launch_rollback(int32_t* state, int to_len, const int32_t* n_acc, int
   return hipGetLastError();
 }
 
+// Policy-B re-pairing: with k = out_counts[0] (brought into [0, n_draft]) and
+// j0 = min(k, n_draft - 1), pending pair j = 0..k - j0 is (out_tokens[j0 + j],
+// hidden row j0 + j); the count k + 1 - j0 goes to *pend_count.  Rows are
+// copied in 16-bit units (elems16 per row).
+__global__ void k_repair(const int32_t* out_tokens, const int32_t* out_counts, const uint16_t* hid, int elems16,
+                         int n_draft, int32_t* pend_tokens, uint16_t* pend_hid, int32_t* pend_count) {
+  int k = out_counts[0];
+  k = k < 0 ? 0 : (k > n_draft ? n_draft : k);
+  const int j0 = n_draft > 0 ? (k < n_draft - 1 ? k : n_draft - 1) : 0;
+  const int cnt = k + 1 - j0;
+  for (int j = 0; j < cnt; ++j) {
+    const uint16_t* src = hid + static_cast<size_t>(j0 + j) * elems16;
+    uint16_t* dst = pend_hid + static_cast<size_t>(j) * elems16;
+    for (int e = threadIdx.x; e < elems16; e += blockDim.x) dst[e] = src[e];
+  }
+  if (threadIdx.x < cnt) pend_tokens[threadIdx.x] = out_tokens[j0 + threadIdx.x];
+  if (threadIdx.x == 0) *pend_count = cnt;
+}
+
+hipError_t launch_repair(const int32_t* out_tokens, const int32_t* out_counts, const void* hid, int elems16,
+                         int n_draft, int32_t* pend_tokens, void* pend_hid, int32_t* pend_count, hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_repair, dim3(1), dim3(256), 0, s, out_tokens, out_counts, static_cast<const uint16_t*>(hid),
+                     elems16, n_draft, pend_tokens, static_cast<uint16_t*>(pend_hid), pend_count);
+  return hipGetLastError();
+}
+
 __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)

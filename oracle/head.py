@@ -108,12 +108,18 @@ class Head:
     lm_head, all given as numpy arrays of their values (fp32 for f32/bf16
     storage; for an int8 lm_head, ``lm_head`` int8 and ``lm_head_scales`` fp16)."""
 
-    def __init__(self, shape, values: dict):
+    def __init__(self, shape, values: dict, cache_fp64: bool = False):
+        """``cache_fp64`` keeps an fp64 copy of every projection matrix (the same
+        values; it only saves re-widening them at each product, for many-row
+        flushes of large heads)."""
         self.s = shape
-        self.w = values
+        self.w = dict(values)
         if values.get("embed") is None or values.get("lm_head") is None:
             raise ValueError("draft head is not bound to a target embedding/lm_head")
         self.group = shape.n_q_heads // shape.n_kv_heads
+        if cache_fp64:
+            for name in ("fc", "q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
+                self.w[name] = np.asarray(values[name], dtype=np.float64)
 
     # -- pieces -----------------------------------------------------------
     def fused_input(self, token, hidden):
@@ -158,13 +164,15 @@ class Head:
         return matvec(w["lm_head"], n)
 
     # -- the two entry points ---------------------------------------------
-    def flush(self, kv, tokens, hiddens, mode=LAST, set_round_base=False):
+    def flush(self, kv, tokens, hiddens, mode=LAST, set_round_base=False, out_rows=None):
         """Pending-pair flush: n complete pairs (tokens[j], hiddens[j]) occupy
         slots kv.len + j.  Every row's K/V is written first (a pair's K/V depends
         only on that pair), then each requested row attends causally over
         [0, slot].  Modes: KV_ONLY (K/V only), LAST (the last row's g, logits and
-        argmax), ALL (every row's g plus the last row's logits and argmax).
-        ``set_round_base`` records kv.base = kv.len after the append.
+        argmax), ALL (every row's g plus the last row's logits and argmax;
+        ``out_rows`` may name a subset of the rows whose g is evaluated, for
+        sampled comparisons of large flushes).  ``set_round_base`` records
+        kv.base = kv.len after the append.
 
         Returns a dict with 'g' ([rows, H] fp64), 'logits' ([V] fp64) and
         'argmax' (int), or {} for KV_ONLY / a device-side error."""
@@ -188,9 +196,10 @@ class Head:
             kv.base = kv.len
         if mode == KV_ONLY:
             return {}
-        rows = range(n) if mode == ALL else [n - 1]
+        rows = (range(n) if out_rows is None else sorted(out_rows)) if mode == ALL else [n - 1]
         g = np.stack([self.finish(xs[j], attend(kvs[j], kv.K, kv.V, off + j + 1)) for j in rows])
-        logits = self.unembed(g[-1])
+        last = g[-1] if rows[-1] == n - 1 else self.finish(xs[n - 1], attend(kvs[n - 1], kv.K, kv.V, off + n))
+        logits = self.unembed(last)
         return {"g": g, "logits": logits, "argmax": int(np.argmax(logits))}
 
     def step(self, kv, token, hidden):

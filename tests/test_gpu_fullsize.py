@@ -27,7 +27,7 @@ from tests.gpu_util import argmax_ok, device_array, host, kv_pair, rel_err, tol_
 pytestmark = pytest.mark.gpu
 
 QWEN_CTX = 4096
-QWEN_CAP = QWEN_CTX + 32
+QWEN_CAP = QWEN_CTX + 256 + 32
 
 
 @pytest.fixture(scope="module")
@@ -37,7 +37,7 @@ def qwen():
     shape, wl = I.QWEN35_27B, I.WL_QWEN
     st = I.head_weights(shape, wl)
     gh = abi.Head(shape, st)
-    oh = OH.Head(shape, I.weight_values(shape, st))
+    oh = OH.Head(shape, I.weight_values(shape, st), cache_fp64=True)
     del st
     kp, vp = I.prefix_kv(shape, wl, QWEN_CTX, QWEN_CAP)
     return {"shape": shape, "gh": gh, "oh": oh, "kp": kp, "vp": vp}
@@ -117,6 +117,40 @@ def test_qwen27b_flush_parity(qwen, n, mode):
         assert rel_err(g[r], ref["g"][j]) <= tol
     if mode == OH.ALL:
         assert np.all(g[n:] == 0)
+
+
+@pytest.mark.timeout(900)
+def test_qwen27b_flush256_parity(qwen):
+    """The pages' full flush at the 27B shape: 256 pending pairs (2.5 MiB of bf16
+    hiddens) after the 4096-slot prefix, ALL mode (the matrix-core path).  Every
+    appended K/V slot, the last row's logits and argmax, and g at sampled rows
+    (first, second, middle, last two) are compared with the oracle."""
+    from mtp_draft_head_step_amd import abi
+    s, gh, oh = qwen["shape"], qwen["gh"], qwen["oh"]
+    tol = tol_of(s)
+    gkv, okv = _qwen_kv(qwen)
+    n = 256
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, n, QWEN_CAP))
+    toks = I.tokens_uniform(I.WL_QWEN, 902, n, s.vocab)
+    hids = I.target_hiddens(s, I.WL_QWEN, 902, n)
+    hout = torch.zeros((n, s.hidden), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros(s.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    abi.mtp_flush_pairs(gh, gkv, device_array(toks), device_array(hids), n, None, OH.ALL, 1, hout, logits, amax,
+                        ws)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 254, 255]
+    ref = oh.flush(okv, [int(t) for t in toks], [I.decode(h, s.act_dtype) for h in hids], OH.ALL,
+                   set_round_base=True, out_rows=rows)
+    assert host(gkv.state).tolist() == [QWEN_CTX + n, QWEN_CTX + n, 0, 0]
+    for lo in range(QWEN_CTX, QWEN_CTX + n, 64):
+        _check_slots(gkv, okv, lo, lo + 64, tol)
+    lg = host(logits)
+    assert rel_err(lg, ref["logits"]) <= tol
+    assert argmax_ok(int(host(amax)[0]), ref["logits"], lg)[0]
+    g = host(hout)
+    for i, r in enumerate(rows):
+        assert rel_err(g[r], ref["g"][i]) <= tol, r
 
 
 # --------------------------------------------------------------------------
@@ -218,9 +252,10 @@ def _planted_target(shape, wl, rnd, n_draft):
 @pytest.mark.parametrize("n_draft", [1, 2, 4, 8])
 def test_depth_rounds_parity(lm, policy, n_draft):
     """Twelve greedy rounds over the 32768-slot prefix, launched as the benchmark
-    launches them (flush with the previous verify's device count, chained steps,
-    verify, rollback); the planted acceptance fixes k, so k, the committed tokens,
-    the KV lengths and every appended K/V entry are compared with the oracle."""
+    launches them (mtp_draft_chain over the pending pairs with their device count,
+    verify, rollback, device re-pairing under policy B); the planted acceptance
+    fixes k, so k, the committed tokens, the re-paired pending pairs, the KV
+    lengths and every appended K/V entry are compared with the oracle."""
     from mtp_draft_head_step_amd import abi
     shape, wl, N = _long_shape(lm), I.WL_DEPTH, n_draft
     tol = tol_of(shape)
@@ -245,30 +280,38 @@ def test_depth_rounds_parity(lm, policy, n_draft):
     pend_h = torch.zeros((N + 1, shape.hidden), dtype=torch.bfloat16, device="cuda")
     pend_h[0] = device_array(hid0[0])
     n_dev = torch.tensor([1], dtype=torch.int32, device="cuda")
+    tgt_h = torch.zeros((N + 1, shape.hidden), dtype=torch.bfloat16, device="cuda")
     gpu_committed = list(committed)
     near_ties = 0
     for rnd in range(12):
         base = int(host(gkv.state)[0])
-        abi.mtp_flush_pairs(gh, gkv, pend_t, pend_h, N + 1, n_dev, abi.LAST, 1, g_buf[0], None, d_buf[0:1], ws)
-        for i in range(1, N):
-            abi.mtp_draft_step(gh, gkv, d_buf[i - 1:i], g_buf[i - 1], g_buf[i], None, d_buf[i:i + 1], ws)
+        # the round as the benchmark launches it: one drafting call, verify, rollback,
+        # and (policy B) the device-side re-pairing
+        abi.mtp_draft_chain(gh, gkv, pend_t, pend_h, N + 1, n_dev, N, d_buf, g_buf, None, ws)
         torch.cuda.synchronize()
         drafts = host(d_buf).tolist()
         k_r, hid_st, fn = _planted_target(shape, wl, rnd, N)
         rows, _ = fn([gpu_committed[-1]] + drafts, len(gpu_committed) - 1)
+        tgt_h.copy_(device_array(hid_st))
         abi.spec_verify(abi.sampling(window=64), N, shape.vocab, device_array(rows), None, d_buf,
                         ring, ring_st, None, out_t, out_c, vws)
         torch.cuda.synchronize()
         appended = int(host(gkv.state)[0])
         abi.kv_rollback(gkv, abi.TO_ROUND_BASE, out_c[0:1] if policy == "B" else None, N)
+        if policy == "B":
+            abi.mtp_repair_pending(out_t, out_c, tgt_h, shape.hidden, abi.MTP_BF16, N, pend_t, pend_h, n_dev)
+        else:
+            pend_t[: N + 1] = out_t
+            pend_h.copy_(tgt_h)
+            n_dev.copy_(out_c[1:2])
+        torch.cuda.synchronize()
         k = int(host(out_c)[0])
         assert k == k_r
         toks = host(out_t)[: k + 1].tolist()
-        j0 = 0 if policy == "A" else min(k, N - 1)
-        pend_t[: k + 1 - j0] = out_t[j0:k + 1]
-        pend_h[: k + 1 - j0] = device_array(hid_st[j0:k + 1])
-        n_dev.fill_(k + 1 - j0)
         gpu_committed += toks
+        j0 = 0 if policy == "A" else min(k, N - 1)
+        assert int(host(n_dev)[0]) == k + 1 - j0
+        assert host(pend_t)[: k + 1 - j0].tolist() == toks[j0:]
         # the oracle round follows the GPU's drafts; where they differ from the
         # oracle's argmax the oracle's top-two margin must be within the logits
         # tolerance (a near tie, where either token is correct)

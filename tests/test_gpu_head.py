@@ -250,3 +250,63 @@ def test_flush_many_rows_parity(name, n, n_max):
     for j in range(n):
         assert rel_err(g[j], ref["g"][j]) <= tol, j
     assert np.all(g[n:] == 0)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("n_draft", [1, 4])
+def test_draft_chain_equals_flush_and_steps(name, n_draft):
+    """mtp_draft_chain enqueues exactly the flush (LAST, round base) and the
+    chained steps: drafts, hiddens, draft logits and the KV are bit-identical."""
+    from mtp_draft_head_step_amd import abi
+    shape = SHAPES[name]
+    N = n_draft
+    _, gh, _ = build(shape, 83)
+    cap = 512
+    kv1, _ = kv_pair(shape, 83, 200, cap)
+    kv2, _ = kv_pair(shape, 83, 200, cap)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, 3, cap))
+    toks = device_array(I.tokens_uniform(83, 4, 3, shape.vocab))
+    hids = device_array(I.target_hiddens(shape, 83, 4, 3))
+    n_dev = torch.tensor([2], dtype=torch.int32, device="cuda")
+    dt = act_dtype(shape)
+    d1 = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    g1 = torch.zeros((N, shape.hidden), dtype=dt, device="cuda")
+    l1 = torch.zeros((N, shape.vocab), dtype=torch.float32, device="cuda")
+    abi.mtp_draft_chain(gh, kv1, toks, hids, 3, n_dev, N, d1, g1, l1, ws)
+    d2 = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    g2 = torch.zeros((N, shape.hidden), dtype=dt, device="cuda")
+    l2 = torch.zeros((N, shape.vocab), dtype=torch.float32, device="cuda")
+    abi.mtp_flush_pairs(gh, kv2, toks, hids, 3, n_dev, OH.LAST, 1, g2[0], l2[0], d2[0:1], ws)
+    for i in range(1, N):
+        abi.mtp_draft_step(gh, kv2, d2[i - 1:i], g2[i - 1], g2[i], l2[i], d2[i:i + 1], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(g1, g2) and torch.equal(l1, l2)
+    assert torch.equal(kv1.state, kv2.state) and int(host(kv1.state)[0]) == 200 + 2 + N - 1
+    assert int(host(kv1.state)[1]) == 202
+    assert torch.equal(kv1.k, kv2.k) and torch.equal(kv1.v, kv2.v)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_draft", [1, 2, 5])
+def test_repair_pending(dtype, n_draft):
+    """Device re-pairing under the keep-accepted policy: for every k the pending
+    pairs are tokens[j0..k] and hidden rows j0..k with j0 = min(k, N-1)."""
+    from mtp_draft_head_step_amd import abi
+    N, H = n_draft, 96
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    code = abi.MTP_BF16 if dtype == "bf16" else abi.MTP_F32
+    rng = np.random.default_rng(N)
+    toks = torch.tensor(rng.integers(0, 1000, N + 1), dtype=torch.int32, device="cuda")
+    hid = torch.tensor(rng.standard_normal((N + 1, H)), dtype=tdt, device="cuda")
+    for k in range(N + 1):
+        counts = torch.tensor([k, k + 1], dtype=torch.int32, device="cuda")
+        pt = torch.full((N + 1,), -7, dtype=torch.int32, device="cuda")
+        ph = torch.zeros((N + 1, H), dtype=tdt, device="cuda")
+        pc = torch.zeros(1, dtype=torch.int32, device="cuda")
+        abi.mtp_repair_pending(toks, counts, hid, H, code, N, pt, ph, pc)
+        torch.cuda.synchronize()
+        j0 = min(k, N - 1)
+        c = k + 1 - j0
+        assert int(pc.item()) == c and c == (1 if k < N else min(2, N + 1 - j0))
+        assert torch.equal(pt[:c], toks[j0:k + 1]) and torch.all(pt[c:] == -7)
+        assert torch.equal(ph[:c], hid[j0:k + 1])
