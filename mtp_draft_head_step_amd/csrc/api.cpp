@@ -1,6 +1,7 @@
 // libmtp C ABI: host-side validation (fail closed before any enqueue), the
 // workspace layout, and the kernel sequences of the draft-head step, the
 // pending-pair flush, verification and rollback.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -100,7 +101,7 @@ int nchunk_for(const mtp_head_config& c, int capacity) {
 }
 
 struct Layout {
-  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, xa, total;
+  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, xa, gpart, total;
   int nchunk;
 };
 
@@ -127,6 +128,19 @@ Layout layout(const mtp_head_config& c, int rows, int capacity) {
   L.g = take(rows * H * 4);
   L.amax = take(amax_parts(c) * 8);
   L.xa = rows > kGemvMaxRows ? take(rows * 2 * H * 2) : off;   // bf16 normalised rows (MFMA path)
+  size_t part = 0;                                             // split partial sums (MFMA path)
+  if (rows > kGemvMaxRows) {
+    const int mq[3] = {static_cast<int>(hq * D), static_cast<int>(hkv * D), static_cast<int>(hkv * D)};
+    const int mh[1] = {static_cast<int>(H)};
+    const int mi[2] = {static_cast<int>(I), static_cast<int>(I)};
+    const int qkv_rows = static_cast<int>((hq + 2 * hkv) * D);
+    part = std::max({gemm_part_floats(rows, H, 2 * H, mh, 1, false),
+                     gemm_part_floats(rows, qkv_rows, H, mq, 3, false),
+                     gemm_part_floats(rows, H, hq * D, mh, 1, false),
+                     gemm_part_floats(rows, I, H, mi, 2, true),
+                     gemm_part_floats(rows, H, I, mh, 1, false)});
+  }
+  L.gpart = part ? take(part * 4) : off;
   L.total = off;
   return L;
 }
@@ -210,12 +224,13 @@ hipError_t timed_gemm(const GemmArgs& g, hipStream_t s) {
   return e;
 }
 
-GemmArgs base_gemm(const mtp_kv* kv, int n_max, const int32_t* n_dev) {
+GemmArgs base_gemm(const mtp_kv* kv, int n_max, const int32_t* n_dev, float* part) {
   GemmArgs g;
   std::memset(&g, 0, sizeof(g));
   g.n_max = n_max;
   g.n_dev = n_dev;
   g.kv_state = kv->state;
+  g.part = part;
   return g;
 }
 
@@ -248,6 +263,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   float* m = reinterpret_cast<float*>(wsp(ws, L.m));
   float* g = reinterpret_cast<float*>(wsp(ws, L.g));
   uint16_t* xa = reinterpret_cast<uint16_t*>(wsp(ws, L.xa));
+  float* gpart = reinterpret_cast<float*>(wsp(ws, L.gpart));
   // many rows with bf16 weights: normalised rows + MFMA tiles instead of GEMV passes
   const bool mfma = h->wt == W_BF16 && n_max > kGemvMaxRows;
   if (mfma) {
@@ -267,7 +283,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     p.embed = h->w.embed; p.embed_bf16 = 1;
     p.hid = hiddens; p.hid_bf16 = c.act_dtype == MTP_BF16; p.ld_hid = H;
     MTP_TRY(launch_rows_prep(p, s));
-    GemmArgs m1 = base_gemm(kv, n_max, n_dev);
+    GemmArgs m1 = base_gemm(kv, n_max, n_dev, gpart);
     m1.w[0] = static_cast<const uint16_t*>(h->w.fc); m1.m[0] = H; m1.M = H; m1.K = 2 * H;
     m1.a = xa; m1.lda = 2 * H; m1.out_mode = OUT_F32; m1.y = x; m1.ldy = H;
     MTP_TRY(timed_gemm(m1, s));
@@ -287,7 +303,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
     p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x; p.ldx = H; p.nw = h->w.input_layernorm;
     MTP_TRY(launch_rows_prep(p, s));
-    GemmArgs m2 = base_gemm(kv, n_max, n_dev);
+    GemmArgs m2 = base_gemm(kv, n_max, n_dev, gpart);
     m2.w[0] = static_cast<const uint16_t*>(h->w.q_proj); m2.m[0] = hq * D;
     m2.w[1] = static_cast<const uint16_t*>(h->w.k_proj); m2.m[1] = hkv * D;
     m2.w[2] = static_cast<const uint16_t*>(h->w.v_proj); m2.m[2] = hkv * D;
@@ -346,6 +362,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   t.part_o = reinterpret_cast<float*>(wsp(ws, L.part_o));
   t.part_ml = reinterpret_cast<float*>(wsp(ws, L.part_ml));
   t.o = o;
+  t.o_bf16 = mfma_out;   // the many-row o product reads bf16 rows
   MTP_TRY(launch_attention(t, s));
 
   // 5. x1 = x + W_o o
@@ -355,9 +372,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.in_mode = IN_F32; a.x = o; a.ldx = hq * D;
   a.out_mode = OUT_RESID; a.res = x; a.ldres = H; a.y = x1; a.ldy = H;
   if (mfma_out) {
-    GemmArgs m5 = base_gemm(kv, n_max, n_dev);
+    GemmArgs m5 = base_gemm(kv, n_max, n_dev, gpart);
     m5.w[0] = static_cast<const uint16_t*>(h->w.o_proj); m5.m[0] = H; m5.M = H; m5.K = hq * D;
-    m5.a = o; m5.a_f32 = 1; m5.lda = hq * D;
+    m5.a = o; m5.lda = hq * D;
     m5.out_mode = OUT_RESID; m5.res = x; m5.ldres = H; m5.y = x1; m5.ldy = H;
     MTP_TRY(timed_gemm(m5, s));
   } else {
@@ -375,10 +392,10 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
     p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x1; p.ldx = H; p.nw = h->w.post_attention_layernorm;
     MTP_TRY(launch_rows_prep(p, s));
-    GemmArgs m6 = base_gemm(kv, n_max, n_dev);
+    GemmArgs m6 = base_gemm(kv, n_max, n_dev, gpart);
     m6.w[0] = static_cast<const uint16_t*>(h->w.gate_proj); m6.m[0] = I;
     m6.w[1] = static_cast<const uint16_t*>(h->w.up_proj); m6.m[1] = I;
-    m6.M = I; m6.K = H; m6.a = xa; m6.lda = H; m6.out_mode = OUT_SWIGLU; m6.y = m; m6.ldy = I;
+    m6.M = I; m6.K = H; m6.a = xa; m6.lda = H; m6.out_mode = OUT_SWIGLU; m6.y = m; m6.ldy = I; m6.y_bf16 = 1;
     MTP_TRY(timed_gemm(m6, s));
   } else {
     MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
@@ -392,9 +409,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.out_mode = OUT_RESID; a.res = x1; a.ldres = H; a.y = g; a.ldy = H;
   a.y2 = hidden_out; a.y2_bf16 = c.act_dtype == MTP_BF16; a.ldy2 = H;
   if (mfma_out) {
-    GemmArgs m7 = base_gemm(kv, n_max, n_dev);
+    GemmArgs m7 = base_gemm(kv, n_max, n_dev, gpart);
     m7.w[0] = static_cast<const uint16_t*>(h->w.down_proj); m7.m[0] = H; m7.M = H; m7.K = I;
-    m7.a = m; m7.a_f32 = 1; m7.lda = I;
+    m7.a = m; m7.lda = I;
     m7.out_mode = OUT_RESID; m7.res = x1; m7.ldres = H; m7.y = g; m7.ldy = H;
     m7.y2 = hidden_out; m7.y2_bf16 = c.act_dtype == MTP_BF16; m7.ldy2 = H;
     MTP_TRY(timed_gemm(m7, s));

@@ -396,7 +396,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
       num3 += wts[c + 3] * po[static_cast<size_t>(c + 3) * D + d];
     }
     for (; c < nc; ++c) num0 += wts[c] * po[static_cast<size_t>(c) * D + d];
-    a.o[static_cast<size_t>(j) * a.hq * D + hq * D + d] = ((num0 + num1) + (num2 + num3)) * inv;
+    const float v = ((num0 + num1) + (num2 + num3)) * inv;
+    const size_t oi = static_cast<size_t>(j) * a.hq * D + hq * D + d;
+    if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(v);
+    else a.o[oi] = v;
   }
 }
 

@@ -295,7 +295,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     const int r = r0 + wr * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
     if (r >= n) continue;
     float v = acc[i];
-    if (SWIGLU) v = silu(v) * accu[i];
+    if (SWIGLU) {
+      v = silu(v) * accu[i];
+      if (a.y_bf16) {
+        static_cast<uint16_t*>(static_cast<void*>(a.y))[static_cast<long long>(r) * a.ldy + col] = f32_to_bf16(v);
+        continue;
+      }
+    }
     if (a.out_mode == OUT_RESID) v += a.res[static_cast<long long>(r) * a.ldres + col];
     a.y[static_cast<long long>(r) * a.ldy + col] = v;
     if (a.y2) {
@@ -307,6 +313,314 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// the weight-streaming product: every flush row in one workgroup
+// ---------------------------------------------------------------------------
+// A workgroup takes up to 256 activation rows and 128 weight rows (SwiGLU: 64
+// gate and the matching 64 up rows) over one range of 64-column reduction
+// steps, with two kinds of wave:
+//
+//   waves 0-3 (products): each owns 32 weight rows and reads them straight from
+//     memory into registers in the layout of the B operand of
+//     v_mfma_f32_32x32x16_bf16: lane l takes the 64 bytes of weight row l % 32
+//     at columns k0 + 32 (l / 32) + [0, 32), and its q-th 16-byte piece feeds
+//     the product of reduction slice q.  The contraction pairs A and B by
+//     position only, so the A operand of slice q is read from LDS at the same
+//     columns, k0 + 32 (l / 32) + 8 q + [0, 8).  Weights are issued three
+//     steps ahead into a ring of three register slots; every weight byte is
+//     loaded once, by one wave.
+//   waves 4-7 (staging): thread t moves activation row t of each step into a
+//     three-stage LDS ring (rows padded by 16 bytes: conflict-free 16-byte
+//     reads), its loads issued two steps ahead.
+//
+// The split keeps each kind's memory counter to its own loads (the counter
+// completes in issue order, so one kind's waits never cover the other's
+// younger loads).  Both kinds pass the same barriers: one per step.  The step
+// loop has no early exit (exits in the middle of the three-step body cost the
+// accumulators a second register set): the step count is rounded up to a
+// multiple of three and the staging waves write zero activations for the
+// extra steps, which then add exactly nothing.  With few
+// output tiles the reduction range is split over workgroups; the partial sums
+// go to a workspace and k_gemm_reduce adds them in split order and applies the
+// epilogue.
+constexpr int kSM = 256;          // activation rows per workgroup
+constexpr int kSN = 128;          // weight rows per workgroup
+constexpr int kSK = 64;           // reduction columns per step
+constexpr int kSLd = kSK + 8;     // bf16 per LDS row
+constexpr int kSWgs = 256;        // workgroups a split aims for (one per compute unit)
+constexpr int kSMinSteps = 4;     // fewest steps a split takes
+// Below this many weights the pipeline's fill and drain outweigh its streaming
+// (the 64 x 64 tiles, many small workgroups, finish first).
+constexpr long long kSMinWeights = 1LL << 22;
+
+bool gemm_stream_supported(int M, int K, const int* m, int nmat, bool swiglu) {
+  if (M <= 0 || K <= 0 || K % kSK) return false;
+  if (static_cast<long long>(M) * K * (swiglu ? 2 : 1) < kSMinWeights) return false;
+  if (swiglu) return M % (kSN / 2) == 0;
+  if (M % kSN) return false;
+  for (int i = 0; i < nmat; ++i)
+    if (m[i] % kSN) return false;
+  return true;
+}
+
+int gemm_split(int M, int K, bool swiglu) {
+  if (swiglu) return 1;
+  const int tiles = M / kSN;
+  int s = kSWgs / (tiles > 0 ? tiles : 1);
+  const int cap = (K / kSK) / kSMinSteps;
+  if (s > cap) s = cap;
+  return s < 1 ? 1 : s;
+}
+
+size_t gemm_part_floats(int rows, int M, int K, const int* m, int nmat, bool swiglu) {
+  if (!gemm_stream_supported(M, K, m, nmat, swiglu)) return 0;
+  const int s = gemm_split(M, K, swiglu);
+  return s > 1 ? static_cast<size_t>(s) * rows * M : 0;
+}
+
+__device__ __forceinline__ void gemm_put(const GemmArgs& a, int r, int col, float v) {
+  if (a.out_mode == OUT_RESID) v += a.res[static_cast<long long>(r) * a.ldres + col];
+  a.y[static_cast<long long>(r) * a.ldy + col] = v;
+  if (a.y2) {
+    if (a.y2_bf16)
+      static_cast<uint16_t*>(a.y2)[static_cast<long long>(r) * a.ldy2 + col] = f32_to_bf16(v);
+    else
+      static_cast<float*>(a.y2)[static_cast<long long>(r) * a.ldy2 + col] = v;
+  }
+}
+
+// The product waves of k_gemm_stream: weights three steps ahead in registers,
+// 32 weight rows a wave, all activation rows from LDS; the sums end in LDS as
+// a row-major fp32 tile (column = wave * 32 + lane % 32).
+template <bool SWIGLU, int NT>
+__device__ __forceinline__ void gemm_stream_products(const GemmArgs& a, uint16_t* As, int kStage, int kTLd,
+                                                     int r0, int sb, int nst, int nst3, int lane, int wave) {
+  // ---- product waves: this wave's 32 weight rows and their output columns
+  const uint16_t* W;
+  int wrow;
+  if (SWIGLU) {
+    W = wave < 2 ? a.w[0] : a.w[1];
+    wrow = blockIdx.x * (kSN / 2) + (wave & 1) * 32;
+  } else {
+    int cl = blockIdx.x * kSN + wave * 32;
+    W = a.w[0];
+    if (cl >= a.m[0]) {
+      cl -= a.m[0];
+      W = a.w[1];
+      if (cl >= a.m[1]) {
+        cl -= a.m[1];
+        W = a.w[2];
+      }
+    }
+    wrow = cl;
+  }
+  const char* bp = reinterpret_cast<const char*>(W + static_cast<long long>(wrow + (lane & 31)) * a.K +
+                                                 static_cast<long long>(sb) * kSK + (lane >> 5) * 32);
+  auto issue = [&](uint4 (&b)[4], int st) {
+    st = min(st, nst - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = load_stream16(bp + static_cast<long long>(st) * kSK * 2 + q * 16);
+  };
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16_t{};
+  const int aoff = (lane & 31) * kSLd + (lane >> 5) * 32;
+  auto compute = [&](int stage, const uint4 (&b)[4]) {
+    const uint16_t* base = As + stage * kStage + aoff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, b[q]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t,
+            *reinterpret_cast<const uint4*>(base + t * 32 * kSLd + q * 8));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+      }
+      // one slice's operand reads in flight at a time (bounds the registers
+      // the scheduler may tie up in early reads)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  uint4 b0[4], b1[4], b2[4];
+  issue(b0, 0);
+  issue(b1, 1);
+  issue(b2, 2);
+  __syncthreads();
+  for (int s = 0; s < nst3; s += 3) {
+    compute(0, b0);
+    issue(b0, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, b1);
+    issue(b1, s + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    compute(2, b2);
+    issue(b2, s + 5);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // accumulator element i of block t: row t * 32 + (i / 4) * 8 + (lane / 32) * 4
+  // + i % 4, column lane % 32 of the wave's 32 (the staging ring is free after
+  // the last step's barrier)
+  float* T = reinterpret_cast<float*>(As);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = t * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      T[r * kTLd + wave * 32 + (lane & 31)] = acc[t][i];
+    }
+}
+
+// NT: 32-row blocks of activations computed (NT * 32 >= the rows a launch sees)
+template <bool SWIGLU, int NT>
+__global__ __launch_bounds__(512) void k_gemm_stream(GemmArgs a) {
+  constexpr int kRows = NT * 32;
+  constexpr int kStage = kSM * kSLd;                  // bf16 per LDS stage (256 rows)
+  constexpr int kTLd = kSN + 4;                       // floats per row of the epilogue tile
+  constexpr int kLds = 3 * kStage * 2 > kRows * kTLd * 4 ? 3 * kStage * 2 : kRows * kTLd * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t As[kLds / 2];
+  if (a.kv_state && a.kv_state[3] != 0) return;
+  int n = a.n_max;
+  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  const int r0 = blockIdx.z * kSM;
+  if (r0 >= n) return;
+  const int rows = min(n - r0, kRows);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // this workgroup's reduction steps
+  const int steps = a.K / kSK;
+  const int sp = blockIdx.y, nsp = gridDim.y;
+  const int sb = static_cast<int>(static_cast<long long>(steps) * sp / nsp);
+  const int nst = static_cast<int>(static_cast<long long>(steps) * (sp + 1) / nsp) - sb;
+  const int nst3 = (nst + 2) / 3 * 3;               // steps run (the extra ones add zeros)
+
+  if (wave >= 4) {
+    // ---- staging waves: row t of every step into LDS stage (step % 3); rows
+    // past n_max clamp (computed, never stored), rows past NT * 32 unread
+    const int t = tid - 256;
+    const int row = min(r0 + t, a.n_max - 1);
+    const uint4* ap = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.a) +
+                                                     static_cast<long long>(row) * a.lda +
+                                                     static_cast<long long>(sb) * kSK);
+    uint4 p0[8], p1[8], p2[8];
+    auto load = [&](uint4 (&p)[8], int st) {
+      st = min(st, nst - 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = ap[static_cast<long long>(st) * (kSK / 8) + i];
+    };
+    auto store = [&](const uint4 (&p)[8], int stage, int st) {
+      const uint32_t keep = st < nst ? 0xFFFFFFFFu : 0u;
+      uint4* dst = reinterpret_cast<uint4*>(As + stage * kStage + t * kSLd);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dst[i] = make_uint4(p[i].x & keep, p[i].y & keep, p[i].z & keep, p[i].w & keep);
+    };
+    load(p0, 0);
+    load(p1, 1);
+    load(p2, 2);
+    store(p0, 0, 0);
+    __syncthreads();
+    // during step s: store step s + 1 (issued two steps back), then issue
+    // step s + 3 into the slot step s used
+    // (the scheduling fences keep each step's register work on its side of
+    // the barrier, so a wait for a slot never moves ahead of its step)
+    for (int s = 0; s < nst3; s += 3) {
+      store(p1, 1, s + 1);
+      load(p0, s + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      store(p2, 2, s + 2);
+      load(p1, s + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      store(p0, 0, s + 3);
+      load(p2, s + 5);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    gemm_stream_products<SWIGLU, NT>(a, As, kStage, kTLd, r0, sb, nst, nst3, lane, wave);
+  }
+  __syncthreads();   // the products' sums are in LDS (row-major, kTLd floats a row)
+
+  // ---- epilogue: every thread, 16-byte pieces of whole rows
+  const float* T = reinterpret_cast<const float*>(As);
+  if (SWIGLU) {
+    // columns [0, 64) hold the gate sums, [64, 128) the up sums of the same outputs
+    for (int e = tid; e < rows * 16; e += 512) {
+      const int r = e >> 4, c = (e & 15) * 4;
+      const float4 g = *reinterpret_cast<const float4*>(T + r * kTLd + c);
+      const float4 u = *reinterpret_cast<const float4*>(T + r * kTLd + 64 + c);
+      const float4 v = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+      const long long o = static_cast<long long>(r0 + r) * a.ldy + blockIdx.x * (kSN / 2) + c;
+      if (a.y_bf16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(static_cast<void*>(a.y)) + o) =
+            make_uint2(f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                       f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16));
+      } else {
+        *reinterpret_cast<float4*>(a.y + o) = v;
+      }
+    }
+    return;
+  }
+  for (int e = tid; e < rows * 32; e += 512) {
+    const int r = e >> 5, c = (e & 31) * 4;
+    float4 v = *reinterpret_cast<const float4*>(T + r * kTLd + c);
+    const long long row = r0 + r;
+    const int col = blockIdx.x * kSN + c;
+    if (nsp > 1) {
+      *reinterpret_cast<float4*>(a.part + (static_cast<long long>(sp) * a.n_max + row) * a.M + col) = v;
+      continue;
+    }
+    if (a.out_mode == OUT_RESID) {
+      const float4 q = *reinterpret_cast<const float4*>(a.res + row * a.ldres + col);
+      v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+    }
+    *reinterpret_cast<float4*>(a.y + row * a.ldy + col) = v;
+    if (a.y2) {
+      if (a.y2_bf16)
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y2) + row * a.ldy2 + col) =
+            make_uint2(f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                       f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16));
+      else
+        *reinterpret_cast<float4*>(static_cast<float*>(a.y2) + row * a.ldy2 + col) = v;
+    }
+  }
+}
+
+// Sum of the split partials in split order, then the epilogue; a thread per
+// four consecutive output columns of one row.
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int nsp) {
+  if (a.kv_state && a.kv_state[3] != 0) return;
+  int n = a.n_max;
+  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  const int per_row = a.M / 4;
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int r = static_cast<int>(idx / per_row);
+  const int c = static_cast<int>(idx % per_row) * 4;
+  if (r >= n) return;
+  const long long stride = static_cast<long long>(a.n_max) * a.M;
+  const float* p = a.part + static_cast<long long>(r) * a.M + c;
+  float4 v = *reinterpret_cast<const float4*>(p);
+  for (int s = 1; s < nsp; ++s) {
+    const float4 w = *reinterpret_cast<const float4*>(p + s * stride);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  gemm_put(a, r, c, v.x);
+  gemm_put(a, r, c + 1, v.y);
+  gemm_put(a, r, c + 2, v.z);
+  gemm_put(a, r, c + 3, v.w);
+}
+
 bool gemm_supported(int M, int K, const int* m, int nmat) {
   if (M <= 0 || K <= 0 || M % kTN || K % kTK) return false;
   for (int i = 0; i < nmat; ++i)
@@ -316,9 +630,37 @@ bool gemm_supported(int M, int K, const int* m, int nmat) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.n_max <= 0) return hipSuccess;
-  const dim3 grid(a.M / kTN, (a.n_max + kTM - 1) / kTM);
+  const bool swiglu = a.out_mode == OUT_SWIGLU;
   (void)hipGetLastError();
-  if (a.out_mode == OUT_SWIGLU)
+  // the streaming epilogue moves 16-byte pieces: leading dimensions in whole
+  // pieces, buffers aligned to them
+  auto al = [](const void* p, int b) { return (reinterpret_cast<uintptr_t>(p) & (b - 1)) == 0; };
+  const bool pieces = a.ldy % 4 == 0 && al(a.y, 16) && al(a.part, 16) &&
+                      (a.out_mode != OUT_RESID || (a.ldres % 4 == 0 && al(a.res, 16))) &&
+                      (!a.y2 || (a.ldy2 % 4 == 0 && al(a.y2, 16)));
+  if (gemm_stream_supported(a.M, a.K, a.m, swiglu ? 2 : 3, swiglu) && !a.a_f32 && pieces) {
+    const int nsp = gemm_split(a.M, a.K, swiglu);
+    if (nsp > 1 && !a.part) return hipErrorInvalidValue;
+    const dim3 grid(a.M / (swiglu ? kSN / 2 : kSN), nsp, (a.n_max + kSM - 1) / kSM);
+    // 32-row blocks computed: enough for every row a launch can see
+    const int nt = a.n_max > 128 ? 8 : (a.n_max > 64 ? 4 : 2);
+#define MTP_STREAM(SW, NT) hipLaunchKernelGGL((k_gemm_stream<SW, NT>), grid, dim3(512), 0, s, a)
+    if (swiglu) {
+      if (nt == 8) MTP_STREAM(true, 8); else if (nt == 4) MTP_STREAM(true, 4); else MTP_STREAM(true, 2);
+    } else {
+      if (nt == 8) MTP_STREAM(false, 8); else if (nt == 4) MTP_STREAM(false, 4); else MTP_STREAM(false, 2);
+    }
+#undef MTP_STREAM
+    if (nsp > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const long long threads = static_cast<long long>(a.n_max) * (a.M / 4);
+      hipLaunchKernelGGL(k_gemm_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a, nsp);
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid(a.M / kTN, (a.n_max + kTM - 1) / kTM);
+  if (swiglu)
     hipLaunchKernelGGL(k_gemm<true>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_gemm<false>, grid, dim3(256), 0, s, a);

@@ -116,9 +116,14 @@ struct GemmArgs {
   void* y2;                  // optional copy of y in the activation dtype
   int y2_bf16;
   int ldy2;
+  float* part;               // split partial sums [split, n_max, M] (gemm_part_floats)
+  int y_bf16;                // OUT_SWIGLU: y holds bf16 (ldy in bf16 elements)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 bool gemm_supported(int M, int K, const int* m, int nmat);
+// fp32 elements of the partial-sum workspace a product of `rows` rows needs
+// (0 when it runs unsplit)
+size_t gemm_part_floats(int rows, int M, int K, const int* m, int nmat, bool swiglu);
 
 // q/k RMSNorm + RoPE for rows j < n at positions state[0] + j, append k, v to
 // the cache, write roped q to `q_out`.  state[0] is advanced later by k_finish.
@@ -158,7 +163,8 @@ struct AttnArgs {
   int mfma;                // ROWS_RANGE over bf16 K/V: the matrix-core flush kernel
   float* part_o;           // [rows, Hq, nchunk, D]
   float* part_ml;          // [rows, Hq, nchunk, 2]
-  float* o;                // [rows, Hq * D]
+  float* o;                // [rows, Hq * D] (bf16 when o_bf16)
+  int o_bf16;
   // ROW_LAST with fuse_rope: the q/k RMSNorm + RoPE and the K/V append of the
   // rows j < n run inside the attention kernel (no separate append launch); the
   // q/k/v projections of the rows are read from qkv.

@@ -205,8 +205,9 @@ def test_token_out_of_range_sets_error(bad):
     assert host(gkv.state).tolist() == [6, 6, 0, abi.DEV_TOKEN]
 
 
-# head_dim 128 and 256 with grouped heads 4 and 6: the matrix-core flush kernels
-# at their other tile shapes (bf16 weights, activations and KV)
+# head_dim 64, 128 and 256 with grouped heads 4 and 6, and a hidden size past
+# the weight-streaming product's threshold: the matrix-core flush kernels at
+# their other shapes (bf16 weights, activations and KV)
 MID_SHAPES = {
     "d128_g4": I.HeadShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
                            vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
@@ -214,6 +215,14 @@ MID_SHAPES = {
     "d256_g6": I.HeadShape(hidden=512, n_q_heads=6, n_kv_heads=1, head_dim=256, intermediate=1536,
                            vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
                                                    lm_head_dtype=I.BF16),
+    "d64_g4": I.HeadShape(hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=64, intermediate=768,
+                          vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
+                                                  lm_head_dtype=I.BF16),
+    # hidden 2048: fc, gate/up and down (4M+ weights) take the weight-streaming
+    # product (split-K partials and the SwiGLU epilogue), q/k/v and o the tiles
+    "h2048": I.HeadShape(hidden=2048, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=2048,
+                         vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
+                                                 lm_head_dtype=I.BF16),
 }
 
 
