@@ -353,9 +353,10 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     t.nw_bf16 = h->wt == W_BF16; t.eps = c.rms_eps; t.theta = c.rope_theta;
   }
   if (mfma_out && c.kv_dtype == MTP_BF16) {
-    // matrix-core flush attention: about 256 workgroups of 64 query vectors
+    // matrix-core flush attention: workgroups of 64 query vectors, at most
+    // about two per compute unit (both fit at every head size)
     const int qblocks = (n_max * (hq / hkv) + 63) / 64;
-    int ns = (256 + qblocks * hkv - 1) / (qblocks * hkv);
+    int ns = 512 / (qblocks * hkv);
     t.mfma = 1;
     t.nchunk = ns < 1 ? 1 : (ns > L.nchunk ? L.nchunk : ns);
   }

@@ -29,7 +29,7 @@ constexpr int kFKeys = 64;     // keys per block
 constexpr int kFQ = 64;        // query vectors per workgroup (16 per wave)
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_flush(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
   constexpr int KLD = D + 8;          // bf16 per LDS K row
   constexpr int VLD = kFKeys + 8;     // bf16 per LDS V^T row
   constexpr int DK = D / 32;          // 32-wide head_dim steps of S^T
@@ -88,27 +88,58 @@ __global__ __launch_bounds__(256) void k_attn_flush(AttnArgs a) {
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + static_cast<size_t>(kvh) * a.capacity * D;
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + static_cast<size_t>(kvh) * a.capacity * D;
-  constexpr int kChunks = kFKeys * D / 8;                    // 16-byte pieces per block
-
-  for (int kb = k0; kb < k1; kb += kFKeys) {
-    __syncthreads();
-    // stage K rows and V^T of keys [kb, kb + 64) (rows past k1 as zeros)
-    for (int e = tid; e < kChunks; e += 256) {
-      const int key = e / (D / 8), d8 = (e % (D / 8)) * 8;
-      uint4 kv4 = make_uint4(0u, 0u, 0u, 0u), vv4 = make_uint4(0u, 0u, 0u, 0u);
-      if (kb + key < k1) {
-        kv4 = *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(kb + key) * D + d8);
-        vv4 = *reinterpret_cast<const uint4*>(vc + static_cast<size_t>(kb + key) * D + d8);
-      }
-      *reinterpret_cast<uint4*>(Ks + key * KLD + d8) = kv4;
-      const uint32_t vw[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+  // staging of a 64-key block (keys past k1 read the last key: their scores are
+  // masked, so their V rows meet zero probabilities):
+  //   K rows  thread t moves 16-byte pieces t, t + 256, ... (row-major)
+  //   V^T     thread t < D takes keys 8 (t % 8) + [0, 8) at dims 8 (t / 8) +
+  //           [0, 8), transposes the 8 x 8 block in registers and writes 8
+  //           16-byte rows of V^T (lanes 8 apart in dims: conflict-free)
+  constexpr int kKPer = kFKeys * D / 8 / 256;                // K pieces per thread
+  uint4 kpf[kKPer], vpf[8];
+  const int vg = tid & 7, vd = (tid >> 3) * 8;
+  auto load_block = [&](int kb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Vt[(d8 + 2 * i) * VLD + key] = static_cast<uint16_t>(vw[i] & 0xFFFFu);
-        Vt[(d8 + 2 * i + 1) * VLD + key] = static_cast<uint16_t>(vw[i] >> 16);
+    for (int u = 0; u < kKPer; ++u) {
+      const int e = tid + 256 * u;
+      const int key = min(kb + e / (D / 8), k1 - 1), d8 = (e % (D / 8)) * 8;
+      kpf[u] = *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(key) * D + d8);
+    }
+    if (tid < D) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = min(kb + vg * 8 + j, k1 - 1);
+        vpf[j] = *reinterpret_cast<const uint4*>(vc + static_cast<size_t>(key) * D + vd);
       }
     }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int u = 0; u < kKPer; ++u) {
+      const int e = tid + 256 * u;
+      *reinterpret_cast<uint4*>(Ks + (e / (D / 8)) * KLD + (e % (D / 8)) * 8) = kpf[u];
+    }
+    if (tid < D) {
+      // word q of a piece holds dims 2q (low half) and 2q + 1 (high half)
+      auto word = [](const uint4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; };
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = word(vpf[2 * p], i >> 1), hi = word(vpf[2 * p + 1], i >> 1);
+          o[p] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+        }
+        *reinterpret_cast<uint4*>(Vt + (vd + i) * VLD + vg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  };
+
+  if (k0 < k1) load_block(k0);
+  for (int kb = k0; kb < k1; kb += kFKeys) {
+    __syncthreads();   // the previous block's operand reads are done
+    store_block();
     __syncthreads();
+    if (kb + kFKeys < k1) load_block(kb + kFKeys);   // the next block's loads fly during the products
 
     // S^T for four 16-key tiles
     f32x4v s[4];
