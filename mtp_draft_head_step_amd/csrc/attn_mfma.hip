@@ -67,16 +67,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
   const float scale = rsqrtf(static_cast<float>(D));
   bf16x8v qf[DK];
   {
+    // (jq, head) is a valid row for every lane, so all loads are issued
+    // unconditionally and at once; lanes past the last query take zeros
     const float* qp = a.q + (static_cast<size_t>(jq) * a.hq + head) * D + (lane >> 4) * 8;
+    const float qs = qok ? scale : 0.f;
+    float4 qv[DK][2];
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
+      qv[dk][0] = *reinterpret_cast<const float4*>(qp + dk * 32);
+      qv[dk][1] = *reinterpret_cast<const float4*>(qp + dk * 32 + 4);
+    }
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      const float x[8] = {qv[dk][0].x, qv[dk][0].y, qv[dk][0].z, qv[dk][0].w,
+                          qv[dk][1].x, qv[dk][1].y, qv[dk][1].z, qv[dk][1].w};
       uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = qok ? qp[dk * 32 + 2 * i] * scale : 0.f;
-        const float x1 = qok ? qp[dk * 32 + 2 * i + 1] * scale : 0.f;
-        w[i] = f32_to_bf16(x0) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
-      }
+      for (int i = 0; i < 4; ++i)
+        w[i] = f32_to_bf16(x[2 * i] * qs) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1] * qs)) << 16);
       qf[dk] = __builtin_bit_cast(bf16x8v, make_uint4(w[0], w[1], w[2], w[3]));
     }
   }
@@ -95,51 +103,52 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
   //           [0, 8), transposes the 8 x 8 block in registers and writes 8
   //           16-byte rows of V^T (lanes 8 apart in dims: conflict-free)
   constexpr int kKPer = kFKeys * D / 8 / 256;                // K pieces per thread
-  uint4 kpf[kKPer], vpf[8];
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  u32x4v kpf[kKPer], vpf[8];     // native vectors: kept in registers across the loop
   const int vg = tid & 7, vd = (tid >> 3) * 8;
-  auto load_block = [&](int kb) {
+  const bool vt = tid < D;
+  // the loads of the block at kb (written out, not in a lambda: the arrays
+  // must stay in registers)
+#define MTP_FLUSH_LOAD(kb)                                                                 \
+  {                                                                                        \
+    _Pragma("unroll") for (int u = 0; u < kKPer; ++u) {                                    \
+      const int e = tid + 256 * u;                                                         \
+      const int key = min((kb) + e / (D / 8), k1 - 1), d8 = (e % (D / 8)) * 8;             \
+      kpf[u] = *reinterpret_cast<const u32x4v*>(kc + static_cast<size_t>(key) * D + d8);   \
+    }                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                        \
+      const int key = min((kb) + vg * 8 + j, k1 - 1);                                      \
+      vpf[j] = *reinterpret_cast<const u32x4v*>(vc + static_cast<size_t>(key) * D + (vt ? vd : 0)); \
+    }                                                                                      \
+  }
+
+  if (k0 < k1) MTP_FLUSH_LOAD(k0);
+  for (int kb = k0; kb < k1; kb += kFKeys) {
+    __syncthreads();   // the previous block's operand reads are done
 #pragma unroll
     for (int u = 0; u < kKPer; ++u) {
       const int e = tid + 256 * u;
-      const int key = min(kb + e / (D / 8), k1 - 1), d8 = (e % (D / 8)) * 8;
-      kpf[u] = *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(key) * D + d8);
+      *reinterpret_cast<u32x4v*>(Ks + (e / (D / 8)) * KLD + (e % (D / 8)) * 8) = kpf[u];
     }
-    if (tid < D) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = min(kb + vg * 8 + j, k1 - 1);
-        vpf[j] = *reinterpret_cast<const uint4*>(vc + static_cast<size_t>(key) * D + vd);
-      }
-    }
-  };
-  auto store_block = [&]() {
-#pragma unroll
-    for (int u = 0; u < kKPer; ++u) {
-      const int e = tid + 256 * u;
-      *reinterpret_cast<uint4*>(Ks + (e / (D / 8)) * KLD + (e % (D / 8)) * 8) = kpf[u];
-    }
-    if (tid < D) {
+    if (vt) {
       // word q of a piece holds dims 2q (low half) and 2q + 1 (high half)
-      auto word = [](const uint4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; };
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t o[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = word(vpf[2 * p], i >> 1), hi = word(vpf[2 * p + 1], i >> 1);
+          const uint32_t lo = vpf[2 * p][i >> 1], hi = vpf[2 * p + 1][i >> 1];
           o[p] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
         }
         *reinterpret_cast<uint4*>(Vt + (vd + i) * VLD + vg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
-  };
-
-  if (k0 < k1) load_block(k0);
-  for (int kb = k0; kb < k1; kb += kFKeys) {
-    __syncthreads();   // the previous block's operand reads are done
-    store_block();
     __syncthreads();
-    if (kb + kFKeys < k1) load_block(kb + kFKeys);   // the next block's loads fly during the products
+    // the next block's loads fly during the products (unconditional: past the
+    // last block they reload the clamped last key, unused; a conditional load
+    // would keep the arrays out of registers)
+    MTP_FLUSH_LOAD(kb + kFKeys);
+#undef MTP_FLUSH_LOAD
 
     // S^T for four 16-key tiles
     f32x4v s[4];
