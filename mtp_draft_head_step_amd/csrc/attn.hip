@@ -123,19 +123,52 @@ __device__ __forceinline__ void unpack16(const uint4& v, float (&f)[KVB ? 8 : 4]
 template <int D, typename Put>
 __device__ __forceinline__ void norm_rope_head(const float* src, const void* nw, int nw_bf16, float eps,
                                                int pos, double l2t, int lane, Put put) {
+  // every load first (one memory round trip), then the arithmetic in the same
+  // per-lane order as an element-at-a-time loop: lane holds d = lane + 64 k
+  constexpr int NE = D / 64;                 // elements per lane (D >= 64)
+  constexpr int NP = (D / 2 + 63) / 64;      // rotation pairs per lane
+  float x[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) x[k] = src[lane + 64 * k];
+  // weights as raw bits (bf16 in the high half once converted); the
+  // conversion waits until after both load forms join
+  uint32_t b1[NP], b2[NP];
+  if (nw_bf16) {
+#pragma unroll
+    for (int r = 0; r < NP; ++r) {
+      const int i = (lane + 64 * r) % (D / 2);   // lanes past D / 2 (D = 64) load a valid weight, unused
+      b1[r] = static_cast<const uint16_t*>(nw)[i];
+      b2[r] = static_cast<const uint16_t*>(nw)[i + D / 2];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NP; ++r) {
+      const int i = (lane + 64 * r) % (D / 2);
+      b1[r] = static_cast<const uint32_t*>(nw)[i];
+      b2[r] = static_cast<const uint32_t*>(nw)[i + D / 2];
+    }
+  }
+  const int wsh = nw_bf16 ? 16 : 0;
   float ss = 0.f;
-  for (int d = lane; d < D; d += 64) ss += src[d] * src[d];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) ss += x[k] * x[k];
   ss = wave_sum(ss);
   const float inv = rsqrtf(ss / static_cast<float>(D) + eps);
-  for (int i = lane; i < D / 2; i += 64) {
-    const float w1 = nw_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(nw)[i]) : static_cast<const float*>(nw)[i];
-    const float w2 = nw_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(nw)[i + D / 2])
-                             : static_cast<const float*>(nw)[i + D / 2];
-    const float x1 = src[i] * inv * w1, x2 = src[i + D / 2] * inv * w2;
-    float c, s;
-    rope_cs(pos, i, D, l2t, c, s);
-    put(i, x1 * c - x2 * s);
-    put(i + D / 2, x1 * s + x2 * c);
+  // element i + D / 2 of pair r: with D >= 128 it is this lane's x[r + NE / 2];
+  // with D = 64 it sits in lane + 32
+  const float up = __shfl_down(x[0], 32, 64);
+#pragma unroll
+  for (int r = 0; r < NP; ++r) {
+    const int i = lane + 64 * r;
+    if (i < D / 2) {
+      const float xa = x[r];
+      const float xb = (D >= 128) ? x[(r + NE / 2) % NE] : up;
+      const float x1 = xa * inv * __uint_as_float(b1[r] << wsh), x2 = xb * inv * __uint_as_float(b2[r] << wsh);
+      float c, sn;
+      rope_cs(pos, i, D, l2t, c, sn);
+      put(i, x1 * c - x2 * sn);
+      put(i + D / 2, x1 * sn + x2 * c);
+    }
   }
 }
 
@@ -207,9 +240,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         else static_cast<float*>(a.kc)[o + d] = v;
       });
       const float* vsrc = row + (a.hq + a.hkv + h) * D;
-      for (int d = lane; d < D; d += 64) {
-        if constexpr (KVB) static_cast<uint16_t*>(a.vc)[o + d] = f32_to_bf16(vsrc[d]);
-        else static_cast<float*>(a.vc)[o + d] = vsrc[d];
+      float vv[D / 64];
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) vv[k] = vsrc[lane + 64 * k];
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        if constexpr (KVB) static_cast<uint16_t*>(a.vc)[o + lane + 64 * k] = f32_to_bf16(vv[k]);
+        else static_cast<float*>(a.vc)[o + lane + 64 * k] = vv[k];
       }
     }
     // the query heads of this kv head, row j, normed and roped
@@ -389,6 +426,20 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   for (int d = tid; d < D; d += 256) {
     float num0 = 0.f, num1 = 0.f, num2 = 0.f, num3 = 0.f;
     int c = 0;
+    // sixteen chunk loads in flight per round trip; accumulator k still takes
+    // the chunks c = k (mod 4) in increasing order
+    for (; c + 16 <= nc; c += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = po[static_cast<size_t>(c + u) * D + d];
+#pragma unroll
+      for (int u = 0; u < 16; u += 4) {
+        num0 += wts[c + u] * v[u];
+        num1 += wts[c + u + 1] * v[u + 1];
+        num2 += wts[c + u + 2] * v[u + 2];
+        num3 += wts[c + u + 3] * v[u + 3];
+      }
+    }
     for (; c + 4 <= nc; c += 4) {
       num0 += wts[c] * po[static_cast<size_t>(c) * D + d];
       num1 += wts[c + 1] * po[static_cast<size_t>(c + 1) * D + d];
