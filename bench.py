@@ -463,7 +463,7 @@ def run_flush(args, big=False):
                      "prefix": prefix, "mode": "ALL (every row's g; last row's logits and argmax)"})
     if big:   # the projections dominate: the roofline is the MFMA GEMMs of one flush
         line = roofline("mfma", gemm_flops / proj_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None,
-                        kernel="the flush's five MFMA GEMMs (fc, qkv, o, gate/up, down; 256 rows, 64x64 tiles)",
+                        kernel="the flush's five MFMA products (fc, qkv, o, gate/up, down; all 256 rows per workgroup, weights streamed once; split-K reduce included)",
                         flops_per_launch=round(gemm_flops / max(1, proj_n // timed_side)),
                         avg_us=round(proj_s * 1e6 / max(1, proj_n // timed_side), 2), launches=proj_n)
     else:     # the attention dominates
