@@ -205,8 +205,10 @@ size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab);
  * {k accepted, k+1 committed}.  Accept d_i iff u_i * q_i(d_i) < p_i(d_i); at the
  * first rejection draw from normalise(max(0, p - q)) (p if that is zero); if all
  * are accepted draw the bonus from p_N.  Sampler order: penalty, temperature,
- * top-k, softmax, top-p, min-p.  With temperature > 0, top_k must be in 1..256
- * and ceil(vocab / 4096) * top_k <= 8192 (MTP_E_UNSUPPORTED otherwise). */
+ * top-k, softmax, top-p, min-p.  Any top_k >= 0 (0 = the whole vocabulary):
+ * top_k in 1..256 with ceil(vocab / 4096) * top_k <= 8192 selects per-chunk
+ * candidates; other values take the whole-vocabulary path (radix passes over
+ * each row's transformed logits, slower). */
 int spec_verify(const spec_sampling *sp, int32_t n_draft, int32_t vocab,
                 const float *target_logits_dev, const float *draft_logits_dev,
                 const int32_t *draft_tokens_dev, int32_t *history_dev,

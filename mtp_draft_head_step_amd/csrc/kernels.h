@@ -215,7 +215,8 @@ struct VerifyArgs {
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s);
 size_t verify_sampled_scratch_bytes(int n_draft, int vocab, int chunk);
-// top_k in [1, 256] and ceil(vocab / 4096) * top_k <= 8192
+// any top_k >= 0 (the whole-vocabulary path takes what the per-chunk
+// candidates cannot hold)
 bool verify_sampled_supported(int top_k, int vocab);
 
 hipError_t launch_rollback(int32_t* state, int to_len, const int32_t* n_acc, int n_draft,

@@ -168,11 +168,17 @@ __host__ __device__ inline SampledScratch sampled_scratch(void* base, int n_draf
   return s;
 }
 
+size_t full_scratch_bytes(int n_draft, int vocab);
+
+// either path's scratch (both start at the same place)
 size_t verify_sampled_scratch_bytes(int n_draft, int vocab, int chunk) {
   (void)chunk;
   const int rows = 2 * n_draft + 1;
   const size_t nb = (static_cast<size_t>(vocab) + kSChunk - 1) / kSChunk;
-  return align256(rows * nb * kSMaxTopK * 8) + align256(rows * 4ull) + 2 * align256(rows * kSMaxTopK * 4ull) + 256;
+  const size_t radix =
+      align256(rows * nb * kSMaxTopK * 8) + align256(rows * 4ull) + 2 * align256(rows * kSMaxTopK * 4ull) + 256;
+  const size_t full = full_scratch_bytes(n_draft, vocab);
+  return radix > full ? radix : full;
 }
 
 __device__ __forceinline__ float key_value(unsigned long long key) {
@@ -473,15 +479,408 @@ __global__ void k_sample_decide(VerifyArgs a, SampledScratch sc) {
   a.ring_state[1] = c;
 }
 
-bool verify_sampled_supported(int top_k, int vocab) {
+// ---------------------------------------------------------------------------
+// Sampled verification over the whole vocabulary (top_k = 0, or top_k past
+// what the per-chunk candidates hold).  The kept set of a row is a prefix of
+// its keys in (value desc, id asc) order, the shortest of three prefixes: the
+// top_k largest, the shortest whose softmax mass (over the top-k set) reaches
+// top_p, and the values with y - y_max >= ln(min_p) (fp32, as elsewhere).  So
+// it is "keys >= T" for T the largest of the three cut keys.
+//  F1. k_full_transform (chunks x rows): y = penalise(x) / T into a row buffer,
+//      chunk maxima.
+//  F2. k_full_select (rows, 1024 threads): y_max; the top-k cut by a radix
+//      select on counts; the top-p cut by a radix select on masses, held as
+//      integers (exp(y - y_max) in units of 2^-40) so every sum is exact and
+//      independent of the order of the atomic adds; the min-p cut from the
+//      smallest value that passes; the normaliser over the kept keys in fp64,
+//      summed in a fixed order.
+//  F3. k_full_decide (1024 threads): the accept tests (one thread), then each
+//      draw as a fixed-order parallel inverse CDF over all ids (per-thread
+//      id ranges, an exclusive scan of their fp64 sums, one thread walks the
+//      range holding u * total).
+constexpr int kFThreads = 1024;
+constexpr double kFMassScale = 1099511627776.0;   // 2^40
+
+struct FullScratch {
+  float* y;                  // [rows][vocab]
+  float* cmax;               // [rows][nb]
+  float* ymax;               // [rows]
+  double* z;                 // [rows] normaliser over the kept keys
+  unsigned long long* cut;   // [rows] smallest kept key
+};
+
+__host__ __device__ inline FullScratch full_scratch(void* base, int n_draft, int vocab) {
+  const int rows = 2 * n_draft + 1;
+  const int nb = (vocab + kSChunk - 1) / kSChunk;
+  char* p = static_cast<char*>(base);
+  FullScratch f;
+  f.y = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(rows) * vocab * 4);
+  f.cmax = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(rows) * nb * 4);
+  f.ymax = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(rows) * 4);
+  f.z = reinterpret_cast<double*>(p);
+  p += align256(static_cast<size_t>(rows) * 8);
+  f.cut = reinterpret_cast<unsigned long long*>(p);
+  return f;
+}
+
+size_t full_scratch_bytes(int n_draft, int vocab) {
+  const size_t rows = 2 * static_cast<size_t>(n_draft) + 1;
+  const size_t nb = (static_cast<size_t>(vocab) + kSChunk - 1) / kSChunk;
+  return align256(rows * vocab * 4) + align256(rows * nb * 4) + align256(rows * 4) + align256(rows * 8) +
+         align256(rows * 8) + 256;
+}
+
+__device__ __forceinline__ unsigned long long mass_fx(float y, float ymax) {
+  return static_cast<unsigned long long>(static_cast<double>(__expf(y - ymax)) * kFMassScale);
+}
+
+__global__ __launch_bounds__(kVThreads) void k_full_transform(VerifyArgs a, FullScratch fs, int nb) {
+  __shared__ uint32_t bits[kSChunk / 32];
+  __shared__ float red[kVThreads / 64];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int n = a.n_draft;
+  const bool draft = row > n;
+  const int i = draft ? row - (n + 1) : row;            // window index of the row
+  const float* src = (draft ? a.draft : a.target) + static_cast<size_t>(i) * a.vocab;
+  const int lo = blockIdx.x * kSChunk;
+  const int hi = min(a.vocab, lo + kSChunk);
+  float v[kSPer];
+#pragma unroll
+  for (int u = 0; u < kSPer; ++u) {
+    const int k = lo + tid + u * kVThreads;
+    v[u] = k < hi ? src[k] : 0.f;
+  }
+  const bool pen = a.penalty != 1.0f;
+  if (pen) {
+    const int head = ring_head(a), count = ring_count(a);
+    for (int w = tid; w < kSChunk / 32; w += kVThreads) bits[w] = 0u;
+    __syncthreads();
+    const int total = count + i;
+    const int start = total > a.window ? total - a.window : 0;
+    for (int t = start + tid; t < total; t += kVThreads) {
+      const int tok = window_token(a.ring, head, count, a.window, a.drafts, t);
+      if (tok >= lo && tok < hi) atomicOr(&bits[(tok - lo) >> 5], 1u << ((tok - lo) & 31));
+    }
+    __syncthreads();
+  }
+  float* y = fs.y + static_cast<size_t>(row) * a.vocab;
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kSPer; ++u) {
+    const int t = tid + u * kVThreads;
+    const int k = lo + t;
+    if (k < hi) {
+      float x = v[u];
+      if (pen && ((bits[t >> 5] >> (t & 31)) & 1u)) x = penalise(x, a.penalty);
+      const float yy = x / a.temperature;
+      y[k] = yy;
+      m = fmaxf(m, yy);
+    }
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float r = red[0];
+    for (int w = 1; w < kVThreads / 64; ++w) r = fmaxf(r, red[w]);
+    fs.cmax[static_cast<size_t>(row) * nb + blockIdx.x] = r;
+  }
+}
+
+__device__ __forceinline__ unsigned long long shfl_down_u64(unsigned long long v, int o) {
+  const uint32_t lo = __shfl_down(static_cast<uint32_t>(v), o, 64);
+  const uint32_t hi = __shfl_down(static_cast<uint32_t>(v >> 32), o, 64);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Radix select over the row's keys at or above `floor`: the largest key T with
+// (sum over keys >= T of c(key)) >= need, c = 1 (MASS false) or the integer
+// mass (MASS true).  Eight-bit digits from the top; counts stop early once the
+// chosen bin is exactly used up.
+template <bool MASS>
+__device__ unsigned long long row_select(const float* y, int vocab, float ymax, unsigned long long floor,
+                                         double need, unsigned long long* hist, unsigned long long* sh) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  unsigned long long prefix = 0ull, mask = 0ull;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int b = tid; b < 256; b += kFThreads) hist[b] = 0ull;
+    __syncthreads();
+    for (int j = tid; j < vocab; j += kFThreads) {
+      const float yy = y[j];
+      const unsigned long long key = argmax_key(yy, static_cast<uint32_t>(j));
+      if (key >= floor && (key & mask) == prefix)
+        atomicAdd(&hist[(key >> shift) & 255], MASS ? mass_fx(yy, ymax) : 1ull);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins 4l..4l+3; inclusive suffix sums over lanes (bins from the top)
+      const unsigned long long b0 = hist[4 * lane], b1 = hist[4 * lane + 1], b2 = hist[4 * lane + 2],
+                               b3 = hist[4 * lane + 3];
+      unsigned long long suf = b0 + b1 + b2 + b3;
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long v = shfl_down_u64(suf, o);
+        if (lane + o < 64) suf += v;
+      }
+      const unsigned long long above = suf - (b0 + b1 + b2 + b3);
+      const bool last = lane == 0;   // lane 0 takes the remainder if rounding leaves need unmet
+      if ((static_cast<double>(above) < need && static_cast<double>(suf) >= need) ||
+          (last && static_cast<double>(suf) < need)) {
+        const unsigned long long bins[4] = {b0, b1, b2, b3};
+        unsigned long long acc = above;
+        int d = 4 * lane;
+        for (int q = 3; q >= 0; --q) {
+          d = 4 * lane + q;
+          if (static_cast<double>(acc + bins[q]) >= need) break;
+          if (q == 0) break;
+          acc += bins[q];
+        }
+        sh[0] = static_cast<unsigned long long>(d);
+        sh[1] = acc;                                   // content of the bins above the chosen one
+        sh[2] = bins[d - 4 * lane];                    // content of the chosen bin
+      }
+    }
+    __syncthreads();
+    const int d = static_cast<int>(sh[0]);
+    need -= static_cast<double>(sh[1]);
+    prefix |= static_cast<unsigned long long>(d) << shift;
+    mask |= 255ull << shift;
+    const bool done = !MASS && static_cast<double>(sh[2]) == need;
+    __syncthreads();
+    if (done) return prefix;
+  }
+  return prefix;
+}
+
+__device__ double block_sum_f64(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kFThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+__global__ __launch_bounds__(kFThreads) void k_full_select(VerifyArgs a, FullScratch fs, int nb) {
+  __shared__ unsigned long long hist[256];
+  __shared__ unsigned long long sh[4];
+  __shared__ double red[kFThreads / 64];
+  __shared__ float fred[kFThreads / 64];
+  __shared__ unsigned long long ured[kFThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const int V = a.vocab;
+  const float* y = fs.y + static_cast<size_t>(row) * V;
+  // y_max over the chunk maxima
+  float m = -INFINITY;
+  for (int c = tid; c < nb; c += kFThreads) m = fmaxf(m, fs.cmax[static_cast<size_t>(row) * nb + c]);
+  m = wave_max(m);
+  if (lane == 0) fred[wave] = m;
+  __syncthreads();
+  float ymax = fred[0];
+  for (int w = 1; w < kFThreads / 64; ++w) ymax = fmaxf(ymax, fred[w]);
+  __syncthreads();
+  // top-k cut
+  const int kk = (a.top_k > 0 && a.top_k < V) ? a.top_k : V;
+  const unsigned long long tk = kk < V ? row_select<false>(y, V, ymax, 0ull, static_cast<double>(kk), hist, sh) : 0ull;
+  // top-p cut within the top-k set
+  unsigned long long tp = 0ull;
+  if (a.top_p < 1.0f) {
+    unsigned long long zk = 0ull;
+    for (int j = tid; j < V; j += kFThreads) {
+      const float yy = y[j];
+      if (argmax_key(yy, static_cast<uint32_t>(j)) >= tk) zk += mass_fx(yy, ymax);
+    }
+    for (int o = 32; o > 0; o >>= 1) zk += __shfl_xor(zk, o, 64);
+    __syncthreads();
+    if (lane == 0) ured[wave] = zk;
+    __syncthreads();
+    unsigned long long tot = 0ull;
+    for (int w = 0; w < kFThreads / 64; ++w) tot += ured[w];
+    __syncthreads();
+    tp = row_select<true>(y, V, ymax, tk, static_cast<double>(a.top_p) * static_cast<double>(tot), hist, sh);
+  }
+  // min-p cut: every value >= the smallest one with y - y_max >= ln(min_p)
+  unsigned long long tm = 0ull;
+  if (a.min_p > 0.0f) {
+    float lo = INFINITY;
+    for (int j = tid; j < V; j += kFThreads) {
+      const float yy = y[j];
+      if ((yy - ymax) >= a.ln_min_p) lo = fminf(lo, yy);
+    }
+    for (int o = 32; o > 0; o >>= 1) lo = fminf(lo, __shfl_xor(lo, o, 64));
+    __syncthreads();
+    if (lane == 0) fred[wave] = lo;
+    __syncthreads();
+    float v = fred[0];
+    for (int w = 1; w < kFThreads / 64; ++w) v = fminf(v, fred[w]);
+    tm = static_cast<unsigned long long>(ord_key(v)) << 32;
+  }
+  const unsigned long long cut = max(tk, max(tp, tm));
+  // normaliser over the kept keys (fp64; per-thread then fixed-order block sum)
+  double z = 0.0;
+  for (int j = tid; j < V; j += kFThreads) {
+    const float yy = y[j];
+    if (argmax_key(yy, static_cast<uint32_t>(j)) >= cut) z += static_cast<double>(__expf(yy - ymax));
+  }
+  z = block_sum_f64(z, red);
+  if (tid == 0) {
+    fs.ymax[row] = ymax;
+    fs.z[row] = z;
+    fs.cut[row] = cut;
+  }
+}
+
+__device__ __forceinline__ double full_prob(const VerifyArgs& a, const FullScratch& fs, int row, int tok) {
+  if (tok < 0 || tok >= a.vocab) return 0.0;             // a draft id outside the vocabulary has no mass
+  const float yy = fs.y[static_cast<size_t>(row) * a.vocab + tok];
+  if (argmax_key(yy, static_cast<uint32_t>(tok)) < fs.cut[row]) return 0.0;
+  return static_cast<double>(__expf(yy - fs.ymax[row])) / fs.z[row];
+}
+
+// Inverse CDF over ids ascending with weight max(0, p_a - p_b) (rb < 0: p_a):
+// the first id whose running sum exceeds u * total, else the last positive-
+// weight id; -1 if the total is 0.  Every thread of the block calls it.
+// Thread i sums the ids of its contiguous range; the range offsets are
+// sequential sums (within each wave, then over the waves), so they never
+// decrease and exactly one thread's [offset, next offset) holds u * total.
+struct DrawShared {
+  double sum[kFThreads];     // per-thread weight sums, then exclusive offsets
+  double wbase[kFThreads / 64 + 1];
+  int res[2];                // claimed id, last positive-weight id
+};
+
+__device__ int full_draw(const VerifyArgs& a, const FullScratch& fs, int ra, int rb, float u, DrawShared& ds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kW = kFThreads / 64;
+  const int V = a.vocab;
+  const int per = (V + kFThreads - 1) / kFThreads;
+  const int j0 = min(V, tid * per), j1 = min(V, j0 + per);
+  auto weight = [&](int x) {
+    const double pa = full_prob(a, fs, ra, x);
+    const double pb = rb >= 0 ? full_prob(a, fs, rb, x) : 0.0;
+    return fmax(pa - pb, 0.0);
+  };
+  double s = 0.0;
+  int lastpos = -1;
+  for (int x = j0; x < j1; ++x) {
+    const double w = weight(x);
+    s += w;
+    if (w > 0.0) lastpos = x;
+  }
+  __syncthreads();                                     // ds is free (a previous draw may have used it)
+  ds.sum[tid] = s;
+  if (tid == 0) { ds.res[0] = -1; ds.res[1] = -1; }
+  __syncthreads();
+  if (lane == 0) {                                     // wave-local exclusive offsets, in order
+    double c = 0.0;
+    for (int l = 0; l < 64; ++l) {
+      const double v = ds.sum[wave * 64 + l];
+      ds.sum[wave * 64 + l] = c;
+      c += v;
+    }
+    ds.wbase[wave + 1] = c;                            // the wave's total, for now
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double c = 0.0;
+    for (int w = 0; w < kW; ++w) {
+      const double t = ds.wbase[w + 1];
+      ds.wbase[w] = c;
+      c += t;
+    }
+    ds.wbase[kW] = c;                                  // the total
+  }
+  __syncthreads();
+  const double total = ds.wbase[kW];
+  const double off = ds.wbase[wave] + ds.sum[tid];
+  const double next = lane < 63 ? ds.wbase[wave] + ds.sum[tid + 1] : ds.wbase[wave + 1];
+  if (lastpos >= 0) atomicMax(&ds.res[1], lastpos);
+  __syncthreads();
+  if (!(total > 0.0)) return -1;                       // the same in every thread
+  const double t = static_cast<double>(u) * total;
+  if (off <= t && t < next) {                          // at most one thread
+    const double tau = t - off;
+    double r = 0.0;
+    int pick = lastpos;
+    for (int x = j0; x < j1; ++x) {
+      r += weight(x);
+      if (tau < r) { pick = x; break; }
+    }
+    ds.res[0] = pick;
+  }
+  __syncthreads();
+  return ds.res[0] >= 0 ? ds.res[0] : ds.res[1];
+}
+
+__global__ __launch_bounds__(kFThreads) void k_full_decide(VerifyArgs a, FullScratch fs) {
+  __shared__ DrawShared ds;
+  __shared__ int s_k;
+  const int n = a.n_draft;
+  if (threadIdx.x == 0) {
+    int k = n;
+    for (int i = 0; i < n; ++i) {
+      const int d = a.drafts[i];
+      const double p = full_prob(a, fs, i, d);
+      const double q = full_prob(a, fs, n + 1 + i, d);
+      if (static_cast<double>(a.uniforms[i]) * q < p) continue;
+      k = i;
+      break;
+    }
+    s_k = k;
+  }
+  __syncthreads();
+  const int k = s_k;
+  int tok;
+  if (k < n) {
+    tok = full_draw(a, fs, k, n + 1 + k, a.uniforms[n], ds);
+    if (tok < 0) tok = full_draw(a, fs, k, -1, a.uniforms[n], ds);
+  } else {
+    tok = full_draw(a, fs, n, -1, a.uniforms[n], ds);
+  }
+  if (threadIdx.x != 0) return;
+  int h = ring_head(a), c = ring_count(a);
+  for (int r = 0; r <= k; ++r) {
+    const int t = r < k ? a.drafts[r] : tok;
+    a.out_tokens[r] = t;
+    a.ring[h] = t;
+    h = (h + 1) % a.window;
+    c = c + 1 < a.window ? c + 1 : a.window;
+  }
+  a.out_counts[0] = k;
+  a.out_counts[1] = k + 1;
+  a.ring_state[0] = h;
+  a.ring_state[1] = c;
+}
+
+// the per-chunk candidate path holds the top_k keys of every chunk
+static bool radix_path(int top_k, int vocab) {
   const int nb = (vocab + kSChunk - 1) / kSChunk;
   return top_k >= 1 && top_k <= kSMaxTopK && static_cast<long>(nb) * (top_k < kSChunk ? top_k : kSChunk) <= kSMaxCand;
 }
+
+bool verify_sampled_supported(int top_k, int vocab) { return top_k >= 0 && vocab >= 1; }
 
 hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
   if (!verify_sampled_supported(a.top_k, a.vocab)) return hipErrorNotSupported;
   const int rows = 2 * a.n_draft + 1;
   const int nb = (a.vocab + kSChunk - 1) / kSChunk;
+  if (!radix_path(a.top_k, a.vocab)) {
+    const FullScratch fs = full_scratch(a.scratch, a.n_draft, a.vocab);
+    (void)hipGetLastError();
+    int slot = -1;
+    time_mark(TIME_VERIFY, true, s, &slot);
+    hipLaunchKernelGGL(k_full_transform, dim3(nb, rows), dim3(kVThreads), 0, s, a, fs, nb);
+    time_mark(TIME_VERIFY, false, s, &slot);
+    hipLaunchKernelGGL(k_full_select, dim3(rows), dim3(kFThreads), 0, s, a, fs, nb);
+    hipLaunchKernelGGL(k_full_decide, dim3(1), dim3(kFThreads), 0, s, a, fs);
+    return hipGetLastError();
+  }
   const int kk = a.top_k < kSChunk ? a.top_k : kSChunk;
   const SampledScratch sc = sampled_scratch(a.scratch, a.n_draft, a.vocab);
   (void)hipGetLastError();

@@ -120,7 +120,7 @@ def test_verify_fails_closed():
     assert call(sampled, 2, 100, draft=None) == abi.MTP_E_INVALID_ARG    # sampled needs them
     assert call(sampled, 2, 100, u=None) == abi.MTP_E_INVALID_ARG
     assert call(greedy, 2, 100, draft=None, wsb=8) == abi.MTP_E_WORKSPACE
-    nucleus_all = abi.sampling(0.7, 1.0, 0, 0.9, 0.0, 64)
-    assert call(nucleus_all, 2, 100) == abi.MTP_E_UNSUPPORTED
+    negative_k = abi.sampling(0.7, 1.0, -1, 0.9, 0.0, 64)
+    assert call(negative_k, 2, 100) == abi.MTP_E_INVALID_ARG
     bad_win = abi.sampling(window=0)
     assert call(bad_win, 2, 100, draft=None) == abi.MTP_E_INVALID_ARG
