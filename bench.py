@@ -23,7 +23,8 @@ Other workloads (one JSON line each, same keys):
   flush256_qwen35_27b   the same flush at the 27B shape after 4096 slots (the
                         pages' 2.5 MiB flush cap; MFMA GEMM roofline)
   verify_sampled        sampled verification: N=4, V=152064, T 0.7, penalty 1.1
-                        over a 64-token ring, top-k 40, top-p 0.9, min-p 0.05
+                        over a 64-token ring, top-k 40 (--top-k; 0 = the whole
+                        vocabulary), top-p 0.9, min-p 0.05
   depth_ctx32768        rounds of the tiny bf16 head over a 32768-slot prefix at
                         depth --depth (1..8), lm_head bf16 or int8-g128 (--lm),
                         planted acceptance p_i = 0.8 * 0.85^i, policy A or B,
@@ -524,7 +525,9 @@ def run_verify(args):
 
     wl, N, V = I.WL_VERIFY, 4, 152064
     steps = args.steps
-    sp = abi.sampling(0.7, 1.1, 40, 0.9, 0.05, 64)
+    top_k = args.top_k
+    sp = abi.sampling(0.7, 1.1, top_k, 0.9, 0.05, 64)
+    full = not (1 <= top_k <= 215)     # past the per-chunk candidates: the whole-vocabulary path
     t0 = time.time()
     rows = np.stack([I.logits_rows(wl, 5, r, N + 1, V, 4.0, spikes=3, spike=12.0)[0] for r in range(VERIFY_POOL)])
     drows = np.stack([I.logits_rows(wl, 6, r, N, V, 4.0)[0] for r in range(VERIFY_POOL)])
@@ -572,32 +575,38 @@ def run_verify(args):
     counts = out_c[args.warmup:].cpu().numpy()
     if counts.min() < 0 or np.any(counts[:, 1] != counts[:, 0] + 1):
         raise RuntimeError("verification returned malformed counts")
-    chunk_bytes = (2 * N + 1) * V * 4 + 64 * 4
+    # the timed first pass reads every row (the whole-vocabulary path also writes
+    # the transformed rows back)
+    chunk_bytes = (2 * N + 1) * V * 4 * (2 if full else 1) + 64 * 4
     avg = ms / nl / 1e3
-    cpu = cpu_verify(rows, drows, ring0, st0, wl, N, args.cpu_seconds, total) if args.cpu_seconds > 0 else None
+    cpu = cpu_verify(rows, drows, ring0, st0, wl, N, args.cpu_seconds, total, top_k) if args.cpu_seconds > 0 \
+        else None
+    name = "verify_sampled_n4_v152064" if top_k == 40 else f"verify_sampled_n4_v152064_topk{top_k}"
     out = base_line(args, round(steps / el, 1), "verify rounds/s", el / steps * 1e3, "f32",
                     "synthetic (seeded N(0,4) fp32 target rows with 3 spikes of +12, N(0,4) draft rows, "
                     "64 resident rounds cycled, fresh uniforms per round)",
-                    {"workload": "verify_sampled_n4_v152064", "n_draft": N, "vocab": V, "temperature": 0.7,
-                     "repeat_penalty": 1.1, "window": 64, "top_k": 40, "top_p": 0.9, "min_p": 0.05})
+                    {"workload": name, "n_draft": N, "vocab": V, "temperature": 0.7,
+                     "repeat_penalty": 1.1, "window": 64, "top_k": top_k, "top_p": 0.9, "min_p": 0.05})
     out.update({
         "us_per_round": round(el / steps * 1e6, 2),
         "round_gbs": round(chunk_bytes / (el / steps) / 1e9, 1),
         "mean_accepted": round(float(counts[:, 0].mean()), 4),
         "roofline": roofline("hbm", chunk_bytes / avg / 1e9, HBM_PEAK_GBS, "GB/s", None,
-                             kernel="per-chunk top-k pass over the 9 rows (penalty, temperature, radix select)",
+                             kernel=("whole-vocabulary transform pass over the 9 rows (penalty, temperature, "
+                                     "row maxima; transformed rows written back)" if full else
+                                     "per-chunk top-k pass over the 9 rows (penalty, temperature, radix select)"),
                              bytes_per_launch=chunk_bytes, avg_us=round(avg * 1e6, 2), launches=nl),
         "cpu_baseline": cpu,
     })
     return out
 
 
-def cpu_verify(rows, drows, ring0, st0, wl, N, seconds, max_rounds):
+def cpu_verify(rows, drows, ring0, st0, wl, N, seconds, max_rounds, top_k=40):
     import numpy as np
 
     from mtp_draft_head_step_amd import inputs as I
     from oracle import verify as OV
-    sp = OV.Sampling(temperature=0.7, repeat_penalty=1.1, top_k=40, top_p=0.9, min_p=0.05, window=64)
+    sp = OV.Sampling(temperature=0.7, repeat_penalty=1.1, top_k=top_k, top_p=0.9, min_p=0.05, window=64)
     state = {"ring": np.array(ring0), "st": np.array(st0)}
 
     def unit(r):
@@ -865,6 +874,8 @@ def main():
     ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"], help="depth_ctx32768: lm_head storage")
     ap.add_argument("--policy", default="B", choices=["A", "B"], help="depth_ctx32768: KV policy")
     ap.add_argument("--sessions", type=int, default=32, help="depth_ctx32768: sessions rotated (1 = warm)")
+    ap.add_argument("--top-k", type=int, default=40,
+                    help="verify_sampled: top_k (0 = the whole vocabulary, served by the whole-vocabulary path)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle sample for cpu_baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
