@@ -363,8 +363,15 @@ bool gemm_stream_supported(int M, int K, const int* m, int nmat, bool swiglu) {
   return true;
 }
 
+// tiles (workgroup column blocks) of a streaming product
+static int stream_tiles(int M, bool swiglu) { return M / (swiglu ? kSN / 2 : kSN); }
+
+// More tiles than workgroups in one round: stream-K (each workgroup an equal
+// share of the (tile, step) units) instead of a second, mostly idle round.
+static bool stream_k(int M, bool swiglu) { return stream_tiles(M, swiglu) > kSWgs; }
+
 int gemm_split(int M, int K, bool swiglu) {
-  if (swiglu) return 1;
+  if (swiglu || stream_k(M, swiglu)) return 1;
   const int tiles = M / kSN;
   int s = kSWgs / (tiles > 0 ? tiles : 1);
   const int cap = (K / kSK) / kSMinSteps;
@@ -374,8 +381,26 @@ int gemm_split(int M, int K, bool swiglu) {
 
 size_t gemm_part_floats(int rows, int M, int K, const int* m, int nmat, bool swiglu) {
   if (!gemm_stream_supported(M, K, m, nmat, swiglu)) return 0;
+  if (stream_k(M, swiglu)) return 2 * static_cast<size_t>(stream_tiles(M, swiglu)) * rows * kSN;   // head + tail
   const int s = gemm_split(M, K, swiglu);
   return s > 1 ? static_cast<size_t>(s) * rows * M : 0;
+}
+
+// residual add, store, optional act-dtype copy of four consecutive columns
+__device__ __forceinline__ void gemm_put4(const GemmArgs& a, long long row, int col, float4 v) {
+  if (a.out_mode == OUT_RESID) {
+    const float4 q = *reinterpret_cast<const float4*>(a.res + row * a.ldres + col);
+    v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+  }
+  *reinterpret_cast<float4*>(a.y + row * a.ldy + col) = v;
+  if (a.y2) {
+    if (a.y2_bf16)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y2) + row * a.ldy2 + col) =
+          make_uint2(f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                     f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16));
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(a.y2) + row * a.ldy2 + col) = v;
+  }
 }
 
 __device__ __forceinline__ void gemm_put(const GemmArgs& a, int r, int col, float v) {
@@ -394,15 +419,16 @@ __device__ __forceinline__ void gemm_put(const GemmArgs& a, int r, int col, floa
 // a row-major fp32 tile (column = wave * 32 + lane % 32).
 template <bool SWIGLU, int NT>
 __device__ __forceinline__ void gemm_stream_products(const GemmArgs& a, uint16_t* As, int kStage, int kTLd,
-                                                     int r0, int sb, int nst, int nst3, int lane, int wave) {
+                                                     int r0, int tile, int sb, int nst, int nst3, int lane,
+                                                     int wave) {
   // ---- product waves: this wave's 32 weight rows and their output columns
   const uint16_t* W;
   int wrow;
   if (SWIGLU) {
     W = wave < 2 ? a.w[0] : a.w[1];
-    wrow = blockIdx.x * (kSN / 2) + (wave & 1) * 32;
+    wrow = tile * (kSN / 2) + (wave & 1) * 32;
   } else {
-    int cl = blockIdx.x * kSN + wave * 32;
+    int cl = tile * kSN + wave * 32;
     W = a.w[0];
     if (cl >= a.m[0]) {
       cl -= a.m[0];
@@ -493,107 +519,161 @@ __global__ __launch_bounds__(512) void k_gemm_stream(GemmArgs a) {
   const int rows = min(n - r0, kRows);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // this workgroup's reduction steps
+  // this workgroup's work: one tile over one range of steps (split K), or with
+  // stream-K a contiguous range of (tile, step) units that may end one tile
+  // and begin the next
   const int steps = a.K / kSK;
   const int sp = blockIdx.y, nsp = gridDim.y;
-  const int sb = static_cast<int>(static_cast<long long>(steps) * sp / nsp);
-  const int nst = static_cast<int>(static_cast<long long>(steps) * (sp + 1) / nsp) - sb;
-  const int nst3 = (nst + 2) / 3 * 3;               // steps run (the extra ones add zeros)
-
-  if (wave >= 4) {
-    // ---- staging waves: row t of every step into LDS stage (step % 3); rows
-    // past n_max clamp (computed, never stored), rows past NT * 32 unread
-    const int t = tid - 256;
-    const int row = min(r0 + t, a.n_max - 1);
-    const uint4* ap = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.a) +
-                                                     static_cast<long long>(row) * a.lda +
-                                                     static_cast<long long>(sb) * kSK);
-    uint4 p0[8], p1[8], p2[8];
-    auto load = [&](uint4 (&p)[8], int st) {
-      st = min(st, nst - 1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = ap[static_cast<long long>(st) * (kSK / 8) + i];
-    };
-    auto store = [&](const uint4 (&p)[8], int stage, int st) {
-      const uint32_t keep = st < nst ? 0xFFFFFFFFu : 0u;
-      uint4* dst = reinterpret_cast<uint4*>(As + stage * kStage + t * kSLd);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dst[i] = make_uint4(p[i].x & keep, p[i].y & keep, p[i].z & keep, p[i].w & keep);
-    };
-    load(p0, 0);
-    load(p1, 1);
-    load(p2, 2);
-    store(p0, 0, 0);
-    __syncthreads();
-    // during step s: store step s + 1 (issued two steps back), then issue
-    // step s + 3 into the slot step s used
-    // (the scheduling fences keep each step's register work on its side of
-    // the barrier, so a wait for a slot never moves ahead of its step)
-    for (int s = 0; s < nst3; s += 3) {
-      store(p1, 1, s + 1);
-      load(p0, s + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      store(p2, 2, s + 2);
-      load(p1, s + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      store(p0, 0, s + 3);
-      load(p2, s + 5);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  int u0, u1;
+  if (a.sk_units) {
+    const long long tot = static_cast<long long>(a.M / (SWIGLU ? kSN / 2 : kSN)) * steps;
+    u0 = blockIdx.x * a.sk_units;
+    u1 = static_cast<int>(min(tot, static_cast<long long>(u0) + a.sk_units));
   } else {
-    gemm_stream_products<SWIGLU, NT>(a, As, kStage, kTLd, r0, sb, nst, nst3, lane, wave);
+    u0 = blockIdx.x * steps + static_cast<int>(static_cast<long long>(steps) * sp / nsp);
+    u1 = blockIdx.x * steps + static_cast<int>(static_cast<long long>(steps) * (sp + 1) / nsp);
   }
-  __syncthreads();   // the products' sums are in LDS (row-major, kTLd floats a row)
+  for (int u = u0; u < u1;) {
+    const int tile = u / steps;
+    const int sb = u % steps;
+    const int nst = min(steps - sb, u1 - u);
+    const int nst3 = (nst + 2) / 3 * 3;             // steps run (the extra ones add zeros)
+    // a stream-K piece of a tile: its sums go to the tile's head or tail slot
+    const bool piece = a.sk_units && nst < steps;
+    u += nst;
 
-  // ---- epilogue: every thread, 16-byte pieces of whole rows
-  const float* T = reinterpret_cast<const float*>(As);
-  if (SWIGLU) {
-    // columns [0, 64) hold the gate sums, [64, 128) the up sums of the same outputs
-    for (int e = tid; e < rows * 16; e += 512) {
-      const int r = e >> 4, c = (e & 15) * 4;
-      const float4 g = *reinterpret_cast<const float4*>(T + r * kTLd + c);
-      const float4 u = *reinterpret_cast<const float4*>(T + r * kTLd + 64 + c);
-      const float4 v = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
-      const long long o = static_cast<long long>(r0 + r) * a.ldy + blockIdx.x * (kSN / 2) + c;
-      if (a.y_bf16) {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(static_cast<void*>(a.y)) + o) =
-            make_uint2(f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
-                       f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16));
-      } else {
-        *reinterpret_cast<float4*>(a.y + o) = v;
+    if (wave >= 4) {
+      // ---- staging waves: row t of every step into LDS stage (step % 3); rows
+      // past n_max clamp (computed, never stored), rows past NT * 32 unread
+      const int t = tid - 256;
+      const int row = min(r0 + t, a.n_max - 1);
+      const uint4* ap = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.a) +
+                                                       static_cast<long long>(row) * a.lda +
+                                                       static_cast<long long>(sb) * kSK);
+      uint4 p0[8], p1[8], p2[8];
+      auto load = [&](uint4 (&p)[8], int st) {
+        st = min(st, nst - 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = ap[static_cast<long long>(st) * (kSK / 8) + i];
+      };
+      auto store = [&](const uint4 (&p)[8], int stage, int st) {
+        const uint32_t keep = st < nst ? 0xFFFFFFFFu : 0u;
+        uint4* dst = reinterpret_cast<uint4*>(As + stage * kStage + t * kSLd);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          dst[i] = make_uint4(p[i].x & keep, p[i].y & keep, p[i].z & keep, p[i].w & keep);
+      };
+      load(p0, 0);
+      load(p1, 1);
+      load(p2, 2);
+      store(p0, 0, 0);
+      __syncthreads();
+      // during step s: store step s + 1 (issued two steps back), then issue
+      // step s + 3 into the slot step s used
+      // (the scheduling fences keep each step's register work on its side of
+      // the barrier, so a wait for a slot never moves ahead of its step)
+      for (int s = 0; s < nst3; s += 3) {
+        store(p1, 1, s + 1);
+        load(p0, s + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        store(p2, 2, s + 2);
+        load(p1, s + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        store(p0, 0, s + 3);
+        load(p2, s + 5);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      gemm_stream_products<SWIGLU, NT>(a, As, kStage, kTLd, r0, tile, sb, nst, nst3, lane, wave);
+    }
+    __syncthreads();   // the products' sums are in LDS (row-major, kTLd floats a row)
+
+    // ---- epilogue: every thread, 16-byte pieces of whole rows
+    const float* T = reinterpret_cast<const float*>(As);
+    if (piece) {
+      // all 128 columns of the tile (SwiGLU: gate, then up) into its head
+      // (pieces starting at step 0) or tail slot; k_gemm_fixup adds them
+      float* slot = a.part + (static_cast<long long>(tile) * 2 + (sb == 0 ? 0 : 1)) * a.n_max * kSN;
+      for (int e = tid; e < rows * 32; e += 512) {
+        const int r = e >> 5, c = (e & 31) * 4;
+        *reinterpret_cast<float4*>(slot + static_cast<long long>(r0 + r) * kSN + c) =
+            *reinterpret_cast<const float4*>(T + r * kTLd + c);
+      }
+    } else if (SWIGLU) {
+      // columns [0, 64) hold the gate sums, [64, 128) the up sums of the same outputs
+      for (int e = tid; e < rows * 16; e += 512) {
+        const int r = e >> 4, c = (e & 15) * 4;
+        const float4 g = *reinterpret_cast<const float4*>(T + r * kTLd + c);
+        const float4 uu = *reinterpret_cast<const float4*>(T + r * kTLd + 64 + c);
+        const float4 v = make_float4(silu(g.x) * uu.x, silu(g.y) * uu.y, silu(g.z) * uu.z, silu(g.w) * uu.w);
+        const long long o = static_cast<long long>(r0 + r) * a.ldy + tile * (kSN / 2) + c;
+        if (a.y_bf16) {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(static_cast<void*>(a.y)) + o) =
+              make_uint2(f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                         f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16));
+        } else {
+          *reinterpret_cast<float4*>(a.y + o) = v;
+        }
+      }
+    } else {
+      for (int e = tid; e < rows * 32; e += 512) {
+        const int r = e >> 5, c = (e & 31) * 4;
+        float4 v = *reinterpret_cast<const float4*>(T + r * kTLd + c);
+        const long long row = r0 + r;
+        const int col = tile * kSN + c;
+        if (nsp > 1) {
+          *reinterpret_cast<float4*>(a.part + (static_cast<long long>(sp) * a.n_max + row) * a.M + col) = v;
+          continue;
+        }
+        gemm_put4(a, row, col, v);
       }
     }
-    return;
+    __syncthreads();   // LDS is reused by the next piece
   }
-  for (int e = tid; e < rows * 32; e += 512) {
-    const int r = e >> 5, c = (e & 31) * 4;
-    float4 v = *reinterpret_cast<const float4*>(T + r * kTLd + c);
-    const long long row = r0 + r;
-    const int col = blockIdx.x * kSN + c;
-    if (nsp > 1) {
-      *reinterpret_cast<float4*>(a.part + (static_cast<long long>(sp) * a.n_max + row) * a.M + col) = v;
-      continue;
+}
+
+// Stream-K tiles cut between two workgroups: head + tail (in that order), then
+// the epilogue; a thread per four output columns of one row.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs a, int steps) {
+  if (a.kv_state && a.kv_state[3] != 0) return;
+  int n = a.n_max;
+  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  constexpr int kOut = SWIGLU ? kSN / 2 : kSN;        // output columns per tile
+  const int tiles = a.M / kOut;
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = tiles * (kOut / 4);
+  const int r = static_cast<int>(idx / per_row);
+  const int q = static_cast<int>(idx % per_row);
+  const int tile = q / (kOut / 4), c = (q % (kOut / 4)) * 4;
+  if (r >= n) return;
+  const long long first = static_cast<long long>(tile) * steps, last = first + steps - 1;
+  if (first / a.sk_units == last / a.sk_units) return;   // one workgroup finished it
+  const float* h = a.part + (static_cast<long long>(tile) * 2 * a.n_max + r) * kSN;
+  const float* t = h + static_cast<long long>(a.n_max) * kSN;
+  auto sum4 = [&](int col) {
+    const float4 x = *reinterpret_cast<const float4*>(h + col), y = *reinterpret_cast<const float4*>(t + col);
+    return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+  };
+  if (SWIGLU) {
+    const float4 g = sum4(c), u = sum4(64 + c);
+    const float4 v = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+    const long long o = static_cast<long long>(r) * a.ldy + tile * kOut + c;
+    if (a.y_bf16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(static_cast<void*>(a.y)) + o) =
+          make_uint2(f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                     f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16));
+    } else {
+      *reinterpret_cast<float4*>(a.y + o) = v;
     }
-    if (a.out_mode == OUT_RESID) {
-      const float4 q = *reinterpret_cast<const float4*>(a.res + row * a.ldres + col);
-      v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
-    }
-    *reinterpret_cast<float4*>(a.y + row * a.ldy + col) = v;
-    if (a.y2) {
-      if (a.y2_bf16)
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y2) + row * a.ldy2 + col) =
-            make_uint2(f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
-                       f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16));
-      else
-        *reinterpret_cast<float4*>(static_cast<float*>(a.y2) + row * a.ldy2 + col) = v;
-    }
+  } else {
+    gemm_put4(a, r, tile * kOut + c, sum4(c));
   }
 }
 
@@ -640,11 +720,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
                       (!a.y2 || (a.ldy2 % 4 == 0 && al(a.y2, 16)));
   if (gemm_stream_supported(a.M, a.K, a.m, swiglu ? 2 : 3, swiglu) && !a.a_f32 && pieces) {
     const int nsp = gemm_split(a.M, a.K, swiglu);
-    if (nsp > 1 && !a.part) return hipErrorInvalidValue;
-    const dim3 grid(a.M / (swiglu ? kSN / 2 : kSN), nsp, (a.n_max + kSM - 1) / kSM);
+    const bool sk = stream_k(a.M, swiglu);
+    if ((nsp > 1 || sk) && !a.part) return hipErrorInvalidValue;
+    GemmArgs b = a;
+    const int tiles = stream_tiles(a.M, swiglu), steps = a.K / kSK;
+    const long long units = static_cast<long long>(tiles) * steps;
+    b.sk_units = sk ? static_cast<int>((units + kSWgs - 1) / kSWgs) : 0;
+    const int gx = sk ? static_cast<int>((units + b.sk_units - 1) / b.sk_units) : tiles;
+    const dim3 grid(gx, nsp, (a.n_max + kSM - 1) / kSM);
     // 32-row blocks computed: enough for every row a launch can see
     const int nt = a.n_max > 128 ? 8 : (a.n_max > 64 ? 4 : 2);
-#define MTP_STREAM(SW, NT) hipLaunchKernelGGL((k_gemm_stream<SW, NT>), grid, dim3(512), 0, s, a)
+#define MTP_STREAM(SW, NT) hipLaunchKernelGGL((k_gemm_stream<SW, NT>), grid, dim3(512), 0, s, b)
     if (swiglu) {
       if (nt == 8) MTP_STREAM(true, 8); else if (nt == 4) MTP_STREAM(true, 4); else MTP_STREAM(true, 2);
     } else {
@@ -656,6 +742,14 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       if (e != hipSuccess) return e;
       const long long threads = static_cast<long long>(a.n_max) * (a.M / 4);
       hipLaunchKernelGGL(k_gemm_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a, nsp);
+    }
+    if (sk) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const long long threads = static_cast<long long>(a.n_max) * (a.M / 4);
+      const dim3 fg(static_cast<unsigned>((threads + 255) / 256));
+      if (swiglu) hipLaunchKernelGGL(k_gemm_fixup<true>, fg, dim3(256), 0, s, b, steps);
+      else hipLaunchKernelGGL(k_gemm_fixup<false>, fg, dim3(256), 0, s, b, steps);
     }
     return hipGetLastError();
   }

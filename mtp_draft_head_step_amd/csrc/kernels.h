@@ -118,6 +118,7 @@ struct GemmArgs {
   int ldy2;
   float* part;               // split partial sums [split, n_max, M] (gemm_part_floats)
   int y_bf16;                // OUT_SWIGLU: y holds bf16 (ldy in bf16 elements)
+  int sk_units;              // set by launch_gemm: stream-K steps per workgroup (0 = off)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 bool gemm_supported(int M, int K, const int* m, int nmat);

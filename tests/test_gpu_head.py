@@ -223,6 +223,11 @@ MID_SHAPES = {
     "h2048": I.HeadShape(hidden=2048, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=2048,
                          vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
                                                  lm_head_dtype=I.BF16),
+    # 260 gate/up tiles over 256 workgroups: stream-K, nearly every tile cut
+    # between two workgroups (head + tail pieces and the fixup)
+    "i16640": I.HeadShape(hidden=512, n_q_heads=4, n_kv_heads=1, head_dim=128, intermediate=16640,
+                          vocab=2048).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
+                                                  lm_head_dtype=I.BF16),
 }
 
 
