@@ -334,7 +334,7 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
                     {"workload": workload, "hidden": H, "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv",
                      "head_dim": shape.head_dim, "intermediate": shape.intermediate, "vocab": V,
                      "draft_kv_context": ctx, "drafts_per_round": N, "block_size": N + 1,
-                     "temperature": 0.0, "batch": 1, "policy": "A"})
+                     "temperature": 0.0, "batch": 1, "policy": "A", "lm_head": shape.lm_head_dtype})
     out.update({
         "rounds_per_s": round(rounds_s, 2),
         "round_gbs": round(round_bytes / (elapsed / args.steps) / 1e9, 1),
@@ -484,6 +484,99 @@ def run_flush(args, big=False):
         "projection_launches_per_flush": proj_n // timed_side,
         "roofline": line,
         "cpu_baseline": cpu,
+    })
+    return out
+
+
+def run_flush_scaling(args):
+    """Flush cost against its size at the 27B shape: n = 1..256 pending pairs
+    after 4096 slots, in LAST mode (the in-round use: every row's K/V, the last
+    row's g, logits and argmax) and in KV_ONLY mode.  A flush of one pair is one
+    draft step; the curve says how much less than n steps' price n positions
+    cost.  The line's value and roofline are the 256-pair LAST flush's."""
+    import torch
+
+    from mtp_draft_head_step_amd import abi
+    from mtp_draft_head_step_amd import inputs as I
+
+    shape, wl, prefix = I.QWEN35_27B, I.WL_QWEN, 4096
+    sizes = sorted({int(x) for x in str(args.rows).split(",")})
+    if not sizes or sizes[0] < 1 or sizes[-1] > 256:
+        raise SystemExit("--rows: pair counts in 1..256")
+    nmax = sizes[-1]
+    cap = prefix + nmax
+    storage = I.head_weights(shape, wl)
+    head = abi.Head(shape, storage)
+    del storage
+    kp, vp = I.prefix_kv(shape, wl, prefix, cap)
+    kv = abi.DraftKV(shape, cap, kp, vp, prefix)
+    toks = abi.to_device(I.tokens_uniform(wl, 0, nmax, shape.vocab))
+    hids = abi.to_device(I.target_hiddens(shape, wl, 0, nmax))
+    ws = abi.Workspace(abi.mtp_workspace_bytes(head.cfg, nmax, cap))
+    hout = torch.zeros((1, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    steps = max(args.steps, 3)
+
+    def timed(n, mode, kind=None):
+        def flush():
+            abi.mtp_flush_pairs(head, kv, toks, hids, n, None, mode, 1, hout, logits, amax, ws, stream)
+            abi.kv_rollback(kv, prefix, None, 0, stream)
+        for _ in range(args.warmup):
+            flush()
+        torch.cuda.synchronize()
+        if kind is not None:
+            abi.mtp_timing_begin(kind, 64 * steps + 4)
+        t = time.perf_counter()
+        for i in range(steps):
+            if kind is not None:
+                abi.mtp_timing_pause(i % TIME_EVERY != 0)
+            flush()
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t) / steps
+        k = abi.mtp_timing_end() if kind is not None else None
+        if int(kv.state[3].item()) != 0:
+            raise RuntimeError("device error word set")
+        return el, k
+
+    curve = {}
+    for n in sizes:
+        t_last, _ = timed(n, abi.LAST)
+        t_kv, _ = timed(n, abi.KV_ONLY)
+        curve[n] = {"last_us": round(t_last * 1e6, 2), "kv_only_us": round(t_kv * 1e6, 2)}
+        log(f"n={n}: LAST {t_last * 1e6:.1f} us, KV_ONLY {t_kv * 1e6:.1f} us")
+    base = curve[sizes[0]]["last_us"] / sizes[0]
+    for n in sizes:
+        c = curve[n]
+        c["cost_vs_n_steps"] = round(c["last_us"] / (n * base), 4)
+        # LAST: every row's fc and q/k/v; the last row's attention (prefix + n keys), o, MLP and unembedding
+        last_flops = 4 * shape.head_dim * shape.n_q_heads * (prefix + n) + flush_projection_flops(shape, n, 1)
+        c["tflops_last"] = round(last_flops / (c["last_us"] * 1e-6) / 1e12, 2)
+    # the largest flush's products, timed with events around their launches
+    _, (proj_ms, proj_n) = timed(nmax, abi.LAST, abi.TIME_PROJECTION)
+    timed_n = (steps + TIME_EVERY - 1) // TIME_EVERY
+    proj_s = proj_ms / timed_n / 1e3
+    gemm_flops = flush_projection_flops(shape, nmax, 1) - 2 * shape.vocab * shape.hidden
+    t_big = curve[nmax]["last_us"] * 1e-6
+    out = base_line(args, round(nmax / t_big, 1), "flushed pairs/s", t_big * 1e3, "bf16",
+                    "synthetic (seeded N(0,0.02) weights of the Qwen3.5-27B-shaped head in bf16; uniform tokens, "
+                    "N(0,1) bf16 hiddens; N(0,1) bf16 prefix K/V)",
+                    {"workload": "flush_scaling_qwen35_27b_prefix4096", "hidden": shape.hidden,
+                     "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv", "head_dim": shape.head_dim,
+                     "intermediate": shape.intermediate, "vocab": shape.vocab, "prefix": prefix,
+                     "pairs": sizes, "mode": "LAST (every row's K/V; last row's g, logits, argmax) and KV_ONLY"})
+    out.update({
+        "cost_curve": {str(n): curve[n] for n in sizes},
+        "cost_curve_note": "cost_vs_n_steps = flush(n) / (n x flush(%d) / %d): below 1 means n positions cost "
+                           "less than n separate steps" % (sizes[0], sizes[0]),
+        "roofline": roofline("mfma", gemm_flops / proj_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None,
+                             kernel=f"the {nmax}-pair LAST flush's projections: fc and q/k/v over every row "
+                                    "(MFMA products past 16 rows, GEMV passes below), o, gate/up and down for "
+                                    "the last row (GEMV)",
+                             flops_per_launch=round(gemm_flops / max(1, proj_n // timed_n)),
+                             avg_us=round(proj_s * 1e6 / max(1, proj_n // timed_n), 2), launches=proj_n),
+        "cpu_baseline": None,
     })
     return out
 
@@ -869,9 +962,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="qwen35_27b_round",
                     choices=["qwen35_27b_round", "tiny_round", "flush256_prefix8192", "flush256_qwen35_27b",
-                             "verify_sampled", "depth_ctx32768"])
+                             "verify_sampled", "depth_ctx32768", "flush_scaling_qwen35_27b"])
     ap.add_argument("--depth", default="4", help="depth_ctx32768: drafts per round (comma list: one line each)")
-    ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"], help="depth_ctx32768: lm_head storage")
+    ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"],
+                    help="qwen35_27b_round, depth_ctx32768: lm_head storage (int8 per (row, 128-column group) "
+                         "with fp16 scales, or bf16)")
+    ap.add_argument("--rows", default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
+                    help="flush_scaling_qwen35_27b: pair counts of the flushes timed (comma list, 1..256)")
     ap.add_argument("--policy", default="B", choices=["A", "B"], help="depth_ctx32768: KV policy")
     ap.add_argument("--sessions", type=int, default=32, help="depth_ctx32768: sessions rotated (1 = warm)")
     ap.add_argument("--top-k", type=int, default=40,
@@ -889,7 +986,7 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     default_steps = {"qwen35_27b_round": 40, "tiny_round": 64, "flush256_prefix8192": 50, "flush256_qwen35_27b": 16,
-                     "verify_sampled": 10000, "depth_ctx32768": 256}
+                     "verify_sampled": 10000, "depth_ctx32768": 256, "flush_scaling_qwen35_27b": 16}
     if args.steps is None:
         args.steps = default_steps[args.workload]
 
@@ -897,9 +994,13 @@ def main():
 
     from mtp_draft_head_step_amd import inputs as I
     if args.workload == "qwen35_27b_round":
-        lines = [run_greedy_rounds(args, I.QWEN35_27B, I.WL_QWEN, 4096, 2, "qwen35_27b_mtp_head_round",
-                                   "synthetic (seeded N(0,0.02) weights of the Qwen3.5-27B MTP head shape; "
-                                   "N(0,3) target logits, N(0,1) target hiddens)")]
+        i8 = args.lm == "i8g128"
+        shape = I.QWEN35_27B.with_dtypes(lm_head_dtype=I.I8G128) if i8 else I.QWEN35_27B
+        lines = [run_greedy_rounds(args, shape, I.WL_QWEN, 4096, 2,
+                                   "qwen35_27b_mtp_head_round" + ("_lm_i8g128" if i8 else ""),
+                                   "synthetic (seeded N(0,0.02) weights of the Qwen3.5-27B MTP head shape"
+                                   + ("; lm_head quantised int8 per (row, 128-column group), fp16 scales" if i8
+                                      else "") + "; N(0,3) target logits, N(0,1) target hiddens)")]
     elif args.workload == "tiny_round":
         lines = [run_greedy_rounds(args, I.TINY_F32, I.WL_TINY, 128, 2, "tiny_f32_head_round",
                                    "synthetic (seeded N(0,0.02) tiny-head weights in fp32; N(0,3) target "
@@ -910,6 +1011,8 @@ def main():
         lines = [run_flush(args, big=True)]
     elif args.workload == "verify_sampled":
         lines = [run_verify(args)]
+    elif args.workload == "flush_scaling_qwen35_27b":
+        lines = [run_flush_scaling(args)]
     else:
         lines = [run_depth(args, int(d), args.lm) for d in str(args.depth).split(",")]
     for line in lines:

@@ -105,8 +105,20 @@ struct Layout {
   int nchunk;
 };
 
-// Flushes of more rows than one GEMV pass covers go through the MFMA tiles.
+// Flushes of more rows than gemv_max_rows go through the MFMA tiles.  Small
+// heads keep the GEMV passes up to 16 rows (one launch per projection; every
+// kernel there is latency-bound).  Large heads switch past 4 rows: the 8- and
+// 16-row GEMV passes hold one accumulator per (row, activation row) and run at
+// one or two waves per SIMD, and at the 27B shape (H 5120) a 6..16-row flush
+// took 0.63..1.02 ms against 0.51 ms for 24 rows on the weight-streaming MFMA
+// product.
 constexpr int kGemvMaxRows = 16;
+constexpr int kGemvMaxRowsLarge = 4;
+constexpr int kLargeHidden = 2048;
+
+int gemv_max_rows(const mtp_head_config& c) {
+  return c.hidden >= kLargeHidden ? kGemvMaxRowsLarge : kGemvMaxRows;
+}
 
 // upper bound on the unembedding GEMV's workgroup count (one argmax key each)
 size_t amax_parts(const mtp_head_config& c) { return static_cast<size_t>(c.vocab) / 4 + 2048; }
@@ -127,9 +139,10 @@ Layout layout(const mtp_head_config& c, int rows, int capacity) {
   L.m = take(rows * I * 4);
   L.g = take(rows * H * 4);
   L.amax = take(amax_parts(c) * 8);
-  L.xa = rows > kGemvMaxRows ? take(rows * 2 * H * 2) : off;   // bf16 normalised rows (MFMA path)
+  const bool mfma_rows = rows > gemv_max_rows(c);
+  L.xa = mfma_rows ? take(rows * 2 * H * 2) : off;             // bf16 normalised rows (MFMA path)
   size_t part = 0;                                             // split partial sums (MFMA path)
-  if (rows > kGemvMaxRows) {
+  if (mfma_rows) {
     const int mq[3] = {static_cast<int>(hq * D), static_cast<int>(hkv * D), static_cast<int>(hkv * D)};
     const int mh[1] = {static_cast<int>(H)};
     const int mi[2] = {static_cast<int>(I), static_cast<int>(I)};
@@ -265,7 +278,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   uint16_t* xa = reinterpret_cast<uint16_t*>(wsp(ws, L.xa));
   float* gpart = reinterpret_cast<float*>(wsp(ws, L.gpart));
   // many rows with bf16 weights: normalised rows + MFMA tiles instead of GEMV passes
-  const bool mfma = h->wt == W_BF16 && n_max > kGemvMaxRows;
+  const bool mfma = h->wt == W_BF16 && n_max > gemv_max_rows(c);
   if (mfma) {
     const int mq[3] = {hq * D, hkv * D, hkv * D};
     const int mh[1] = {H};

@@ -543,25 +543,32 @@ __global__ __launch_bounds__(512) void k_gemm_stream(GemmArgs a) {
     u += nst;
 
     if (wave >= 4) {
-      // ---- staging waves: row t of every step into LDS stage (step % 3); rows
-      // past n_max clamp (computed, never stored), rows past NT * 32 unread
+      // ---- staging waves: the step's slice of the NT * 32 activation rows into
+      // LDS stage (step % 3).  Piece i of thread t is 16 bytes of row i * 32 +
+      // t / 8 at column (t % 8) * 8, so eight neighbouring lanes read one row's
+      // whole 128-byte slice (8 cache lines an instruction, not 64).  Rows past
+      // n_max clamp (computed, never stored).
       const int t = tid - 256;
-      const int row = min(r0 + t, a.n_max - 1);
-      const uint4* ap = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.a) +
-                                                       static_cast<long long>(row) * a.lda +
-                                                       static_cast<long long>(sb) * kSK);
-      uint4 p0[8], p1[8], p2[8];
-      auto load = [&](uint4 (&p)[8], int st) {
+      const uint4* ap[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const int row = min(r0 + i * 32 + (t >> 3), a.n_max - 1);
+        ap[i] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.a) + static_cast<long long>(row) * a.lda +
+                                               static_cast<long long>(sb) * kSK + (t & 7) * 8);
+      }
+      uint4 p0[NT], p1[NT], p2[NT];
+      auto load = [&](uint4 (&p)[NT], int st) {
         st = min(st, nst - 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = ap[static_cast<long long>(st) * (kSK / 8) + i];
+        for (int i = 0; i < NT; ++i) p[i] = ap[i][static_cast<long long>(st) * (kSK / 8)];
       };
-      auto store = [&](const uint4 (&p)[8], int stage, int st) {
+      auto store = [&](const uint4 (&p)[NT], int stage, int st) {
         const uint32_t keep = st < nst ? 0xFFFFFFFFu : 0u;
-        uint4* dst = reinterpret_cast<uint4*>(As + stage * kStage + t * kSLd);
+        uint16_t* dst = As + stage * kStage + (t >> 3) * kSLd + (t & 7) * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          dst[i] = make_uint4(p[i].x & keep, p[i].y & keep, p[i].z & keep, p[i].w & keep);
+        for (int i = 0; i < NT; ++i)
+          *reinterpret_cast<uint4*>(dst + i * 32 * kSLd) =
+              make_uint4(p[i].x & keep, p[i].y & keep, p[i].z & keep, p[i].w & keep);
       };
       load(p0, 0);
       load(p1, 1);

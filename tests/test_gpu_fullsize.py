@@ -4,6 +4,7 @@ benchmark times, through the C ABI:
 * the Qwen3.5-27B-shaped head (H 5120, 24/4 heads, D 256, I 17408, V 152064,
   bf16) at a 4096-slot draft KV: one chained step and the in-round flush of up
   to three pending pairs (host bound 3, device count 2 or 3);
+* the same head with an int8-g128 lm_head: a step and a 3-pair LAST flush;
 * the 256-pair flush of the tiny head in bf16 over an 8192-slot prefix, in all
   three output modes;
 * the tiny bf16 head over a 32768-slot prefix with a bf16 or an int8-g128
@@ -85,15 +86,16 @@ def test_qwen27b_step_parity(qwen):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("n, mode", [(3, OH.ALL), (2, OH.LAST)])
-def test_qwen27b_flush_parity(qwen, n, mode):
+@pytest.mark.parametrize("n, n_max, mode", [(3, 3, OH.ALL), (2, 3, OH.LAST), (5, 5, OH.ALL), (8, 12, OH.ALL),
+                                            (16, 16, OH.LAST)])
+def test_qwen27b_flush_parity(qwen, n, n_max, mode):
     """The round's flush: host bound 3 rows (two drafts + one), device count n,
-    round base recorded; ALL mode returns every row's g."""
+    round base recorded; ALL mode returns every row's g.  Past 4 rows the 27B
+    head runs the MFMA products (5, 8 of 12, 16 rows)."""
     from mtp_draft_head_step_amd import abi
     s, gh, oh = qwen["shape"], qwen["gh"], qwen["oh"]
     tol = tol_of(s)
     gkv, okv = _qwen_kv(qwen)
-    n_max = 3
     ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, n_max, QWEN_CAP))
     toks = I.tokens_uniform(I.WL_QWEN, 901, n_max, s.vocab)
     hids = I.target_hiddens(s, I.WL_QWEN, 901, n_max)
@@ -151,6 +153,63 @@ def test_qwen27b_flush256_parity(qwen):
     g = host(hout)
     for i, r in enumerate(rows):
         assert rel_err(g[r], ref["g"][i]) <= tol, r
+
+
+@pytest.fixture(scope="module")
+def qwen_i8():
+    """The 27B-shaped head with its borrowed lm_head stored int8 per (row,
+    128-column group) with fp16 scales (the quantised draft output head), on
+    the GPU and in the oracle.  The other tensors are the bf16 head's."""
+    from mtp_draft_head_step_amd import abi
+    shape, wl = I.QWEN35_27B.with_dtypes(lm_head_dtype=I.I8G128), I.WL_QWEN
+    st = I.head_weights(shape, wl)
+    gh = abi.Head(shape, st)
+    oh = OH.Head(shape, I.weight_values(shape, st), cache_fp64=True)
+    del st
+    kp, vp = I.prefix_kv(shape, wl, QWEN_CTX, QWEN_CAP)
+    return {"shape": shape, "gh": gh, "oh": oh, "kp": kp, "vp": vp}
+
+
+@pytest.mark.timeout(900)
+def test_qwen27b_i8_lm_head_step_and_flush(qwen_i8):
+    """The int8-g128 lm_head at the 27B shape (152064 x 5120 int8 + fp16 scales):
+    one chained step (every logit, the fused argmax, g, the appended K/V) and
+    the round's flush of 3 pairs in LAST mode (last row's logits and argmax)."""
+    from mtp_draft_head_step_amd import abi
+    s, gh, oh = qwen_i8["shape"], qwen_i8["gh"], qwen_i8["oh"]
+    tol = tol_of(s)
+    gkv, okv = _qwen_kv(qwen_i8)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, 3, QWEN_CAP))
+    tok = int(I.tokens_uniform(I.WL_QWEN, 903, 1, s.vocab)[0])
+    hid = I.target_hiddens(s, I.WL_QWEN, 903, 1)
+    hout = torch.empty(s.hidden, dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    abi.mtp_draft_step(gh, gkv, torch.tensor([tok], dtype=torch.int32, device="cuda"),
+                       device_array(hid[0]), hout, logits, amax, ws)
+    torch.cuda.synchronize()
+    ref = oh.step(okv, tok, I.decode(hid[0], s.act_dtype))
+    lg = host(logits)
+    assert rel_err(lg, ref["logits"]) <= tol
+    assert rel_err(host(hout), ref["g"][0]) <= tol
+    assert argmax_ok(int(host(amax)[0]), ref["logits"], lg)[0]
+    assert int(host(amax)[0]) == int(np.argmax(lg))
+    _check_slots(gkv, okv, QWEN_CTX, QWEN_CTX + 1, tol)
+
+    toks = I.tokens_uniform(I.WL_QWEN, 904, 3, s.vocab)
+    hids = I.target_hiddens(s, I.WL_QWEN, 904, 3)
+    h1 = torch.zeros((1, s.hidden), dtype=torch.bfloat16, device="cuda")
+    abi.mtp_flush_pairs(gh, gkv, device_array(toks), device_array(hids), 3, None, OH.LAST, 1,
+                        h1, logits, amax, ws)
+    torch.cuda.synchronize()
+    ref = oh.flush(okv, [int(t) for t in toks], [I.decode(h, s.act_dtype) for h in hids], OH.LAST,
+                   set_round_base=True)
+    assert host(gkv.state).tolist() == [QWEN_CTX + 4, QWEN_CTX + 4, 0, 0]
+    _check_slots(gkv, okv, QWEN_CTX + 1, QWEN_CTX + 4, tol)
+    lg = host(logits)
+    assert rel_err(lg, ref["logits"]) <= tol
+    assert rel_err(host(h1)[0], ref["g"][0]) <= tol
+    assert argmax_ok(int(host(amax)[0]), ref["logits"], lg)[0]
 
 
 # --------------------------------------------------------------------------
