@@ -107,13 +107,13 @@ struct Layout {
 
 // Flushes of more rows than gemv_max_rows go through the MFMA tiles.  Small
 // heads keep the GEMV passes up to 16 rows (one launch per projection; every
-// kernel there is latency-bound).  Large heads switch past 4 rows: the 8- and
-// 16-row GEMV passes hold one accumulator per (row, activation row) and run at
-// one or two waves per SIMD, and at the 27B shape (H 5120) a 6..16-row flush
-// took 0.63..1.02 ms against 0.51 ms for 24 rows on the weight-streaming MFMA
-// product.
+// kernel there is latency-bound).  Large heads switch past one row: the
+// weight-streaming MFMA product reads each weight once with coalesced loads
+// for any row count, while the few-row GEMV passes stage every row per
+// workgroup and run at fewer waves per SIMD (27B shape, fc + q/k/v of a flush:
+// 3 rows 94 us as GEMV passes, 5 rows 67 us as products).
 constexpr int kGemvMaxRows = 16;
-constexpr int kGemvMaxRowsLarge = 4;
+constexpr int kGemvMaxRowsLarge = 1;
 constexpr int kLargeHidden = 2048;
 
 int gemv_max_rows(const mtp_head_config& c) {

@@ -320,18 +320,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 // gate and the matching 64 up rows) over one range of 64-column reduction
 // steps, with two kinds of wave:
 //
-//   waves 0-3 (products): each owns 32 weight rows and reads them straight from
-//     memory into registers in the layout of the B operand of
-//     v_mfma_f32_32x32x16_bf16: lane l takes the 64 bytes of weight row l % 32
-//     at columns k0 + 32 (l / 32) + [0, 32), and its q-th 16-byte piece feeds
-//     the product of reduction slice q.  The contraction pairs A and B by
-//     position only, so the A operand of slice q is read from LDS at the same
-//     columns, k0 + 32 (l / 32) + 8 q + [0, 8).  Weights are issued three
+//   waves 0-3 (products): each owns 32 weight rows.  Its loads are coalesced:
+//     load q of a step brings rows 8q .. 8q + 7, eight lanes per row's
+//     128-byte slice (eight whole cache lines per instruction), issued three
 //     steps ahead into a ring of three register slots; every weight byte is
-//     loaded once, by one wave.
-//   waves 4-7 (staging): thread t moves activation row t of each step into a
-//     three-stage LDS ring (rows padded by 16 bytes: conflict-free 16-byte
-//     reads), its loads issued two steps ahead.
+//     loaded once, by one wave.  At its step the wave passes the slice through
+//     a private padded LDS tile into the layout of the B operand of
+//     v_mfma_f32_32x32x16_bf16: lane l takes weight row l % 32 at columns
+//     k0 + 32 (l / 32) + 8 q + [0, 8) for reduction slice q.  The contraction
+//     pairs A and B by position only, so the A operand of slice q is read from
+//     LDS at the same columns.  (Loading straight into the B layout puts 32
+//     rows, 32 bytes each, in every instruction; at the 27B shape that pattern
+//     moved about a third of the bytes per second.)
+//   waves 4-7 (staging): the activation rows of each step into a three-stage
+//     LDS ring (rows padded by 16 bytes: conflict-free 16-byte reads), eight
+//     lanes per row's slice, loads issued two steps ahead.
 //
 // The split keeps each kind's memory counter to its own loads (the counter
 // completes in issue order, so one kind's waits never cover the other's
@@ -420,7 +423,7 @@ __device__ __forceinline__ void gemm_put(const GemmArgs& a, int r, int col, floa
 template <bool SWIGLU, int NT>
 __device__ __forceinline__ void gemm_stream_products(const GemmArgs& a, uint16_t* As, int kStage, int kTLd,
                                                      int r0, int tile, int sb, int nst, int nst3, int lane,
-                                                     int wave) {
+                                                     int wave, uint16_t* Wl) {
   // ---- product waves: this wave's 32 weight rows and their output columns
   const uint16_t* W;
   int wrow;
@@ -440,22 +443,30 @@ __device__ __forceinline__ void gemm_stream_products(const GemmArgs& a, uint16_t
     }
     wrow = cl;
   }
-  const char* bp = reinterpret_cast<const char*>(W + static_cast<long long>(wrow + (lane & 31)) * a.K +
-                                                 static_cast<long long>(sb) * kSK + (lane >> 5) * 32);
+  // load q: row wrow + 8q + lane / 8, the 16 bytes at step column (lane % 8) * 8
+  const char* bp = reinterpret_cast<const char*>(W + static_cast<long long>(wrow + (lane >> 3)) * a.K +
+                                                 static_cast<long long>(sb) * kSK + (lane & 7) * 8);
+  const long long qstride = static_cast<long long>(a.K) * 16;   // 8 rows, in bytes
   auto issue = [&](uint4 (&b)[4], int st) {
     st = min(st, nst - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = load_stream16(bp + static_cast<long long>(st) * kSK * 2 + q * 16);
+    for (int q = 0; q < 4; ++q) b[q] = load_stream16(bp + static_cast<long long>(st) * kSK * 2 + q * qstride);
   };
   f32x16_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x16_t{};
   const int aoff = (lane & 31) * kSLd + (lane >> 5) * 32;
+  uint16_t* wput = Wl + (lane >> 3) * kSLd + (lane & 7) * 8;
   auto compute = [&](int stage, const uint4 (&b)[4]) {
     const uint16_t* base = As + stage * kStage + aoff;
+    // the step's 32 x 64 weight slice through the wave's LDS tile (only this
+    // wave touches it; its LDS operations complete in issue order)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(wput + q * 8 * kSLd) = b[q];
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, b[q]);
+      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Wl + aoff + q * 8));
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t,
@@ -466,6 +477,7 @@ __device__ __forceinline__ void gemm_stream_products(const GemmArgs& a, uint16_t
       // the scheduler may tie up in early reads)
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_wave_barrier();   // the next step's writes follow these reads
   };
   uint4 b0[4], b1[4], b2[4];
   issue(b0, 0);
@@ -509,7 +521,9 @@ __global__ __launch_bounds__(512) void k_gemm_stream(GemmArgs a) {
   constexpr int kRows = NT * 32;
   constexpr int kStage = kSM * kSLd;                  // bf16 per LDS stage (256 rows)
   constexpr int kTLd = kSN + 4;                       // floats per row of the epilogue tile
-  constexpr int kLds = 3 * kStage * 2 > kRows * kTLd * 4 ? 3 * kStage * 2 : kRows * kTLd * 4;
+  constexpr int kWTile = 32 * kSLd;                    // bf16 per product wave's weight tile
+  constexpr int kLoop = (3 * kStage + 4 * kWTile) * 2;  // bytes: staging ring + weight tiles
+  constexpr int kLds = kLoop > kRows * kTLd * 4 ? kLoop : kRows * kTLd * 4;
   __shared__ __attribute__((aligned(16))) uint16_t As[kLds / 2];
   if (a.kv_state && a.kv_state[3] != 0) return;
   int n = a.n_max;
@@ -597,7 +611,8 @@ __global__ __launch_bounds__(512) void k_gemm_stream(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      gemm_stream_products<SWIGLU, NT>(a, As, kStage, kTLd, r0, tile, sb, nst, nst3, lane, wave);
+      gemm_stream_products<SWIGLU, NT>(a, As, kStage, kTLd, r0, tile, sb, nst, nst3, lane, wave,
+                                       As + 3 * kStage + wave * kWTile);
     }
     __syncthreads();   // the products' sums are in LDS (row-major, kTLd floats a row)
 
