@@ -248,6 +248,38 @@ int mtp_timing_pause(int32_t paused);
 int mtp_timing_elapsed(int32_t first, int32_t count, float *total_ms);
 int mtp_timing_end(float *total_ms, int32_t *launches);
 
+/* Draft-depth controller (host object, no device work).  It chooses how many
+ * tokens to draft in each round: argmax over N of committed(N) / cost(N), from
+ * live per-position acceptance and a per-depth round cost, N from 0 (plain
+ * decode: nothing drafted) up to one past the deepest position drafted so far;
+ * every few rounds it drafts one deeper than its choice (a probe: after 4
+ * rounds, then 8, 16, ... up to every 512; back to 4 when the choice changes).
+ * Its state persists across requests for as long as the object lives.  (The
+ * depth-control Facts of "Ollama qwen3_5 MTP loader and SelfDraft path"; the
+ * Ollama x/mlxrunner commit choosing the draft length for throughput.)
+ *   acceptance of position i: (accepts_i + 1) / (attempts_i + 2)
+ *   committed(N) = 1 + sum_{i=1..N} prod_{j<=i} a_j (the round stops at its
+ *                  first rejection; the correction or bonus token always commits)
+ *   cost: seeded per depth by the caller (any unit, > 0; e.g. the measured round
+ *         time at each depth), then cost[d] = 3/4 cost[d] + 1/4 reported time.
+ * Ties go to the smaller depth.  fp64, fixed order: decisions are reproducible.
+ *
+ * mtp_depth_ctl_create: max_depth in [0, MTP_MAX_DRAFT]; cost: HOST double
+ *   [max_depth + 1], every entry > 0 (copied).  INVALID_ARG otherwise, *out NULL.
+ * mtp_depth_ctl_next: the depth to draft this round (advances the probe
+ *   counter); negative status on a NULL controller.
+ * mtp_depth_ctl_report: the round drafted `depth`, `accepted` of them were
+ *   accepted (0 <= accepted <= depth), and it took `round_cost` (> 0).
+ * mtp_depth_ctl_state: the current choice, probe interval and cost table
+ *   (HOST double [max_depth + 1]); each output pointer may be NULL.
+ * Not thread-safe per controller; distinct controllers are independent. */
+typedef struct mtp_depth_ctl mtp_depth_ctl;
+int mtp_depth_ctl_create(int32_t max_depth, const double *cost, mtp_depth_ctl **out);
+void mtp_depth_ctl_destroy(mtp_depth_ctl *ctl);
+int32_t mtp_depth_ctl_next(mtp_depth_ctl *ctl);
+int mtp_depth_ctl_report(mtp_depth_ctl *ctl, int32_t depth, int32_t accepted, double round_cost);
+int mtp_depth_ctl_state(const mtp_depth_ctl *ctl, int32_t *choice, int32_t *interval, double *cost);
+
 #ifdef __cplusplus
 }
 #endif

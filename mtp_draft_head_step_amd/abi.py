@@ -33,7 +33,8 @@ WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
 EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_destroy", "mtp_workspace_bytes",
            "mtp_workspace_init", "mtp_draft_step", "mtp_flush_pairs", "mtp_draft_chain", "mtp_repair_pending",
            "spec_verify_workspace_bytes", "spec_verify", "kv_rollback", "mtp_timing_begin",
-           "mtp_timing_pause", "mtp_timing_elapsed", "mtp_timing_end")
+           "mtp_timing_pause", "mtp_timing_elapsed", "mtp_timing_end", "mtp_depth_ctl_create",
+           "mtp_depth_ctl_destroy", "mtp_depth_ctl_next", "mtp_depth_ctl_report", "mtp_depth_ctl_state")
 
 
 class mtp_head_config(C.Structure):
@@ -99,6 +100,16 @@ def _load():
     lib.mtp_timing_elapsed.argtypes = [i32, i32, C.POINTER(C.c_float)]
     lib.mtp_timing_end.restype = C.c_int
     lib.mtp_timing_end.argtypes = [C.POINTER(C.c_float), C.POINTER(i32)]
+    lib.mtp_depth_ctl_create.restype = C.c_int
+    lib.mtp_depth_ctl_create.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(vp)]
+    lib.mtp_depth_ctl_destroy.restype = None
+    lib.mtp_depth_ctl_destroy.argtypes = [vp]
+    lib.mtp_depth_ctl_next.restype = i32
+    lib.mtp_depth_ctl_next.argtypes = [vp]
+    lib.mtp_depth_ctl_report.restype = C.c_int
+    lib.mtp_depth_ctl_report.argtypes = [vp, i32, i32, C.c_double]
+    lib.mtp_depth_ctl_state.restype = C.c_int
+    lib.mtp_depth_ctl_state.argtypes = [vp, C.POINTER(i32), C.POINTER(i32), C.POINTER(C.c_double)]
     return lib
 
 
@@ -237,6 +248,40 @@ def mtp_timing_end():
     n = C.c_int32()
     _check(lib.mtp_timing_end(C.byref(ms), C.byref(n)), "mtp_timing_end")
     return ms.value, n.value
+
+
+class DepthController:
+    """The library's draft-depth controller (host object): next() -> depth to
+    draft this round; report(depth, accepted, round_cost) after the round."""
+
+    def __init__(self, max_depth: int, cost):
+        if max_depth < 0 or len(cost) != max_depth + 1:
+            raise MtpError(MTP_E_INVALID_ARG, "mtp_depth_ctl_create")
+        arr = (C.c_double * (max_depth + 1))(*[float(c) for c in cost])
+        h = C.c_void_p()
+        _check(lib.mtp_depth_ctl_create(max_depth, arr, C.byref(h)), "mtp_depth_ctl_create")
+        self.max_depth = max_depth
+        self.h = h
+
+    def next(self) -> int:
+        d = lib.mtp_depth_ctl_next(self.h)
+        _check(min(d, 0), "mtp_depth_ctl_next")
+        return d
+
+    def report(self, depth: int, accepted: int, round_cost: float):
+        _check(lib.mtp_depth_ctl_report(self.h, depth, accepted, float(round_cost)), "mtp_depth_ctl_report")
+
+    def state(self):
+        """-> (choice, probe interval, cost table)."""
+        ch, iv = C.c_int32(), C.c_int32()
+        cost = (C.c_double * (self.max_depth + 1))()
+        _check(lib.mtp_depth_ctl_state(self.h, C.byref(ch), C.byref(iv), cost), "mtp_depth_ctl_state")
+        return ch.value, iv.value, list(cost)
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            lib.mtp_depth_ctl_destroy(self.h)
+            self.h = None
 
 
 # ----------------------------------------------------------------------------

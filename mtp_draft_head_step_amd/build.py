@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmtp.so")
-SOURCES = ["gemv.hip", "gemm.hip", "attn.hip", "attn_mfma.hip", "verify.hip", "kv.hip", "api.cpp"]
+SOURCES = ["gemv.hip", "gemm.hip", "attn.hip", "attn_mfma.hip", "verify.hip", "kv.hip", "api.cpp", "depth.cpp"]
 ARCH = os.environ.get("MTP_OFFLOAD_ARCH", "gfx950")
 
 
