@@ -464,17 +464,29 @@ __device__ __forceinline__ void gemm_stream_products(const GemmArgs& a, uint16_t
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(wput + q * 8 * kSLd) = b[q];
     __builtin_amdgcn_wave_barrier();
+    // The operands of the next unit (a slice's A fragments for HT row blocks
+    // and its B fragment) are read while the products of this unit run: two
+    // register sets, so the LDS latency hides behind the matrix cores.  At 8
+    // row blocks a unit is half a slice (a whole slice twice over would spill).
+    constexpr int HT = NT > 4 ? NT / 2 : NT;    // row blocks per unit
+    constexpr int UPQ = NT / HT;                // units per reduction slice
+    uint4 av[2][HT], bv[2];
+    auto fetch = [&](int u, uint4 (&ar)[HT], uint4& br) {
+      const int q = u / UPQ, t0 = (u % UPQ) * HT;
+      br = *reinterpret_cast<const uint4*>(Wl + aoff + q * 8);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Wl + aoff + q * 8));
+      for (int t = 0; t < HT; ++t) ar[t] = *reinterpret_cast<const uint4*>(base + (t0 + t) * 32 * kSLd + q * 8);
+    };
+    fetch(0, av[0], bv[0]);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t,
-            *reinterpret_cast<const uint4*>(base + t * 32 * kSLd + q * 8));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
-      }
-      // one slice's operand reads in flight at a time (bounds the registers
-      // the scheduler may tie up in early reads)
+    for (int u = 0; u < 4 * UPQ; ++u) {
+      if (u + 1 < 4 * UPQ) fetch(u + 1, av[(u + 1) & 1], bv[(u + 1) & 1]);
+      const int t0 = (u % UPQ) * HT;
+      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bv[u & 1]);
+#pragma unroll
+      for (int t = 0; t < HT; ++t)
+        acc[t0 + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[u & 1][t]), bf,
+                                                              acc[t0 + t], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_wave_barrier();   // the next step's writes follow these reads
