@@ -900,8 +900,10 @@ def run_depth(args, N, lm):
     ks = np.array(k_of[args.warmup:])
     expected = 1.0 + sum(float(np.prod([0.8 * 0.85 ** i for i in range(j)])) for j in range(1, N + 1))
     committed_tok = int(sum(int(k) + 1 for k in ks))
+    # the oracle runs one session in the same capacity: at most as many rounds as fit
+    cpu_rounds_max = max(1, min(R, (cap - ctx - 64) // (N + 1)))
     cpu = cpu_depth(shape, storage, kp, vp, cap, ctx, N, policy, base_rows, args.cpu_seconds / len(
-        str(args.depth).split(",")), R) if args.cpu_seconds > 0 else None
+        str(args.depth).split(",")), cpu_rounds_max) if args.cpu_seconds > 0 else None
     out = base_line(args, round(N * args.steps / el, 2), "draft tokens/s", el / args.steps * 1e3, "bf16",
                     "synthetic (seeded N(0,0.02) tiny-head weights in bf16, N(0,1) bf16 prefix K/V, N(0,3) "
                     "target rows with planted greedy acceptance p_i = 0.8*0.85^i)",
