@@ -121,6 +121,29 @@ def test_qwen27b_flush_parity(qwen, n, n_max, mode):
         assert np.all(g[n:] == 0)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n_max, mode", [(3, OH.LAST), (8, OH.ALL)])
+def test_qwen27b_flush_zero_pairs(qwen, n_max, mode):
+    """The MFMA flush path with a device count of 0: nothing appended, the round
+    base recorded at the unchanged length, the outputs untouched."""
+    from mtp_draft_head_step_amd import abi
+    s, gh = qwen["shape"], qwen["gh"]
+    gkv, _ = _qwen_kv(qwen)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, n_max, QWEN_CAP))
+    toks = I.tokens_uniform(I.WL_QWEN, 905, n_max, s.vocab)
+    hids = I.target_hiddens(s, I.WL_QWEN, 905, n_max)
+    hout = torch.zeros((n_max, s.hidden), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros(s.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    n_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    abi.mtp_flush_pairs(gh, gkv, device_array(toks), device_array(hids), n_max, n_dev, mode, 1,
+                        hout if mode == OH.ALL else hout[:1], logits, amax, ws)
+    torch.cuda.synchronize()
+    assert host(gkv.state).tolist() == [QWEN_CTX, QWEN_CTX, 0, 0]
+    assert not host(gkv.k)[:, QWEN_CTX:QWEN_CTX + n_max].any()
+    assert np.all(host(logits) == 0) and int(host(amax)[0]) == -1 and np.all(host(hout) == 0)
+
+
 @pytest.mark.timeout(900)
 def test_qwen27b_flush256_parity(qwen):
     """The pages' full flush at the 27B shape: 256 pending pairs (2.5 MiB of bf16

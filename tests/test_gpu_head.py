@@ -95,6 +95,34 @@ def test_chained_steps(name):
 
 @pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("mode", [OH.KV_ONLY, OH.LAST, OH.ALL])
+def test_flush_zero_pairs(name, mode):
+    """A device count of 0 (nothing pending): no slot is written, the length
+    stays, the round base is recorded at it, and the outputs are untouched --
+    what the oracle's empty flush does."""
+    from mtp_draft_head_step_amd import abi
+    shape = SHAPES[name]
+    wl, n_max, cap, prefix = 60, 3, 512, 200
+    _, gh, oh = build(shape, wl)
+    gkv, okv = kv_pair(shape, wl, prefix, cap)
+    k0, v0 = host(gkv.k).copy(), host(gkv.v).copy()
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, n_max, cap))
+    toks = I.tokens_uniform(wl, 1, n_max, shape.vocab)
+    hids = I.target_hiddens(shape, wl, 1, n_max)
+    hout = torch.zeros((n_max, shape.hidden), dtype=act_dtype(shape), device="cuda")
+    logits = torch.zeros(shape.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    n_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    abi.mtp_flush_pairs(gh, gkv, device_array(toks), device_array(hids), n_max, n_dev, mode, 1,
+                        hout if mode == OH.ALL else hout[:1], logits, amax, ws)
+    torch.cuda.synchronize()
+    assert oh.flush(okv, [], [], mode, set_round_base=True) == {}
+    assert host(gkv.state).tolist() == [okv.len, okv.base, 0, 0] == [prefix, prefix, 0, 0]
+    assert np.array_equal(host(gkv.k), k0) and np.array_equal(host(gkv.v), v0)
+    assert np.all(host(logits) == 0) and int(host(amax)[0]) == -1 and np.all(host(hout) == 0)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("mode", [OH.KV_ONLY, OH.LAST, OH.ALL])
 @pytest.mark.parametrize("n, n_max, use_dev", [(5, 5, False), (3, 8, True), (37, 40, True), (1, 1, False)])
 def test_flush_parity(name, mode, n, n_max, use_dev):
     """Flush of n pairs (device count n <= host bound n_max when use_dev) in each
