@@ -926,6 +926,209 @@ def run_depth(args, N, lm):
     return out
 
 
+def run_depth_auto(args):
+    """Rounds of the tiny bf16 head over a 32768-slot prefix whose depth is chosen
+    every round by the library's depth controller (mtp_depth_ctl_*): it maximises
+    committed tokens per unit of round time from the per-position acceptance it
+    observes and a per-depth cost table.  Acceptance is planted with p_i = 0.8 *
+    0.85^i per position, greedy, policy A; depth 0 is a plain-decode round (the
+    pending pairs flushed KV_ONLY and one target row verified).  The cost table
+    is seeded by timing 4 rounds at each depth, then every round reports its own
+    GPU time (HIP events around its launches) plus --target-ms, a modelled target
+    forward per round (no target model runs here; the pages' cost is the
+    per-width forward cost, which the target's forward dominates).  One host
+    synchronisation per round.  value = committed tokens over the controller's
+    rounds / (their wall-clock time + rounds x target-ms)."""
+    import numpy as np
+    import torch
+
+    from mtp_draft_head_step_amd import abi
+    from mtp_draft_head_step_amd import inputs as I
+
+    ctx, Dm = 32768, int(args.max_depth)
+    shape = I.TINY_BF16
+    wl, V, H = I.WL_DEPTH, shape.vocab, shape.hidden
+    calib = 4
+    R = (Dm + 1) * calib + args.warmup + args.steps
+    cap = ctx + R * (Dm + 1) + 2 * (Dm + 1) + 64
+    storage = I.head_weights(shape, wl)
+    head = abi.Head(shape, storage)
+    kp, vp = I.prefix_kv(shape, wl, ctx, cap)
+    iost = torch.zeros(4 + 2 + Dm + 1, dtype=torch.int32, device="cuda")   # {state | k, k+1, tokens}
+    kv = abi.DraftKV(shape, cap, kp, vp, ctx, state=iost[0:4])
+    io = iost[4:]
+    pool_hid = abi.to_device(np.stack([I.target_hiddens(shape, wl, r, Dm + 1) for r in range(POOL)]))
+    base_rows = abi.to_device(np.stack([I.logits_rows(wl, 5, r, Dm + 1, V, 3.0)[0] for r in range(POOL)]))
+    rows = torch.zeros((Dm + 1, V), dtype=torch.float32, device="cuda")
+    first_hid = torch.zeros((Dm + 1, H), dtype=torch.bfloat16, device="cuda")
+    first_hid[0].copy_(abi.to_device(I.target_hiddens(shape, wl, 1000, 1)[0]))
+    d_buf = torch.zeros(Dm, dtype=torch.int32, device="cuda")
+    g_buf = torch.zeros((Dm, H), dtype=torch.bfloat16, device="cuda")
+    ring = torch.zeros(64, dtype=torch.int32, device="cuda")
+    ring_st = torch.zeros(2, dtype=torch.int32, device="cuda")
+    ws = abi.Workspace(abi.mtp_workspace_bytes(head.cfg, Dm + 1, cap))
+    vws = abi.Workspace(abi.spec_verify_workspace_bytes(Dm, V))
+    sp = abi.sampling(window=64)
+    io[1] = 1
+    io[2] = int(I.tokens_uniform(wl, 1, ctx + 2, V)[-1])
+    host = torch.zeros(iost.numel(), dtype=torch.int32).pin_memory()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    state = {"hid": first_hid, "len": ctx}
+
+    def round_(r, d):
+        """Enqueue round r at depth d, wait for it; -> (k, GPU ms, kv length before, pending)."""
+        k_plan = I.acceptance_draws(wl, (77, r), d) if d else 0
+        before, n_pend = state["len"], int(host[5]) if r else 1
+        e0.record(stream)
+        if d:
+            abi.mtp_draft_chain(head, kv, io[2:], state["hid"], Dm + 1, io[1:2], d, d_buf, g_buf, None, ws, stream)
+        else:
+            abi.mtp_flush_pairs(head, kv, io[2:], state["hid"], Dm + 1, io[1:2], abi.KV_ONLY, 1, None, None, None,
+                                ws, stream)
+        rows[: d + 1].copy_(base_rows[r % POOL][: d + 1])
+        if d:
+            I.plant_acceptance(rows, d_buf[:d].long(), k_plan)
+        abi.spec_verify(sp, d, V, rows, None, d_buf, ring, ring_st, None, io[2:], io[0:2], vws, stream)
+        if d:
+            abi.kv_rollback(kv, abi.TO_ROUND_BASE, None, d, stream)
+        e1.record(stream)
+        host.copy_(iost, non_blocking=True)
+        stream.synchronize()
+        if int(host[3]) != 0:
+            raise RuntimeError(f"device error word {int(host[3])} in round {r}")
+        k = int(host[4])
+        if k != k_plan:
+            raise RuntimeError(f"planted acceptance {k_plan} but verification accepted {k} in round {r}")
+        state["hid"] = pool_hid[r % POOL]
+        state["len"] = int(host[0])
+        return k, e0.elapsed_time(e1), before, n_pend
+
+    # seed: 4 rounds at each depth
+    tgt = float(args.target_ms)
+    r = 0
+    seed = []
+    for d in range(Dm + 1):
+        ts = []
+        for _ in range(calib):
+            ts.append(round_(r, d)[1])
+            r += 1
+        seed.append(float(np.median(ts)) + tgt)
+    ctl = abi.DepthController(Dm, seed)
+    for _ in range(args.warmup):
+        d = ctl.next()
+        k, ms, _, _ = round_(r, d)
+        ctl.report(d, k, ms + tgt)
+        r += 1
+    hist = [0] * (Dm + 1)
+    committed = 0
+    att = []                                     # (before, pending, depth) of rounds with timed attention
+    abi.mtp_timing_begin(abi.TIME_ATTENTION, args.steps * Dm + 4)
+    t = time.perf_counter()
+    for i in range(args.steps):
+        d = ctl.next()
+        timed = i % TIME_EVERY == 0
+        abi.mtp_timing_pause(not timed)
+        k, ms, before, n_pend = round_(r, d)
+        ctl.report(d, k, ms + tgt)
+        hist[d] += 1
+        committed += k + 1
+        if timed:
+            att.append((before, n_pend, d))
+        r += 1
+    el = time.perf_counter() - t
+    att_ms, att_n = abi.mtp_timing_end()
+    choice, interval, cost = ctl.state()
+    p = [0.8 * 0.85 ** i for i in range(Dm)]
+
+    def exp_committed(n):
+        tot, run = 1.0, 1.0
+        for i in range(n):
+            run *= p[i]
+            tot += run
+        return tot
+    predicted = {str(n): round(exp_committed(n) / (seed[n] * 1e-3), 1) for n in range(Dm + 1)}   # seed includes tgt
+    att_bytes = sum(attention_bytes(shape, b + n + i) for b, n, d in att for i in range(d))
+    att_avg = att_ms / att_n / 1e3 if att_n else None
+    cpu = cpu_depth_auto(shape, storage, kp, vp, cap, ctx, Dm, seed, tgt, args.cpu_seconds) \
+        if args.cpu_seconds > 0 else None
+    span = el + args.steps * tgt / 1e3
+    out = base_line(args, round(committed / span, 2), "committed tokens/s", span / args.steps * 1e3, "bf16",
+                    "synthetic (seeded N(0,0.02) tiny-head weights in bf16, N(0,1) bf16 prefix K/V, N(0,3) "
+                    "target logits with planted acceptance p_i = 0.8*0.85^i)",
+                    {"workload": "depth_auto_ctx32768", "hidden": H, "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv",
+                     "head_dim": shape.head_dim, "vocab": V, "draft_kv_context": ctx, "max_depth": Dm,
+                     "batch": 1, "temperature": 0.0, "policy": "A", "depth": "chosen per round by the controller",
+                     "target_forward_ms_modelled": tgt})
+    out.update({
+        "depth_histogram": {str(n): hist[n] for n in range(Dm + 1) if hist[n]},
+        "final_choice": choice, "probe_interval": interval,
+        "seed_round_ms": [round(c, 4) for c in seed],
+        "final_cost_ms": [round(c, 4) for c in cost],
+        "fixed_depth_committed_per_gpu_s": predicted,
+        "committed_per_round": round(committed / args.steps, 4),
+        "measured_committed_per_s_without_target": round(committed / el, 2),
+        "launch": "eager, one host sync per round (the controller needs each round's outcome)",
+        "roofline": roofline("hbm", att_bytes / (att_ms / 1e3) / 1e9 if att_n else None, HBM_PEAK_GBS, "GB/s",
+                             None, kernel="decode attention over the 32768-slot draft KV (chunk partials)",
+                             avg_us=round(att_avg * 1e6, 2) if att_avg else None, launches=att_n),
+        "cpu_baseline": cpu,
+    })
+    return out
+
+
+def cpu_depth_auto(shape, storage, kp, vp, cap, ctx, Dm, seed, tgt, seconds):
+    """The oracle as it stands on the same controller-driven workload: oracle
+    rounds at the depth the oracle controller picks, its cost table seeded with
+    the GPU's per-depth round times and fed the oracle's own round times (both
+    plus the same modelled target forward)."""
+    import numpy as np
+
+    from mtp_draft_head_step_amd import inputs as I
+    from oracle import depth as OD
+    from oracle import head as OH
+    from oracle import rounds as OR
+    from oracle import verify as OV
+    from oracle.kvcache import DraftKV
+    wl, V = I.WL_DEPTH, shape.vocab
+    oh = OH.Head(shape, I.weight_values(shape, storage))
+    okv = DraftKV(shape.n_kv_heads, cap, shape.head_dim, I.decode(kp, shape.kv_dtype), I.decode(vp, shape.kv_dtype),
+                  ctx)
+    committed = [int(t) for t in I.tokens_uniform(wl, 1, ctx + 2, V)]
+    hid0 = I.decode(I.target_hiddens(shape, wl, 1000, 1)[0], shape.act_dtype)
+    st = OR.RoundState(oh, okv, [(committed[-1], hid0)], committed, window=64)
+    ctl = OD.DepthController(Dm, seed)
+    base = [I.logits_rows(wl, 5, r, Dm + 1, V, 3.0)[0] for r in range(POOL)]
+    total = {"tokens": 0}
+
+    def unit(r):
+        d = ctl.next_depth()
+        k_plan = I.acceptance_draws(wl, (77, r), d) if d else 0
+        hid = I.decode(I.target_hiddens(shape, wl, r % POOL, Dm + 1), shape.act_dtype)
+        t0 = time.perf_counter()
+        if d:
+            def fn(tokens, start):
+                rows = base[r % POOL][: d + 1].copy()
+                I.plant_acceptance(rows, np.asarray(tokens[1:], np.int64), k_plan)
+                return rows, hid[: d + 1]
+            k = OR.run_round(st, d, fn)["k"]
+        else:
+            oh.flush(okv, [t for t, _ in st.pending], [h for _, h in st.pending], OH.KV_ONLY, set_round_base=True)
+            res = OV.verify(OV.Sampling(), base[r % POOL][:1], None, [], st.ring, st.ring_state)
+            st.ring, st.ring_state = res["ring"], res["state"]
+            st.pending = [(res["tokens"][0], hid[0])]
+            st.committed.extend(res["tokens"])
+            k = 0
+        ctl.report(d, k, (time.perf_counter() - t0) * 1e3 + tgt)
+        total["tokens"] += k + 1
+    with single_thread_blas():
+        n_rounds, el = timed_sample(unit, seconds, max(1, (cap - ctx - 64) // (Dm + 1) - 2))
+    return {"value": round(total["tokens"] / (el + n_rounds * tgt / 1e3), 3), "unit": "committed tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{n_rounds} controller-driven rounds of one session (oracle controller, planted acceptance) "
+                      f"over the 32768-slot prefix, numpy fp64, one BLAS thread"}
+
+
 def cpu_depth(shape, storage, kp, vp, cap, ctx, N, policy, base_rows, seconds, max_rounds):
     import numpy as np
 
@@ -964,13 +1167,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="qwen35_27b_round",
                     choices=["qwen35_27b_round", "tiny_round", "flush256_prefix8192", "flush256_qwen35_27b",
-                             "verify_sampled", "depth_ctx32768", "flush_scaling_qwen35_27b"])
+                             "verify_sampled", "depth_ctx32768", "flush_scaling_qwen35_27b",
+                             "depth_auto_ctx32768"])
     ap.add_argument("--depth", default="4", help="depth_ctx32768: drafts per round (comma list: one line each)")
     ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"],
                     help="qwen35_27b_round, depth_ctx32768: lm_head storage (int8 per (row, 128-column group) "
                          "with fp16 scales, or bf16)")
     ap.add_argument("--rows", default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
                     help="flush_scaling_qwen35_27b: pair counts of the flushes timed (comma list, 1..256)")
+    ap.add_argument("--max-depth", type=int, default=8, help="depth_auto_ctx32768: deepest draft the controller may pick")
+    ap.add_argument("--target-ms", type=float, default=2.0,
+                    help="depth_auto_ctx32768: modelled target forward per round, added to each round's cost "
+                         "(0 = the drafting machinery alone)")
     ap.add_argument("--policy", default="B", choices=["A", "B"], help="depth_ctx32768: KV policy")
     ap.add_argument("--sessions", type=int, default=32, help="depth_ctx32768: sessions rotated (1 = warm)")
     ap.add_argument("--top-k", type=int, default=40,
@@ -988,7 +1196,7 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     default_steps = {"qwen35_27b_round": 40, "tiny_round": 64, "flush256_prefix8192": 50, "flush256_qwen35_27b": 16,
-                     "verify_sampled": 10000, "depth_ctx32768": 256, "flush_scaling_qwen35_27b": 16}
+                     "verify_sampled": 10000, "depth_ctx32768": 256, "flush_scaling_qwen35_27b": 16, "depth_auto_ctx32768": 600}
     if args.steps is None:
         args.steps = default_steps[args.workload]
 
@@ -1015,6 +1223,8 @@ def main():
         lines = [run_verify(args)]
     elif args.workload == "flush_scaling_qwen35_27b":
         lines = [run_flush_scaling(args)]
+    elif args.workload == "depth_auto_ctx32768":
+        lines = [run_depth_auto(args)]
     else:
         lines = [run_depth(args, int(d), args.lm) for d in str(args.depth).split(",")]
     for line in lines:
