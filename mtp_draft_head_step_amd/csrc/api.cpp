@@ -229,10 +229,10 @@ hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t
   return hipSuccess;
 }
 
-hipError_t timed_gemm(const GemmArgs& g, hipStream_t s) {
+hipError_t timed_gemm(const GemmArgs& g, hipStream_t s, const RowNorm* rn = nullptr, bool* normed = nullptr) {
   int slot = -1;
   time_mark(TIME_PROJECTION, true, s, &slot);
-  const hipError_t e = launch_gemm(g, s);
+  const hipError_t e = launch_gemm(g, s, rn, normed);
   time_mark(TIME_PROJECTION, false, s, &slot);
   return e;
 }
@@ -288,6 +288,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
       return MTP_E_UNSUPPORTED;
   }
   // 1. x = W_fc [RMSNorm(E[t]) | RMSNorm(h)]
+  bool normed_qkv = false, normed_mlp = false;
   if (mfma) {
     PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
     p.in_mode = IN_EMBED; p.K = 2 * H; p.ld_out = 2 * H;
@@ -299,7 +300,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     GemmArgs m1 = base_gemm(kv, n_max, n_dev, gpart);
     m1.w[0] = static_cast<const uint16_t*>(h->w.fc); m1.m[0] = H; m1.M = H; m1.K = 2 * H;
     m1.a = xa; m1.lda = 2 * H; m1.out_mode = OUT_F32; m1.y = x; m1.ldy = H;
-    MTP_TRY(timed_gemm(m1, s));
+    // a split-K reduce also writes the q/k/v input rows, RMSNorm(x; w_in)
+    const RowNorm rn{h->w.input_layernorm, h->wt == W_BF16, c.rms_eps, xa, H};
+    MTP_TRY(timed_gemm(m1, s, &rn, &normed_qkv));
   }
   GemvArgs a = base_gemv(h, kv);
   a.w[0] = h->w.fc; a.m[0] = H; a.M = H; a.K = 2 * H; a.lpr = lpr_for(2 * H, h->wt);
@@ -313,9 +316,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
 
   // 2. q, k, v = W_{q,k,v} RMSNorm(x; w_in)
   if (mfma) {
-    PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
-    p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x; p.ldx = H; p.nw = h->w.input_layernorm;
-    MTP_TRY(launch_rows_prep(p, s));
+    if (!normed_qkv) {
+      PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+      p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x; p.ldx = H; p.nw = h->w.input_layernorm;
+      MTP_TRY(launch_rows_prep(p, s));
+    }
     GemmArgs m2 = base_gemm(kv, n_max, n_dev, gpart);
     m2.w[0] = static_cast<const uint16_t*>(h->w.q_proj); m2.m[0] = hq * D;
     m2.w[1] = static_cast<const uint16_t*>(h->w.k_proj); m2.m[1] = hkv * D;
@@ -390,7 +395,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     m5.w[0] = static_cast<const uint16_t*>(h->w.o_proj); m5.m[0] = H; m5.M = H; m5.K = hq * D;
     m5.a = o; m5.lda = hq * D;
     m5.out_mode = OUT_RESID; m5.res = x; m5.ldres = H; m5.y = x1; m5.ldy = H;
-    MTP_TRY(timed_gemm(m5, s));
+    // a split-K reduce also writes the MLP input rows, RMSNorm(x1; w_post)
+    const RowNorm rn{h->w.post_attention_layernorm, h->wt == W_BF16, c.rms_eps, xa, H};
+    MTP_TRY(timed_gemm(m5, s, &rn, &normed_mlp));
   } else {
     MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
   }
@@ -403,9 +410,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.in_mode = IN_RMS; a.x = x1; a.ldx = H; a.nw = h->w.post_attention_layernorm;
   a.out_mode = OUT_SWIGLU; a.y = m; a.ldy = I;
   if (mfma_out) {
-    PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
-    p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x1; p.ldx = H; p.nw = h->w.post_attention_layernorm;
-    MTP_TRY(launch_rows_prep(p, s));
+    if (!normed_mlp) {
+      PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+      p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x1; p.ldx = H; p.nw = h->w.post_attention_layernorm;
+      MTP_TRY(launch_rows_prep(p, s));
+    }
     GemmArgs m6 = base_gemm(kv, n_max, n_dev, gpart);
     m6.w[0] = static_cast<const uint16_t*>(h->w.gate_proj); m6.m[0] = I;
     m6.w[1] = static_cast<const uint16_t*>(h->w.up_proj); m6.m[1] = I;

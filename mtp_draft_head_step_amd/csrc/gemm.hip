@@ -735,6 +735,71 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int nsp) {
   gemm_put(a, r, c + 3, v.w);
 }
 
+// The split reduce of a product whose output feeds a normalised row: one
+// workgroup per row sums the partials in split order, applies the epilogue
+// (residual, act-dtype copy), keeps the row in registers and writes
+// bf16(y * w * (1 / rms(y))) -- the row preparation the next product reads.
+constexpr int kNormPer = 8;   // float4 columns per thread: rows of up to 8192
+__global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, int nsp, RowNorm rn) {
+  __shared__ float red[4];
+  if (a.kv_state && a.kv_state[3] != 0) return;
+  int n = a.n_max;
+  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  const int r = blockIdx.x;
+  if (r >= n) return;
+  const int per = a.M / 4;
+  const long long stride = static_cast<long long>(a.n_max) * a.M;
+  float4 v[kNormPer];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int c4 = threadIdx.x + i * 256;
+    if (c4 >= per) continue;
+    const int c = c4 * 4;
+    const float* p = a.part + static_cast<long long>(r) * a.M + c;
+    float4 t = *reinterpret_cast<const float4*>(p);
+    for (int q = 1; q < nsp; ++q) {
+      const float4 w = *reinterpret_cast<const float4*>(p + q * stride);
+      t.x += w.x; t.y += w.y; t.z += w.z; t.w += w.w;
+    }
+    if (a.out_mode == OUT_RESID) {
+      const float4 e = *reinterpret_cast<const float4*>(a.res + static_cast<long long>(r) * a.ldres + c);
+      t.x += e.x; t.y += e.y; t.z += e.z; t.w += e.w;
+    }
+    *reinterpret_cast<float4*>(a.y + static_cast<long long>(r) * a.ldy + c) = t;
+    if (a.y2) {
+      if (a.y2_bf16)
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y2) + static_cast<long long>(r) * a.ldy2 + c) =
+            make_uint2(f32_to_bf16(t.x) | (static_cast<uint32_t>(f32_to_bf16(t.y)) << 16),
+                       f32_to_bf16(t.z) | (static_cast<uint32_t>(f32_to_bf16(t.w)) << 16));
+      else
+        *reinterpret_cast<float4*>(static_cast<float*>(a.y2) + static_cast<long long>(r) * a.ldy2 + c) = t;
+    }
+    v[i] = t;
+    ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+  }
+  const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(a.M) + rn.eps);
+  uint16_t* out = rn.out + static_cast<long long>(r) * rn.ld_out;
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int c4 = threadIdx.x + i * 256;
+    if (c4 >= per) continue;
+    const int c = c4 * 4;
+    float w[4];
+    if (rn.nw_bf16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(rn.nw) + c);
+      w[0] = __uint_as_float(u.x << 16); w[1] = __uint_as_float(u.x & 0xFFFF0000u);
+      w[2] = __uint_as_float(u.y << 16); w[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else {
+      const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(rn.nw) + c);
+      w[0] = f.x; w[1] = f.y; w[2] = f.z; w[3] = f.w;
+    }
+    *reinterpret_cast<uint2*>(out + c) =
+        make_uint2(f32_to_bf16(v[i].x * w[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(v[i].y * w[1] * inv)) << 16),
+                   f32_to_bf16(v[i].z * w[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(v[i].w * w[3] * inv)) << 16));
+  }
+}
+
 bool gemm_supported(int M, int K, const int* m, int nmat) {
   if (M <= 0 || K <= 0 || M % kTN || K % kTK) return false;
   for (int i = 0; i < nmat; ++i)
@@ -742,7 +807,8 @@ bool gemm_supported(int M, int K, const int* m, int nmat) {
   return true;
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn, bool* normed) {
+  if (normed) *normed = false;
   if (a.n_max <= 0) return hipSuccess;
   const bool swiglu = a.out_mode == OUT_SWIGLU;
   (void)hipGetLastError();
@@ -774,8 +840,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (nsp > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      const long long threads = static_cast<long long>(a.n_max) * (a.M / 4);
-      hipLaunchKernelGGL(k_gemm_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a, nsp);
+      if (rn && a.out_mode != OUT_SWIGLU && a.M <= 256 * 4 * kNormPer && a.M % 4 == 0 &&
+          rn->ld_out % 4 == 0 && al(rn->out, 8)) {
+        hipLaunchKernelGGL(k_gemm_reduce_norm, dim3(static_cast<unsigned>(a.n_max)), dim3(256), 0, s, a, nsp, *rn);
+        if (normed) *normed = true;
+      } else {
+        const long long threads = static_cast<long long>(a.n_max) * (a.M / 4);
+        hipLaunchKernelGGL(k_gemm_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a,
+                           nsp);
+      }
     }
     if (sk) {
       const hipError_t e = hipGetLastError();

@@ -120,7 +120,18 @@ struct GemmArgs {
   int y_bf16;                // OUT_SWIGLU: y holds bf16 (ldy in bf16 elements)
   int sk_units;              // set by launch_gemm: stream-K steps per workgroup (0 = off)
 };
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// The next projection's input row, RMSNorm(y; nw) in bf16, produced by the
+// product's split-K reduce when it runs (one launch instead of two).
+struct RowNorm {
+  const void* nw;            // norm weight [M]
+  int nw_bf16;
+  float eps;
+  uint16_t* out;             // bf16 rows [n, ld_out]
+  int ld_out;
+};
+// rn (nullable): also write RMSNorm(y) rows when the product reduces split-K
+// partials; *normed (nullable) tells whether it did (else the caller preps).
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn = nullptr, bool* normed = nullptr);
 bool gemm_supported(int M, int K, const int* m, int nmat);
 // fp32 elements of the partial-sum workspace a product of `rows` rows needs
 // (0 when it runs unsplit)
