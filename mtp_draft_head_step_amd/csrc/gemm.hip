@@ -736,12 +736,15 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int nsp) {
 }
 
 // The split reduce of a product whose output feeds a normalised row: one
-// workgroup per row sums the partials in split order, applies the epilogue
-// (residual, act-dtype copy), keeps the row in registers and writes
-// bf16(y * w * (1 / rms(y))) -- the row preparation the next product reads.
-constexpr int kNormPer = 8;   // float4 columns per thread: rows of up to 8192
-__global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, int nsp, RowNorm rn) {
-  __shared__ float red[4];
+// workgroup of 1024 threads per row sums the partials in split order (all of a
+// column's split loads issued together), applies the epilogue (residual,
+// act-dtype copy), keeps the row in registers and writes bf16(y * w * (1 /
+// rms(y))) -- the row preparation the next product reads.
+constexpr int kNormThreads = 1024;
+constexpr int kNormPer = 2;        // float4 columns per thread: rows of up to 8192
+constexpr int kNormMaxSplit = 8;   // more splits take the separate reduce and prep
+__global__ __launch_bounds__(kNormThreads) void k_gemm_reduce_norm(GemmArgs a, int nsp, RowNorm rn) {
+  __shared__ float red[kNormThreads / kWave];
   if (a.kv_state && a.kv_state[3] != 0) return;
   int n = a.n_max;
   if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
@@ -753,15 +756,20 @@ __global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, int nsp, R
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kNormPer; ++i) {
-    const int c4 = threadIdx.x + i * 256;
+    const int c4 = threadIdx.x + i * kNormThreads;
     if (c4 >= per) continue;
     const int c = c4 * 4;
     const float* p = a.part + static_cast<long long>(r) * a.M + c;
-    float4 t = *reinterpret_cast<const float4*>(p);
-    for (int q = 1; q < nsp; ++q) {
-      const float4 w = *reinterpret_cast<const float4*>(p + q * stride);
-      t.x += w.x; t.y += w.y; t.z += w.z; t.w += w.w;
-    }
+    float4 pv[kNormMaxSplit];
+#pragma unroll
+    for (int q = 0; q < kNormMaxSplit; ++q)
+      if (q < nsp) pv[q] = *reinterpret_cast<const float4*>(p + q * stride);
+    float4 t = pv[0];
+#pragma unroll
+    for (int q = 1; q < kNormMaxSplit; ++q)
+      if (q < nsp) {
+        t.x += pv[q].x; t.y += pv[q].y; t.z += pv[q].z; t.w += pv[q].w;
+      }
     if (a.out_mode == OUT_RESID) {
       const float4 e = *reinterpret_cast<const float4*>(a.res + static_cast<long long>(r) * a.ldres + c);
       t.x += e.x; t.y += e.y; t.z += e.z; t.w += e.w;
@@ -782,7 +790,7 @@ __global__ __launch_bounds__(256) void k_gemm_reduce_norm(GemmArgs a, int nsp, R
   uint16_t* out = rn.out + static_cast<long long>(r) * rn.ld_out;
 #pragma unroll
   for (int i = 0; i < kNormPer; ++i) {
-    const int c4 = threadIdx.x + i * 256;
+    const int c4 = threadIdx.x + i * kNormThreads;
     if (c4 >= per) continue;
     const int c = c4 * 4;
     float w[4];
@@ -840,9 +848,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn, bool
     if (nsp > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      if (rn && a.out_mode != OUT_SWIGLU && a.M <= 256 * 4 * kNormPer && a.M % 4 == 0 &&
-          rn->ld_out % 4 == 0 && al(rn->out, 8)) {
-        hipLaunchKernelGGL(k_gemm_reduce_norm, dim3(static_cast<unsigned>(a.n_max)), dim3(256), 0, s, a, nsp, *rn);
+      if (rn && a.out_mode != OUT_SWIGLU && a.M <= kNormThreads * 4 * kNormPer && a.M % 4 == 0 &&
+          nsp <= kNormMaxSplit && rn->ld_out % 4 == 0 && al(rn->out, 8)) {
+        hipLaunchKernelGGL(k_gemm_reduce_norm, dim3(static_cast<unsigned>(a.n_max)), dim3(kNormThreads), 0, s, a,
+                           nsp, *rn);
         if (normed) *normed = true;
       } else {
         const long long threads = static_cast<long long>(a.n_max) * (a.M / 4);
