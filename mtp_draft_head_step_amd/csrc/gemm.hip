@@ -69,7 +69,12 @@ struct PrepRow {
   int half;
 };
 
-constexpr int kPrepU = 4;   // jobs in flight per thread
+constexpr int kPrepU = 4;          // jobs in flight per thread
+constexpr int kPrepThreads = 1024; // a row's jobs in one pass up to 4096 jobs (32768 columns)
+// split reduces (k_gemm_reduce, k_gemm_reduce_norm)
+constexpr int kNormThreads = 1024;
+constexpr int kNormPer = 2;        // float4 columns per thread: rows of up to 8192
+constexpr int kNormMaxSplit = 8;   // splits whose loads are issued together (more: a plain loop)
 
 __device__ __forceinline__ void prep_load(const PrepRow& r, int k, float (&v)[8]) {
   if (k < r.half) {
@@ -82,8 +87,8 @@ __device__ __forceinline__ void prep_load(const PrepRow& r, int k, float (&v)[8]
   }
 }
 
-__global__ __launch_bounds__(256) void k_rows_prep(PrepArgs a) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(kPrepThreads) void k_rows_prep(PrepArgs a) {
+  __shared__ float red[kPrepThreads / kWave];
   if (a.kv_state && a.kv_state[3] != 0) return;
   int n = a.n_max;
   if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
@@ -108,14 +113,14 @@ __global__ __launch_bounds__(256) void k_rows_prep(PrepArgs a) {
   // pass 1: sums of squares (first part / second part)
   float se = 0.f, sh = 0.f;
   if (a.in_mode != IN_F32) {
-    for (int f0 = threadIdx.x; f0 < njobs; f0 += 256 * kPrepU) {
+    for (int f0 = threadIdx.x; f0 < njobs; f0 += kPrepThreads * kPrepU) {
       float v[kPrepU][8];
 #pragma unroll
       for (int u = 0; u < kPrepU; ++u)
-        if (f0 + u * 256 < njobs) prep_load(r, (f0 + u * 256) * 8, v[u]);
+        if (f0 + u * kPrepThreads < njobs) prep_load(r, (f0 + u * kPrepThreads) * 8, v[u]);
 #pragma unroll
       for (int u = 0; u < kPrepU; ++u) {
-        const int k = (f0 + u * 256) * 8;
+        const int k = (f0 + u * kPrepThreads) * 8;
         if (k >= K) continue;
         float t = 0.f;
 #pragma unroll
@@ -132,11 +137,11 @@ __global__ __launch_bounds__(256) void k_rows_prep(PrepArgs a) {
     inv1 = 1.0f / sqrtf(block_sum(sh, red) / static_cast<float>(r.half) + a.eps);
   }
   // pass 2: bf16(x * w * inv) (IN_F32: bf16(x))
-  for (int f0 = threadIdx.x; f0 < njobs; f0 += 256 * kPrepU) {
+  for (int f0 = threadIdx.x; f0 < njobs; f0 += kPrepThreads * kPrepU) {
     float v[kPrepU][8], w[kPrepU][8];
 #pragma unroll
     for (int u = 0; u < kPrepU; ++u) {
-      const int k = (f0 + u * 256) * 8;
+      const int k = (f0 + u * kPrepThreads) * 8;
       if (k >= K) continue;
       prep_load(r, k, v[u]);
       if (a.in_mode == IN_F32) {
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(256) void k_rows_prep(PrepArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kPrepU; ++u) {
-      const int k = (f0 + u * 256) * 8;
+      const int k = (f0 + u * kPrepThreads) * 8;
       if (k >= K) continue;
       const float inv = k < r.half ? inv0 : inv1;
       uint32_t o[4];
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(256) void k_rows_prep(PrepArgs a) {
 hipError_t launch_rows_prep(const PrepArgs& a, hipStream_t s) {
   if (a.n_max <= 0) return hipSuccess;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_rows_prep, dim3(a.n_max), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_rows_prep, dim3(a.n_max), dim3(kPrepThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -725,9 +730,22 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int nsp) {
   const long long stride = static_cast<long long>(a.n_max) * a.M;
   const float* p = a.part + static_cast<long long>(r) * a.M + c;
   float4 v = *reinterpret_cast<const float4*>(p);
-  for (int s = 1; s < nsp; ++s) {
-    const float4 w = *reinterpret_cast<const float4*>(p + s * stride);
-    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  if (nsp <= kNormMaxSplit) {
+    // every split's load issued together, then added in split order
+    float4 pv[kNormMaxSplit];
+#pragma unroll
+    for (int q = 1; q < kNormMaxSplit; ++q)
+      if (q < nsp) pv[q] = *reinterpret_cast<const float4*>(p + q * stride);
+#pragma unroll
+    for (int q = 1; q < kNormMaxSplit; ++q)
+      if (q < nsp) {
+        v.x += pv[q].x; v.y += pv[q].y; v.z += pv[q].z; v.w += pv[q].w;
+      }
+  } else {
+    for (int q = 1; q < nsp; ++q) {
+      const float4 w = *reinterpret_cast<const float4*>(p + q * stride);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
   }
   gemm_put(a, r, c, v.x);
   gemm_put(a, r, c + 1, v.y);
@@ -740,9 +758,6 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int nsp) {
 // column's split loads issued together), applies the epilogue (residual,
 // act-dtype copy), keeps the row in registers and writes bf16(y * w * (1 /
 // rms(y))) -- the row preparation the next product reads.
-constexpr int kNormThreads = 1024;
-constexpr int kNormPer = 2;        // float4 columns per thread: rows of up to 8192
-constexpr int kNormMaxSplit = 8;   // more splits take the separate reduce and prep
 __global__ __launch_bounds__(kNormThreads) void k_gemm_reduce_norm(GemmArgs a, int nsp, RowNorm rn) {
   __shared__ float red[kNormThreads / kWave];
   if (a.kv_state && a.kv_state[3] != 0) return;
