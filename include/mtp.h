@@ -155,7 +155,8 @@ int mtp_draft_step(const mtp_head *head, const mtp_kv *kv, const int32_t *token_
  * out_mode KV_ONLY: only K/V.  LAST: hidden_out [hidden] (last row's g), logits
  * and argmax of the last row.  ALL: hidden_out [n, hidden] for every row, logits
  * and argmax of the last row.  set_round_base != 0 records state[1] = state[0]
- * after the append (the first provisional slot of a round). */
+ * after the append (the first provisional slot of a round).  A device count of
+ * 0 appends nothing and leaves every output untouched (state[1] is still set). */
 int mtp_flush_pairs(const mtp_head *head, const mtp_kv *kv, const int32_t *tokens_dev,
                     const void *hiddens_dev, int32_t n_max, const int32_t *n_dev,
                     int32_t out_mode, int32_t set_round_base, void *hidden_out_dev,
