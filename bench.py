@@ -664,10 +664,30 @@ def run_verify(args):
     torch.cuda.synchronize()
     el = time.perf_counter() - t
     ms, nl = abi.mtp_timing_end()
-    calibrate_copy(args)
     counts = out_c[args.warmup:].cpu().numpy()
     if counts.min() < 0 or np.any(counts[:, 1] != counts[:, 0] + 1):
         raise RuntimeError("verification returned malformed counts")
+
+    # greedy mode: temperature 0, 2 drafts, 3 target rows (1.82 MB) of the same pool
+    gsp = abi.sampling(window=64)
+    gws = abi.Workspace(abi.spec_verify_workspace_bytes(2, V))
+    gring, gst = ring.clone(), ring_st.clone()
+
+    def one_greedy(r):
+        p = r % VERIFY_POOL
+        abi.spec_verify(gsp, 2, V, t_rows[p], None, drafts[p], gring, gst, None, out_t[r % total],
+                        out_c[r % total], gws, stream)
+    g_steps = max(steps // 4, 100)
+    for r in range(args.warmup):
+        one_greedy(r)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for r in range(g_steps):
+        one_greedy(r)
+    torch.cuda.synchronize()
+    g_el = time.perf_counter() - t
+    g_bytes = 3 * V * 4 + 64 * 4
+    calibrate_copy(args)
     # the timed first pass reads every row (the whole-vocabulary path also writes
     # the transformed rows back)
     chunk_bytes = (2 * N + 1) * V * 4 * (2 if full else 1) + 64 * 4
@@ -684,6 +704,11 @@ def run_verify(args):
         "us_per_round": round(el / steps * 1e6, 2),
         "round_gbs": round(chunk_bytes / (el / steps) / 1e9, 1),
         "mean_accepted": round(float(counts[:, 0].mean()), 4),
+        "greedy": {"rows": 3, "drafts": 2, "rounds_per_s": round(g_steps / g_el, 1),
+                   "us_per_round": round(g_el / g_steps * 1e6, 2),
+                   "gbs": round(g_bytes / (g_el / g_steps) / 1e9, 1),
+                   "hbm_frac": round(g_bytes / (g_el / g_steps) / 1e9 / HBM_PEAK_GBS, 4),
+                   "note": "temperature 0 (argmax match), 3 target rows of the same pool, eager launches"},
         "roofline": roofline("hbm", chunk_bytes / avg / 1e9, HBM_PEAK_GBS, "GB/s", None,
                              kernel=("whole-vocabulary transform pass over the 9 rows (penalty, temperature, "
                                      "row maxima; transformed rows written back)" if full else
