@@ -63,7 +63,7 @@ def _load():
     # makes libmtp bind to that one copy, so both share one runtime and device.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"libmtp.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        raise RuntimeError(f"libmtp.so is not built ({LIB_PATH}); run python -m mtp_draft_head_step_amd.build")
     lib = C.CDLL(LIB_PATH)
     vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
     lib.mtp_status_string.restype = C.c_char_p
