@@ -186,6 +186,75 @@ def test_rounds_match_oracle_and_classic(policy, n_draft, headkind):
         assert max(ks) == N and min(ks) == 0
 
 
+@pytest.mark.parametrize("headkind", ["random", "successor"])
+def test_rounds_with_changing_depth_match_classic(headkind):
+    """Rounds whose depth changes every round, plain decode (depth 0) included,
+    as the depth controller drives them: the flush takes the host bound of the
+    deepest round and the previous round's device count; a depth-0 round flushes
+    its pending pairs KV_ONLY and verifies one target row.  The GPU commits the
+    oracle's stream, which is classic greedy decoding, with the same draft KV
+    lengths (policy A)."""
+    from mtp_draft_head_step_amd import abi
+    storage = I.head_weights(SHAPE, 23) if headkind == "random" else successor_storage()
+    tgt = I.ToyTarget(33, SHAPE.vocab, SHAPE.hidden, follow=0.8 if headkind == "successor" else 0.0)
+    Dm = 3
+    gh, oh, gkv, okv, committed, pending = gpu_session(storage, tgt, Dm)
+    ost = R.RoundState(oh, okv, pending, committed, window=16)
+    start = list(committed)
+    ws = abi.Workspace(abi.mtp_workspace_bytes(gh.cfg, Dm + 1, CAP))
+    vws = abi.Workspace(abi.spec_verify_workspace_bytes(Dm, SHAPE.vocab))
+    ring = torch.zeros(16, dtype=torch.int32, device="cuda")
+    ring_st = torch.zeros(2, dtype=torch.int32, device="cuda")
+    d_buf = torch.zeros(Dm, dtype=torch.int32, device="cuda")
+    g_buf = torch.zeros((Dm, SHAPE.hidden), dtype=torch.float32, device="cuda")
+    out_t = torch.zeros(Dm + 1, dtype=torch.int32, device="cuda")
+    out_c = torch.zeros(2, dtype=torch.int32, device="cuda")
+    pend_t = device_array(np.array([t for t, _ in pending] + [0] * Dm, np.int32))
+    pend_h = device_array(np.concatenate([np.stack([h for _, h in pending]),
+                                          np.zeros((Dm, SHAPE.hidden), np.float32)]))
+    n_dev = torch.tensor([len(pending)], dtype=torch.int32, device="cuda")
+    gpu_committed = list(committed)
+    depths = [2, 0, 3, 1, 0, 3, 3, 1, 2, 0, 0, 3, 2, 1]
+    diverged = False
+    for rnd, d in enumerate(depths):
+        c = len(gpu_committed) - 1
+        if d:
+            abi.mtp_draft_chain(gh, gkv, pend_t, pend_h, Dm + 1, n_dev, d, d_buf, g_buf, None, ws)
+            drafts = host(d_buf)[:d].tolist()
+        else:
+            abi.mtp_flush_pairs(gh, gkv, pend_t, pend_h, Dm + 1, n_dev, abi.KV_ONLY, 1, None, None, None, ws)
+            drafts = []
+        rows, hid_rows = tgt.forward([gpu_committed[-1]] + drafts, c)
+        abi.spec_verify(abi.sampling(window=16), d, SHAPE.vocab, device_array(rows), None, d_buf,
+                        ring, ring_st, None, out_t, out_c, vws)
+        if d:
+            abi.kv_rollback(gkv, abi.TO_ROUND_BASE, None, d)
+        k = int(host(out_c)[0])
+        toks = host(out_t)[: k + 1].tolist()
+        pend_t[: k + 1] = out_t[: k + 1]
+        pend_h[: k + 1] = device_array(hid_rows[: k + 1])
+        n_dev.fill_(k + 1)
+        gpu_committed += toks
+        # the oracle on the same inputs
+        if d:
+            out = R.run_round(ost, d, lambda tk, s: tgt.forward(tk, s), policy="A")
+            diverged = diverged or out["drafts"] != drafts
+        else:
+            oh.flush(okv, [t for t, _ in ost.pending], [h for _, h in ost.pending], OH.KV_ONLY,
+                     set_round_base=True)
+            orow, ohid = tgt.forward([ost.committed[-1]], len(ost.committed) - 1)
+            res = OV.verify(OV.Sampling(window=16), orow, None, [], ost.ring, ost.ring_state)
+            ost.ring, ost.ring_state = res["ring"], res["state"]
+            ost.pending = [(res["tokens"][0], ohid[0])]
+            ost.committed.extend(res["tokens"])
+        st = host(gkv.state)
+        assert st[3] == 0
+        if not diverged:
+            assert st[0] == ost.kv.len, (rnd, d, st, ost.kv.len)
+    assert gpu_committed == ost.committed
+    assert gpu_committed == R.classic_greedy(lambda tk, s: tgt.forward(tk, s), start, len(gpu_committed) - len(start))
+
+
 def _round_session(shape, wl, n_draft, pool, cap):
     from mtp_draft_head_step_amd import abi
     st = I.head_weights(shape, wl)
