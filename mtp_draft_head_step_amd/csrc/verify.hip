@@ -255,6 +255,30 @@ __device__ void bitonic_small(unsigned long long* s, int n) {
     }
 }
 
+// Descending sort of n (a power of two) nonzero keys in LDS.  Up to 64 keys one
+// wave sorts them in registers (the same bitonic network over 64 lanes, the
+// slots past n holding 0, which sorts last): no workgroup barrier per stage.
+// Larger n: the workgroup network.
+__device__ void sort_small(unsigned long long* s, int n) {
+  if (n <= 64) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      unsigned long long v = lane < n ? s[lane] : 0ull;
+      for (int size = 2; size <= 64; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const unsigned long long o = shfl_xor_u64(v, stride);
+          const bool desc = (lane & size) == 0;
+          const bool lower = (lane & stride) == 0;
+          v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+        }
+      if (lane < n) s[lane] = v;
+    }
+    __syncthreads();
+    return;
+  }
+  bitonic_small(s, n);
+}
+
 constexpr int kSPer = kSChunk / kVThreads;   // chunk keys per thread
 
 __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, SampledScratch sc, int nb, int kk) {
@@ -358,7 +382,7 @@ __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledS
       if (pos < k2) s[pos] = key[u];
     }
   __syncthreads();
-  bitonic_small(s, k2);                                  // the top-k by (value desc, id asc)
+  sort_small(s, k2);                                     // the top-k by (value desc, id asc)
   if (tid == 0) {
     const float y0 = key_value(s[0]);
     float tot = 0.f;
@@ -399,7 +423,7 @@ __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledS
   __syncthreads();
   if (tid < k3) s[tid] = ~mine;                          // descending of ~v = ascending of v
   __syncthreads();
-  bitonic_small(s, k3);
+  sort_small(s, k3);
   for (int j = tid; j < keep; j += kVThreads) {
     const unsigned long long vv = ~s[j];
     sc.ids[static_cast<size_t>(row) * kSMaxTopK + j] = static_cast<int>(vv >> 32);
