@@ -255,6 +255,14 @@ def test_rounds_with_changing_depth_match_classic(headkind):
     assert gpu_committed == R.classic_greedy(lambda tk, s: tgt.forward(tk, s), start, len(gpu_committed) - len(start))
 
 
+GRAPH_SHAPES = {
+    "tiny_bf16": I.TINY_BF16,
+    "h2048_bf16": I.HeadShape(hidden=2048, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=4096,
+                              vocab=8192).with_dtypes(weight_dtype=I.BF16, act_dtype=I.BF16, kv_dtype=I.BF16,
+                                                      lm_head_dtype=I.BF16),
+}
+
+
 def _round_session(shape, wl, n_draft, pool, cap):
     from mtp_draft_head_step_amd import abi
     st = I.head_weights(shape, wl)
@@ -293,11 +301,14 @@ def _enqueue(s, r, N, pool, stream):
 
 
 @pytest.mark.parametrize("n_draft", [2, 3])
-def test_graph_replayed_rounds_equal_eager(n_draft):
+@pytest.mark.parametrize("shape_name", ["tiny_bf16", "h2048_bf16"])
+def test_graph_replayed_rounds_equal_eager(n_draft, shape_name):
     """Rounds captured once into graphs and replayed many times (with eager work
     and host syncs between replays) commit the same tokens and leave the same
-    draft KV as the same rounds launched eagerly."""
-    shape = I.TINY_BF16
+    draft KV as the same rounds launched eagerly.  The hidden-2048 head runs its
+    flushes on the matrix cores (the weight-streaming fc product with the fused
+    split reduce and row norm, 64 x 64 tiles for q/k/v)."""
+    shape = GRAPH_SHAPES[shape_name]
     pool, rounds, cap = 4, 12, 512
     eager = _round_session(shape, 55, n_draft, pool, cap)
     graph = _round_session(shape, 55, n_draft, pool, cap)
