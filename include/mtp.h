@@ -8,9 +8,10 @@
  *    pointers; structs passed by pointer (config, weights, kv descriptor,
  *    sampling) are HOST memory read during the call only.
  *  - The library never allocates device memory.  Scratch lives in a caller-owned
- *    workspace sized by mtp_workspace_bytes / spec_verify_workspace_bytes; it
- *    must be zeroed once before first use (mtp_workspace_init) and is left
- *    zeroed-where-it-matters by every call (self-resetting counters).
+ *    workspace sized by mtp_workspace_bytes / spec_verify_workspace_bytes.  No
+ *    kernel relies on its previous contents (every scratch value is written
+ *    before it is read in the same call); mtp_workspace_init zeroes one anyway
+ *    so a fresh workspace holds no stale values from the allocator.
  *  - Every compute call is asynchronous on `stream` and does not synchronise.
  *  - Host-checkable problems return a negative mtp_status BEFORE anything is
  *    enqueued (fail closed).  Problems only the device can see (a device-side
@@ -115,24 +116,35 @@ enum { MTP_FLUSH_KV_ONLY = 0, MTP_FLUSH_LAST = 1, MTP_FLUSH_ALL = 2 };
 #define MTP_MAX_FLUSH 256  /* pending-pair flush cap ("Facts": flush batches of up to 256) */
 #define MTP_MAX_DRAFT 16   /* drafts per verify */
 
-/* Human-readable name of a status code (static string). */
+/* Library infrastructure (no passage of the pages defines these): the name of a
+ * status code (static string, never NULL; "MTP_E_UNKNOWN" for other values). */
 const char *mtp_status_string(int status);
 
-/* Text of the last HIP error this thread's calls returned MTP_E_HIP for. */
+/* Library infrastructure: text of the last HIP error this thread's calls
+ * returned MTP_E_HIP for (static string owned by the HIP runtime). */
 const char *mtp_last_error(void);
 
-/* Validate the config and weights and build the host-side head object.
+/* Validate the config and weights and build the host-side head object
+ * ("feat(inference): support the qwen3_5_mtp drafter ...", section "Upstream
+ * contract to port": the drafter holds its own layer, pre-fc norms, fc and final
+ * norm, borrows the target's embedding table and lm_head through a bind step,
+ * and its drafting raises when bind was skipped -- here that is creation).
  * Returns MTP_E_NOT_BOUND if embed or lm_head is NULL (the head owns neither),
  * MTP_E_INVALID_ARG for other NULL tensors or bad sizes, MTP_E_UNSUPPORTED for
- * shapes outside the kernels.  *out is set only on success. */
+ * shapes outside the kernels.  *out is set only on success; nothing is
+ * allocated on the device and no HIP call is made.  The weight pointers are
+ * borrowed: they must outlive the head.  mtp_head_destroy(NULL) is a no-op. */
 int mtp_head_create(const mtp_head_config *cfg, const mtp_head_weights *w, mtp_head **out);
 void mtp_head_destroy(mtp_head *head);
 
-/* Workspace bytes for calls with at most max_rows pairs (1..256) on a KV of at
- * most max_capacity slots.  0 on invalid arguments. */
+/* Library infrastructure: workspace bytes for calls with at most max_rows
+ * pairs (1..256) on a KV of at most max_capacity slots.  It takes the config,
+ * not a head, so a caller can size (and allocate) the workspace before the
+ * weights are bound.  0 on invalid arguments. */
 size_t mtp_workspace_bytes(const mtp_head_config *cfg, int32_t max_rows, int32_t max_capacity);
 
-/* Zero a workspace (either kind) with a fill kernel on `stream`. */
+/* Library infrastructure: zero a workspace (either kind) with a fill kernel on
+ * `stream` (asynchronous; no hipMemset node, so it may be graph-captured). */
 int mtp_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* One draft-head step ("Facts", MTP drafting: one head call per draft token) at
@@ -171,7 +183,11 @@ int mtp_flush_pairs(const mtp_head *head, const mtp_kv *kv, const int32_t *token
  * d_0..d_{n-1}; hiddens_out_dev [n_draft, hidden] (act dtype, must not overlap
  * the pending hiddens) the g of every draft; draft_logits_dev (nullable) fp32
  * [n_draft, vocab] the draft rows (sampled verification needs them).  The
- * workspace must hold n_max rows.  1 <= n_draft <= MTP_MAX_DRAFT. */
+ * workspace must hold n_max rows.  1 <= n_draft <= MTP_MAX_DRAFT.  A round
+ * always has at least one pending pair (the last committed token with its
+ * target hidden), so a device count of 0 (like one above n_max) sets state[3] =
+ * MTP_DEV_COUNT and every kernel of the call, the chained steps included, is
+ * then a no-op. */
 int mtp_draft_chain(const mtp_head *head, const mtp_kv *kv, const int32_t *pend_tokens_dev,
                     const void *pend_hiddens_dev, int32_t n_max, const int32_t *n_dev, int32_t n_draft,
                     int32_t *drafts_dev, void *hiddens_out_dev, float *draft_logits_dev, void *ws,

@@ -273,13 +273,42 @@ PrepArgs base_prep(const mtp_head* h, const mtp_kv* kv, int n_max, const int32_t
   return p;
 }
 
-// The head forward for n rows (n_max host bound, n_dev device count).
-// mode: KV_ONLY / LAST / ALL.  hidden_out: [1 or n, H] in act dtype (nullable).
+// The unembedding launch: logits = W_lm RMSNorm(g; w_norm) of the last row with
+// the per-workgroup argmax keys.
+GemvArgs unembed_args(const mtp_head* h, const mtp_kv* kv, const Layout& L, int n_max, const int32_t* n_dev,
+                      const float* g, float* logits, void* ws) {
+  const mtp_head_config& c = h->cfg;
+  GemvArgs a = base_gemv(h, kv);
+  a.w[0] = h->w.lm_head; a.m[0] = c.vocab; a.M = c.vocab; a.K = c.hidden; a.lpr = lpr_unembed(c.hidden, h->lmt);
+  a.scales = static_cast<const uint16_t*>(h->w.lm_head_scales);
+  a.n_max = n_max; a.n_dev = n_dev;
+  a.in_mode = IN_RMS; a.x = g; a.ldx = c.hidden; a.nw = h->w.norm;
+  a.out_mode = OUT_LOGITS; a.logits = logits;
+  a.amax_part = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax));
+  a.row_sel = ROW_LAST;
+  a.row_base = 0;
+  a.kp = kp_for(a.K, h->lmt, 1);
+  a.grid_stride = a.kp == a.K;
+  return a;
+}
+
+// The head forward for n rows (n_max host bound, n_dev device count; a device
+// count below n_min sets MTP_DEV_COUNT).  mode: KV_ONLY / LAST / ALL.
+// hidden_out: [1 or n, H] in act dtype (nullable).
 int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, const void* hiddens,
                  int n_max, const int32_t* n_dev, int mode, int set_base, void* hidden_out,
-                 float* logits, int32_t* argmax, void* ws, hipStream_t s) {
+                 float* logits, int32_t* argmax, void* ws, hipStream_t s, int n_min = 0) {
   const mtp_head_config& c = h->cfg;
   const Layout L = layout(c, n_max, kv->capacity);
+  // host-checkable limits before anything is enqueued: the unembedding's
+  // workgroups each write one argmax key into a buffer of amax_parts entries
+  if (mode != MTP_FLUSH_KV_ONLY) {
+    GemvArgs u = unembed_args(h, kv, L, n_max, n_dev, nullptr, nullptr, ws);
+    u.dry_run = 1;
+    int grid = 0;
+    MTP_TRY(launch_gemv(u, h->lmt, 1, s, &grid));
+    if (grid < 1 || static_cast<size_t>(grid) > amax_parts(c)) return MTP_E_UNSUPPORTED;
+  }
   const int H = c.hidden, D = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, I = c.intermediate;
   const int qkv_rows = (hq + 2 * hkv) * D;
   float* x = reinterpret_cast<float*>(wsp(ws, L.x));
@@ -359,7 +388,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   r.q_norm = h->w.q_norm; r.k_norm = h->w.k_norm; r.nw_bf16 = h->wt == W_BF16;
   r.eps = c.rms_eps; r.theta = c.rope_theta; r.hq = hq; r.hkv = hkv; r.d = D;
   r.kc = kv->k; r.vc = kv->v; r.kv_bf16 = c.kv_dtype == MTP_BF16; r.capacity = kv->capacity;
-  r.state = kv->state; r.n_max = n_max; r.n_dev = n_dev;
+  r.state = kv->state; r.n_max = n_max; r.n_dev = n_dev; r.n_min = n_min;
   // LAST mode: the norm/RoPE/append runs inside the attention kernel
   const bool fuse_rope = mode == MTP_FLUSH_LAST;
   if (!fuse_rope) MTP_TRY(launch_rope_append(r, s));
@@ -378,7 +407,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   AttnArgs t;
   std::memset(&t, 0, sizeof(t));
   t.q = qr; t.kc = kv->k; t.vc = kv->v; t.kv_bf16 = c.kv_dtype == MTP_BF16; t.capacity = kv->capacity;
-  t.state = kv->state; t.hq = hq; t.hkv = hkv; t.d = D; t.n_max = n_max; t.n_dev = n_dev;
+  t.state = kv->state; t.hq = hq; t.hkv = hkv; t.d = D; t.n_max = n_max; t.n_dev = n_dev; t.n_min = n_min;
   t.row_sel = rsel; t.nchunk = L.nchunk;
   if (fuse_rope) {
     t.fuse_rope = 1; t.qkv = qkv; t.ld_qkv = qkv_rows; t.q_norm = h->w.q_norm; t.k_norm = h->w.k_norm;
@@ -457,18 +486,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   }
 
   // 8. logits = W_lm RMSNorm(g; w_norm) of the last row, with its argmax
-  a = base_gemv(h, kv);
-  a.w[0] = h->w.lm_head; a.m[0] = c.vocab; a.M = c.vocab; a.K = H; a.lpr = lpr_unembed(H, h->lmt);
-  a.scales = static_cast<const uint16_t*>(h->w.lm_head_scales);
-  a.n_max = n_max; a.n_dev = n_dev;
-  a.in_mode = IN_RMS; a.x = g; a.ldx = H; a.nw = h->w.norm;
-  a.out_mode = OUT_LOGITS; a.logits = logits;
-  a.amax_part = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax));
+  a = unembed_args(h, kv, L, n_max, n_dev, g, logits, ws);
   int tslot = -1, grid = 0;
   time_mark(TIME_UNEMBED, true, s, &tslot);
-  MTP_TRY(run_gemv(a, h->lmt, 1, ROW_LAST, s, &grid, -1));
+  MTP_TRY(launch_gemv(a, h->lmt, 1, s, &grid));
   time_mark(TIME_UNEMBED, false, s, &tslot);
-  if (static_cast<size_t>(grid) > amax_parts(c)) return MTP_E_UNSUPPORTED;   // cannot happen: sized above
   // 9. argmax of the partial keys, commit the append (len, round base)
   f.parts = a.amax_part; f.nparts = grid; f.amax_out = argmax;
   MTP_TRY(launch_finish(f, s));
@@ -584,8 +606,9 @@ int mtp_draft_chain(const mtp_head* head, const mtp_kv* kv, const int32_t* pend_
   const size_t row_bytes = static_cast<size_t>(c.hidden) * (c.act_dtype == MTP_BF16 ? 2 : 4);
   char* hout = static_cast<char*>(hiddens_out_dev);
   // the flush of the pending pairs gives d_0 and g_0
+  // (a pending count of 0 is a device error here: a round always has a pending pair)
   st = head_forward(head, kv, pend_tokens_dev, pend_hiddens_dev, n_max, n_dev, MTP_FLUSH_LAST, 1, hout,
-                    draft_logits_dev, drafts_dev, ws, stream);
+                    draft_logits_dev, drafts_dev, ws, stream, 1);
   if (st != MTP_OK) return st;
   // chained steps: (d_{i-1}, g_{i-1}) -> d_i, g_i
   for (int i = 1; i < n_draft; ++i) {

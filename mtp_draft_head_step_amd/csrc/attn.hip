@@ -23,7 +23,7 @@ __global__ __launch_bounds__(64) void k_rope_append(RopeArgs a) {
   if (st[3] != 0) return;
   const int ndev = a.n_dev ? *a.n_dev : a.n_max;
   const int len0 = st[0];
-  const bool bad_count = ndev < 0 || ndev > a.n_max;
+  const bool bad_count = ndev < a.n_min || ndev < 0 || ndev > a.n_max;
   const int n = bad_count ? 0 : ndev;
   if (bad_count || len0 + n > a.capacity) {
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   if constexpr (FUSE) {
     // the append's checks (once per launch, by the first workgroup)
     const int ndev = a.n_dev ? *a.n_dev : a.n_max;
-    const bool bad_count = ndev < 0 || ndev > a.n_max;
+    const bool bad_count = ndev < a.n_min || ndev < 0 || ndev > a.n_max;
     if (bad_count || st[0] + ndev > a.capacity) {
       if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) st[3] = bad_count ? 3 : 1;
       return;

@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 kernels: bf16 conversion, wave64
-// reductions, orderable argmax keys, the grid-completion ticket.
+// reductions, orderable argmax keys, the RoPE angle.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -17,6 +17,10 @@
 //  * no workgroup waits for or signals another: on gfx950 a device-scope fence
 //    writes back and invalidates the XCD's L2, which costs far more than the
 //    extra one-workgroup kernel that merges the partial keys.
+#include <map>
+#include <mutex>
+#include <set>
+#include <tuple>
 #include <type_traits>
 
 #include "common.h"
@@ -27,7 +31,6 @@ namespace mtp {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;   // 16-byte loads per slot in flight
-constexpr int kCUs = 256;
 constexpr int kMaxLds = 144 * 1024;   // dynamic LDS a GEMV may ask for
 
 template <int WT> struct WTraits;
@@ -498,7 +501,61 @@ struct GemvTuning {
   int few_rows = 6144;
   int long_k = 12288;
 };
-GemvTuning g_gemv_tuning;
+constexpr GemvTuning kGemvTuning{};
+
+// Launch facts per device, behind one lock: the compute-unit count, a kernel's
+// occupancy at a dynamic LDS size, and whether its dynamic LDS limit was raised.
+struct LaunchFacts {
+  std::mutex mu;
+  std::map<int, int> cus;
+  std::map<std::tuple<int, const void*, size_t>, int> occ;
+  std::set<std::pair<int, const void*>> raised;
+};
+LaunchFacts& launch_facts() {
+  static LaunchFacts f;
+  return f;
+}
+
+// Workgroups of `fn` (256 threads, `lds` bytes of dynamic LDS) that fit on one
+// compute unit of the current device, and that device's compute units.
+hipError_t occupancy_of(const void* fn, size_t lds, int* per_cu, int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  LaunchFacts& f = launch_facts();
+  std::lock_guard<std::mutex> lk(f.mu);
+  auto c = f.cus.find(dev);
+  if (c == f.cus.end()) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    c = f.cus.emplace(dev, n > 0 ? n : 1).first;
+  }
+  *cus = c->second;
+  const auto key = std::make_tuple(dev, fn, lds);
+  auto o = f.occ.find(key);
+  if (o == f.occ.end()) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, lds) != hipSuccess || n < 1)
+      n = static_cast<int>((160 * 1024) / (lds + 2048));
+    o = f.occ.emplace(key, n < 1 ? 1 : n).first;
+  }
+  *per_cu = o->second;
+  return hipSuccess;
+}
+
+// Allow `fn` up to kMaxLds of dynamic LDS on the current device (once).
+hipError_t raise_lds_limit(const void* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  LaunchFacts& f = launch_facts();
+  std::lock_guard<std::mutex> lk(f.mu);
+  if (f.raised.count({dev, fn})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  if (e == hipSuccess) f.raised.insert({dev, fn});
+  return e;
+}
 
 template <int WT, int NR, int RPW, bool TWO, bool WSK = false>
 static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int max_per_cu) {
@@ -510,33 +567,23 @@ static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int
   const int nblocks = (a.M + rows_per_wg - 1) / rows_per_wg;
   const size_t lds = static_cast<size_t>(NR) * a.kp * (XB ? 2 : 4);
   int grid = nblocks;
+  const void* fn = reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO, XB, WSK>);
   if (a.grid_stride) {
     // workgroups per CU: the kernel's real occupancy (registers and LDS) at this
     // LDS size, capped by the tuning
-    static int occ_lds = -1, occ_val = 1;
-    if (occ_lds != static_cast<int>(lds)) {
-      int o = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_gemv<WT, NR, RPW, TWO, XB, WSK>, kThreads, lds) !=
-              hipSuccess || o < 1)
-        o = static_cast<int>((160 * 1024) / (lds + 2048));
-      occ_lds = static_cast<int>(lds);
-      occ_val = o;
-    }
-    int occ = occ_val;
+    int occ = 1, cus = 1;
+    const hipError_t e = occupancy_of(fn, lds, &occ, &cus);
+    if (e != hipSuccess) return e;
     occ = occ < 1 ? 1 : (occ > max_per_cu ? max_per_cu : occ);
-    const int cap = kCUs * occ;
+    const int cap = cus * occ;
     const int per = (nblocks + cap - 1) / cap;          // row blocks per workgroup
     grid = (nblocks + per - 1) / per;
   }
   if (grid_out) *grid_out = grid;
+  if (a.dry_run) return hipSuccess;
   if (lds > 64 * 1024) {   // gfx950 gives a workgroup up to 160 KB of LDS on request
-    static bool raised = false;
-    if (!raised) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO, XB, WSK>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+    const hipError_t e = raise_lds_limit(fn);
+    if (e != hipSuccess) return e;
   }
   (void)hipGetLastError();
   hipLaunchKernelGGL((k_gemv<WT, NR, RPW, TWO, XB, WSK>), dim3(grid), dim3(kThreads), lds, s, a);
@@ -545,7 +592,7 @@ static hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int
 
 template <int WT, int NR>
 static hipError_t launch_r(const GemvArgs& a, hipStream_t s, int* g) {
-  const GemvTuning& t = g_gemv_tuning;
+  const GemvTuning& t = kGemvTuning;
   const bool swiglu = a.out_mode == OUT_SWIGLU;
   int rpw, per_cu, wsk;
   if (a.in_mode == IN_EMBED) { rpw = t.rpw_embed; per_cu = t.wg_per_cu_embed; wsk = t.wsk_embed; }

@@ -60,6 +60,7 @@ struct GemvArgs {
   float* logits;           // OUT_LOGITS (nullable)
   unsigned long long* amax_part;  // OUT_LOGITS: one argmax key per workgroup
   const int32_t* kv_state; // nullable: skip everything when state[3] != 0
+  int dry_run;             // compute the launch shape only (*grid_out), enqueue nothing
 };
 
 // *grid_out (nullable) receives the number of workgroups launched.
@@ -156,6 +157,7 @@ struct RopeArgs {
   int32_t* state;
   int n_max;
   const int32_t* n_dev;
+  int n_min;               // a device count below n_min (or above n_max) sets MTP_DEV_COUNT
 };
 hipError_t launch_rope_append(const RopeArgs& a, hipStream_t s);
 
@@ -170,6 +172,7 @@ struct AttnArgs {
   int hq, hkv, d;
   int n_max;
   const int32_t* n_dev;
+  int n_min;               // fuse_rope: a device count below n_min sets MTP_DEV_COUNT
   int row_sel;             // ROWS_RANGE: rows 0..n-1; ROW_LAST: row n-1
   int nchunk;              // chunks per (row, kv head)
   int mfma;                // ROWS_RANGE over bf16 K/V: the matrix-core flush kernel

@@ -55,7 +55,7 @@ def run_round(st: RoundState, n_draft: int, target_fn, sp: Sampling = GREEDY,
     """Run one round in place.  ``target_fn(tokens_in, start_pos)`` returns
     (logits [N + 1, V] fp32, hiddens [N + 1, H]) for tokens_in = [current] + drafts
     processed at positions start_pos + j.  Returns a dict with the drafts, k, the
-    committed tokens and each draft step's logits.
+    committed tokens and each draft step's logits and hidden output g.
 
     ``forced_drafts`` (comparisons only) replaces each step's argmax by the given
     token when the chain continues, so a run can follow another implementation
@@ -70,11 +70,13 @@ def run_round(st: RoundState, n_draft: int, target_fn, sp: Sampling = GREEDY,
     drafts = [pick(0, out)]
     draft_logits = [out["logits"]]
     g = out["g"][-1]
+    draft_g = [g]
     for i in range(1, n_draft):
         o = head.step(kv, drafts[-1], g)
         drafts.append(pick(i, o))
         draft_logits.append(o["logits"])
         g = o["g"][-1]
+        draft_g.append(g)
     c = len(st.committed) - 1                    # position of the current token
     rows, hid_rows = target_fn([st.committed[-1]] + drafts, c)
     draft_rows = draft_rows_fn(drafts) if draft_rows_fn is not None else None
@@ -91,7 +93,7 @@ def run_round(st: RoundState, n_draft: int, target_fn, sp: Sampling = GREEDY,
         raise ValueError(policy)
     st.pending = [(committed[j], hid_rows[j]) for j in range(j0, k + 1)]
     st.committed.extend(committed)
-    return {"drafts": drafts, "k": k, "tokens": committed, "draft_logits": draft_logits}
+    return {"drafts": drafts, "k": k, "tokens": committed, "draft_logits": draft_logits, "draft_g": draft_g}
 
 
 def classic_greedy(target_fn, committed, n_new: int, sp: Sampling = GREEDY, ring=None, ring_state=None):

@@ -23,7 +23,8 @@ from mtp_draft_head_step_amd import inputs as I
 from oracle import head as OH
 from oracle import rounds as R
 from oracle.kvcache import DraftKV
-from tests.gpu_util import argmax_ok, device_array, host, kv_pair, rel_err, tol_of
+from tests.gpu_util import (argmax_ok, assert_vectors, compare_rounds, device_array, host, kv_pair,
+                            rel_err, tol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,8 +55,9 @@ def _qwen_kv(q):
 
 
 def _check_slots(gkv, okv, lo, hi, tol):
-    assert rel_err(host(gkv.k)[:, lo:hi], okv.K[:, lo:hi]) <= tol
-    assert rel_err(host(gkv.v)[:, lo:hi], okv.V[:, lo:hi]) <= tol
+    """Every K and V entry of slots [lo, hi), per head and slot."""
+    assert_vectors(host(gkv.k)[:, lo:hi], okv.K[:, lo:hi], tol, "K")
+    assert_vectors(host(gkv.v)[:, lo:hi], okv.V[:, lo:hi], tol, "V")
 
 
 @pytest.mark.timeout(600)
@@ -176,6 +178,31 @@ def test_qwen27b_flush256_parity(qwen):
     g = host(hout)
     for i, r in enumerate(rows):
         assert rel_err(g[r], ref["g"][i]) <= tol, r
+
+
+@pytest.mark.timeout(1200)
+def test_qwen27b_rounds_parity(qwen):
+    """Whole greedy rounds at the 27B shape (two drafts, policy A), launched as
+    the benchmark launches them.  Acceptance is planted so the rounds commit 1,
+    2, 3 and 1 tokens: the rounds' flushes take 1, 1, 2 and 3 pending pairs with
+    the device count from the previous verify, so the one-, two- and three-row
+    flushes all run through mtp_draft_chain, spec_verify and kv_rollback.  Each
+    round is compared with the oracle (draft logits and hiddens, drafts, k,
+    tokens, KV lengths, every appended K/V entry)."""
+    s, gh, oh = qwen["shape"], qwen["gh"], qwen["oh"]
+    gkv, okv = _qwen_kv(qwen)
+    N = 2
+    plan = [0, 1, 2, 0]
+    committed = I.tokens_uniform(I.WL_QWEN, 910, QWEN_CTX + 2, s.vocab)
+    hid0 = I.target_hiddens(s, I.WL_QWEN, 911, 1)[0]
+
+    def targets(rnd, drafts):
+        rows = I.logits_rows(I.WL_QWEN, 5, (912, rnd), N + 1, s.vocab, 3.0)[0]
+        I.plant_acceptance(rows, np.asarray(drafts, np.int64), plan[rnd])
+        return rows, I.target_hiddens(s, I.WL_QWEN, (913, rnd), N + 1)
+
+    ks, near = compare_rounds(gh, oh, gkv, okv, s, committed, hid0, N, targets, len(plan))
+    assert ks == plan and near <= 1
 
 
 @pytest.fixture(scope="module")

@@ -1,10 +1,16 @@
 """GPU parity of sampled verification (temperature > 0) against the oracle.
 
-Given identical inputs, k and the committed tokens must be equal; the oracle
-reports the smallest decision margin on the path it took (top-p crossing,
-accept test, inverse-CDF step), and rounds whose margin is below 2e-5 are fp32
-vs fp64 boundary cases where either outcome is correct: there the GPU result
-must still be a valid outcome (its tokens in the right supports)."""
+Given identical inputs, k, the committed tokens, the history ring and its state
+must be equal.  The oracle reports the smallest decision margin on the path it
+took (top-p crossing, accept test, inverse-CDF step); a round whose margin is
+below the band is an fp32-vs-fp64 boundary case where more than one outcome is
+correct.  Such a round is still checked in full: every accept decision the GPU
+took must be consistent with the oracle's p and q (or lie inside the band), the
+final token must lie in the support of normalise(max(0, p_k - q_k)) (p_k if that
+is empty; p_N for the bonus), where a top-p cut inside the band admits the cut
+one token either side, and the ring and its state must equal the oracle's push
+of the GPU's own tokens.  The number of boundary rounds is fixed by the oracle
+alone (seeded inputs) and each test bounds it by the count the oracle flags."""
 import numpy as np
 import pytest
 
@@ -13,6 +19,7 @@ torch = pytest.importorskip("torch")
 from mtp_draft_head_step_amd import inputs as I
 from oracle import verify as OV
 from tests.gpu_util import device_array, host
+from tests.verify_checks import check_boundary
 
 pytestmark = pytest.mark.gpu
 MARGIN = 2e-5
@@ -49,9 +56,7 @@ def check(sp_o, sp_g, rows, drows, d, ring, st, u, margin=MARGIN):
     ref = OV.verify(sp_o, rows, drows, d, ring, st, u)
     got = gpu_verify(sp_g, rows, drows, d, ring, st, u)
     if ref["margin"] < margin:
-        # a boundary case: either outcome is correct, but it must be a well-formed one
-        k = got["k"]
-        assert 0 <= k <= len(d) and got["count"] == k + 1 and got["tokens"][:k] == list(d[:k])
+        check_boundary(sp_o, rows, drows, d, ring, st, u, got, margin)
         return ref, got, True
     assert got["k"] == ref["k"], (got, ref["k"], ref["tokens"])
     assert got["tokens"] == ref["tokens"]
@@ -82,7 +87,9 @@ def test_verify_workload_parity(coverage):
         ref, got, near = check(sp_o, sp_g, rows, drows, d, ring, st, u)
         flagged += near
         ks.append(ref["k"])
-    assert flagged <= 4
+    print(f"boundary rounds: {flagged} of 12")
+    # the oracle flags round 9 (independent drafts) and rounds 8 and 9 (coverage)
+    assert flagged <= (2 if coverage else 1)
     if coverage:
         assert max(ks) >= 2          # the accept paths ran
 
@@ -114,7 +121,7 @@ def test_sampled_parity_sweep(vocab, params, n):
         u = rng.random(n + 1).astype(np.float32)
         _, _, near = check(sp_o, sp_g, base, drows if n else np.zeros((0, vocab), np.float32), d, ring, st, u)
         flagged += near
-    assert flagged <= 3
+    assert flagged <= 1                      # at most one flagged round per case (oracle, seeded)
 
 
 # top_k = 0 (the whole vocabulary) or past what the per-chunk candidates hold:
@@ -153,7 +160,7 @@ def test_sampled_full_vocab_parity(vocab, params, n):
         _, _, near = check(sp_o, sp_g, base, drows if n else np.zeros((0, vocab), np.float32), d, ring, st, u,
                            margin=FULL_MARGIN)
         flagged += near
-    assert flagged <= 3
+    assert flagged <= 1                      # at most one flagged round per case (oracle, seeded)
 
 
 def test_sampled_full_vocab_at_full_size():
@@ -175,7 +182,7 @@ def test_sampled_full_vocab_at_full_size():
         u = rng.random(n + 1).astype(np.float32)
         _, _, near = check(sp_o, sp_g, base, drows, d, ring, st, u, margin=FULL_MARGIN)
         flagged += near
-    assert flagged <= 2
+    assert flagged == 0                      # every margin of these rounds is above the band
 
 
 def test_identical_rows_always_accept():
