@@ -159,6 +159,24 @@ int mtp_draft_step(const mtp_head *head, const mtp_kv *kv, const int32_t *token_
                    const void *hidden_in_dev, void *hidden_out_dev, float *logits_dev,
                    int32_t *argmax_dev, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mtp_draft_step
+ * without a workspace argument.  Its scratch is a static array of
+ * MTP_STATIC_SCRATCH_BYTES held by the library on each device it runs on (for
+ * the life of the process); nothing is allocated and no allocating routine is
+ * called.  Arguments, results and device errors are those of mtp_draft_step.
+ * Returns MTP_E_WORKSPACE, before anything is enqueued, when the step needs more
+ * scratch than the array holds (mtp_workspace_bytes(cfg, 1, capacity) >
+ * MTP_STATIC_SCRATCH_BYTES; the 27B-shaped head at any capacity needs about
+ * 2 MiB).  Every call on one device shares that device's array: calls that may
+ * overlap on one device (two streams, two threads) race and give wrong results;
+ * order them on one stream.  No scratch value survives from one call to the
+ * next in any way that matters (each is written before it is read). */
+#define MTP_STATIC_SCRATCH_BYTES (4 << 20)
+int mtp_draft_step_static(const mtp_head *head, const mtp_kv *kv, const int32_t *token_dev,
+                          const void *hidden_in_dev, void *hidden_out_dev, float *logits_dev,
+                          int32_t *argmax_dev, hipStream_t stream);
+
 /* Pending-pair flush ("Facts", MTP drafting: pending pairs flush in batches of
  * up to 256): n complete pairs (tokens_dev[j], hiddens_dev[j]) are appended at
  * slots state[0] + j, causal within the batch and over the whole prefix.

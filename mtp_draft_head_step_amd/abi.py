@@ -31,7 +31,7 @@ WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
                  "up_proj", "down_proj", "norm")
 
 EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_destroy", "mtp_workspace_bytes",
-           "mtp_workspace_init", "mtp_draft_step", "mtp_flush_pairs", "mtp_draft_chain", "mtp_repair_pending",
+           "mtp_workspace_init", "mtp_draft_step", "mtp_draft_step_static", "mtp_flush_pairs", "mtp_draft_chain", "mtp_repair_pending",
            "spec_verify_workspace_bytes", "spec_verify", "kv_rollback", "mtp_timing_begin",
            "mtp_timing_pause", "mtp_timing_elapsed", "mtp_timing_end", "mtp_depth_ctl_create",
            "mtp_depth_ctl_destroy", "mtp_depth_ctl_next", "mtp_depth_ctl_report", "mtp_depth_ctl_state")
@@ -80,6 +80,8 @@ def _load():
     lib.mtp_workspace_init.argtypes = [vp, sz, vp]
     lib.mtp_draft_step.restype = C.c_int
     lib.mtp_draft_step.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mtp_draft_step_static.restype = C.c_int
+    lib.mtp_draft_step_static.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, vp, vp, vp, vp]
     lib.mtp_flush_pairs.restype = C.c_int
     lib.mtp_flush_pairs.argtypes = [vp, C.POINTER(mtp_kv), vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.mtp_draft_chain.restype = C.c_int
@@ -180,6 +182,12 @@ def mtp_draft_step(head, kv, token, hidden_in, hidden_out, logits, argmax, ws, s
                             _ptr(hidden_out), _ptr(logits), _ptr(argmax), _ptr(ws), ws.nbytes,
                             _stream(stream))
     _check(st, "mtp_draft_step")
+
+
+def mtp_draft_step_static(head, kv, token, hidden_in, hidden_out, logits, argmax, stream=None):
+    st = lib.mtp_draft_step_static(head.handle, C.byref(kv.desc), _ptr(token), _ptr(hidden_in),
+                                   _ptr(hidden_out), _ptr(logits), _ptr(argmax), _stream(stream))
+    _check(st, "mtp_draft_step_static")
 
 
 def mtp_flush_pairs(head, kv, tokens, hiddens, n_max, n_dev, out_mode, set_round_base,

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -569,6 +570,61 @@ int mtp_draft_step(const mtp_head* head, const mtp_kv* kv, const int32_t* token_
   if (ws_bytes < layout(head->cfg, 1, kv->capacity).total) return MTP_E_WORKSPACE;
   return head_forward(head, kv, token_dev, hidden_in_dev, 1, nullptr, MTP_FLUSH_LAST, 0,
                       hidden_out_dev, logits_dev, argmax_dev, ws, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The library's own scratch for mtp_draft_step_static: one array per device
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes `scratch` itself to a kernel -- in host code that
+// name is a stand-in, not a device address; the address comes from
+// hipGetSymbolAddress once per device and is kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[MTP_STATIC_SCRATCH_BYTES];
+
+namespace {
+struct ScratchTable {
+  std::mutex mu;
+  std::map<int, void*> addr;   // device ordinal -> address of that device's scratch
+} g_scratch;
+
+// The current device's scratch address (looked up on the first call there).
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  auto it = g_scratch.addr.find(dev);
+  if (it == g_scratch.addr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    it = g_scratch.addr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+int mtp_draft_step_static(const mtp_head* head, const mtp_kv* kv, const int32_t* token_dev,
+                          const void* hidden_in_dev, void* hidden_out_dev, float* logits_dev,
+                          int32_t* argmax_dev, hipStream_t stream) {
+  if (!head || !token_dev || !hidden_in_dev || !hidden_out_dev) return MTP_E_INVALID_ARG;
+  if (hidden_in_dev == hidden_out_dev) return MTP_E_INVALID_ARG;
+  int st = validate_kv(head, kv);
+  if (st != MTP_OK) return st;
+  // the step's scratch must fit the static array (host check, nothing enqueued)
+  if (layout(head->cfg, 1, kv->capacity).total > static_cast<size_t>(MTP_STATIC_SCRATCH_BYTES))
+    return MTP_E_WORKSPACE;
+  void* ws = nullptr;
+  MTP_TRY(static_scratch(&ws));
+  // every scratch value the step reads it first writes in the same call: no
+  // clearing is needed between calls
+  return head_forward(head, kv, token_dev, hidden_in_dev, 1, nullptr, MTP_FLUSH_LAST, 0, hidden_out_dev,
+                      logits_dev, argmax_dev, ws, stream);
 }
 
 int mtp_flush_pairs(const mtp_head* head, const mtp_kv* kv, const int32_t* tokens_dev,

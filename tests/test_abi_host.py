@@ -124,3 +124,20 @@ def test_verify_fails_closed():
     assert call(negative_k, 2, 100) == abi.MTP_E_INVALID_ARG
     bad_win = abi.sampling(window=0)
     assert call(bad_win, 2, 100, draft=None) == abi.MTP_E_INVALID_ARG
+
+
+def test_static_step_rejects_oversized_scratch_on_host():
+    """The no-workspace draft step refuses, before any HIP call, a step whose
+    scratch would not fit the library's static array (4 MiB per device)."""
+    big = I.HeadShape(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, intermediate=1 << 20, vocab=1024)
+    assert abi.lib.mtp_workspace_bytes(C.byref(abi.config_of(big)), 1, 256) > (4 << 20)
+    h = C.c_void_p()
+    assert abi.lib.mtp_head_create(C.byref(abi.config_of(big)), C.byref(fake_weights(big)), C.byref(h)) == 0
+    try:
+        kv = abi.mtp_kv(0x1000, 0x2000, 256, 0x3000)
+        st = abi.lib.mtp_draft_step_static(h, C.byref(kv), 0x4000, 0x5000, 0x6000, None, None, None)
+        assert st == abi.MTP_E_WORKSPACE
+        assert abi.lib.mtp_draft_step_static(None, C.byref(kv), 0x4000, 0x5000, 0x6000, None, None,
+                                             None) == abi.MTP_E_INVALID_ARG
+    finally:
+        abi.lib.mtp_head_destroy(h)
