@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmtp.so")
-SOURCES = ["gemv.hip", "gemm.hip", "attn.hip", "attn_mfma.hip", "verify.hip", "kv.hip", "api.cpp", "depth.cpp"]
+SOURCES = ["gemv_bf16_1.hip", "gemv_bf16_4.hip", "gemv_bf16_2.hip", "gemv_f32.hip", "gemv_i8.hip", "gemv.hip",
+           "gemm.hip", "attn.hip", "attn_mfma.hip", "verify.hip", "kv.hip", "api.cpp", "depth.cpp"]
 ARCH = os.environ.get("MTP_OFFLOAD_ARCH", "gfx950")
 
 
@@ -44,7 +45,7 @@ def build(verbose: bool = False) -> str:
             print(r.stderr, file=sys.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(min(os.cpu_count() or 8, 16, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
