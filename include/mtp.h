@@ -115,6 +115,7 @@ enum { MTP_FLUSH_KV_ONLY = 0, MTP_FLUSH_LAST = 1, MTP_FLUSH_ALL = 2 };
 #define MTP_TO_ROUND_BASE (-1)
 #define MTP_MAX_FLUSH 256  /* pending-pair flush cap ("Facts": flush batches of up to 256) */
 #define MTP_MAX_DRAFT 16   /* drafts per verify */
+#define MTP_MAX_BATCH 16   /* sessions per batched call */
 
 /* Library infrastructure (no passage of the pages defines these): the name of a
  * status code (static string, never NULL; "MTP_E_UNKNOWN" for other values). */
@@ -224,6 +225,75 @@ int mtp_repair_pending(const int32_t *out_tokens_dev, const int32_t *out_counts_
                        const void *target_hiddens_dev, int32_t hidden, int32_t act_dtype, int32_t n_draft,
                        int32_t *pend_tokens_dev, void *pend_hiddens_dev, int32_t *pend_count_dev,
                        hipStream_t stream);
+
+/* ---- B > 1 independent sessions with ragged acceptance ------------------
+ * ("feat(inference): support the qwen3_5_mtp drafter ...": section "Upstream
+ * contract to port" advertises ragged batch acceptance, "Implementation plan"
+ * and "Acceptance criteria" gate B > 1 behind ragged-acceptance tests, and the
+ * #1174 comment trims each row by its own accepted count.)
+ * A batch of B sessions (1 <= B <= MTP_MAX_BATCH) shares one draft-KV
+ * allocation: mtp_kv.k and .v hold [B, n_kv_heads, capacity, head_dim] (session
+ * b's cache starts b * n_kv_heads * capacity * head_dim elements in) and
+ * mtp_kv.state holds [B, 4] state words, one {len, round_base, -, err} per
+ * session.  Every session keeps its own length, so sessions that accepted
+ * different numbers of drafts simply sit at different slots: nothing is padded
+ * and no tail needs zeroing (a slot past a session's length is never read).
+ * Weights stream once per launch for every session's rows.  Device errors are
+ * per session: a set error word makes that session's rows no-ops while the
+ * other sessions proceed.  Per-session arrays are session-major. */
+
+/* Workspace bytes for mtp_draft_chain_batch with `batch` sessions of at most
+ * max_rows pending pairs each on caches of at most max_capacity slots. */
+size_t mtp_batch_workspace_bytes(const mtp_head_config *cfg, int32_t batch, int32_t max_rows,
+                                 int32_t max_capacity);
+
+/* mtp_draft_chain for `batch` sessions in one call: one flush of every
+ * session's pending pairs (LAST mode, round base recorded per session), then
+ * n_draft - 1 chained steps with one row per session.  pend_tokens_dev int32
+ * [batch, n_max]; pend_hiddens_dev [batch, n_max, hidden] (act dtype); session
+ * b flushes min(n_dev[b * n_dev_stride], n_max) pairs (n_dev nullable: n_max
+ * each; a count of 0, below 0 or above n_max sets that session's error word to
+ * MTP_DEV_COUNT).  Outputs: drafts_dev int32 [batch, n_draft];
+ * hiddens_out_dev [batch, n_draft, hidden]; draft_logits_dev (nullable) fp32
+ * [batch, n_draft, vocab].  With the pending pairs taken straight from
+ * spec_verify_batch's outputs (tokens [batch, n_draft + 1], target hiddens
+ * [batch, n_draft + 1, hidden], n_max = n_draft + 1) the counts are
+ * out_counts + 1 with n_dev_stride 2.  Returns MTP_E_UNSUPPORTED for shapes the
+ * batched kernels do not take. */
+int mtp_draft_chain_batch(const mtp_head *head, const mtp_kv *kv, int32_t batch,
+                          const int32_t *pend_tokens_dev, const void *pend_hiddens_dev, int32_t n_max,
+                          const int32_t *n_dev, int32_t n_dev_stride, int32_t n_draft, int32_t *drafts_dev,
+                          void *hiddens_out_dev, float *draft_logits_dev, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* spec_verify for `batch` independent sessions in one launch sequence: every
+ * array of spec_verify gains a leading [batch] dimension (target logits
+ * [batch, n_draft + 1, vocab], draft logits [batch, n_draft, vocab], drafts
+ * [batch, n_draft], history [batch, window], history state [batch, 2],
+ * uniforms [batch, n_draft + 1], out_tokens [batch, n_draft + 1], out_counts
+ * [batch, 2]); each session accepts its own k.  ws_bytes >= batch *
+ * spec_verify_workspace_bytes(n_draft, vocab). */
+int spec_verify_batch(const spec_sampling *sp, int32_t batch, int32_t n_draft, int32_t vocab,
+                      const float *target_logits_dev, const float *draft_logits_dev,
+                      const int32_t *draft_tokens_dev, int32_t *history_dev, int32_t *history_state_dev,
+                      const float *uniforms_dev, int32_t *out_tokens_dev, int32_t *out_counts_dev, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* kv_rollback for `batch` sessions: each session's length moves on its own
+ * (to_len >= 0 for every session, or MTP_TO_ROUND_BASE to its own round base;
+ * with counts_dev = spec_verify_batch's out_counts [batch, 2] each session
+ * keeps min(k_b, n_draft - 1) chained entries). */
+int kv_rollback_batch(const mtp_kv *kv, int32_t batch, int32_t to_len, const int32_t *counts_dev,
+                      int32_t n_draft, hipStream_t stream);
+
+/* mtp_repair_pending for `batch` sessions (out_tokens [batch, n_draft + 1],
+ * out_counts [batch, 2], target hiddens [batch, n_draft + 1, hidden]; pending
+ * tokens [batch, n_draft + 1], hiddens [batch, n_draft + 1, hidden], counts
+ * [batch], so the next mtp_draft_chain_batch takes n_dev_stride 1). */
+int mtp_repair_pending_batch(int32_t batch, const int32_t *out_tokens_dev, const int32_t *out_counts_dev,
+                             const void *target_hiddens_dev, int32_t hidden, int32_t act_dtype, int32_t n_draft,
+                             int32_t *pend_tokens_dev, void *pend_hiddens_dev, int32_t *pend_counts_dev,
+                             hipStream_t stream);
 
 /* Workspace bytes for spec_verify with n_draft drafts over vocab logits. */
 size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab);

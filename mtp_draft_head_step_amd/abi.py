@@ -34,6 +34,8 @@ EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_d
            "mtp_workspace_init", "mtp_draft_step", "mtp_draft_step_static", "mtp_flush_pairs", "mtp_draft_chain", "mtp_repair_pending",
            "spec_verify_workspace_bytes", "spec_verify", "kv_rollback", "mtp_timing_begin",
            "mtp_timing_pause", "mtp_timing_elapsed", "mtp_timing_end", "mtp_depth_ctl_create",
+           "mtp_batch_workspace_bytes", "mtp_draft_chain_batch", "spec_verify_batch", "kv_rollback_batch",
+           "mtp_repair_pending_batch",
            "mtp_depth_ctl_destroy", "mtp_depth_ctl_next", "mtp_depth_ctl_report", "mtp_depth_ctl_state")
 
 
@@ -92,6 +94,18 @@ def _load():
     lib.spec_verify_workspace_bytes.argtypes = [i32, i32]
     lib.spec_verify.restype = C.c_int
     lib.spec_verify.argtypes = [C.POINTER(spec_sampling), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mtp_batch_workspace_bytes.restype = sz
+    lib.mtp_batch_workspace_bytes.argtypes = [C.POINTER(mtp_head_config), i32, i32, i32]
+    lib.mtp_draft_chain_batch.restype = C.c_int
+    lib.mtp_draft_chain_batch.argtypes = [vp, C.POINTER(mtp_kv), i32, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp,
+                                          sz, vp]
+    lib.spec_verify_batch.restype = C.c_int
+    lib.spec_verify_batch.argtypes = [C.POINTER(spec_sampling), i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      sz, vp]
+    lib.kv_rollback_batch.restype = C.c_int
+    lib.kv_rollback_batch.argtypes = [C.POINTER(mtp_kv), i32, i32, vp, i32, vp]
+    lib.mtp_repair_pending_batch.restype = C.c_int
+    lib.mtp_repair_pending_batch.argtypes = [i32, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     lib.kv_rollback.restype = C.c_int
     lib.kv_rollback.argtypes = [C.POINTER(mtp_kv), i32, vp, i32, vp]
     lib.mtp_timing_begin.restype = C.c_int
@@ -231,6 +245,41 @@ def kv_rollback(kv, to_len, n_accepted=None, n_draft=0, stream=None):
     _check(st, "kv_rollback")
 
 
+def mtp_batch_workspace_bytes(cfg: mtp_head_config, batch: int, max_rows: int, max_capacity: int) -> int:
+    return lib.mtp_batch_workspace_bytes(C.byref(cfg), int(batch), int(max_rows), int(max_capacity))
+
+
+def mtp_draft_chain_batch(head, kv, batch, pend_tokens, pend_hiddens, n_max, n_dev, n_dev_stride, n_draft, drafts,
+                          hiddens_out, draft_logits, ws, stream=None):
+    st = lib.mtp_draft_chain_batch(head.handle, C.byref(kv.desc), int(batch), _ptr(pend_tokens), _ptr(pend_hiddens),
+                                   int(n_max), _ptr(n_dev), int(n_dev_stride), int(n_draft), _ptr(drafts),
+                                   _ptr(hiddens_out), _ptr(draft_logits), _ptr(ws), ws.nbytes, _stream(stream))
+    _check(st, "mtp_draft_chain_batch")
+
+
+def spec_verify_batch(sp: spec_sampling, batch, n_draft, vocab, target_logits, draft_logits, draft_tokens,
+                      history, history_state, uniforms, out_tokens, out_counts, ws, stream=None):
+    st = lib.spec_verify_batch(C.byref(sp), int(batch), int(n_draft), int(vocab), _ptr(target_logits),
+                               _ptr(draft_logits), _ptr(draft_tokens), _ptr(history), _ptr(history_state),
+                               _ptr(uniforms), _ptr(out_tokens), _ptr(out_counts), _ptr(ws), ws.nbytes,
+                               _stream(stream))
+    _check(st, "spec_verify_batch")
+
+
+def kv_rollback_batch(kv, batch, to_len, counts=None, n_draft=0, stream=None):
+    st = lib.kv_rollback_batch(C.byref(kv.desc), int(batch), int(to_len), _ptr(counts), int(n_draft),
+                               _stream(stream))
+    _check(st, "kv_rollback_batch")
+
+
+def mtp_repair_pending_batch(batch, out_tokens, out_counts, target_hiddens, hidden, act_dtype, n_draft, pend_tokens,
+                             pend_hiddens, pend_counts, stream=None):
+    st = lib.mtp_repair_pending_batch(int(batch), _ptr(out_tokens), _ptr(out_counts), _ptr(target_hiddens),
+                                      int(hidden), int(act_dtype), int(n_draft), _ptr(pend_tokens),
+                                      _ptr(pend_hiddens), _ptr(pend_counts), _stream(stream))
+    _check(st, "mtp_repair_pending_batch")
+
+
 TIME_UNEMBED, TIME_ATTENTION, TIME_VERIFY, TIME_PROJECTION = 0, 1, 2, 3
 
 
@@ -353,6 +402,24 @@ class DraftKV:
             state.copy_(torch.tensor([length, length, 0, 0], dtype=torch.int32))
             self.state = state
         self.capacity = capacity
+        self.desc = mtp_kv(self.k.data_ptr(), self.v.data_ptr(), capacity, self.state.data_ptr())
+
+
+class BatchKV:
+    """The draft KV of ``batch`` independent sessions in one allocation: K, V
+    [batch, n_kv_heads, capacity, head_dim] and the state words [batch, 4]
+    ({len, base, -, err} per session)."""
+
+    def __init__(self, shape, batch: int, capacity: int, k=None, v=None, lengths=None, device="cuda"):
+        import torch
+        dt = torch.bfloat16 if shape.kv_dtype == "bf16" else torch.float32
+        size = (batch, shape.n_kv_heads, capacity, shape.head_dim)
+        self.k = to_device(k, device) if k is not None else torch.zeros(size, dtype=dt, device=device)
+        self.v = to_device(v, device) if v is not None else torch.zeros(size, dtype=dt, device=device)
+        assert tuple(self.k.shape) == size and self.k.dtype == dt
+        lengths = [0] * batch if lengths is None else [int(x) for x in lengths]
+        self.state = torch.tensor([[n, n, 0, 0] for n in lengths], dtype=torch.int32, device=device)
+        self.batch, self.capacity = batch, capacity
         self.desc = mtp_kv(self.k.data_ptr(), self.v.data_ptr(), capacity, self.state.data_ptr())
 
 

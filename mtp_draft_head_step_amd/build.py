@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmtp.so")
-SOURCES = ["gemv_bf16_1.hip", "gemv_bf16_4.hip", "gemv_bf16_2.hip", "gemv_f32.hip", "gemv_i8.hip", "gemv.hip",
+SOURCES = ["gemv_bf16_1.hip", "gemv_bf16_4.hip", "gemv_bf16_2.hip", "gemv_f32.hip", "gemv_i8.hip", "gemv_i8_n.hip", "gemv.hip",
            "gemm.hip", "attn.hip", "attn_mfma.hip", "verify.hip", "kv.hip", "api.cpp", "depth.cpp"]
 ARCH = os.environ.get("MTP_OFFLOAD_ARCH", "gfx950")
 

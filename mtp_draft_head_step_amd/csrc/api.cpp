@@ -138,7 +138,9 @@ int gemv_max_rows(const mtp_head_config& c) {
 // upper bound on the unembedding GEMV's workgroup count (one argmax key each)
 size_t amax_parts(const mtp_head_config& c) { return static_cast<size_t>(c.vocab) / 4 + 2048; }
 
-Layout layout(const mtp_head_config& c, int rows, int capacity) {
+// rows: workspace rows (every session's rows, flattened); slots: unembedding
+// rows of one launch (one per session), each with its own argmax keys
+Layout layout(const mtp_head_config& c, int rows, int capacity, int slots = 1) {
   Layout L{};
   const size_t H = c.hidden, D = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, I = c.intermediate;
   L.nchunk = nchunk_for(c, capacity);
@@ -153,7 +155,7 @@ Layout layout(const mtp_head_config& c, int rows, int capacity) {
   L.x1 = take(rows * H * 4);
   L.m = take(rows * I * 4);
   L.g = take(rows * H * 4);
-  L.amax = take(amax_parts(c) * 8);
+  L.amax = take(static_cast<size_t>(slots) * amax_parts(c) * 8);
   const bool mfma_rows = rows > gemv_max_rows(c);
   L.xa = mfma_rows ? take(rows * 2 * H * 2) : off;             // bf16 normalised rows (MFMA path)
   size_t part = 0;                                             // split partial sums (MFMA path)
@@ -205,12 +207,31 @@ int validate_kv(const mtp_head* h, const mtp_kv* kv) {
 
 inline char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
-GemvArgs base_gemv(const mtp_head* h, const mtp_kv* kv) {
+// Independent sessions in one call; batch 1 is the single-session path.  With
+// batch > 1 session b's K/V start b * kv_sb elements in and its state words at
+// state + 4 b; its pending token j is tokens[b * tok_sb + j], its hidden row
+// b * hid_sb + j and its count n_dev[b * ndev_sb]; its outputs (hidden, logits,
+// argmax) go to row b * out_sb of each output.  Workspace rows are flattened
+// b * n_max + j.
+struct Sessions {
+  int batch = 1;
+  int tok_sb = 0, hid_sb = 0, out_sb = 0, ndev_sb = 0;
+  long long kv_sb = 0;
+  bool multi() const { return batch > 1; }
+};
+const Sessions kOneSession{};
+
+// unembedding rows per launch (one per session; the GEMV row counts are 1, 2, 3, 4, 8, 16)
+int slots_of(const Sessions& ss) { return ss.multi() ? nr_for(ss.batch) : 1; }
+
+GemvArgs base_gemv(const mtp_head* h, const mtp_kv* kv, const Sessions& ss = kOneSession) {
   GemvArgs a;
   std::memset(&a, 0, sizeof(a));
   a.nw_bf16 = h->wt == W_BF16;
   a.eps = h->cfg.rms_eps;
   a.kv_state = kv->state;
+  a.batch = ss.batch;
+  a.tok_sb = ss.tok_sb; a.hid_sb = ss.hid_sb; a.out_sb = ss.out_sb; a.ndev_sb = ss.ndev_sb;
   return a;
 }
 
@@ -226,12 +247,14 @@ hipError_t timed_gemv(const GemvArgs& a, int wt, int nr, hipStream_t s, int* gri
 hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t s,
                     int* grid_out = nullptr, int kind = TIME_PROJECTION) {
   // ROWS_RANGE: blocks of up to 16 activation rows share one pass over the weights
+  // ROW_LAST: the last row of each session (one slot per session)
   a.row_sel = row_sel;
   if (row_sel == ROW_LAST) {
+    const int nr = a.batch > 1 ? nr_for(a.batch) : 1;
     a.row_base = 0;
-    a.kp = kp_for(a.K, wt, 1);
+    a.kp = kp_for(a.K, wt, nr);
     a.grid_stride = a.kp == a.K;
-    return timed_gemv(a, wt, 1, s, grid_out, kind);
+    return timed_gemv(a, wt, nr, s, grid_out, kind);
   }
   const int nr = nr_for(rows_total);
   a.kp = kp_for(a.K, wt, nr);
@@ -252,17 +275,21 @@ hipError_t timed_gemm(const GemmArgs& g, hipStream_t s, const RowNorm* rn = null
   return e;
 }
 
-GemmArgs base_gemm(const mtp_kv* kv, int n_max, const int32_t* n_dev, float* part) {
+// Several sessions: the products run over every flattened row (rows past a
+// session's count were prepared as zeros and are never read back).
+GemmArgs base_gemm(const mtp_kv* kv, int n_max, const int32_t* n_dev, float* part,
+                   const Sessions& ss = kOneSession) {
   GemmArgs g;
   std::memset(&g, 0, sizeof(g));
-  g.n_max = n_max;
-  g.n_dev = n_dev;
-  g.kv_state = kv->state;
+  g.n_max = ss.multi() ? ss.batch * n_max : n_max;
+  g.n_dev = ss.multi() ? nullptr : n_dev;
+  g.kv_state = ss.multi() ? nullptr : kv->state;
   g.part = part;
   return g;
 }
 
-PrepArgs base_prep(const mtp_head* h, const mtp_kv* kv, int n_max, const int32_t* n_dev, uint16_t* out) {
+PrepArgs base_prep(const mtp_head* h, const mtp_kv* kv, int n_max, const int32_t* n_dev, uint16_t* out,
+                   const Sessions& ss = kOneSession) {
   PrepArgs p;
   std::memset(&p, 0, sizeof(p));
   p.n_max = n_max;
@@ -271,15 +298,17 @@ PrepArgs base_prep(const mtp_head* h, const mtp_kv* kv, int n_max, const int32_t
   p.nw_bf16 = h->wt == W_BF16;
   p.eps = h->cfg.rms_eps;
   p.out = out;
+  p.batch = ss.batch;
+  p.tok_sb = ss.tok_sb; p.hid_sb = ss.hid_sb; p.ndev_sb = ss.ndev_sb;
   return p;
 }
 
 // The unembedding launch: logits = W_lm RMSNorm(g; w_norm) of the last row with
 // the per-workgroup argmax keys.
 GemvArgs unembed_args(const mtp_head* h, const mtp_kv* kv, const Layout& L, int n_max, const int32_t* n_dev,
-                      const float* g, float* logits, void* ws) {
+                      const float* g, float* logits, void* ws, const Sessions& ss = kOneSession) {
   const mtp_head_config& c = h->cfg;
-  GemvArgs a = base_gemv(h, kv);
+  GemvArgs a = base_gemv(h, kv, ss);
   a.w[0] = h->w.lm_head; a.m[0] = c.vocab; a.M = c.vocab; a.K = c.hidden; a.lpr = lpr_unembed(c.hidden, h->lmt);
   a.scales = static_cast<const uint16_t*>(h->w.lm_head_scales);
   a.n_max = n_max; a.n_dev = n_dev;
@@ -288,7 +317,7 @@ GemvArgs unembed_args(const mtp_head* h, const mtp_kv* kv, const Layout& L, int 
   a.amax_part = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax));
   a.row_sel = ROW_LAST;
   a.row_base = 0;
-  a.kp = kp_for(a.K, h->lmt, 1);
+  a.kp = kp_for(a.K, h->lmt, slots_of(ss));
   a.grid_stride = a.kp == a.K;
   return a;
 }
@@ -298,16 +327,21 @@ GemvArgs unembed_args(const mtp_head* h, const mtp_kv* kv, const Layout& L, int 
 // hidden_out: [1 or n, H] in act dtype (nullable).
 int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, const void* hiddens,
                  int n_max, const int32_t* n_dev, int mode, int set_base, void* hidden_out,
-                 float* logits, int32_t* argmax, void* ws, hipStream_t s, int n_min = 0) {
+                 float* logits, int32_t* argmax, void* ws, hipStream_t s, int n_min = 0,
+                 const Sessions& ss = kOneSession) {
   const mtp_head_config& c = h->cfg;
-  const Layout L = layout(c, n_max, kv->capacity);
+  const int rows_total = ss.multi() ? ss.batch * n_max : n_max;   // workspace rows
+  const int slots = slots_of(ss);
+  const Layout L = layout(c, rows_total, kv->capacity, slots);
+  if (ss.multi() && mode != MTP_FLUSH_LAST) return MTP_E_UNSUPPORTED;
   // host-checkable limits before anything is enqueued: the unembedding's
-  // workgroups each write one argmax key into a buffer of amax_parts entries
+  // workgroups each write one argmax key per slot into a buffer of amax_parts
+  // entries per slot
   if (mode != MTP_FLUSH_KV_ONLY) {
-    GemvArgs u = unembed_args(h, kv, L, n_max, n_dev, nullptr, nullptr, ws);
+    GemvArgs u = unembed_args(h, kv, L, n_max, n_dev, nullptr, nullptr, ws, ss);
     u.dry_run = 1;
     int grid = 0;
-    MTP_TRY(launch_gemv(u, h->lmt, 1, s, &grid));
+    MTP_TRY(launch_gemv(u, h->lmt, slots, s, &grid));
     if (grid < 1 || static_cast<size_t>(grid) > amax_parts(c)) return MTP_E_UNSUPPORTED;
   }
   const int H = c.hidden, D = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, I = c.intermediate;
@@ -322,7 +356,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   uint16_t* xa = reinterpret_cast<uint16_t*>(wsp(ws, L.xa));
   float* gpart = reinterpret_cast<float*>(wsp(ws, L.gpart));
   // many rows with bf16 weights: normalised rows + MFMA tiles instead of GEMV passes
-  const bool mfma = h->wt == W_BF16 && n_max > gemv_max_rows(c);
+  const bool mfma = h->wt == W_BF16 && rows_total > gemv_max_rows(c);
   if (mfma) {
     const int mq[3] = {hq * D, hkv * D, hkv * D};
     const int mh[1] = {H};
@@ -334,21 +368,21 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   // 1. x = W_fc [RMSNorm(E[t]) | RMSNorm(h)]
   bool normed_qkv = false, normed_mlp = false;
   if (mfma) {
-    PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+    PrepArgs p = base_prep(h, kv, n_max, n_dev, xa, ss);
     p.in_mode = IN_EMBED; p.K = 2 * H; p.ld_out = 2 * H;
     p.nw = h->w.pre_fc_norm_embedding; p.nw2 = h->w.pre_fc_norm_hidden;
     p.tok = tokens; p.vocab_tok = c.vocab; p.err = kv->state + 3;
     p.embed = h->w.embed; p.embed_bf16 = 1;
     p.hid = hiddens; p.hid_bf16 = c.act_dtype == MTP_BF16; p.ld_hid = H;
     MTP_TRY(launch_rows_prep(p, s));
-    GemmArgs m1 = base_gemm(kv, n_max, n_dev, gpart);
+    GemmArgs m1 = base_gemm(kv, n_max, n_dev, gpart, ss);
     m1.w[0] = static_cast<const uint16_t*>(h->w.fc); m1.m[0] = H; m1.M = H; m1.K = 2 * H;
     m1.a = xa; m1.lda = 2 * H; m1.out_mode = OUT_F32; m1.y = x; m1.ldy = H;
     // a split-K reduce also writes the q/k/v input rows, RMSNorm(x; w_in)
     const RowNorm rn{h->w.input_layernorm, h->wt == W_BF16, c.rms_eps, xa, H};
     MTP_TRY(timed_gemm(m1, s, &rn, &normed_qkv));
   }
-  GemvArgs a = base_gemv(h, kv);
+  GemvArgs a = base_gemv(h, kv, ss);
   a.w[0] = h->w.fc; a.m[0] = H; a.M = H; a.K = 2 * H; a.lpr = lpr_for(2 * H, h->wt);
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_EMBED; a.nw = h->w.pre_fc_norm_embedding; a.nw2 = h->w.pre_fc_norm_hidden;
@@ -356,23 +390,23 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.embed = h->w.embed; a.embed_bf16 = h->wt == W_BF16;
   a.hid = hiddens; a.hid_bf16 = c.act_dtype == MTP_BF16; a.ld_hid = H;
   a.out_mode = OUT_F32; a.y = x; a.ldy = H;
-  if (!mfma) MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
+  if (!mfma) MTP_TRY(run_gemv(a, h->wt, rows_total, ROWS_RANGE, s));
 
   // 2. q, k, v = W_{q,k,v} RMSNorm(x; w_in)
   if (mfma) {
     if (!normed_qkv) {
-      PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+      PrepArgs p = base_prep(h, kv, n_max, n_dev, xa, ss);
       p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x; p.ldx = H; p.nw = h->w.input_layernorm;
       MTP_TRY(launch_rows_prep(p, s));
     }
-    GemmArgs m2 = base_gemm(kv, n_max, n_dev, gpart);
+    GemmArgs m2 = base_gemm(kv, n_max, n_dev, gpart, ss);
     m2.w[0] = static_cast<const uint16_t*>(h->w.q_proj); m2.m[0] = hq * D;
     m2.w[1] = static_cast<const uint16_t*>(h->w.k_proj); m2.m[1] = hkv * D;
     m2.w[2] = static_cast<const uint16_t*>(h->w.v_proj); m2.m[2] = hkv * D;
     m2.M = qkv_rows; m2.K = H; m2.a = xa; m2.lda = H; m2.out_mode = OUT_F32; m2.y = qkv; m2.ldy = qkv_rows;
     MTP_TRY(timed_gemm(m2, s));
   }
-  a = base_gemv(h, kv);
+  a = base_gemv(h, kv, ss);
   a.w[0] = h->w.q_proj; a.m[0] = hq * D;
   a.w[1] = h->w.k_proj; a.m[1] = hkv * D;
   a.w[2] = h->w.v_proj; a.m[2] = hkv * D;
@@ -380,7 +414,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_RMS; a.x = x; a.ldx = H; a.nw = h->w.input_layernorm;
   a.out_mode = OUT_F32; a.y = qkv; a.ldy = qkv_rows;
-  if (!mfma) MTP_TRY(run_gemv(a, h->wt, n_max, ROWS_RANGE, s));
+  if (!mfma) MTP_TRY(run_gemv(a, h->wt, rows_total, ROWS_RANGE, s));
 
   // 3. q/k norm + RoPE, append K/V at slots len + j, advance len
   RopeArgs r;
@@ -396,6 +430,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   FinishArgs f;
   std::memset(&f, 0, sizeof(f));
   f.state = kv->state; f.n_max = n_max; f.n_dev = n_dev; f.set_base = set_base;
+  f.batch = ss.batch; f.out_sb = ss.out_sb; f.ndev_sb = ss.ndev_sb;
   if (mode == MTP_FLUSH_KV_ONLY) {
     MTP_TRY(launch_finish(f, s));
     return MTP_OK;
@@ -410,6 +445,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   t.q = qr; t.kc = kv->k; t.vc = kv->v; t.kv_bf16 = c.kv_dtype == MTP_BF16; t.capacity = kv->capacity;
   t.state = kv->state; t.hq = hq; t.hkv = hkv; t.d = D; t.n_max = n_max; t.n_dev = n_dev; t.n_min = n_min;
   t.row_sel = rsel; t.nchunk = L.nchunk;
+  t.batch = ss.batch; t.kv_sb = ss.kv_sb; t.ndev_sb = ss.ndev_sb;
   if (fuse_rope) {
     t.fuse_rope = 1; t.qkv = qkv; t.ld_qkv = qkv_rows; t.q_norm = h->w.q_norm; t.k_norm = h->w.k_norm;
     t.nw_bf16 = h->wt == W_BF16; t.eps = c.rms_eps; t.theta = c.rope_theta;
@@ -429,13 +465,13 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   MTP_TRY(launch_attention(t, s));
 
   // 5. x1 = x + W_o o
-  a = base_gemv(h, kv);
+  a = base_gemv(h, kv, ss);
   a.w[0] = h->w.o_proj; a.m[0] = H; a.M = H; a.K = hq * D; a.lpr = lpr_for(hq * D, h->wt);
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_F32; a.x = o; a.ldx = hq * D;
   a.out_mode = OUT_RESID; a.res = x; a.ldres = H; a.y = x1; a.ldy = H;
   if (mfma_out) {
-    GemmArgs m5 = base_gemm(kv, n_max, n_dev, gpart);
+    GemmArgs m5 = base_gemm(kv, n_max, n_dev, gpart, ss);
     m5.w[0] = static_cast<const uint16_t*>(h->w.o_proj); m5.m[0] = H; m5.M = H; m5.K = hq * D;
     m5.a = o; m5.lda = hq * D;
     m5.out_mode = OUT_RESID; m5.res = x; m5.ldres = H; m5.y = x1; m5.ldy = H;
@@ -443,11 +479,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     const RowNorm rn{h->w.post_attention_layernorm, h->wt == W_BF16, c.rms_eps, xa, H};
     MTP_TRY(timed_gemm(m5, s, &rn, &normed_mlp));
   } else {
-    MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+    MTP_TRY(run_gemv(a, h->wt, rows_total, rsel, s));
   }
 
   // 6. m = silu(W_g b) * (W_u b), b = RMSNorm(x1; w_post)
-  a = base_gemv(h, kv);
+  a = base_gemv(h, kv, ss);
   a.w[0] = h->w.gate_proj; a.m[0] = I; a.w[1] = h->w.up_proj; a.m[1] = I;
   a.M = I; a.K = H; a.lpr = lpr_for(H, h->wt);
   a.n_max = n_max; a.n_dev = n_dev;
@@ -455,42 +491,42 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.out_mode = OUT_SWIGLU; a.y = m; a.ldy = I;
   if (mfma_out) {
     if (!normed_mlp) {
-      PrepArgs p = base_prep(h, kv, n_max, n_dev, xa);
+      PrepArgs p = base_prep(h, kv, n_max, n_dev, xa, ss);
       p.in_mode = IN_RMS; p.K = H; p.ld_out = H; p.x = x1; p.ldx = H; p.nw = h->w.post_attention_layernorm;
       MTP_TRY(launch_rows_prep(p, s));
     }
-    GemmArgs m6 = base_gemm(kv, n_max, n_dev, gpart);
+    GemmArgs m6 = base_gemm(kv, n_max, n_dev, gpart, ss);
     m6.w[0] = static_cast<const uint16_t*>(h->w.gate_proj); m6.m[0] = I;
     m6.w[1] = static_cast<const uint16_t*>(h->w.up_proj); m6.m[1] = I;
     m6.M = I; m6.K = H; m6.a = xa; m6.lda = H; m6.out_mode = OUT_SWIGLU; m6.y = m; m6.ldy = I; m6.y_bf16 = 1;
     MTP_TRY(timed_gemm(m6, s));
   } else {
-    MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+    MTP_TRY(run_gemv(a, h->wt, rows_total, rsel, s));
   }
 
   // 7. g = x1 + W_d m  (also written to hidden_out in the activation dtype)
-  a = base_gemv(h, kv);
+  a = base_gemv(h, kv, ss);
   a.w[0] = h->w.down_proj; a.m[0] = H; a.M = H; a.K = I; a.lpr = lpr_for(I, h->wt);
   a.n_max = n_max; a.n_dev = n_dev;
   a.in_mode = IN_F32; a.x = m; a.ldx = I;
   a.out_mode = OUT_RESID; a.res = x1; a.ldres = H; a.y = g; a.ldy = H;
   a.y2 = hidden_out; a.y2_bf16 = c.act_dtype == MTP_BF16; a.ldy2 = H;
   if (mfma_out) {
-    GemmArgs m7 = base_gemm(kv, n_max, n_dev, gpart);
+    GemmArgs m7 = base_gemm(kv, n_max, n_dev, gpart, ss);
     m7.w[0] = static_cast<const uint16_t*>(h->w.down_proj); m7.m[0] = H; m7.M = H; m7.K = I;
     m7.a = m; m7.lda = I;
     m7.out_mode = OUT_RESID; m7.res = x1; m7.ldres = H; m7.y = g; m7.ldy = H;
     m7.y2 = hidden_out; m7.y2_bf16 = c.act_dtype == MTP_BF16; m7.ldy2 = H;
     MTP_TRY(timed_gemm(m7, s));
   } else {
-    MTP_TRY(run_gemv(a, h->wt, n_max, rsel, s));
+    MTP_TRY(run_gemv(a, h->wt, rows_total, rsel, s));
   }
 
   // 8. logits = W_lm RMSNorm(g; w_norm) of the last row, with its argmax
-  a = unembed_args(h, kv, L, n_max, n_dev, g, logits, ws);
+  a = unembed_args(h, kv, L, n_max, n_dev, g, logits, ws, ss);
   int tslot = -1, grid = 0;
   time_mark(TIME_UNEMBED, true, s, &tslot);
-  MTP_TRY(launch_gemv(a, h->lmt, 1, s, &grid));
+  MTP_TRY(launch_gemv(a, h->lmt, slots, s, &grid));
   time_mark(TIME_UNEMBED, false, s, &tslot);
   // 9. argmax of the partial keys, commit the append (len, round base)
   f.parts = a.amax_part; f.nparts = grid; f.amax_out = argmax;
@@ -677,6 +713,64 @@ int mtp_draft_chain(const mtp_head* head, const mtp_kv* kv, const int32_t* pend_
   return MTP_OK;
 }
 
+size_t mtp_batch_workspace_bytes(const mtp_head_config* cfg, int32_t batch, int32_t max_rows,
+                                 int32_t max_capacity) {
+  if (validate_cfg(cfg) != MTP_OK || batch < 1 || batch > MTP_MAX_BATCH || max_rows < 1 ||
+      max_rows > MTP_MAX_FLUSH || max_capacity < 1)
+    return 0;
+  Sessions ss;
+  ss.batch = batch;
+  return layout(*cfg, batch * max_rows, max_capacity, slots_of(ss)).total;
+}
+
+int mtp_draft_chain_batch(const mtp_head* head, const mtp_kv* kv, int32_t batch, const int32_t* pend_tokens_dev,
+                          const void* pend_hiddens_dev, int32_t n_max, const int32_t* n_dev, int32_t n_dev_stride,
+                          int32_t n_draft, int32_t* drafts_dev, void* hiddens_out_dev, float* draft_logits_dev,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!head || !pend_tokens_dev || !pend_hiddens_dev || !drafts_dev || !hiddens_out_dev || !ws)
+    return MTP_E_INVALID_ARG;
+  if (batch < 1 || batch > MTP_MAX_BATCH) return MTP_E_INVALID_ARG;
+  if (n_draft < 1 || n_draft > MTP_MAX_DRAFT || n_max < 1) return MTP_E_INVALID_ARG;
+  if (n_dev && n_dev_stride < 1) return MTP_E_INVALID_ARG;
+  if (n_max > MTP_MAX_FLUSH) return MTP_E_CAPACITY;
+  int st = validate_kv(head, kv);
+  if (st != MTP_OK) return st;
+  if (!n_dev && n_max > kv->capacity) return MTP_E_CAPACITY;
+  const mtp_head_config& c = head->cfg;
+  if (ws_bytes < mtp_batch_workspace_bytes(&c, batch, n_max, kv->capacity)) return MTP_E_WORKSPACE;
+  const size_t row_bytes = static_cast<size_t>(c.hidden) * (c.act_dtype == MTP_BF16 ? 2 : 4);
+  // the hidden outputs must not overlap the pending hiddens they are computed from
+  const char* hs = static_cast<const char*>(pend_hiddens_dev);
+  char* hout = static_cast<char*>(hiddens_out_dev);
+  const size_t in_span = static_cast<size_t>(batch) * n_max * row_bytes;
+  const size_t out_span = static_cast<size_t>(batch) * n_draft * row_bytes;
+  if (hout < hs + in_span && hs < hout + out_span) return MTP_E_INVALID_ARG;
+  Sessions ss;
+  ss.batch = batch;
+  ss.kv_sb = static_cast<long long>(c.n_kv_heads) * kv->capacity * c.head_dim;
+  ss.tok_sb = n_max;
+  ss.hid_sb = n_max;
+  ss.out_sb = n_draft;
+  ss.ndev_sb = n_dev_stride;
+  // every session's pending pairs in one flush: d_0 and g_0 of each session
+  st = head_forward(head, kv, pend_tokens_dev, pend_hiddens_dev, n_max, n_dev, MTP_FLUSH_LAST, 1, hout,
+                    draft_logits_dev, drafts_dev, ws, stream, 1, ss);
+  if (st != MTP_OK) return st;
+  // chained steps, one row per session: (d_{i-1}, g_{i-1}) -> d_i, g_i
+  Sessions sc = ss;
+  sc.tok_sb = n_draft;
+  sc.hid_sb = n_draft;
+  sc.ndev_sb = 0;
+  for (int i = 1; i < n_draft; ++i) {
+    st = head_forward(head, kv, drafts_dev + (i - 1), hout + (i - 1) * row_bytes, 1, nullptr, MTP_FLUSH_LAST, 0,
+                      hout + i * row_bytes,
+                      draft_logits_dev ? draft_logits_dev + static_cast<size_t>(i) * c.vocab : nullptr,
+                      drafts_dev + i, ws, stream, 0, sc);
+    if (st != MTP_OK) return st;
+  }
+  return MTP_OK;
+}
+
 int mtp_repair_pending(const int32_t* out_tokens_dev, const int32_t* out_counts_dev,
                        const void* target_hiddens_dev, int32_t hidden, int32_t act_dtype, int32_t n_draft,
                        int32_t* pend_tokens_dev, void* pend_hiddens_dev, int32_t* pend_count_dev,
@@ -697,6 +791,26 @@ int mtp_repair_pending(const int32_t* out_tokens_dev, const int32_t* out_counts_
   return MTP_OK;
 }
 
+int mtp_repair_pending_batch(int32_t batch, const int32_t* out_tokens_dev, const int32_t* out_counts_dev,
+                             const void* target_hiddens_dev, int32_t hidden, int32_t act_dtype, int32_t n_draft,
+                             int32_t* pend_tokens_dev, void* pend_hiddens_dev, int32_t* pend_counts_dev,
+                             hipStream_t stream) {
+  if (!out_tokens_dev || !out_counts_dev || !target_hiddens_dev || !pend_tokens_dev || !pend_hiddens_dev ||
+      !pend_counts_dev)
+    return MTP_E_INVALID_ARG;
+  if (batch < 1 || batch > MTP_MAX_BATCH) return MTP_E_INVALID_ARG;
+  if (hidden < 1 || n_draft < 1 || n_draft > MTP_MAX_DRAFT) return MTP_E_INVALID_ARG;
+  if (act_dtype != MTP_F32 && act_dtype != MTP_BF16) return MTP_E_INVALID_ARG;
+  const size_t row_bytes = static_cast<size_t>(hidden) * (act_dtype == MTP_BF16 ? 2 : 4);
+  const char* hs = static_cast<const char*>(target_hiddens_dev);
+  const char* hd = static_cast<const char*>(pend_hiddens_dev);
+  const size_t span = static_cast<size_t>(batch) * (n_draft + 1) * row_bytes;
+  if (hd < hs + span && hs < hd + span) return MTP_E_INVALID_ARG;
+  MTP_TRY(launch_repair(out_tokens_dev, out_counts_dev, target_hiddens_dev, static_cast<int>(row_bytes / 2),
+                        n_draft, pend_tokens_dev, pend_hiddens_dev, pend_counts_dev, stream, batch));
+  return MTP_OK;
+}
+
 size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab) {
   if (n_draft < 0 || n_draft > MTP_MAX_DRAFT || vocab < 1) return 0;
   const size_t nb = (static_cast<size_t>(vocab) + kVerifyChunk - 1) / kVerifyChunk;
@@ -704,14 +818,20 @@ size_t spec_verify_workspace_bytes(int32_t n_draft, int32_t vocab) {
          align_up(verify_sampled_scratch_bytes(n_draft, vocab, kVerifyChunk));
 }
 
-int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
-                const float* target_logits_dev, const float* draft_logits_dev,
-                const int32_t* draft_tokens_dev, int32_t* history_dev, int32_t* history_state_dev,
-                const float* uniforms_dev, int32_t* out_tokens_dev, int32_t* out_counts_dev,
-                void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// spec_verify over `batch` independent sessions (arrays session-major, one
+// workspace of spec_verify_workspace_bytes per session)
+int verify_sessions(const spec_sampling* sp, int32_t batch, int32_t n_draft, int32_t vocab,
+                    const float* target_logits_dev, const float* draft_logits_dev,
+                    const int32_t* draft_tokens_dev, int32_t* history_dev, int32_t* history_state_dev,
+                    const float* uniforms_dev, int32_t* out_tokens_dev, int32_t* out_counts_dev,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!sp || !target_logits_dev || !history_dev || !history_state_dev || !out_tokens_dev ||
       !out_counts_dev || !ws)
     return MTP_E_INVALID_ARG;
+  if (batch < 1 || batch > MTP_MAX_BATCH) return MTP_E_INVALID_ARG;
   if (n_draft < 0 || n_draft > MTP_MAX_DRAFT || vocab < 1) return MTP_E_INVALID_ARG;
   if (n_draft > 0 && !draft_tokens_dev) return MTP_E_INVALID_ARG;
   if (sp->window < 1 || sp->window > 1024) return MTP_E_INVALID_ARG;
@@ -719,7 +839,8 @@ int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
   if (!(sp->repeat_penalty > 0.f) || !std::isfinite(sp->repeat_penalty)) return MTP_E_INVALID_ARG;
   if (!(sp->top_p > 0.f) || !(sp->min_p >= 0.f) || !(sp->min_p <= 1.f) || sp->top_k < 0)
     return MTP_E_INVALID_ARG;
-  if (ws_bytes < spec_verify_workspace_bytes(n_draft, vocab)) return MTP_E_WORKSPACE;
+  const size_t per = spec_verify_workspace_bytes(n_draft, vocab);
+  if (per == 0 || ws_bytes < static_cast<size_t>(batch) * per) return MTP_E_WORKSPACE;
   const bool greedy = sp->temperature == 0.f;
   if (greedy != (draft_logits_dev == nullptr) && n_draft > 0) return MTP_E_INVALID_ARG;
   if (!greedy && !uniforms_dev) return MTP_E_INVALID_ARG;
@@ -737,10 +858,34 @@ int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
   const size_t nb = (static_cast<size_t>(vocab) + kVerifyChunk - 1) / kVerifyChunk;
   a.parts = reinterpret_cast<unsigned long long*>(wsp(ws, kHeadBytes));
   a.scratch = wsp(ws, kHeadBytes + align_up((n_draft + 1) * nb * 8));
+  a.batch = batch;
+  a.sess_bytes = per;
   const hipError_t e = greedy ? launch_verify_greedy(a, stream) : launch_verify_sampled(a, stream);
   if (e == hipErrorNotSupported) return MTP_E_UNSUPPORTED;
   MTP_TRY(e);
   return MTP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
+                const float* target_logits_dev, const float* draft_logits_dev,
+                const int32_t* draft_tokens_dev, int32_t* history_dev, int32_t* history_state_dev,
+                const float* uniforms_dev, int32_t* out_tokens_dev, int32_t* out_counts_dev,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  return verify_sessions(sp, 1, n_draft, vocab, target_logits_dev, draft_logits_dev, draft_tokens_dev, history_dev,
+                         history_state_dev, uniforms_dev, out_tokens_dev, out_counts_dev, ws, ws_bytes, stream);
+}
+
+int spec_verify_batch(const spec_sampling* sp, int32_t batch, int32_t n_draft, int32_t vocab,
+                      const float* target_logits_dev, const float* draft_logits_dev,
+                      const int32_t* draft_tokens_dev, int32_t* history_dev, int32_t* history_state_dev,
+                      const float* uniforms_dev, int32_t* out_tokens_dev, int32_t* out_counts_dev,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  return verify_sessions(sp, batch, n_draft, vocab, target_logits_dev, draft_logits_dev, draft_tokens_dev,
+                         history_dev, history_state_dev, uniforms_dev, out_tokens_dev, out_counts_dev, ws, ws_bytes,
+                         stream);
 }
 
 int mtp_timing_begin(int32_t kind, int32_t max_launches) {
@@ -816,6 +961,18 @@ int kv_rollback(const mtp_kv* kv, int32_t to_len, const int32_t* n_accepted_dev,
   if (n_draft < 0 || n_draft > MTP_MAX_DRAFT) return MTP_E_INVALID_ARG;
   if (n_accepted_dev && to_len != MTP_TO_ROUND_BASE) return MTP_E_INVALID_ARG;
   MTP_TRY(launch_rollback(kv->state, to_len, n_accepted_dev, n_draft, kv->capacity, stream));
+  return MTP_OK;
+}
+
+int kv_rollback_batch(const mtp_kv* kv, int32_t batch, int32_t to_len, const int32_t* counts_dev, int32_t n_draft,
+                      hipStream_t stream) {
+  if (!kv || !kv->state || kv->capacity <= 0) return MTP_E_INVALID_ARG;
+  if (batch < 1 || batch > MTP_MAX_BATCH) return MTP_E_INVALID_ARG;
+  if (to_len < MTP_TO_ROUND_BASE) return MTP_E_INVALID_ARG;
+  if (to_len > kv->capacity) return MTP_E_CAPACITY;
+  if (n_draft < 0 || n_draft > MTP_MAX_DRAFT) return MTP_E_INVALID_ARG;
+  if (counts_dev && to_len != MTP_TO_ROUND_BASE) return MTP_E_INVALID_ARG;
+  MTP_TRY(launch_rollback(kv->state, to_len, counts_dev, n_draft, kv->capacity, stream, batch, 2));
   return MTP_OK;
 }
 

@@ -183,15 +183,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   __shared__ float s_o[kAttnWaves][G][D];
   __shared__ float s_q[FUSE ? G : 1][FUSE ? D : 1];
 
-  int32_t* st = a.state;
+  // several sessions (ROW_LAST with the fused append only): blockIdx.z is the
+  // session, with its own state words, K/V and workspace rows
+  const bool multi = FUSE && a.batch > 1;
+  const int sess = multi ? static_cast<int>(blockIdx.z) : 0;
+  int32_t* st = a.state + 4 * sess;
+  constexpr int ebytes = KVB ? 2 : 4;
+  void* kcs = static_cast<char*>(a.kc) + (multi ? sess * a.kv_sb * ebytes : 0ll);
+  void* vcs = static_cast<char*>(a.vc) + (multi ? sess * a.kv_sb * ebytes : 0ll);
+  const int rb = sess * a.n_max;    // the session's first workspace row
   if (st[3] != 0) return;
   int n = a.n_max;
   if constexpr (FUSE) {
-    // the append's checks (once per launch, by the first workgroup)
-    const int ndev = a.n_dev ? *a.n_dev : a.n_max;
+    // the append's checks (once per launch and session, by its first workgroup)
+    const int ndev = a.n_dev ? a.n_dev[multi ? sess * a.ndev_sb : 0] : a.n_max;
     const bool bad_count = ndev < a.n_min || ndev < 0 || ndev > a.n_max;
     if (bad_count || st[0] + ndev > a.capacity) {
-      if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) st[3] = bad_count ? 3 : 1;
+      if (blockIdx.x == 0 && blockIdx.y == 0 && (multi || blockIdx.z == 0) && threadIdx.x == 0)
+        st[3] = bad_count ? 3 : 1;
       return;
     }
     n = ndev;
@@ -200,6 +209,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   }
   const int j = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.z);
   if (j < 0 || j >= n) return;
+  const int jf = rb + j;            // workspace row
   const int off = st[0];            // pre-append length (committed by k_finish)
   const int L = off + j + 1;        // keys visible to row j
   const int h = blockIdx.y;
@@ -209,7 +219,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   const int k0 = c * ck;
   const int k1 = min(L, k0 + ck);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t pbase = (static_cast<size_t>(j) * a.hq + h * G) * a.nchunk + c;
+  const size_t pbase = (static_cast<size_t>(jf) * a.hq + h * G) * a.nchunk + c;
 
   if (k0 >= k1) {
     for (int idx = tid; idx < G * D; idx += kAttnThreads) {
@@ -233,11 +243,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     // new slots in this chunk: k normed and roped, k and v appended (a wave per slot)
     const int s0 = max(off, k0), s1 = min(off + n, k1);
     for (int sl = s0 + wave; sl < s1; sl += kAttnWaves) {
-      const float* row = a.qkv + static_cast<size_t>(sl - off) * a.ld_qkv;
+      const float* row = a.qkv + static_cast<size_t>(rb + sl - off) * a.ld_qkv;
       const size_t o = (static_cast<size_t>(h) * a.capacity + sl) * D;
       norm_rope_head<D>(row + (a.hq + h) * D, a.k_norm, a.nw_bf16, a.eps, sl, l2t, lane, [&](int d, float v) {
-        if constexpr (KVB) static_cast<uint16_t*>(a.kc)[o + d] = f32_to_bf16(v);
-        else static_cast<float*>(a.kc)[o + d] = v;
+        if constexpr (KVB) static_cast<uint16_t*>(kcs)[o + d] = f32_to_bf16(v);
+        else static_cast<float*>(kcs)[o + d] = v;
       });
       const float* vsrc = row + (a.hq + a.hkv + h) * D;
       float vv[D / 64];
@@ -245,12 +255,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       for (int k = 0; k < D / 64; ++k) vv[k] = vsrc[lane + 64 * k];
 #pragma unroll
       for (int k = 0; k < D / 64; ++k) {
-        if constexpr (KVB) static_cast<uint16_t*>(a.vc)[o + lane + 64 * k] = f32_to_bf16(vv[k]);
-        else static_cast<float*>(a.vc)[o + lane + 64 * k] = vv[k];
+        if constexpr (KVB) static_cast<uint16_t*>(vcs)[o + lane + 64 * k] = f32_to_bf16(vv[k]);
+        else static_cast<float*>(vcs)[o + lane + 64 * k] = vv[k];
       }
     }
     // the query heads of this kv head, row j, normed and roped
-    const float* qrow = a.qkv + static_cast<size_t>(j) * a.ld_qkv;
+    const float* qrow = a.qkv + static_cast<size_t>(jf) * a.ld_qkv;
     for (int g = wave; g < G; g += kAttnWaves) {
       float* qd = s_q[g];
       norm_rope_head<D>(qrow + (h * G + g) * D, a.q_norm, a.nw_bf16, a.eps, off + j, l2t, lane,
@@ -270,10 +280,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     }
   }
 
-  constexpr int ebytes = KVB ? 2 : 4;
   const size_t head_off = static_cast<size_t>(h) * a.capacity * D;
-  const char* kbase = static_cast<const char*>(a.kc) + (head_off + d0) * ebytes;
-  const char* vbase = static_cast<const char*>(a.vc) + (head_off + d0) * ebytes;
+  const char* kbase = static_cast<const char*>(kcs) + (head_off + d0) * ebytes;
+  const char* vbase = static_cast<const char*>(vcs) + (head_off + d0) * ebytes;
   constexpr int row_bytes = D * ebytes;
   constexpr int kstride = KPI * kAttnWaves;   // keys between a group's consecutive keys
 
@@ -389,12 +398,16 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   __shared__ float wts[kMaxChunks];
   __shared__ float red[4];
   __shared__ float s_m, s_den;
-  const int32_t* st = a.state;
+  // several sessions (ROW_LAST): blockIdx.y is the session
+  const bool multi = a.batch > 1 && a.row_sel == ROW_LAST;
+  const int sess = multi ? static_cast<int>(blockIdx.y) : 0;
+  const int32_t* st = a.state + 4 * sess;
   if (st[3] != 0) return;
   int n = a.n_max;
-  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
-  const int j = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.y);
-  if (j < 0 || j >= n) return;
+  if (a.n_dev) n = min(max(a.n_dev[multi ? sess * a.ndev_sb : 0], 0), a.n_max);
+  const int jl = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.y);
+  if (jl < 0 || jl >= n) return;
+  const int j = sess * a.n_max + jl;   // workspace row
   const int hq = blockIdx.x;
   const int D = a.d;
   const int nc = a.nchunk;
@@ -477,7 +490,8 @@ static hipError_t attn_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  const int rows = (a.row_sel == ROW_LAST) ? 1 : a.n_max;
+  if (a.batch > 1 && !(a.row_sel == ROW_LAST && a.fuse_rope)) return hipErrorNotSupported;
+  const int rows = (a.row_sel == ROW_LAST) ? (a.batch > 1 ? a.batch : 1) : a.n_max;
   const dim3 grid(a.nchunk, a.hkv, rows);
   hipError_t e;
   int slot = -1;
@@ -511,13 +525,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 namespace mtp {
 
 __global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
-  int32_t* st = a.state;
+  const int sess = a.batch > 1 ? static_cast<int>(blockIdx.x) : 0;   // one workgroup per session
+  int32_t* st = a.state + 4 * sess;
   if (st[3] != 0) return;
   int n = a.n_max;
-  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+  if (a.n_dev) n = min(max(a.n_dev[sess * a.ndev_sb], 0), a.n_max);
   if (a.parts) {
-    const unsigned long long b = block_max_u64(a.parts, a.nparts);
-    if (threadIdx.x == 0 && a.amax_out && n > 0) *a.amax_out = argmax_index(b);
+    const unsigned long long b = block_max_u64(a.parts + static_cast<size_t>(sess) * a.nparts, a.nparts);
+    if (threadIdx.x == 0 && a.amax_out && n > 0) a.amax_out[sess * a.out_sb] = argmax_index(b);
   }
   if (threadIdx.x == 0) {
     const int len = st[0] + n;
@@ -528,7 +543,7 @@ __global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t s) {
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_finish, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_finish, dim3(a.batch > 1 ? a.batch : 1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

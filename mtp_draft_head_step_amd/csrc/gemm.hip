@@ -89,21 +89,37 @@ __device__ __forceinline__ void prep_load(const PrepRow& r, int k, float (&v)[8]
 
 __global__ __launch_bounds__(kPrepThreads) void k_rows_prep(PrepArgs a) {
   __shared__ float red[kPrepThreads / kWave];
-  if (a.kv_state && a.kv_state[3] != 0) return;
-  int n = a.n_max;
-  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
   const int j = blockIdx.x;
-  if (j >= n) return;
-  uint16_t* out = a.out + static_cast<long long>(j) * a.ld_out;
   const int K = a.K;
+  uint16_t* out = a.out + static_cast<long long>(j) * a.ld_out;
+  int tj = j, hj = j;           // token index and hidden row of this row
+  int32_t* err = a.err;
+  if (a.batch <= 1) {
+    if (a.kv_state && a.kv_state[3] != 0) return;
+    int n = a.n_max;
+    if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+    if (j >= n) return;
+  } else {
+    // session b's pair jj; rows past its count (or of a session in error) are zeros
+    const int b = j / a.n_max, jj = j - b * a.n_max;
+    const int32_t* sb = a.kv_state + 4 * b;
+    const int nb = sb[3] != 0 ? 0 : (a.n_dev ? min(max(a.n_dev[b * a.ndev_sb], 0), a.n_max) : a.n_max);
+    if (jj >= nb) {
+      for (int k = threadIdx.x; k < K; k += kPrepThreads) out[k] = 0;
+      return;
+    }
+    tj = b * a.tok_sb + jj;
+    hj = b * a.hid_sb + jj;
+    err = const_cast<int32_t*>(a.kv_state) + 4 * b + 3;   // the state words are writable
+  }
   PrepRow r;
   if (a.in_mode == IN_EMBED) {
-    const int tk = a.tok[j];
+    const int tk = a.tok[tj];
     const bool ok = tk >= 0 && tk < a.vocab_tok;
-    if (!ok && a.err && threadIdx.x == 0) *a.err = 4;   // token outside the vocabulary
+    if (!ok && err && threadIdx.x == 0) *err = 4;   // token outside the vocabulary
     r.half = K / 2;
     r.src0 = ok ? a.embed : nullptr; r.off0 = static_cast<long long>(ok ? tk : 0) * r.half; r.bf0 = a.embed_bf16;
-    r.src1 = a.hid; r.off1 = static_cast<long long>(j) * a.ld_hid; r.bf1 = a.hid_bf16;
+    r.src1 = a.hid; r.off1 = static_cast<long long>(hj) * a.ld_hid; r.bf1 = a.hid_bf16;
   } else {
     r.half = K;
     r.src0 = a.x; r.off0 = static_cast<long long>(j) * a.ldx; r.bf0 = 0;
@@ -170,8 +186,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_rows_prep(PrepArgs a) {
 
 hipError_t launch_rows_prep(const PrepArgs& a, hipStream_t s) {
   if (a.n_max <= 0) return hipSuccess;
+  const int rows = a.batch > 1 ? a.batch * a.n_max : a.n_max;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_rows_prep, dim3(a.n_max), dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(k_rows_prep, dim3(rows), dim3(kPrepThreads), 0, s, a);
   return hipGetLastError();
 }
 

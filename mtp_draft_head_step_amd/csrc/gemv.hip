@@ -73,9 +73,8 @@ hipError_t raise_lds_limit(const void* fn) {
 
 template <int WT>
 static hipError_t launch_w(const GemvArgs& a, int nr, hipStream_t s, int* g) {
-  if constexpr (WT == W_I8) {
-    return nr == 1 ? launch_r<WT, 1>(a, s, g) : hipErrorInvalidValue;   // unembedding only
-  } else {
+  if (WT == W_I8 && a.out_mode != OUT_LOGITS) return hipErrorInvalidValue;   // unembedding only
+  {
     switch (nr) {
       case 1: return launch_r<WT, 1>(a, s, g);
       case 2: return launch_r<WT, 2>(a, s, g);

@@ -238,26 +238,57 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   XT* xs = reinterpret_cast<XT*>(xs_f);
   __shared__ float s_red[kWaves][2 * NR];
   __shared__ float s_inv[2 * NR];
-  __shared__ unsigned long long s_best[kWaves];
+  __shared__ unsigned long long s_best[kWaves][NR];
   __shared__ float s_wsk[WSK ? kWaves : 1][WSK ? RPW * 8 * NR : 1][2];
   constexpr int EPC = WTraits<WT>::EPC;
 
-  if (a.kv_state && a.kv_state[3] != 0) return;
+  if (a.batch <= 1 && a.kv_state && a.kv_state[3] != 0) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
 
-  // ---- activation rows handled by this launch
-  int n = a.n_max;
-  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
-  int j0, nrows;
-  if (a.row_sel == ROW_LAST) {
-    j0 = n - 1;
-    nrows = n > 0 ? 1 : 0;
+  // ---- activation rows handled by this launch.  Slot r (of NR) reads
+  // workspace row jr[r], token tr[r] and hidden row hr[r]; ROW_LAST outputs of
+  // the hidden copy and the logits go to row orw[r]; vr[r] tells whether the
+  // slot holds a row at all.  One session: rows j < n (device count), ROW_LAST
+  // the row n - 1.  Several sessions: flattened rows b * n_max + j, valid when j
+  // is below session b's count and its error word is clear; ROW_LAST slot r is
+  // session row_base + r's last row.
+  int jr[NR], tr[NR], hr[NR], orw[NR];
+  bool vr[NR];
+  int32_t* er[NR];
+  bool any = false;
+  if (a.batch <= 1) {
+    int n = a.n_max;
+    if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int j = (a.row_sel == ROW_LAST) ? n - 1 : a.row_base + r;
+      vr[r] = (a.row_sel == ROW_LAST) ? (r == 0 && n > 0) : (j < n);
+      jr[r] = tr[r] = hr[r] = vr[r] ? j : 0;
+      orw[r] = (a.row_sel == ROW_LAST) ? 0 : jr[r];
+      er[r] = a.err;
+      any = any || vr[r];
+    }
   } else {
-    j0 = a.row_base;
-    nrows = min(NR, n - a.row_base);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int b = (a.row_sel == ROW_LAST) ? a.row_base + r : (a.row_base + r) / a.n_max;
+      int nb = 0;
+      if (b < a.batch) {
+        const int32_t* sb = a.kv_state + 4 * b;
+        nb = sb[3] != 0 ? 0 : (a.n_dev ? min(max(a.n_dev[b * a.ndev_sb], 0), a.n_max) : a.n_max);
+      }
+      const int jj = (a.row_sel == ROW_LAST) ? nb - 1 : (a.row_base + r) - b * a.n_max;
+      vr[r] = b < a.batch && jj >= 0 && jj < nb;
+      jr[r] = vr[r] ? b * a.n_max + jj : 0;
+      tr[r] = vr[r] ? b * a.tok_sb + jj : 0;
+      hr[r] = vr[r] ? b * a.hid_sb + jj : 0;
+      orw[r] = vr[r] ? b * a.out_sb : 0;
+      er[r] = (b < a.batch) ? const_cast<int32_t*>(a.kv_state) + 4 * b + 3 : nullptr;   // the state is writable
+      any = any || vr[r];
+    }
   }
-  if (nrows <= 0) {
-    if (a.out_mode == OUT_LOGITS && threadIdx.x == 0) a.amax_part[blockIdx.x] = 0ull;
+  if (!any) {
+    if (a.out_mode == OUT_LOGITS && threadIdx.x < NR) a.amax_part[threadIdx.x * gridDim.x + blockIdx.x] = 0ull;
     return;
   }
   const int K = a.K;
@@ -284,7 +315,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   bool have_inv = (a.in_mode == IN_F32);
   if (have_inv && tid < 2 * NR) s_inv[tid] = (tid & 1) ? 0.f : 1.f;
 
-  unsigned long long best = 0ull;
+  unsigned long long best[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) best[r] = 0ull;
 
   for (int blk = blockIdx.x; blk < nblocks; blk += (a.grid_stride ? gridDim.x : nblocks)) {
     // row slots: plain mode slot s -> its row; swiglu slot pair (2p, 2p+1) -> (gate r, up r)
@@ -311,14 +344,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
         for (int r = 0; r < NR; ++r) {
           XT* dst = xs + r * a.kp;
           float se = 0.f, sh = 0.f;   // sums of squares: whole input / hidden half
-          if (r < nrows) {
-            const int jr = j0 + r;
+          if (vr[r]) {
             if (a.in_mode != IN_EMBED) {
-              stage_range<XB>(dst, a.x, static_cast<long long>(jr) * a.ldx, 0,
+              stage_range<XB>(dst, a.x, static_cast<long long>(jr[r]) * a.ldx, 0,
                           (a.in_mode == IN_RMS) ? a.nw : nullptr, 0, a.nw_bf16, k0, k0 + klen, k0, se);
             } else {
               const int ea = k0, eb = min(k0 + klen, half);
-              const int tk = a.tok[jr];
+              const int tk = a.tok[tr[r]];
               if (tk >= 0 && tk < a.vocab_tok) {
                 if (ea < eb)
                   stage_range<XB>(dst, a.embed, static_cast<long long>(tk) * half, a.embed_bf16, a.nw, 0,
@@ -327,11 +359,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
                 // a token outside the vocabulary: its embedding half stays zero and
                 // the KV error word is set (every later kernel is then a no-op)
                 for (int k = ea + tid; k < eb; k += kThreads) dst[k - k0] = XT(0);
-                if (a.err && blockIdx.x == 0 && tid == 0) *a.err = 4;
+                if (er[r] && blockIdx.x == 0 && tid == 0) *er[r] = 4;
               }
               const int ha = max(k0, half), hb = k0 + klen;
               if (ha < hb)
-                stage_range<XB>(dst, a.hid, static_cast<long long>(jr) * a.ld_hid - half, a.hid_bf16, a.nw2,
+                stage_range<XB>(dst, a.hid, static_cast<long long>(hr[r]) * a.ld_hid - half, a.hid_bf16, a.nw2,
                             -static_cast<long long>(half), a.nw_bf16, ha, hb, k0, sh);
             }
           } else {
@@ -438,9 +470,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
           if (!valid[s]) continue;
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
-            if (r >= nrows) continue;
-            const int j = j0 + r;
-            a.y[static_cast<size_t>(j) * a.ldy + rowid[s]] = silu(acc[s][r]) * acc[s + 1][r];
+            if (!vr[r]) continue;
+            a.y[static_cast<size_t>(jr[r]) * a.ldy + rowid[s]] = silu(acc[s][r]) * acc[s + 1][r];
           }
         }
       } else {
@@ -450,19 +481,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
           const int row = blk * rows_per_wg + (wrow * RPW + s) * rps + sub;
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
-            if (r >= nrows) continue;
-            const int j = j0 + r;
+            if (!vr[r]) continue;
+            const int j = jr[r];
             float v = acc[s][r];
             if (a.out_mode == OUT_LOGITS) {
-              if (a.logits) a.logits[row] = v;
+              if (a.logits) a.logits[static_cast<size_t>(orw[r]) * a.M + row] = v;
               const unsigned long long key = argmax_key(v, static_cast<uint32_t>(row));
-              best = key > best ? key : best;
+              best[r] = key > best[r] ? key : best[r];
               continue;
             }
             if (a.out_mode == OUT_RESID) v += a.res[static_cast<size_t>(j) * a.ldres + row];
             a.y[static_cast<size_t>(j) * a.ldy + row] = v;
             if (a.y2) {
-              const size_t o = (a.row_sel == ROW_LAST) ? row : static_cast<size_t>(j) * a.ldy2 + row;
+              const size_t o = static_cast<size_t>(orw[r]) * a.ldy2 + row;
               if (a.y2_bf16) static_cast<uint16_t*>(a.y2)[o] = f32_to_bf16(v);
               else static_cast<float*>(a.y2)[o] = v;
             }
@@ -473,13 +504,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   }
 
   if (a.out_mode == OUT_LOGITS) {
-    best = wave_max_u64(best);
-    if (lane == 0) s_best[wave] = best;
+    // one key per (slot, workgroup), merged per slot by the finishing kernel
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const unsigned long long b = wave_max_u64(best[r]);
+      if (lane == 0) s_best[wave][r] = b;
+    }
     __syncthreads();
-    if (tid == 0) {
-      unsigned long long b = s_best[0];
-      for (int w = 1; w < kWaves; ++w) b = s_best[w] > b ? s_best[w] : b;
-      a.amax_part[blockIdx.x] = b;     // merged by the step's finishing kernel
+    if (tid < NR) {
+      unsigned long long b = s_best[0][tid];
+      for (int w = 1; w < kWaves; ++w) b = s_best[w][tid] > b ? s_best[w][tid] : b;
+      a.amax_part[tid * gridDim.x + blockIdx.x] = b;
     }
   }
 }

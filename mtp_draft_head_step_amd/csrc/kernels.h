@@ -61,6 +61,14 @@ struct GemvArgs {
   unsigned long long* amax_part;  // OUT_LOGITS: one argmax key per workgroup
   const int32_t* kv_state; // nullable: skip everything when state[3] != 0
   int dry_run;             // compute the launch shape only (*grid_out), enqueue nothing
+  // batch > 1: independent sessions in one launch.  n_max is the rows per
+  // session and workspace rows are flattened b * n_max + j; session b's state
+  // words are kv_state + 4 b (a set error word drops its rows) and its count
+  // n_dev[b * ndev_sb]; its token j is tok[b * tok_sb + j], its hidden row
+  // b * hid_sb + j.  ROW_LAST: slot r is session row_base + r, whose hidden copy
+  // and logits go to row b * out_sb of y2 and logits ([rows, vocab]).
+  int batch;
+  int tok_sb, hid_sb, out_sb, ndev_sb;
 };
 
 // *grid_out (nullable) receives the number of workgroups launched.
@@ -91,6 +99,13 @@ struct PrepArgs {
   int ld_hid;
   uint16_t* out;             // [n_max, ld_out] bf16
   int ld_out;
+  // batch > 1: n_max rows per session, batch * n_max rows in all (flattened
+  // b * n_max + j); rows past a session's count (or of a session whose error
+  // word is set) are written as zeros; session b's token j is tok[b * tok_sb +
+  // j], its hidden row b * hid_sb + j, its count n_dev[b * ndev_sb], its state
+  // words kv_state + 4 b.
+  int batch;
+  int tok_sb, hid_sb, ndev_sb;
 };
 hipError_t launch_rows_prep(const PrepArgs& a, hipStream_t s);
 
@@ -173,6 +188,12 @@ struct AttnArgs {
   int n_max;
   const int32_t* n_dev;
   int n_min;               // fuse_rope: a device count below n_min sets MTP_DEV_COUNT
+  // batch > 1 (ROW_LAST with fuse_rope only): session b's K/V start kv_sb
+  // elements after session b - 1's, its state words are state + 4 b, its count
+  // n_dev[b * ndev_sb]; its rows are the workspace rows b * n_max + j
+  int batch;
+  long long kv_sb;
+  int ndev_sb;
   int row_sel;             // ROWS_RANGE: rows 0..n-1; ROW_LAST: row n-1
   int nchunk;              // chunks per (row, kv head)
   int mfma;                // ROWS_RANGE over bf16 K/V: the matrix-core flush kernel
@@ -206,6 +227,10 @@ struct FinishArgs {
   const unsigned long long* parts;  // nullable
   int nparts;
   int32_t* amax_out;                // nullable
+  // batch > 1: one workgroup per session b: state + 4 b, count n_dev[b *
+  // ndev_sb], argmax keys parts[b * nparts ..], result amax_out[b * out_sb]
+  int batch;
+  int out_sb, ndev_sb;
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t s);
 
@@ -226,6 +251,11 @@ struct VerifyArgs {
   unsigned long long* parts;   // [n_draft + 1][blocks per row] argmax keys
   void* scratch;               // sampled path candidates
   int chunk;                   // elements per workgroup
+  // batch > 1: blockIdx.z is the session b; every per-session array above
+  // advances by b times its own size (rows, drafts, ring, ring state,
+  // uniforms, outputs) and parts / scratch by b * sess_bytes
+  int batch;
+  size_t sess_bytes;
 };
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s);
@@ -234,10 +264,12 @@ size_t verify_sampled_scratch_bytes(int n_draft, int vocab, int chunk);
 // candidates cannot hold)
 bool verify_sampled_supported(int top_k, int vocab);
 
+// batch sessions (state words state + 4 b, accepted count n_acc[b * acc_stride])
 hipError_t launch_rollback(int32_t* state, int to_len, const int32_t* n_acc, int n_draft,
-                           int capacity, hipStream_t s);
+                           int capacity, hipStream_t s, int batch = 1, int acc_stride = 0);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_repair(const int32_t* out_tokens, const int32_t* out_counts, const void* hid, int elems16,
-                         int n_draft, int32_t* pend_tokens, void* pend_hid, int32_t* pend_count, hipStream_t s);
+                         int n_draft, int32_t* pend_tokens, void* pend_hid, int32_t* pend_count, hipStream_t s,
+                         int batch = 1);
 
 }  // namespace mtp

@@ -5,8 +5,14 @@
 
 namespace mtp {
 
-__global__ void k_rollback(int32_t* st, int to_len, const int32_t* n_acc, int n_draft) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// Thread b rolls back session b (state words st + 4 b; its accepted count, when
+// given, n_acc[b * acc_stride]).
+__global__ void k_rollback(int32_t* st0, int to_len, const int32_t* n_acc0, int n_draft, int batch,
+                           int acc_stride) {
+  const int b = threadIdx.x;
+  if (blockIdx.x != 0 || b >= batch) return;
+  int32_t* st = st0 + 4 * b;
+  const int32_t* n_acc = n_acc0 ? n_acc0 + b * acc_stride : nullptr;
   if (st[3] != 0) return;
   int to = to_len;
   if (to_len < 0) {
@@ -26,10 +32,11 @@ __global__ void k_rollback(int32_t* st, int to_len, const int32_t* n_acc, int n_
 }
 
 hipError_t launch_rollback(int32_t* state, int to_len, const int32_t* n_acc, int n_draft,
-                           int capacity, hipStream_t s) {
+                           int capacity, hipStream_t s, int batch, int acc_stride) {
   (void)capacity;
+  if (batch < 1 || batch > 64) return hipErrorInvalidValue;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_rollback, dim3(1), dim3(64), 0, s, state, to_len, n_acc, n_draft);
+  hipLaunchKernelGGL(k_rollback, dim3(1), dim3(64), 0, s, state, to_len, n_acc, n_draft, batch, acc_stride);
   return hipGetLastError();
 }
 
@@ -37,8 +44,16 @@ hipError_t launch_rollback(int32_t* state, int to_len, const int32_t* n_acc, int
 // j0 = min(k, n_draft - 1), pending pair j = 0..k - j0 is (out_tokens[j0 + j],
 // hidden row j0 + j); the count k + 1 - j0 goes to *pend_count.  Rows are
 // copied in 16-bit units (elems16 per row).
+// Workgroup b re-pairs session b (its rows of every array, n_draft + 1 rows each).
 __global__ void k_repair(const int32_t* out_tokens, const int32_t* out_counts, const uint16_t* hid, int elems16,
                          int n_draft, int32_t* pend_tokens, uint16_t* pend_hid, int32_t* pend_count) {
+  const size_t b = blockIdx.x, rows = n_draft + 1;
+  out_tokens += b * rows;
+  out_counts += 2 * b;
+  hid += b * rows * elems16;
+  pend_tokens += b * rows;
+  pend_hid += b * rows * elems16;
+  pend_count += b;
   int k = out_counts[0];
   k = k < 0 ? 0 : (k > n_draft ? n_draft : k);
   const int j0 = n_draft > 0 ? (k < n_draft - 1 ? k : n_draft - 1) : 0;
@@ -53,9 +68,11 @@ __global__ void k_repair(const int32_t* out_tokens, const int32_t* out_counts, c
 }
 
 hipError_t launch_repair(const int32_t* out_tokens, const int32_t* out_counts, const void* hid, int elems16,
-                         int n_draft, int32_t* pend_tokens, void* pend_hid, int32_t* pend_count, hipStream_t s) {
+                         int n_draft, int32_t* pend_tokens, void* pend_hid, int32_t* pend_count, hipStream_t s,
+                         int batch) {
+  if (batch < 1) return hipErrorInvalidValue;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_repair, dim3(1), dim3(256), 0, s, out_tokens, out_counts, static_cast<const uint16_t*>(hid),
+  hipLaunchKernelGGL(k_repair, dim3(batch), dim3(256), 0, s, out_tokens, out_counts, static_cast<const uint16_t*>(hid),
                      elems16, n_draft, pend_tokens, static_cast<uint16_t*>(pend_hid), pend_count);
   return hipGetLastError();
 }

@@ -38,7 +38,27 @@ __device__ __forceinline__ int ring_count(const VerifyArgs& a) { return min(max(
 
 __device__ __forceinline__ float penalise(float v, float pen) { return v > 0.f ? v / pen : v * pen; }
 
+// Session blockIdx.z's view of the arguments (several independent sessions in
+// one launch); the identity for one session.
+__device__ __forceinline__ VerifyArgs at_session(VerifyArgs a) {
+  if (a.batch <= 1) return a;
+  const size_t b = blockIdx.z;
+  const size_t n = a.n_draft, v = a.vocab;
+  a.target += b * (n + 1) * v;
+  if (a.draft) a.draft += b * n * v;
+  if (a.drafts) a.drafts += b * n;
+  a.ring += b * a.window;
+  a.ring_state += 2 * b;
+  if (a.uniforms) a.uniforms += b * (n + 1);
+  a.out_tokens += b * (n + 1);
+  a.out_counts += 2 * b;
+  a.parts = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(a.parts) + b * a.sess_bytes);
+  a.scratch = static_cast<char*>(a.scratch) + b * a.sess_bytes;
+  return a;
+}
+
 __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
+  a = at_session(a);
   __shared__ uint32_t bits[kVMaxChunk / 32];
   __shared__ unsigned long long s_best[kVThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -89,6 +109,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
 }
 
 __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a, int nb) {
+  a = at_session(a);
   __shared__ int am[MTP_MAX_DRAFT_DEV + 1];
   const int n = a.n_draft;
   for (int r = 0; r <= n; ++r) {
@@ -117,13 +138,14 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
   if (a.chunk != kVGreedyChunk) return hipErrorInvalidValue;
+  const unsigned bz = a.batch > 1 ? a.batch : 1;
   const int nb = (a.vocab + a.chunk - 1) / a.chunk;
   (void)hipGetLastError();
   int slot = -1;
   time_mark(TIME_VERIFY, true, s, &slot);
-  hipLaunchKernelGGL(k_verify_greedy, dim3(nb, a.n_draft + 1), dim3(kVThreads), 0, s, a);
+  hipLaunchKernelGGL(k_verify_greedy, dim3(nb, a.n_draft + 1, bz), dim3(kVThreads), 0, s, a);
   time_mark(TIME_VERIFY, false, s, &slot);
-  hipLaunchKernelGGL(k_verify_greedy_finish, dim3(1), dim3(kVThreads), 0, s, a, nb);
+  hipLaunchKernelGGL(k_verify_greedy_finish, dim3(1, 1, bz), dim3(kVThreads), 0, s, a, nb);
   return hipGetLastError();
 }
 
@@ -282,6 +304,10 @@ __device__ void sort_small(unsigned long long* s, int n) {
 constexpr int kSPer = kSChunk / kVThreads;   // chunk keys per thread
 
 __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, SampledScratch sc, int nb, int kk) {
+  if (a.batch > 1) {
+    a = at_session(a);
+    sc = sampled_scratch(a.scratch, a.n_draft, a.vocab);
+  }
   __shared__ uint32_t bits[kSChunk / 32];
   __shared__ int hist[256];
   __shared__ int sh[4];
@@ -344,6 +370,10 @@ constexpr int kSRowPer = kSMaxCand / kVThreads;   // merge keys per thread
 
 __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledScratch sc, int nb, int kk,
                                                          int topk) {
+  if (a.batch > 1) {
+    a = at_session(a);
+    sc = sampled_scratch(a.scratch, a.n_draft, a.vocab);
+  }
   __shared__ unsigned long long s[kSMaxTopK];
   __shared__ float sp[kSMaxTopK];
   __shared__ int hist[256];
@@ -475,6 +505,10 @@ __device__ int draw(const SampledScratch& sc, int ra, int rb, float u) {
 }
 
 __global__ void k_sample_decide(VerifyArgs a, SampledScratch sc) {
+  if (a.batch > 1) {
+    a = at_session(a);
+    sc = sampled_scratch(a.scratch, a.n_draft, a.vocab);
+  }
   if (threadIdx.x != 0) return;
   const int n = a.n_draft;
   int k = n, tok = -1;
@@ -562,6 +596,10 @@ __device__ __forceinline__ unsigned long long mass_fx(float y, float ymax) {
 }
 
 __global__ __launch_bounds__(kVThreads) void k_full_transform(VerifyArgs a, FullScratch fs, int nb) {
+  if (a.batch > 1) {
+    a = at_session(a);
+    fs = full_scratch(a.scratch, a.n_draft, a.vocab);
+  }
   __shared__ uint32_t bits[kSChunk / 32];
   __shared__ float red[kVThreads / 64];
   const int tid = threadIdx.x;
@@ -691,6 +729,10 @@ __device__ double block_sum_f64(double v, double* red) {
 }
 
 __global__ __launch_bounds__(kFThreads) void k_full_select(VerifyArgs a, FullScratch fs, int nb) {
+  if (a.batch > 1) {
+    a = at_session(a);
+    fs = full_scratch(a.scratch, a.n_draft, a.vocab);
+  }
   __shared__ unsigned long long hist[256];
   __shared__ unsigned long long sh[4];
   __shared__ double red[kFThreads / 64];
@@ -843,6 +885,10 @@ __device__ int full_draw(const VerifyArgs& a, const FullScratch& fs, int ra, int
 }
 
 __global__ __launch_bounds__(kFThreads) void k_full_decide(VerifyArgs a, FullScratch fs) {
+  if (a.batch > 1) {
+    a = at_session(a);
+    fs = full_scratch(a.scratch, a.n_draft, a.vocab);
+  }
   __shared__ DrawShared ds;
   __shared__ int s_k;
   const int n = a.n_draft;
@@ -894,15 +940,16 @@ hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
   if (!verify_sampled_supported(a.top_k, a.vocab)) return hipErrorNotSupported;
   const int rows = 2 * a.n_draft + 1;
   const int nb = (a.vocab + kSChunk - 1) / kSChunk;
+  const unsigned bz = a.batch > 1 ? a.batch : 1;
   if (!radix_path(a.top_k, a.vocab)) {
     const FullScratch fs = full_scratch(a.scratch, a.n_draft, a.vocab);
     (void)hipGetLastError();
     int slot = -1;
     time_mark(TIME_VERIFY, true, s, &slot);
-    hipLaunchKernelGGL(k_full_transform, dim3(nb, rows), dim3(kVThreads), 0, s, a, fs, nb);
+    hipLaunchKernelGGL(k_full_transform, dim3(nb, rows, bz), dim3(kVThreads), 0, s, a, fs, nb);
     time_mark(TIME_VERIFY, false, s, &slot);
-    hipLaunchKernelGGL(k_full_select, dim3(rows), dim3(kFThreads), 0, s, a, fs, nb);
-    hipLaunchKernelGGL(k_full_decide, dim3(1), dim3(kFThreads), 0, s, a, fs);
+    hipLaunchKernelGGL(k_full_select, dim3(rows, 1, bz), dim3(kFThreads), 0, s, a, fs, nb);
+    hipLaunchKernelGGL(k_full_decide, dim3(1, 1, bz), dim3(kFThreads), 0, s, a, fs);
     return hipGetLastError();
   }
   const int kk = a.top_k < kSChunk ? a.top_k : kSChunk;
@@ -910,10 +957,10 @@ hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
   (void)hipGetLastError();
   int slot = -1;
   time_mark(TIME_VERIFY, true, s, &slot);
-  hipLaunchKernelGGL(k_sample_chunk, dim3(nb, rows), dim3(kVThreads), 0, s, a, sc, nb, kk);
+  hipLaunchKernelGGL(k_sample_chunk, dim3(nb, rows, bz), dim3(kVThreads), 0, s, a, sc, nb, kk);
   time_mark(TIME_VERIFY, false, s, &slot);
-  hipLaunchKernelGGL(k_sample_row, dim3(rows), dim3(kVThreads), 0, s, a, sc, nb, kk, a.top_k);
-  hipLaunchKernelGGL(k_sample_decide, dim3(1), dim3(64), 0, s, a, sc);
+  hipLaunchKernelGGL(k_sample_row, dim3(rows, 1, bz), dim3(kVThreads), 0, s, a, sc, nb, kk, a.top_k);
+  hipLaunchKernelGGL(k_sample_decide, dim3(1, 1, bz), dim3(64), 0, s, a, sc);
   return hipGetLastError();
 }
 

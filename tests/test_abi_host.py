@@ -141,3 +141,39 @@ def test_static_step_rejects_oversized_scratch_on_host():
                                              None) == abi.MTP_E_INVALID_ARG
     finally:
         abi.lib.mtp_head_destroy(h)
+
+
+def test_batch_calls_fail_closed_on_the_host():
+    """The batched calls reject a batch outside 1..MTP_MAX_BATCH, a bad count
+    stride and a short workspace before anything is enqueued."""
+    s = I.TINY_F32
+    cfg = abi.config_of(s)
+    assert abi.lib.mtp_batch_workspace_bytes(C.byref(cfg), 0, 3, 256) == 0
+    assert abi.lib.mtp_batch_workspace_bytes(C.byref(cfg), 17, 3, 256) == 0
+    one = abi.lib.mtp_batch_workspace_bytes(C.byref(cfg), 1, 3, 256)
+    four = abi.lib.mtp_batch_workspace_bytes(C.byref(cfg), 4, 3, 256)
+    assert 0 < one < four
+    h = C.c_void_p()
+    assert abi.lib.mtp_head_create(C.byref(cfg), C.byref(fake_weights(s)), C.byref(h)) == 0
+    try:
+        kv = abi.mtp_kv(0x1000, 0x2000, 256, 0x3000)
+        args = lambda b, stride, ws: (h, C.byref(kv), b, 0x4000, 0x5000, 3, 0x6000, stride, 2, 0x7000, 0x8000000,
+                                      None, 0x9000, ws, None)
+        f = abi.lib.mtp_draft_chain_batch
+        assert f(*args(17, 1, four)) == abi.MTP_E_INVALID_ARG
+        assert f(*args(0, 1, four)) == abi.MTP_E_INVALID_ARG
+        assert f(*args(4, 0, four)) == abi.MTP_E_INVALID_ARG
+        assert f(*args(4, 1, four - 1)) == abi.MTP_E_WORKSPACE
+        sp = abi.sampling()
+        v = abi.lib.spec_verify_batch
+        per = abi.lib.spec_verify_workspace_bytes(2, 1000)
+        assert v(C.byref(sp), 17, 2, 1000, 0x1, None, 0x2, 0x3, 0x4, None, 0x5, 0x6, 0x7, 17 * per, None) == \
+            abi.MTP_E_INVALID_ARG
+        assert v(C.byref(sp), 3, 2, 1000, 0x1, None, 0x2, 0x3, 0x4, None, 0x5, 0x6, 0x7, 3 * per - 1, None) == \
+            abi.MTP_E_WORKSPACE
+        assert abi.lib.kv_rollback_batch(C.byref(kv), 17, -1, None, 2, None) == abi.MTP_E_INVALID_ARG
+        assert abi.lib.kv_rollback_batch(C.byref(kv), 2, 5, 0x10, 2, None) == abi.MTP_E_INVALID_ARG
+        assert abi.lib.mtp_repair_pending_batch(17, 0x1, 0x2, 0x3, 256, abi.MTP_F32, 2, 0x4, 0x900000, 0x5,
+                                                None) == abi.MTP_E_INVALID_ARG
+    finally:
+        abi.lib.mtp_head_destroy(h)

@@ -205,6 +205,27 @@ def test_qwen27b_rounds_parity(qwen):
     assert ks == plan and near <= 1
 
 
+@pytest.mark.timeout(900)
+def test_batch_qwen27b_rounds(qwen):
+    """Two sessions of the 27B-shaped head (prefixes 4096 and 4000) for three
+    rounds with ragged planted acceptance: the flushes and steps of both
+    sessions share one pass over the weights (matrix-core products for the
+    flush and step projections, two-row unembedding)."""
+    from tests.test_gpu_batch import batch_session, run_batch_rounds
+    shape, gh, oh = qwen["shape"], qwen["gh"], qwen["oh"]
+    cap = QWEN_CTX + 64
+    gh, oh, gkv, states, hid0s = batch_session(shape, I.WL_QWEN, [QWEN_CTX, QWEN_CTX - 96], cap, gh=gh, oh=oh)
+    plan = [[0, 2], [2, 1], [1, 0]]
+
+    def targets(rnd, b, drafts_b):
+        rows = I.logits_rows(I.WL_QWEN, 5, (930, rnd, b), 3, shape.vocab, 3.0)[0]
+        I.plant_acceptance(rows, np.asarray(drafts_b, np.int64), plan[rnd][b])
+        return rows, I.target_hiddens(shape, I.WL_QWEN, (931, rnd, b), 3)
+
+    ks = run_batch_rounds(shape, gh, gkv, states, hid0s, 2, targets, 3, "A")
+    assert ks == plan
+
+
 @pytest.fixture(scope="module")
 def qwen_i8():
     """The 27B-shaped head with its borrowed lm_head stored int8 per (row,

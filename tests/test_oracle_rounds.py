@@ -192,3 +192,32 @@ def test_planted_rows_give_planted_k():
         I.plant_acceptance(rows, d, k)
         out = verify(Sampling(), rows, None, list(d), np.zeros(4, np.int32), np.array([0, 0], np.int32))
         assert out["k"] == k and out["tokens"][:k] == [int(t) for t in d[:k]]
+
+
+@pytest.mark.parametrize("policy", ["A", "B"])
+def test_batch_ragged_acceptance_equals_classic_per_session(policy):
+    """B = 3 sessions with different prompt lengths, targets and head behaviour
+    (two follow their successor heads' drafts with different rates, one never
+    does), driven together round by round: acceptance is ragged (the sessions'
+    k differ within rounds), every session's committed stream is its own classic
+    greedy decode, and every session keeps its own invariant
+    kv.len + pending = committed - 1."""
+    from oracle import batch as Bt
+    head = successor_head()
+    tgts = [I.ToyTarget(40 + b, SHAPE.vocab, SHAPE.hidden, follow=f) for b, f in enumerate([0.9, 0.5, 0.0])]
+    states, starts = [], []
+    for b, tgt in enumerate(tgts):
+        st, _ = session(head, tgt, prompt_len=L0 + 2 + b)
+        states.append(st)
+        starts.append(list(st.committed))
+    fns = [target_fn_of(t) for t in tgts]
+    ragged = 0
+    for _ in range(10):
+        outs = Bt.run_batch_round(states, 3, fns, policy=policy)
+        ks = [o["k"] for o in outs]
+        ragged += len(set(ks)) > 1
+        assert all(st.invariant() for st in states)
+    assert ragged >= 3
+    for st, start, fn in zip(states, starts, fns):
+        assert st.committed == R.classic_greedy(fn, start, len(st.committed) - len(start))
+    assert len({st.kv.len for st in states}) > 1          # the sessions sit at different lengths
