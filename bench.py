@@ -126,8 +126,13 @@ def source_digest(files):
     return h.hexdigest()[:16]
 
 
+# the sources of the unembedding GEMV launch (kernel template, its bf16
+# single-row instantiation, the dispatch, shared headers)
+UNEMBED_SOURCES = ("gemv_impl.h", "gemv_bf16_1.hip", "gemv.hip", "common.h", "kernels.h")
+
+
 def gemv_source_digest():
-    return source_digest(("gemv.hip", "common.h", "kernels.h"))
+    return source_digest(UNEMBED_SOURCES)
 
 
 def measured_traffic(name, files):
@@ -175,6 +180,36 @@ def timed_sample(unit_fn, seconds, max_units):
     return n, time.perf_counter() - t
 
 
+def host_info():
+    """The host the oracle baseline runs on: CPU model, logical CPUs, 1-minute load."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus": os.cpu_count(), "load_1m": round(os.getloadavg()[0], 2)}
+
+
+def with_host(cpu):
+    """A cpu_baseline entry with the host's CPU model and load added."""
+    if cpu is not None:
+        h = host_info()
+        cpu.update({"cpu_model": h["cpu_model"], "host_cpus": h["cpus"], "load_1m": h["load_1m"]})
+    return cpu
+
+
+def spread(values, digits=3):
+    """Median of repeated measurements with their min and max (the pages' method:
+    each arm run several times, median reported with its range)."""
+    import statistics
+    return {"median": round(statistics.median(values), digits), "min": round(min(values), digits),
+            "max": round(max(values), digits), "n": len(values)}
+
+
 def roofline(bound, achieved, peak, unit, traffic, **extra):
     if achieved is None:
         return None
@@ -206,7 +241,7 @@ def calibrate_copy(args):
 # ---------------------------------------------------------------------------
 # greedy rounds (the 27B-shaped head; the tiny fp32 head)
 # ---------------------------------------------------------------------------
-def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
+def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False):
     import numpy as np
     import torch
 
@@ -218,7 +253,7 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
     storage = I.head_weights(shape, wl)
     log(f"weights generated in {time.time() - t0:.1f}s")
     head = abi.Head(shape, storage)
-    cap = ctx + 1 + (args.warmup + args.steps + 4) * (N + 1) + 64
+    cap = ctx + 1 + (args.warmup + 2 * args.repeats * args.steps + POOL + 4) * (N + 1) + 64
     kp, vp = I.prefix_kv(shape, wl, ctx, cap)
     # one device buffer {KV state words | k, k+1, committed tokens}: the round's
     # results reach the host in one copy
@@ -251,7 +286,7 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
     io[2:] = abi.to_device(first_tok)
     t_hid[POOL - 1].copy_(abi.to_device(first_hid))
     host = torch.zeros((POOL, iost.numel()), dtype=torch.int32).pin_memory()
-    totals = {"committed": 0, "accepted": 0}
+    totals = {"committed": 0, "accepted": 0, "rounds": 0}
 
     def enqueue_round(r, st):
         prev = (r - 1) % POOL
@@ -268,6 +303,7 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
             raise RuntimeError(f"device error word {int(row[3])} in round {r}")
         totals["committed"] += int(row[5])
         totals["accepted"] += int(row[4])
+        totals["rounds"] += 1
 
     for r in range(args.warmup):                       # eager rounds
         enqueue_round(r, stream)
@@ -275,53 +311,69 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
         consume(r)
     log(f"warmup {args.warmup} rounds done")
 
-    graphs = None
-    if args.graph:
-        # one graph per pool slot (kernel timing is not available for captured
-        # launches, so the roofline is left null in this mode)
+    def repeat(graphs, first):
+        """One timed repeat of args.steps rounds starting at round `first`;
+        returns its elapsed seconds."""
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        done = [torch.cuda.Event(), torch.cuda.Event()]
+        prev = None
+        for r in range(first, first + args.steps):
+            if graphs is not None:
+                graphs[r % POOL].replay()
+            else:
+                if r % TIME_EVERY == 0 or r == first:
+                    abi.mtp_timing_pause(False)
+                enqueue_round(r, stream)
+                abi.mtp_timing_pause(True)
+            done[r % 2].record(stream)
+            if prev is not None:                          # the one host sync per round,
+                done[prev % 2].synchronize()              # overlapped with the next round
+                consume(prev)
+            prev = r
+        done[prev % 2].synchronize()
+        consume(prev)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t_start
+
+    host0 = host_info()
+    eager_el, graph_el = [], []
+    r0 = args.warmup
+    if not args.graph:
+        abi.mtp_timing_begin(abi.TIME_UNEMBED, args.repeats * args.steps * N + 4)
+        for _ in range(args.repeats):
+            eager_el.append(repeat(None, r0))
+            r0 += args.steps
+        lm_ms, lm_n = abi.mtp_timing_end()
+    else:
+        lm_ms, lm_n = 0.0, 0
+    if args.graph or use_graphs:
+        # one graph per pool slot, replayed round by round (every pointer of a
+        # round is fixed; the counts and tokens are device-resident)
         cap_stream = torch.cuda.Stream()
         graphs = {}
         for p_ in range(POOL):
-            r = args.warmup + p_
+            r = r0 + p_
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap_stream):
                 enqueue_round(r, torch.cuda.current_stream())
             graphs[r % POOL] = g
         torch.cuda.synchronize()
         log("captured %d round graphs" % POOL)
-    else:
-        abi.mtp_timing_begin(abi.TIME_UNEMBED, args.steps * N + 4)
-
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    done = [torch.cuda.Event(), torch.cuda.Event()]
-    prev = None
-    for r in range(args.warmup, args.warmup + args.steps):
-        if graphs is not None:
-            graphs[r % POOL].replay()
-        else:
-            if r % TIME_EVERY == 0 or r == args.warmup:
-                abi.mtp_timing_pause(False)
-            enqueue_round(r, stream)
-            abi.mtp_timing_pause(True)
-        done[r % 2].record(stream)
-        if prev is not None:                          # the one host sync per round,
-            done[prev % 2].synchronize()              # overlapped with the next round
-            consume(prev)
-        prev = r
-    done[prev % 2].synchronize()
-    consume(prev)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    lm_ms, lm_n = (0.0, 0) if graphs is not None else abi.mtp_timing_end()
-    log(f"timed {args.steps} rounds in {elapsed * 1e3:.1f} ms; unembedding {lm_n} launches")
+        for _ in range(args.repeats):
+            graph_el.append(repeat(graphs, r0))
+            r0 += args.steps
+    host1 = host_info()
+    els = graph_el if graph_el else eager_el
+    elapsed = sorted(els)[len(els) // 2]                 # the median repeat
+    log(f"timed {args.repeats} x {args.steps} rounds; median {elapsed * 1e3:.1f} ms; unembedding {lm_n} launches")
     calibrate_copy(args)
 
     rounds_s = args.steps / elapsed
     lm_avg_s = lm_ms / lm_n / 1e3 if lm_n else None
     ub = unembed_bytes(shape)
     round_bytes = N * step_bytes(shape, ctx + 2) + (N + 1) * V * 4
-    traffic = measured_traffic("unembed_qwen35_27b_traffic", ("gemv.hip", "common.h", "kernels.h")) \
+    traffic = measured_traffic("unembed_qwen35_27b_traffic", UNEMBED_SOURCES) \
         if workload == "qwen35_27b_mtp_head_round" else None
 
     cpu = None
@@ -339,14 +391,18 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data):
         "rounds_per_s": round(rounds_s, 2),
         "round_gbs": round(round_bytes / (elapsed / args.steps) / 1e9, 1),
         "round_hbm_frac": round(round_bytes / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
-        "committed_per_round": round(totals["committed"] / (args.warmup + args.steps), 4),
-        "launch": ("hip graph per round" if args.graph else "eager") +
+        "repeats": {"draft_tokens_per_s": spread([N * args.steps / e for e in els], 2),
+                    "ms_per_round": spread([e / args.steps * 1e3 for e in els], 4)},
+        "eager_draft_tokens_per_s": spread([N * args.steps / e for e in eager_el], 2) if eager_el else None,
+        "committed_per_round": round(totals["committed"] / max(1, totals["rounds"]), 4),
+        "launch": ("hip graph per round" if graph_el else "eager") +
                   ", host sync per round overlapped with the next round",
+        "host": {"before": host0, "after": host1},
         "roofline": roofline("hbm", ub / lm_avg_s / 1e9 if lm_avg_s else None, HBM_PEAK_GBS, "GB/s", traffic,
                              kernel=f"unembedding GEMV (lm_head {V}x{H} {shape.lm_head_dtype})",
                              bytes_per_launch=ub, avg_us=round(lm_avg_s * 1e6, 2) if lm_avg_s else None,
                              launches=lm_n),
-        "cpu_baseline": cpu,
+        "cpu_baseline": with_host(cpu),
     })
     return out
 
@@ -414,10 +470,11 @@ def run_flush(args, big=False):
     amax = torch.zeros(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def flush(mode):
+    def flush(mode, st=None):
+        st = stream if st is None else st
         abi.mtp_flush_pairs(head, kv, toks, hids, n, None, mode, 1, hout if mode == abi.ALL else hout[:1],
-                            logits, amax, ws, stream)
-        abi.kv_rollback(kv, prefix, None, 0, stream)
+                            logits, amax, ws, st)
+        abi.kv_rollback(kv, prefix, None, 0, st)
 
     def timed(mode, steps, kind=None):
         for _ in range(args.warmup):
@@ -443,6 +500,24 @@ def run_flush(args, big=False):
     _, (proj_ms, proj_n) = timed(abi.ALL, side, abi.TIME_PROJECTION)
     t_last, _ = timed(abi.LAST, side)
     t_kv, _ = timed(abi.KV_ONLY, side)
+    # the same ALL-mode flush (and its rollback) replayed from one HIP graph:
+    # no host launch gaps between its kernels
+    graph = torch.cuda.CUDAGraph()
+    cap_stream = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap_stream):
+        flush(abi.ALL, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g_els = []
+    for _ in range(args.repeats):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_els.append((time.perf_counter() - t) / args.steps)
+    if int(kv.state[3].item()) != 0:
+        raise RuntimeError("device error word set")
+    t_graph = sorted(g_els)[len(g_els) // 2]
     calibrate_copy(args)
     att_flops = flush_attention_flops(shape, prefix, n)
     proj_flops = flush_projection_flops(shape, n, n)
@@ -456,7 +531,7 @@ def run_flush(args, big=False):
                         cache_fp64=big)
     heads = f"{shape.n_q_heads}q/{shape.n_kv_heads}kv"
     name = "flush256_qwen35_27b_prefix4096" if big else "flush256_prefix8192"
-    out = base_line(args, round(n / t_all, 1), "flushed pairs/s", t_all * 1e3, "bf16",
+    out = base_line(args, round(n / t_graph, 1), "flushed pairs/s", t_graph * 1e3, "bf16",
                     f"synthetic (seeded N(0,0.02) weights of the {'Qwen3.5-27B-shaped' if big else 'tiny'} head "
                     "in bf16; 256 uniform tokens, N(0,1) bf16 hiddens; N(0,1) bf16 prefix K/V)",
                     {"workload": name, "hidden": shape.hidden, "heads": heads, "head_dim": shape.head_dim,
@@ -473,9 +548,12 @@ def run_flush(args, big=False):
                                "8193..8448 keys; split-K partials)",
                         flops_per_launch=att_flops, avg_us=round(att_avg * 1e6, 2), launches=att_n)
     out.update({
-        "flush_us": {"all": round(t_all * 1e6, 2), "last": round(t_last * 1e6, 2), "kv_only": round(t_kv * 1e6, 2)},
-        "flush_tflops": round(total_flops / t_all / 1e12, 3),
-        "flush_mfma_frac": round(total_flops / t_all / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+        "launch": "one HIP graph per flush (with its rollback to the prefix), replayed",
+        "repeats": {"flush_us": spread([t * 1e6 for t in g_els], 2)},
+        "flush_us": {"all_graph": round(t_graph * 1e6, 2), "all_eager": round(t_all * 1e6, 2),
+                     "last_eager": round(t_last * 1e6, 2), "kv_only_eager": round(t_kv * 1e6, 2)},
+        "flush_tflops": round(total_flops / t_graph / 1e12, 3),
+        "flush_mfma_frac": round(total_flops / t_graph / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
         "algorithmic_gflop": {"attention": round(att_flops / 1e9, 4), "projections": round(proj_flops / 1e9, 4)},
         "attention_us": round(att_avg * 1e6, 2),
         "attention_tflops": round(att_flops / att_avg / 1e12, 2),
@@ -483,7 +561,7 @@ def run_flush(args, big=False):
         "projection_tflops": round(gemm_flops / proj_s / 1e12, 2),
         "projection_launches_per_flush": proj_n // timed_side,
         "roofline": line,
-        "cpu_baseline": cpu,
+        "cpu_baseline": with_host(cpu),
     })
     return out
 
@@ -714,7 +792,7 @@ def run_verify(args):
                                      "row maxima; transformed rows written back)" if full else
                                      "per-chunk top-k pass over the 9 rows (penalty, temperature, radix select)"),
                              bytes_per_launch=chunk_bytes, avg_us=round(avg * 1e6, 2), launches=nl),
-        "cpu_baseline": cpu,
+        "cpu_baseline": with_host(cpu),
     })
     return out
 
@@ -946,7 +1024,7 @@ def run_depth(args, N, lm):
                              kernel="split-K attention over the 32768+ slot draft KV (2 kv heads, D 64, bf16)",
                              bytes_per_launch=round(att_bytes / att_n), avg_us=round(att_avg * 1e6, 2),
                              launches=att_n),
-        "cpu_baseline": cpu,
+        "cpu_baseline": with_host(cpu),
     })
     return out
 
@@ -1097,7 +1175,7 @@ def run_depth_auto(args):
         "roofline": roofline("hbm", att_bytes / (att_ms / 1e3) / 1e9 if att_n else None, HBM_PEAK_GBS, "GB/s",
                              None, kernel="decode attention over the 32768-slot draft KV (chunk partials)",
                              avg_us=round(att_avg * 1e6, 2) if att_avg else None, launches=att_n),
-        "cpu_baseline": cpu,
+        "cpu_baseline": with_host(cpu),
     })
     return out
 
@@ -1214,7 +1292,9 @@ def main():
                     help="also run three 1 GiB device-to-device copies (a plain copy kernel of known "
                          "size, to scale HBM traffic counters)")
     ap.add_argument("--graph", action="store_true",
-                    help="greedy rounds: replay rounds from HIP graphs (no kernel timing in this mode)")
+                    help="qwen35_27b_round: replay rounds from HIP graphs only (no kernel timing in this mode)")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed repeats of --steps steps; the line reports the median with min and max")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the MTP round is a batch-1 path on a single MI355X; "
@@ -1239,7 +1319,7 @@ def main():
     elif args.workload == "tiny_round":
         lines = [run_greedy_rounds(args, I.TINY_F32, I.WL_TINY, 128, 2, "tiny_f32_head_round",
                                    "synthetic (seeded N(0,0.02) tiny-head weights in fp32; N(0,3) target "
-                                   "logits, N(0,1) target hiddens)")]
+                                   "logits, N(0,1) target hiddens)", use_graphs=True)]
     elif args.workload == "flush256_prefix8192":
         lines = [run_flush(args)]
     elif args.workload == "flush256_qwen35_27b":
