@@ -823,6 +823,19 @@ def cpu_verify(rows, drows, ring0, st0, wl, N, seconds, max_rounds, top_k=40):
 # ---------------------------------------------------------------------------
 # depth sweep over a 32768-slot prefix
 # ---------------------------------------------------------------------------
+def committed_check(committed, expected):
+    """The mean committed tokens per round against the closed form
+    1 + sum_j prod_{i<j} p_i: a z-score over the rounds' own spread, passing
+    within 4 standard errors."""
+    import numpy as np
+    c = np.asarray(committed, dtype=np.float64)
+    R = len(c)
+    se = float(c.std(ddof=1)) / np.sqrt(R) if R > 1 else float("nan")
+    z = (float(c.mean()) - expected) / se if se > 0 else 0.0
+    return {"rounds": R, "mean": round(float(c.mean()), 4), "std_err": round(se, 4), "z": round(z, 2),
+            "within_4_se": bool(abs(z) <= 4.0)}
+
+
 def run_depth(args, N, lm):
     import numpy as np
     import torch
@@ -1019,6 +1032,7 @@ def run_depth(args, N, lm):
         "us_per_draft_step": round(step_us, 2),
         "committed_per_round": round(committed_tok / args.steps, 4),
         "committed_per_round_closed_form": round(expected, 4),
+        "committed_check": committed_check(ks + 1, expected),
         "committed_tokens_per_s": round(committed_tok / el, 1),
         "roofline": roofline("hbm", att_bytes / (att_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s", None,
                              kernel="split-K attention over the 32768+ slot draft KV (2 kv heads, D 64, bf16)",

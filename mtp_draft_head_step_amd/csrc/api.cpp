@@ -66,6 +66,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr size_t kHeadBytes = 256;   // reserved at offset 0
 constexpr int kVerifyChunk = 4096;   // logits per verify workgroup
+constexpr int kFlushWgs = 512;       // flush attention workgroups (about two per compute unit)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -451,10 +452,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     t.nw_bf16 = h->wt == W_BF16; t.eps = c.rms_eps; t.theta = c.rope_theta;
   }
   if (mfma_out && c.kv_dtype == MTP_BF16) {
-    // matrix-core flush attention: workgroups of 64 query vectors, at most
-    // about two per compute unit (both fit at every head size)
+    // matrix-core flush attention: workgroups of 64 query vectors over
+    // kFlushWgs workgroups in all (key chunks of at least one block each)
     const int qblocks = (n_max * (hq / hkv) + 63) / 64;
-    int ns = 512 / (qblocks * hkv);
+    int ns = kFlushWgs / (qblocks * hkv);
+    ns = ns > kFlushMaxChunks ? kFlushMaxChunks : ns;
     t.mfma = 1;
     t.nchunk = ns < 1 ? 1 : (ns > L.nchunk ? L.nchunk : ns);
   }

@@ -493,12 +493,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.batch > 1 && !(a.row_sel == ROW_LAST && a.fuse_rope)) return hipErrorNotSupported;
   const int rows = (a.row_sel == ROW_LAST) ? (a.batch > 1 ? a.batch : 1) : a.n_max;
   const dim3 grid(a.nchunk, a.hkv, rows);
+  // the matrix-core flush attention launches its own merge
+  if (a.mfma && a.kv_bf16 && a.row_sel == ROWS_RANGE) return launch_attention_flush(a, s);
   hipError_t e;
   int slot = -1;
   time_mark(TIME_ATTENTION, true, s, &slot);
-  if (a.mfma && a.kv_bf16 && a.row_sel == ROWS_RANGE) {
-    e = launch_attention_flush(a, s);
-  } else if (a.kv_bf16) {
+  if (a.kv_bf16) {
     switch (a.d) {
       case 64: e = attn_d<true, 64>(a, grid, s); break;
       case 128: e = attn_d<true, 128>(a, grid, s); break;

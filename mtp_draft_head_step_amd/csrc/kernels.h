@@ -214,7 +214,9 @@ struct AttnArgs {
   float theta;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attention_flush(const AttnArgs& a, hipStream_t s);   // the mfma path's first kernel
+// the matrix-core flush attention and its merge (chunks at most kFlushMaxChunks)
+constexpr int kFlushMaxChunks = 128;
+hipError_t launch_attention_flush(const AttnArgs& a, hipStream_t s);
 
 // End of a step or flush: merge the unembedding's per-workgroup argmax keys
 // (if any) into *amax_out and commit the append: state[0] += n (state[1] too
