@@ -122,7 +122,9 @@ __device__ __forceinline__ void unpack16(const uint4& v, float (&f)[KVB ? 8 : 4]
 // value by the lane that computed it.
 template <int D, typename Put>
 __device__ __forceinline__ void norm_rope_head(const float* src, const void* nw, int nw_bf16, float eps,
-                                               int pos, double l2t, int lane, Put put) {
+                                               int pos, double l2t, int lane, Put put,
+                                               const float2* cs = nullptr) {
+  // cs: (cos, sin) of every rotation pair at `pos`, if the caller has them
   // every load first (one memory round trip), then the arithmetic in the same
   // per-lane order as an element-at-a-time loop: lane holds d = lane + 64 k
   constexpr int NE = D / 64;                 // elements per lane (D >= 64)
@@ -152,7 +154,7 @@ __device__ __forceinline__ void norm_rope_head(const float* src, const void* nw,
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < NE; ++k) ss += x[k] * x[k];
-  ss = wave_sum(ss);
+  ss = group_sum_all(ss, 64);
   const float inv = rsqrtf(ss / static_cast<float>(D) + eps);
   // element i + D / 2 of pair r: with D >= 128 it is this lane's x[r + NE / 2];
   // with D = 64 it sits in lane + 32
@@ -165,7 +167,12 @@ __device__ __forceinline__ void norm_rope_head(const float* src, const void* nw,
       const float xb = (D >= 128) ? x[(r + NE / 2) % NE] : up;
       const float x1 = xa * inv * __uint_as_float(b1[r] << wsh), x2 = xb * inv * __uint_as_float(b2[r] << wsh);
       float c, sn;
-      rope_cs(pos, i, D, l2t, c, sn);
+      if (cs) {
+        c = cs[i].x;
+        sn = cs[i].y;
+      } else {
+        rope_cs(pos, i, D, l2t, c, sn);
+      }
       put(i, x1 * c - x2 * sn);
       put(i + D / 2, x1 * sn + x2 * c);
     }
@@ -182,6 +189,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
   __shared__ float s_o[kAttnWaves][G][D];
   __shared__ float s_q[FUSE ? G : 1][FUSE ? D : 1];
+  __shared__ float2 s_cs[FUSE ? D / 2 : 1];   // RoPE (cos, sin) at the query's position
 
   // several sessions (ROW_LAST with the fused append only): blockIdx.z is the
   // session, with its own state words, K/V and workspace rows
@@ -237,9 +245,35 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   const int li = lane % LPK;
   const int d0 = li * EPL;
   const float scale = rsqrtf(static_cast<float>(D));
+
+  // The first step's K and V rows are loaded before anything else: they do not
+  // depend on the query, so their memory latency overlaps the fused norm / RoPE
+  // prologue.  Rows of slots appended by this launch (>= off) are read again
+  // after the prologue's barrier.
+  const size_t head_off = static_cast<size_t>(h) * a.capacity * D;
+  const char* kbase = static_cast<const char*>(kcs) + (head_off + d0) * ebytes;
+  const char* vbase = static_cast<const char*>(vcs) + (head_off + d0) * ebytes;
+  constexpr int row_bytes = D * ebytes;
+  constexpr int kstride = KPI * kAttnWaves;   // keys between a group's consecutive keys
+  const int base0 = k0 + wave * KPI;
+  uint4 kv[KB], vv[KB];
+#pragma unroll
+  for (int b = 0; b < KB; ++b) {
+    const int kk = base0 + grp + b * kstride;
+    const int kc = kk < k1 ? kk : k0;           // a valid row; result masked below
+    kv[b] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(kc) * row_bytes);
+    vv[b] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(kc) * row_bytes);
+  }
+
   float qr[G][EPL];
   if constexpr (FUSE) {
     const double l2t = log2(static_cast<double>(a.theta));
+    // the rotation of the query position, once per workgroup for all its heads
+    if (tid < D / 2) {
+      float c, sn;
+      rope_cs(off + j, tid, D, l2t, c, sn);
+      s_cs[tid] = make_float2(c, sn);
+    }
     // new slots in this chunk: k normed and roped, k and v appended (a wave per slot)
     const int s0 = max(off, k0), s1 = min(off + n, k1);
     for (int sl = s0 + wave; sl < s1; sl += kAttnWaves) {
@@ -260,17 +294,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       }
     }
     // the query heads of this kv head, row j, normed and roped
+    __syncthreads();   // the rotation table is complete
     const float* qrow = a.qkv + static_cast<size_t>(jf) * a.ld_qkv;
     for (int g = wave; g < G; g += kAttnWaves) {
       float* qd = s_q[g];
       norm_rope_head<D>(qrow + (h * G + g) * D, a.q_norm, a.nw_bf16, a.eps, off + j, l2t, lane,
-                        [&](int d, float v) { qd[d] = v; });
+                        [&](int d, float v) { qd[d] = v; }, s_cs);
     }
     __syncthreads();   // the appended rows and the queries are visible to the whole workgroup
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) qr[g][e] = s_q[g][d0 + e] * scale;
+    if (k1 > off) {   // this chunk holds appended slots: their rows again
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        const int kk = base0 + grp + b * kstride;
+        if (kk >= off && kk < k1) {
+          kv[b] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(kk) * row_bytes);
+          vv[b] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(kk) * row_bytes);
+        }
+      }
+    }
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -279,12 +324,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       for (int e = 0; e < EPL; ++e) qr[g][e] = qp[e] * scale;
     }
   }
-
-  const size_t head_off = static_cast<size_t>(h) * a.capacity * D;
-  const char* kbase = static_cast<const char*>(kcs) + (head_off + d0) * ebytes;
-  const char* vbase = static_cast<const char*>(vcs) + (head_off + d0) * ebytes;
-  constexpr int row_bytes = D * ebytes;
-  constexpr int kstride = KPI * kAttnWaves;   // keys between a group's consecutive keys
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -295,17 +334,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  // wave-uniform trip count so every lane takes part in the group reductions
-  for (int base = k0 + wave * KPI; base < k1; base += KB * kstride) {
-    uint4 kv[KB], vv[KB];
+  // wave-uniform trip count so every lane takes part in the group reductions;
+  // the next step's rows are loaded while this step's are used
+  for (int base = base0; base < k1; base += KB * kstride) {
     bool ok[KB];
 #pragma unroll
+    for (int b = 0; b < KB; ++b) ok[b] = base + grp + b * kstride < k1;
+    uint4 kn[KB], vn[KB];
+#pragma unroll
     for (int b = 0; b < KB; ++b) {
-      const int kk = base + grp + b * kstride;
-      ok[b] = kk < k1;
-      const int kc = ok[b] ? kk : k0;           // a valid row; result masked below
-      kv[b] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(kc) * row_bytes);
-      vv[b] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(kc) * row_bytes);
+      const int kk = base + KB * kstride + grp + b * kstride;
+      const int kc = kk < k1 ? kk : k0;         // past the chunk: a valid row, unused
+      kn[b] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(kc) * row_bytes);
+      vn[b] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(kc) * row_bytes);
     }
     float sc[KB][G];
 #pragma unroll
@@ -317,7 +358,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         float p = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) p += qr[g][e] * kf[e];
-        p = group_sum(p, LPK);
+        p = group_sum_all(p, LPK);
         sc[b][g] = ok[b] ? p : kNeg;
       }
     }
@@ -345,23 +386,32 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         for (int e = 0; e < EPL; ++e) acc[g][e] += p * vf[e];
       }
     }
-  }
-
-  // merge the wave's lane groups (same head_dim slice, different keys)
 #pragma unroll
-  for (int o = LPK; o < 64; o <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], o, 64);
-      const float lo = __shfl_xor(l[g], o, 64);
-      const float mnew = fmaxf(m[g], mo);
-      const float ra = __expf(m[g] - mnew), rb = __expf(mo - mnew);
-      l[g] = l[g] * ra + lo * rb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * ra + __shfl_xor(acc[g][e], o, 64) * rb;
-      m[g] = mnew;
+    for (int b = 0; b < KB; ++b) {
+      kv[b] = kn[b];
+      vv[b] = vn[b];
     }
   }
+
+  // merge the wave's lane groups (same head_dim slice, different keys): the
+  // partner of a lane is lane ^ o, o = LPK, 2 LPK, .., 32
+#define MTP_ATTN_MERGE(O)                                                                  \
+  if constexpr (LPK <= (O)) {                                                              \
+    _Pragma("unroll") for (int g = 0; g < G; ++g) {                                        \
+      const float mo = xor_lane<O>(m[g]);                                                  \
+      const float lo = xor_lane<O>(l[g]);                                                  \
+      const float mnew = fmaxf(m[g], mo);                                                  \
+      const float ra = __expf(m[g] - mnew), rb = __expf(mo - mnew);                        \
+      l[g] = l[g] * ra + lo * rb;                                                          \
+      _Pragma("unroll") for (int e = 0; e < EPL; ++e)                                      \
+        acc[g][e] = acc[g][e] * ra + xor_lane<O>(acc[g][e]) * rb;                          \
+      m[g] = mnew;                                                                         \
+    }                                                                                      \
+  }
+  MTP_ATTN_MERGE(8)
+  MTP_ATTN_MERGE(16)
+  MTP_ATTN_MERGE(32)
+#undef MTP_ATTN_MERGE
   if (grp == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -393,7 +443,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 }
 
 // One workgroup per (row, query head): chunk weights exp(m_c - M) in LDS, then
-// every thread sums its head_dim column over the chunks (independent loads).
+// every thread sums its head_dim column over the chunks.  The column loads of
+// the first kMergePre chunks are issued with the (m, l) loads, before the
+// weights are known, so the merge costs about one memory round trip.
+constexpr int kMergePre = 64;
+
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   __shared__ float wts[kMaxChunks];
   __shared__ float red[4];
@@ -413,6 +467,15 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int nc = a.nchunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t base = (static_cast<size_t>(j) * a.hq + hq) * nc;
+  const float* po = a.part_o + base * D;
+  const int d = tid;                   // this thread's column (D <= 256)
+  const int npre = nc < kMergePre ? nc : kMergePre;
+  float v[kMergePre];
+  if (d < D) {
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u)
+      if (u < npre) v[u] = po[static_cast<size_t>(u) * D + d];
+  }
   float m = -INFINITY;
   for (int c = tid; c < nc; c += 256) m = fmaxf(m, a.part_ml[(base + c) * 2]);
   m = wave_max(m);
@@ -434,37 +497,44 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   __syncthreads();
   if (tid == 0) s_den = red[0] + red[1] + red[2] + red[3];
   __syncthreads();
+  if (d >= D) return;
   const float inv = 1.0f / s_den;
-  const float* po = a.part_o + base * D;
-  for (int d = tid; d < D; d += 256) {
-    float num0 = 0.f, num1 = 0.f, num2 = 0.f, num3 = 0.f;
-    int c = 0;
-    // sixteen chunk loads in flight per round trip; accumulator k still takes
-    // the chunks c = k (mod 4) in increasing order
-    for (; c + 16 <= nc; c += 16) {
-      float v[16];
+  // accumulator k takes the chunks c = k (mod 4) in increasing order
+  float num0 = 0.f, num1 = 0.f, num2 = 0.f, num3 = 0.f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = po[static_cast<size_t>(c + u) * D + d];
-#pragma unroll
-      for (int u = 0; u < 16; u += 4) {
-        num0 += wts[c + u] * v[u];
-        num1 += wts[c + u + 1] * v[u + 1];
-        num2 += wts[c + u + 2] * v[u + 2];
-        num3 += wts[c + u + 3] * v[u + 3];
-      }
-    }
-    for (; c + 4 <= nc; c += 4) {
-      num0 += wts[c] * po[static_cast<size_t>(c) * D + d];
-      num1 += wts[c + 1] * po[static_cast<size_t>(c + 1) * D + d];
-      num2 += wts[c + 2] * po[static_cast<size_t>(c + 2) * D + d];
-      num3 += wts[c + 3] * po[static_cast<size_t>(c + 3) * D + d];
-    }
-    for (; c < nc; ++c) num0 += wts[c] * po[static_cast<size_t>(c) * D + d];
-    const float v = ((num0 + num1) + (num2 + num3)) * inv;
-    const size_t oi = static_cast<size_t>(j) * a.hq * D + hq * D + d;
-    if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(v);
-    else a.o[oi] = v;
+  for (int u = 0; u < kMergePre; u += 4) {
+    if (u < npre) num0 += wts[u] * v[u];
+    if (u + 1 < npre) num1 += wts[u + 1] * v[u + 1];
+    if (u + 2 < npre) num2 += wts[u + 2] * v[u + 2];
+    if (u + 3 < npre) num3 += wts[u + 3] * v[u + 3];
   }
+  int c = npre;
+  // the rest: sixteen chunk loads in flight per round trip
+  for (; c + 16 <= nc; c += 16) {
+    float w16[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) w16[u] = po[static_cast<size_t>(c + u) * D + d];
+#pragma unroll
+    for (int u = 0; u < 16; u += 4) {
+      num0 += wts[c + u] * w16[u];
+      num1 += wts[c + u + 1] * w16[u + 1];
+      num2 += wts[c + u + 2] * w16[u + 2];
+      num3 += wts[c + u + 3] * w16[u + 3];
+    }
+  }
+  for (; c < nc; ++c) {
+    const float x = wts[c] * po[static_cast<size_t>(c) * D + d];
+    switch (c & 3) {
+      case 0: num0 += x; break;
+      case 1: num1 += x; break;
+      case 2: num2 += x; break;
+      default: num3 += x; break;
+    }
+  }
+  const float out = ((num0 + num1) + (num2 + num3)) * inv;
+  const size_t oi = static_cast<size_t>(j) * a.hq * D + hq * D + d;
+  if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(out);
+  else a.o[oi] = out;
 }
 
 template <bool KVB, int D, bool FUSE>

@@ -50,8 +50,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
   constexpr int DK = D / 32;          // 32-wide head_dim steps of S^T
   constexpr int DT = D / 16;          // 16-row head_dim tiles of O^T
   constexpr float kNeg = -INFINITY;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kFKeys * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VLD];
+  // S register stages of K/V loads in flight and NB LDS buffers: head_dim
+  // 64 and 128 keep two blocks in flight and double-buffer LDS (one barrier
+  // per block); head_dim 256 needs its registers for the accumulators
+  constexpr int S = D <= 128 ? 2 : 1;
+  constexpr int NB = D <= 128 ? 2 : 1;
+  constexpr int KSZ = kFKeys * KLD, VSZ = D * VLD;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NB * KSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[NB * VSZ];
 
   const int32_t* st = a.state;
   if (st[3] != 0) return;
@@ -122,42 +128,54 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
   constexpr int KB = D / 32;                                 // V keys per thread
   constexpr int NG = kFKeys / KB;                            // V key groups
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-  u32x4v kpf[kKPer], vpf[KB];    // native vectors: kept in registers across the loop
+  u32x4v kpf[S][kKPer], vpf[S][KB];   // native vectors: kept in registers across the loop
   const int vg = tid % NG, vd = (tid / NG) * 8;
-  // the loads of the block at kb (written out, not in a lambda: the arrays
-  // must stay in registers)
-#define MTP_FLUSH_LOAD(kb)                                                                 \
+  // the loads of the block at kb into stage q (written out, not in a lambda:
+  // the arrays must stay in registers)
+#define MTP_FLUSH_LOAD(q, kb)                                                              \
   {                                                                                        \
     _Pragma("unroll") for (int u = 0; u < kKPer; ++u) {                                    \
       const int e = tid + 256 * u;                                                         \
       const int key = min((kb) + e / (D / 8), k1 - 1), d8 = (e % (D / 8)) * 8;             \
-      kpf[u] = *reinterpret_cast<const u32x4v*>(kc + static_cast<size_t>(key) * D + d8);   \
+      kpf[q][u] = *reinterpret_cast<const u32x4v*>(kc + static_cast<size_t>(key) * D + d8); \
     }                                                                                      \
     _Pragma("unroll") for (int j = 0; j < KB; ++j) {                                       \
       const int key = min((kb) + vg * KB + j, k1 - 1);                                     \
-      vpf[j] = *reinterpret_cast<const u32x4v*>(vc + static_cast<size_t>(key) * D + vd);   \
+      vpf[q][j] = *reinterpret_cast<const u32x4v*>(vc + static_cast<size_t>(key) * D + vd); \
     }                                                                                      \
   }
 
-  if (k0 < k1) MTP_FLUSH_LOAD(k0);
-  for (int kb = k0; kb < k1; kb += kFKeys) {
-    __syncthreads();   // the previous block's operand reads are done
+  if (k0 < k1) {
+#pragma unroll
+    for (int q = 0; q < S; ++q) MTP_FLUSH_LOAD(q, k0 + q * kFKeys);
+  }
+  for (int kb0 = k0; kb0 < k1; kb0 += S * kFKeys) {
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int kb = kb0 + q * kFKeys;
+    if (kb >= k1) break;   // uniform over the workgroup
+    uint16_t* const Kb = Ks + (q % NB) * KSZ;
+    uint16_t* const Vb = Vt + (q % NB) * VSZ;
+    // one LDS buffer: wait until the previous block's operand reads are done;
+    // two: the barrier of the previous block already ordered the reads of this
+    // buffer (two blocks back) before these writes
+    if (NB == 1) __syncthreads();
 #pragma unroll
     for (int u = 0; u < kKPer; ++u) {
       const int e = tid + 256 * u;
-      *reinterpret_cast<u32x4v*>(Ks + (e / (D / 8)) * KLD + (e % (D / 8)) * 8) = kpf[u];
+      *reinterpret_cast<u32x4v*>(Kb + (e / (D / 8)) * KLD + (e % (D / 8)) * 8) = kpf[q][u];
     }
     {
-      // word q of a piece holds dims 2q (low half) and 2q + 1 (high half)
+      // word w of a piece holds dims 2w (low half) and 2w + 1 (high half)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t o[KB / 2];
 #pragma unroll
         for (int p = 0; p < KB / 2; ++p) {
-          const uint32_t lo = vpf[2 * p][i >> 1], hi = vpf[2 * p + 1][i >> 1];
+          const uint32_t lo = vpf[q][2 * p][i >> 1], hi = vpf[q][2 * p + 1][i >> 1];
           o[p] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
         }
-        uint16_t* dst = Vt + (vd + i) * VLD + vg * KB;
+        uint16_t* dst = Vb + (vd + i) * VLD + vg * KB;
         if constexpr (KB == 2) {
           *reinterpret_cast<uint32_t*>(dst) = o[0];
         } else {
@@ -168,11 +186,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
       }
     }
     __syncthreads();
-    // the next block's loads fly during the products (unconditional: past the
-    // last block they reload the clamped last key, unused; a conditional load
-    // would keep the arrays out of registers)
-    MTP_FLUSH_LOAD(kb + kFKeys);
-#undef MTP_FLUSH_LOAD
+    // the loads S blocks ahead fly during the products (unconditional: past
+    // the last block they reload the clamped last key, unused; a conditional
+    // load would keep the arrays out of registers)
+    MTP_FLUSH_LOAD(q, kb + S * kFKeys);
 
     // S^T for four 16-key tiles
     f32x4v s[4];
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
 #pragma unroll
       for (int dk = 0; dk < DK; ++dk) {
         const bf16x8v kf = __builtin_bit_cast(bf16x8v,
-            *reinterpret_cast<const uint4*>(Ks + (kt * 16 + (lane & 15)) * KLD + dk * 32 + (lane >> 4) * 8));
+            *reinterpret_cast<const uint4*>(Kb + (kt * 16 + (lane & 15)) * KLD + dk * 32 + (lane >> 4) * 8));
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[dk], s[kt], 0, 0, 0);
       }
     }
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
           make_uint4(pw[2 * ks][0], pw[2 * ks][1], pw[2 * ks + 1][0], pw[2 * ks + 1][1]));
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const uint16_t* vrow = Vt + (t * 16 + (lane & 15)) * VLD + ks * 32 + (lane >> 4) * 4;
+        const uint16_t* vrow = Vb + (t * 16 + (lane & 15)) * VLD + ks * 32 + (lane >> 4) * 4;
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
         const bf16x8v vf = __builtin_bit_cast(bf16x8v, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -239,6 +256,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_flush(AttnArgs a) {
       }
     }
   }
+  }
+#undef MTP_FLUSH_LOAD
 
   // the chunk's partial: o (unnormalised), m, l for each query vector
   l += __shfl_xor(l, 16, 64);
@@ -274,6 +293,16 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
   const bool ok = j < n;
   const int nc = a.nchunk;
   const size_t base = (static_cast<size_t>(ok ? j : 0) * a.hq + h) * nc;
+  const float* po = a.part_o + base * D + lane * DPL;
+  // the column loads of the first kPre chunks go out with the (m, l) loads
+  constexpr int kPre = 32 / DPL;
+  const int npre = nc < kPre ? nc : kPre;
+  float vp[kPre][DPL];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+    if (u < npre)
+#pragma unroll
+      for (int q = 0; q < DPL; ++q) vp[u][q] = po[static_cast<size_t>(u) * D + q];
   float mc0 = -INFINITY, mc1 = -INFINITY, lc0 = 0.f, lc1 = 0.f;
   if (lane < nc) {
     mc0 = a.part_ml[(base + lane) * 2];
@@ -291,12 +320,16 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
   wts[wave][lane + 64] = w1;
   __syncthreads();
   if (!ok) return;
-  const float* po = a.part_o + base * D + lane * DPL;
   float num[DPL];
 #pragma unroll
   for (int q = 0; q < DPL; ++q) num[q] = 0.f;
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+    if (u < npre)
+#pragma unroll
+      for (int q = 0; q < DPL; ++q) num[q] += wts[wave][u] * vp[u][q];
   constexpr int kIn = 8;   // chunk loads in flight per round trip
-  int c = 0;
+  int c = npre;
   for (; c + kIn <= nc; c += kIn) {
     float v[kIn][DPL];
 #pragma unroll

@@ -53,6 +53,37 @@ __device__ __forceinline__ float group_sum_last(float v, int width) {
   return v;
 }
 
+// Sum over aligned groups of `width` lanes (8, 16, 32 or 64), valid in EVERY
+// lane of the group, bit-identical across the group (each step adds a lane's
+// value to its partner's, whose own step adds the same two numbers): xor 1 and
+// xor 2 by quad permutes, then the 8- and 16-lane mirrors (DPP, no LDS
+// traffic), then xor 16 by a swizzle and xor 32 by a lane permute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_all(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// The value of lane ^ O (O = 1, 2, 4, 8, 16 by a bit-mode swizzle within each
+// 32 lanes; O = 32 by a lane permute).
+template <int O>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (O == 32) {
+    return __shfl_xor(v, 32, kWave);
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F | (O << 10)));
+  }
+}
+
+__device__ __forceinline__ float group_sum_all(float v, int width) {
+  v += dpp_all<0xB1>(v);                           // quad_perm [1,0,3,2]
+  v += dpp_all<0x4E>(v);                           // quad_perm [2,3,0,1]
+  v += dpp_all<0x141>(v);                          // row_half_mirror: the other quad of the 8
+  if (width >= 16) v += dpp_all<0x140>(v);         // row_mirror: the other 8 of the 16
+  if (width >= 32)                                 // xor 16 within each 32 (bit-mode swizzle)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  if (width >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
 // 16-byte streaming load: a non-temporal hint for data read once (weights), so
 // it does not displace reusable lines from the caches.
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
