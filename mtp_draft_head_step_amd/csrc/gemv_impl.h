@@ -132,6 +132,132 @@ __device__ __forceinline__ void stage_range(void* dst, const void* src, long lon
   }
 }
 
+// One segment of a staged input row: dst[k - k0] = src[off + k] * nw[noff + k]
+// for k in [kb, ke) (nw null: factor 1).
+struct StageSeg {
+  const void* src;
+  long long off;
+  const void* nw;
+  long long noff;
+  int kb, ke;
+};
+
+// 8 consecutive values from raw 16-byte pieces (bf16: piece 0; fp32: pieces 0, 1).
+template <bool BF>
+__device__ __forceinline__ void unpack8(const uint4 (&r)[2], float (&v)[8]) {
+  if constexpr (BF) {
+    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(r[0].x); v[1] = __uint_as_float(r[0].y);
+    v[2] = __uint_as_float(r[0].z); v[3] = __uint_as_float(r[0].w);
+    v[4] = __uint_as_float(r[1].x); v[5] = __uint_as_float(r[1].y);
+    v[6] = __uint_as_float(r[1].z); v[7] = __uint_as_float(r[1].w);
+  }
+}
+
+template <bool BF>
+__device__ __forceinline__ void load8raw(const void* p, long long i, uint4 (&r)[2]) {
+  if constexpr (BF) {
+    r[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+  } else {
+    r[0] = *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i);
+    r[1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i + 4);
+  }
+}
+
+// Staging of one or two adjacent segments (A then B, B possibly empty) in one
+// pass: 8 values per thread per step in 16-byte loads, KB steps of loads in
+// flight.  Every workgroup of a launch stages the same row, so the launch's
+// staging time follows its count of cache requests; wide loads and a single
+// pass over both halves of the fc input keep that count low.  Adds the sums of
+// squares of the src values of A and B to sa and sb.
+template <bool XB, bool SBF, int NWK, int KB>   // NWK: 0 no norm weight, 1 bf16, 2 fp32
+__device__ __forceinline__ void stage_segs(void* dst, const StageSeg& A, const StageSeg& B, int k0,
+                                           float& sa, float& sb) {
+  const int kb = A.kb < A.ke ? A.kb : B.kb;
+  const int ke = B.kb < B.ke ? B.ke : A.ke;
+  for (int base = kb + threadIdx.x * 8; base < ke; base += KB * kThreads * 8) {
+    uint4 xr[KB][2], wr[KB][2];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int k = base + u * kThreads * 8;
+      if (k < ke) {
+        const StageSeg& S = k < A.ke ? A : B;
+        load8raw<SBF>(S.src, S.off + k, xr[u]);
+        if constexpr (NWK == 1) load8raw<true>(S.nw, S.noff + k, wr[u]);
+        if constexpr (NWK == 2) load8raw<false>(S.nw, S.noff + k, wr[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int k = base + u * kThreads * 8;
+      if (k < ke) {
+        float x[8], w[8];
+        unpack8<SBF>(xr[u], x);
+        if constexpr (NWK == 1) unpack8<true>(wr[u], w);
+        if constexpr (NWK == 2) unpack8<false>(wr[u], w);
+        if constexpr (NWK == 0)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = 1.f;
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += x[e] * x[e];
+        if (k < A.ke) sa += t; else sb += t;
+        if constexpr (XB) {
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            o[q] = f32_to_bf16(x[2 * q] * w[2 * q]) | (static_cast<uint32_t>(f32_to_bf16(x[2 * q + 1] * w[2 * q + 1])) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + (k - k0)) = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+          float* d = static_cast<float*>(dst) + (k - k0);
+          *reinterpret_cast<float4*>(d) = make_float4(x[0] * w[0], x[1] * w[1], x[2] * w[2], x[3] * w[3]);
+          *reinterpret_cast<float4*>(d + 4) = make_float4(x[4] * w[4], x[5] * w[5], x[6] * w[6], x[7] * w[7]);
+        }
+      }
+    }
+  }
+}
+
+// The 16-byte staging for the source / norm-weight types of a launch; false if
+// the segments are not in whole, aligned 8-value groups (the caller then stages
+// 4 values at a time).
+template <bool XB>
+__device__ __forceinline__ bool stage_wide(void* dst, const StageSeg& A, const StageSeg& B, int src_bf16,
+                                           int nw_bf16, int k0, float& sa, float& sb) {
+  const bool has_nw = A.nw != nullptr;
+  long long al = A.off | A.kb | A.ke | k0;                       // whole 8-value groups
+  uintptr_t ap = reinterpret_cast<uintptr_t>(A.src);             // 16-byte aligned bases
+  if (has_nw) {
+    al |= A.noff;
+    ap |= reinterpret_cast<uintptr_t>(A.nw);
+  }
+  if (B.kb < B.ke) {
+    al |= B.off | B.kb | B.ke;
+    ap |= reinterpret_cast<uintptr_t>(B.src);
+    if (has_nw) {
+      al |= B.noff;
+      ap |= reinterpret_cast<uintptr_t>(B.nw);
+    }
+  }
+  if ((al & 7) || (ap & 15)) return false;
+  if (src_bf16) {
+    if (!has_nw) stage_segs<XB, true, 0, 8>(dst, A, B, k0, sa, sb);
+    else if (nw_bf16) stage_segs<XB, true, 1, 8>(dst, A, B, k0, sa, sb);
+    else stage_segs<XB, true, 2, 4>(dst, A, B, k0, sa, sb);
+  } else {
+    if (!has_nw) stage_segs<XB, false, 0, 8>(dst, A, B, k0, sa, sb);
+    else if (nw_bf16) stage_segs<XB, false, 1, 6>(dst, A, B, k0, sa, sb);
+    else return false;   // fp32 rows and weights: 16 bytes per request already
+  }
+  return true;
+}
+
 __device__ __forceinline__ float4 mul4(float4 a, float4 b, float s) {
   return make_float4(a.x * b.x * s, a.y * b.y * s, a.z * b.z * s, a.w * b.w * s);
 }
@@ -346,8 +472,28 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
           float se = 0.f, sh = 0.f;   // sums of squares: whole input / hidden half
           if (vr[r]) {
             if (a.in_mode != IN_EMBED) {
-              stage_range<XB>(dst, a.x, static_cast<long long>(jr[r]) * a.ldx, 0,
-                          (a.in_mode == IN_RMS) ? a.nw : nullptr, 0, a.nw_bf16, k0, k0 + klen, k0, se);
+              const StageSeg A{a.x, static_cast<long long>(jr[r]) * a.ldx, (a.in_mode == IN_RMS) ? a.nw : nullptr,
+                               0, k0, k0 + klen};
+              const StageSeg B{nullptr, 0, nullptr, 0, 0, 0};
+              if (WT == W_F32 || !stage_wide<XB>(dst, A, B, 0, a.nw_bf16, k0, se, sh))
+                stage_range<XB>(dst, a.x, static_cast<long long>(jr[r]) * a.ldx, 0,
+                            (a.in_mode == IN_RMS) ? a.nw : nullptr, 0, a.nw_bf16, k0, k0 + klen, k0, se);
+            } else if (WT != W_F32 && a.embed_bf16 == a.hid_bf16 && a.tok[tr[r]] >= 0 &&
+                       a.tok[tr[r]] < a.vocab_tok) {
+              // both halves in one pass (the embedding and hidden rows share a type)
+              const int tk = a.tok[tr[r]];
+              const int ea = k0, eb = min(k0 + klen, half), ha = max(k0, half), hb = k0 + klen;
+              const StageSeg A{a.embed, static_cast<long long>(tk) * half, a.nw, 0, ea, ea < eb ? eb : ea};
+              const StageSeg B{a.hid, static_cast<long long>(hr[r]) * a.ld_hid - half, a.nw2,
+                               -static_cast<long long>(half), ha, ha < hb ? hb : ha};
+              if (!stage_wide<XB>(dst, A, B, a.embed_bf16, a.nw_bf16, k0, se, sh)) {
+                if (ea < eb)
+                  stage_range<XB>(dst, a.embed, static_cast<long long>(tk) * half, a.embed_bf16, a.nw, 0,
+                              a.nw_bf16, ea, eb, k0, se);
+                if (ha < hb)
+                  stage_range<XB>(dst, a.hid, static_cast<long long>(hr[r]) * a.ld_hid - half, a.hid_bf16, a.nw2,
+                              -static_cast<long long>(half), a.nw_bf16, ha, hb, k0, sh);
+              }
             } else {
               const int ea = k0, eb = min(k0 + klen, half);
               const int tk = a.tok[tr[r]];
