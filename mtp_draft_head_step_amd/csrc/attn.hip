@@ -20,9 +20,11 @@ namespace mtp {
 __global__ __launch_bounds__(64) void k_rope_append(RopeArgs a) {
   __shared__ float sv[256];
   int32_t* st = a.state;
-  if (st[3] != 0) return;
+  // every entry word in one memory round trip
+  const int err0 = st[3];
   const int ndev = a.n_dev ? *a.n_dev : a.n_max;
   const int len0 = st[0];
+  if (err0 != 0) return;
   const bool bad_count = ndev < a.n_min || ndev < 0 || ndev > a.n_max;
   const int n = bad_count ? 0 : ndev;
   if (bad_count || len0 + n > a.capacity) {
@@ -200,25 +202,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   void* kcs = static_cast<char*>(a.kc) + (multi ? sess * a.kv_sb * ebytes : 0ll);
   void* vcs = static_cast<char*>(a.vc) + (multi ? sess * a.kv_sb * ebytes : 0ll);
   const int rb = sess * a.n_max;    // the session's first workspace row
-  if (st[3] != 0) return;
+  // every entry word in one memory round trip
+  const int err0 = st[3];
+  const int off = st[0];            // pre-append length (committed by k_finish)
+  const int nd0 = a.n_dev ? a.n_dev[multi ? sess * a.ndev_sb : 0] : a.n_max;
+  if (err0 != 0) return;
   int n = a.n_max;
   if constexpr (FUSE) {
     // the append's checks (once per launch and session, by its first workgroup)
-    const int ndev = a.n_dev ? a.n_dev[multi ? sess * a.ndev_sb : 0] : a.n_max;
+    const int ndev = nd0;
     const bool bad_count = ndev < a.n_min || ndev < 0 || ndev > a.n_max;
-    if (bad_count || st[0] + ndev > a.capacity) {
+    if (bad_count || off + ndev > a.capacity) {
       if (blockIdx.x == 0 && blockIdx.y == 0 && (multi || blockIdx.z == 0) && threadIdx.x == 0)
         st[3] = bad_count ? 3 : 1;
       return;
     }
     n = ndev;
   } else if (a.n_dev) {
-    n = min(max(*a.n_dev, 0), a.n_max);
+    n = min(max(nd0, 0), a.n_max);
   }
   const int j = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.z);
   if (j < 0 || j >= n) return;
   const int jf = rb + j;            // workspace row
-  const int off = st[0];            // pre-append length (committed by k_finish)
   const int L = off + j + 1;        // keys visible to row j
   const int h = blockIdx.y;
   const int c = blockIdx.x;
@@ -456,9 +461,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const bool multi = a.batch > 1 && a.row_sel == ROW_LAST;
   const int sess = multi ? static_cast<int>(blockIdx.y) : 0;
   const int32_t* st = a.state + 4 * sess;
-  if (st[3] != 0) return;
-  int n = a.n_max;
-  if (a.n_dev) n = min(max(a.n_dev[multi ? sess * a.ndev_sb : 0], 0), a.n_max);
+  const int err0 = st[3];
+  const int nd0 = a.n_dev ? a.n_dev[multi ? sess * a.ndev_sb : 0] : a.n_max;
+  if (err0 != 0) return;
+  const int n = min(max(nd0, 0), a.n_max);
   const int jl = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.y);
   if (jl < 0 || jl >= n) return;
   const int j = sess * a.n_max + jl;   // workspace row
@@ -597,15 +603,22 @@ namespace mtp {
 __global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
   const int sess = a.batch > 1 ? static_cast<int>(blockIdx.x) : 0;   // one workgroup per session
   int32_t* st = a.state + 4 * sess;
-  if (st[3] != 0) return;
-  int n = a.n_max;
-  if (a.n_dev) n = min(max(a.n_dev[sess * a.ndev_sb], 0), a.n_max);
-  if (a.parts) {
-    const unsigned long long b = block_max_u64(a.parts + static_cast<size_t>(sess) * a.nparts, a.nparts);
+  // every load first (one memory round trip): the entry words and this
+  // thread's first argmax keys
+  const int err0 = st[3];
+  const int len0 = st[0];
+  const int nd0 = a.n_dev ? a.n_dev[sess * a.ndev_sb] : a.n_max;
+  const unsigned long long* parts = a.parts ? a.parts + static_cast<size_t>(sess) * a.nparts : nullptr;
+  unsigned long long b0 = 0ull;
+  if (parts) b0 = block_max_u64_first(parts, a.nparts);
+  if (err0 != 0) return;
+  const int n = min(max(nd0, 0), a.n_max);
+  if (parts) {
+    const unsigned long long b = block_max_u64_rest(parts, a.nparts, b0);
     if (threadIdx.x == 0 && a.amax_out && n > 0) a.amax_out[sess * a.out_sb] = argmax_index(b);
   }
   if (threadIdx.x == 0) {
-    const int len = st[0] + n;
+    const int len = len0 + n;
     st[0] = len;
     if (a.set_base) st[1] = len;
   }

@@ -129,6 +129,35 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 // Largest key of n partial argmax keys, reduced by one workgroup (blockDim 256).
+// The same maximum in two parts, so a caller can issue the key loads with its
+// other entry loads: _first loads up to 4 keys per thread (strided by the block)
+// and keeps their maximum; _rest adds the remaining keys and reduces over the
+// block (every thread must call it).
+__device__ __forceinline__ unsigned long long block_max_u64_first(const unsigned long long* parts, int n) {
+  unsigned long long v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = threadIdx.x + u * static_cast<int>(blockDim.x);
+    v[u] = i < n ? parts[i] : 0ull;
+  }
+  unsigned long long b = v[0];
+#pragma unroll
+  for (int u = 1; u < 4; ++u) b = v[u] > b ? v[u] : b;
+  return b;
+}
+__device__ __forceinline__ unsigned long long block_max_u64_rest(const unsigned long long* parts, int n,
+                                                                 unsigned long long b) {
+  __shared__ unsigned long long s_part[4];
+  for (int i = threadIdx.x + 4 * static_cast<int>(blockDim.x); i < n; i += blockDim.x) b = parts[i] > b ? parts[i] : b;
+  b = wave_max_u64(b);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = b;
+  __syncthreads();
+  b = s_part[0];
+  for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) b = s_part[w] > b ? s_part[w] : b;
+  __syncthreads();
+  return b;
+}
+
 __device__ __forceinline__ unsigned long long block_max_u64(const unsigned long long* parts, int n) {
   __shared__ unsigned long long s_part[4];
   unsigned long long b = 0ull;

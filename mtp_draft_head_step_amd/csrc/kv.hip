@@ -13,18 +13,20 @@ __global__ void k_rollback(int32_t* st0, int to_len, const int32_t* n_acc0, int 
   if (blockIdx.x != 0 || b >= batch) return;
   int32_t* st = st0 + 4 * b;
   const int32_t* n_acc = n_acc0 ? n_acc0 + b * acc_stride : nullptr;
-  if (st[3] != 0) return;
+  // every load first (one memory round trip)
+  const int err0 = st[3], len0 = st[0], base0 = st[1];
+  const int k0 = n_acc ? *n_acc : 0;
+  if (err0 != 0) return;
   int to = to_len;
   if (to_len < 0) {
-    to = st[1];
+    to = base0;
     if (n_acc) {
       const int keep_max = n_draft > 0 ? n_draft - 1 : 0;
-      int k = *n_acc;
-      k = k < 0 ? 0 : k;
+      const int k = k0 < 0 ? 0 : k0;
       to += k < keep_max ? k : keep_max;
     }
   }
-  if (to < 0 || to > st[0]) {
+  if (to < 0 || to > len0) {
     st[3] = 2;
     return;
   }

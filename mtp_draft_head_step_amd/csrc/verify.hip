@@ -108,23 +108,43 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
   }
 }
 
+// Every load first (one memory round trip): the argmax keys of all rows
+// (flattened [rows][nb]), the drafts and the ring state; each row's maximum by
+// LDS atomics (order-free), then thread 0 walks the acceptance.
 __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a, int nb) {
   a = at_session(a);
-  __shared__ int am[MTP_MAX_DRAFT_DEV + 1];
+  __shared__ unsigned long long s_row[MTP_MAX_DRAFT_DEV + 1];
+  __shared__ int s_dr[MTP_MAX_DRAFT_DEV];
+  const int tid = threadIdx.x;
   const int n = a.n_draft;
-  for (int r = 0; r <= n; ++r) {
-    const unsigned long long b = block_max_u64(a.parts + static_cast<size_t>(r) * nb, nb);
-    if (threadIdx.x == 0) am[r] = argmax_index(b);
+  const int tot = (n + 1) * nb;
+  constexpr int kPer = 4;
+  unsigned long long v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = tid + u * kVThreads;
+    v[u] = e < tot ? a.parts[e] : 0ull;
   }
+  const int dr = tid < n ? a.drafts[tid] : 0;
+  const int h0 = ring_head(a), c0 = ring_count(a);
+  if (tid <= n) s_row[tid] = 0ull;
+  if (tid < n) s_dr[tid] = dr;
   __syncthreads();
-  if (threadIdx.x != 0) return;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = tid + u * kVThreads;
+    if (e < tot) atomicMax(&s_row[e / nb], v[u]);
+  }
+  for (int e = tid + kPer * kVThreads; e < tot; e += kVThreads) atomicMax(&s_row[e / nb], a.parts[e]);
+  __syncthreads();
+  if (tid != 0) return;
   int k = n;
   for (int r = 0; r < n; ++r) {
-    if (a.drafts[r] != am[r]) { k = r; break; }
+    if (s_dr[r] != argmax_index(s_row[r])) { k = r; break; }
   }
-  int h = ring_head(a), c = ring_count(a);
+  int h = h0, c = c0;
   for (int r = 0; r <= k; ++r) {
-    const int t = r < k ? a.drafts[r] : am[k];
+    const int t = r < k ? s_dr[r] : argmax_index(s_row[k]);
     a.out_tokens[r] = t;
     a.ring[h] = t;
     h = (h + 1) % a.window;
