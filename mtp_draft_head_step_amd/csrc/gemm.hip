@@ -95,9 +95,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_rows_prep(PrepArgs a) {
   int tj = j, hj = j;           // token index and hidden row of this row
   int32_t* err = a.err;
   if (a.batch <= 1) {
-    if (a.kv_state && a.kv_state[3] != 0) return;
-    int n = a.n_max;
-    if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
+    const int err0 = a.kv_state ? a.kv_state[3] : 0;   // both words in one round trip
+    const int nd0 = a.n_dev ? *a.n_dev : a.n_max;
+    if (err0 != 0) return;
+    const int n = min(max(nd0, 0), a.n_max);
     if (j >= n) return;
   } else {
     // session b's pair jj; rows past its count (or of a session in error) are zeros
@@ -736,23 +737,29 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs a, int steps) {
 // Sum of the split partials in split order, then the epilogue; a thread per
 // four consecutive output columns of one row.
 __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int nsp) {
-  if (a.kv_state && a.kv_state[3] != 0) return;
-  int n = a.n_max;
-  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
   const int per_row = a.M / 4;
   const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   const int r = static_cast<int>(idx / per_row);
   const int c = static_cast<int>(idx % per_row) * 4;
-  if (r >= n) return;
+  if (r >= a.n_max) return;
+  // the entry words and this thread's split partials in one memory round trip
+  // (rows past the device count are read, not written)
+  const int err0 = a.kv_state ? a.kv_state[3] : 0;
+  const int nd0 = a.n_dev ? *a.n_dev : a.n_max;
   const long long stride = static_cast<long long>(a.n_max) * a.M;
   const float* p = a.part + static_cast<long long>(r) * a.M + c;
   float4 v = *reinterpret_cast<const float4*>(p);
+  float4 pv[kNormMaxSplit];
   if (nsp <= kNormMaxSplit) {
-    // every split's load issued together, then added in split order
-    float4 pv[kNormMaxSplit];
 #pragma unroll
     for (int q = 1; q < kNormMaxSplit; ++q)
       if (q < nsp) pv[q] = *reinterpret_cast<const float4*>(p + q * stride);
+  }
+  if (err0 != 0) return;
+  const int n = min(max(nd0, 0), a.n_max);
+  if (r >= n) return;
+  if (nsp <= kNormMaxSplit) {
+    // added in split order
 #pragma unroll
     for (int q = 1; q < kNormMaxSplit; ++q)
       if (q < nsp) {
@@ -777,13 +784,33 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int nsp) {
 // rms(y))) -- the row preparation the next product reads.
 __global__ __launch_bounds__(kNormThreads) void k_gemm_reduce_norm(GemmArgs a, int nsp, RowNorm rn) {
   __shared__ float red[kNormThreads / kWave];
-  if (a.kv_state && a.kv_state[3] != 0) return;
-  int n = a.n_max;
-  if (a.n_dev) n = min(max(*a.n_dev, 0), a.n_max);
   const int r = blockIdx.x;
-  if (r >= n) return;
   const int per = a.M / 4;
   const long long stride = static_cast<long long>(a.n_max) * a.M;
+  // every load first (one memory round trip): the entry words, the split
+  // partials, the residual and the norm weight of this thread's columns (rows
+  // past the device count are read, not written)
+  const int err0 = a.kv_state ? a.kv_state[3] : 0;
+  const int nd0 = a.n_dev ? *a.n_dev : a.n_max;
+  float4 pv[kNormPer][kNormMaxSplit], rv[kNormPer];
+  uint2 wb[kNormPer];
+  float4 wf[kNormPer];
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) {
+    const int c4 = threadIdx.x + i * kNormThreads;
+    if (c4 >= per) continue;
+    const int c = c4 * 4;
+    const float* p = a.part + static_cast<long long>(r) * a.M + c;
+#pragma unroll
+    for (int q = 0; q < kNormMaxSplit; ++q)
+      if (q < nsp) pv[i][q] = *reinterpret_cast<const float4*>(p + q * stride);
+    if (a.out_mode == OUT_RESID) rv[i] = *reinterpret_cast<const float4*>(a.res + static_cast<long long>(r) * a.ldres + c);
+    if (rn.nw_bf16) wb[i] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(rn.nw) + c);
+    else wf[i] = *reinterpret_cast<const float4*>(static_cast<const float*>(rn.nw) + c);
+  }
+  if (err0 != 0) return;
+  const int n = min(max(nd0, 0), a.n_max);
+  if (r >= n) return;
   float4 v[kNormPer];
   float ss = 0.f;
 #pragma unroll
@@ -791,20 +818,14 @@ __global__ __launch_bounds__(kNormThreads) void k_gemm_reduce_norm(GemmArgs a, i
     const int c4 = threadIdx.x + i * kNormThreads;
     if (c4 >= per) continue;
     const int c = c4 * 4;
-    const float* p = a.part + static_cast<long long>(r) * a.M + c;
-    float4 pv[kNormMaxSplit];
-#pragma unroll
-    for (int q = 0; q < kNormMaxSplit; ++q)
-      if (q < nsp) pv[q] = *reinterpret_cast<const float4*>(p + q * stride);
-    float4 t = pv[0];
+    float4 t = pv[i][0];
 #pragma unroll
     for (int q = 1; q < kNormMaxSplit; ++q)
       if (q < nsp) {
-        t.x += pv[q].x; t.y += pv[q].y; t.z += pv[q].z; t.w += pv[q].w;
+        t.x += pv[i][q].x; t.y += pv[i][q].y; t.z += pv[i][q].z; t.w += pv[i][q].w;
       }
     if (a.out_mode == OUT_RESID) {
-      const float4 e = *reinterpret_cast<const float4*>(a.res + static_cast<long long>(r) * a.ldres + c);
-      t.x += e.x; t.y += e.y; t.z += e.z; t.w += e.w;
+      t.x += rv[i].x; t.y += rv[i].y; t.z += rv[i].z; t.w += rv[i].w;
     }
     *reinterpret_cast<float4*>(a.y + static_cast<long long>(r) * a.ldy + c) = t;
     if (a.y2) {
@@ -827,11 +848,11 @@ __global__ __launch_bounds__(kNormThreads) void k_gemm_reduce_norm(GemmArgs a, i
     const int c = c4 * 4;
     float w[4];
     if (rn.nw_bf16) {
-      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(rn.nw) + c);
+      const uint2 u = wb[i];
       w[0] = __uint_as_float(u.x << 16); w[1] = __uint_as_float(u.x & 0xFFFF0000u);
       w[2] = __uint_as_float(u.y << 16); w[3] = __uint_as_float(u.y & 0xFFFF0000u);
     } else {
-      const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(rn.nw) + c);
+      const float4 f = wf[i];
       w[0] = f.x; w[1] = f.y; w[2] = f.z; w[3] = f.w;
     }
     *reinterpret_cast<uint2*>(out + c) =
