@@ -433,7 +433,37 @@ __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledS
     }
   __syncthreads();
   sort_small(s, k2);                                     // the top-k by (value desc, id asc)
-  if (tid == 0) {
+  if (nv <= 64) {
+    // one wave, entry j in lane j: softmax weights, their running sum by a
+    // lane scan, the top-p and min-p cuts by ballots (the scores are sorted,
+    // so each cut keeps a prefix), and the renormalisation
+    if (tid < 64) {
+      const int j = tid;
+      const float y0 = key_value(s[0]);
+      const float yj = j < nv ? key_value(s[j]) : 0.f;
+      const float pj = j < nv ? expf(yj - y0) : 0.f;
+      float c = pj;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(c, o, 64);
+        if (j >= o) c += t;
+      }
+      const float tot = __shfl(c, nv - 1, 64);
+      int keep = nv;
+      if (a.top_p < 1.0f) {
+        const unsigned long long hit = __ballot(j < nv && c >= a.top_p * tot);
+        if (hit) keep = __ffsll(static_cast<long long>(hit));   // first j reaching the mass, plus one
+      }
+      if (a.min_p > 0.0f) {
+        const int m = __popcll(__ballot(j < keep && (yj - y0) >= a.ln_min_p));
+        keep = m < keep ? m : keep;
+      }
+      const float z = __shfl(c, keep - 1, 64);
+      const float inv = 1.0f / z;
+      if (j < keep) sp[j] = pj * inv;
+      if (j == 0) s_keep = keep;
+    }
+  } else if (tid == 0) {
     const float y0 = key_value(s[0]);
     float tot = 0.f;
     for (int j = 0; j < nv; ++j) {
