@@ -120,6 +120,35 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
+// The value of lane ^ o for o in {1, 2, 4, 8, 16, 32}, 32-bit: xor 1 and 2 by
+// quad permutes, xor 4 and 8 by DPP row shifts (lane i reads i + o in the lower
+// half of each o-pair block, i - o in the upper), xor 16 by a bit-mode swizzle,
+// xor 32 by a lane permute.  o must fold to a constant.
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int o, int lane) {
+  const int x = static_cast<int>(v);
+  switch (o) {
+    case 1: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    case 2: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    case 4: {
+      const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);     // row_shl:4
+      const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);     // row_shr:4
+      return static_cast<uint32_t>((lane & 4) ? dn : up);
+    }
+    case 8: {
+      const int up = __builtin_amdgcn_update_dpp(0, x, 0x108, 0xF, 0xF, false);     // row_shl:8
+      const int dn = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);     // row_shr:8
+      return static_cast<uint32_t>((lane & 8) ? dn : up);
+    }
+    case 16: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(x, 0x401F));
+    default: return static_cast<uint32_t>(__shfl_xor(x, 32, kWave));
+  }
+}
+__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v, int o, int lane) {
+  const uint32_t lo = xor_lane_u32(static_cast<uint32_t>(v), o, lane);
+  const uint32_t hi = xor_lane_u32(static_cast<uint32_t>(v >> 32), o, lane);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
   for (int o = 32; o > 0; o >>= 1) {
     unsigned long long w = shfl_xor_u64(v, o);

@@ -175,9 +175,11 @@ hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
 //  A. k_sample_chunk  (chunks x rows): a chunk's logits are penalised (window of
 //     its row), divided by the temperature and turned into 64-bit keys (value
 //     desc, id asc); a radix select finds the chunk's kk-th key and the kk keys
-//     at or above it are kept.
-//  B. k_sample_row    (rows): a radix select over the row's candidates gives the
-//     exact top-k, sorted in LDS; softmax over it, top-p prefix, min-p cut,
+//     at or above it are kept (sorted when kk <= 64).
+//  B. k_sample_row    (rows): the row's exact top-k: for k <= 64 the chunks'
+//     lists arrive sorted and are folded by bitonic merges in registers (one
+//     list per merge, a running top 64 per wave); larger k by a radix select
+//     over every candidate.  Softmax over it, top-p prefix, min-p cut,
 //     renormalise; the support is written sorted by token id.
 //  C. k_sample_decide (1 thread): accept d_i iff u_i q_i(d_i) < p_i(d_i); at the
 //     first rejection draw from normalise(max(0, p - q)) (p if that is zero) with
@@ -306,9 +308,11 @@ __device__ void sort_small(unsigned long long* s, int n) {
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
       unsigned long long v = lane < n ? s[lane] : 0ull;
+#pragma unroll
       for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          const unsigned long long o = shfl_xor_u64(v, stride);
+          const unsigned long long o = xor_lane_u64(v, stride, lane);
           const bool desc = (lane & size) == 0;
           const bool lower = (lane & stride) == 0;
           v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
@@ -332,6 +336,7 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
   __shared__ int hist[256];
   __shared__ int sh[4];
   __shared__ int s_cnt;
+  __shared__ unsigned long long s_sel[64];
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int n = a.n_draft;
@@ -374,9 +379,26 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
   }
   const int take = min(kk, hi - lo);
   const unsigned long long thr = kth_largest<kSPer>(key, take, hist, sh);
+  unsigned long long* out = sc.cand + (static_cast<size_t>(row) * nb + blockIdx.x) * kk;
+  if (kk <= 64) {
+    // the chunk's keys sorted (value desc, id asc; zeros after), so the row
+    // kernel merges sorted lists
+    if (tid < 64) s_sel[tid] = 0ull;
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u)
+      if (key[u] != 0ull && key[u] >= thr) {             // exactly `take` keys
+        const int pos = atomicAdd(&s_cnt, 1);
+        if (pos < 64) s_sel[pos] = key[u];
+      }
+    __syncthreads();
+    sort_small(s_sel, 64);
+    if (tid < kk) out[tid] = s_sel[tid];
+    return;
+  }
   if (tid == 0) s_cnt = 0;
   __syncthreads();
-  unsigned long long* out = sc.cand + (static_cast<size_t>(row) * nb + blockIdx.x) * kk;
 #pragma unroll
   for (int u = 0; u < kSPer; ++u)
     if (key[u] != 0ull && key[u] >= thr) {                // exactly `take` keys
@@ -387,6 +409,103 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
 }
 
 constexpr int kSRowPer = kSMaxCand / kVThreads;   // merge keys per thread
+
+// The 64 largest of a descending 64-key list a and an ascending one rb, one
+// key per lane (lane i: element i): their elementwise maximum is bitonic and
+// holds them; half-cleaners at strides 32..1 sort it descending.
+__device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long rb, int lane) {
+  unsigned long long m = a > rb ? a : rb;
+#pragma unroll
+  for (int st = 32; st > 0; st >>= 1) {
+    const unsigned long long o = xor_lane_u64(m, st, lane);
+    m = (lane & st) ? (m < o ? m : o) : (m > o ? m : o);
+  }
+  return m;
+}
+
+// The row's top-k (s[0..nv), value desc, id asc) to its support: softmax
+// weights, the top-p and min-p prefixes, renormalised, written by token id.
+__device__ __forceinline__ void sample_row_tail(const VerifyArgs& a, const SampledScratch& sc, unsigned long long* s,
+                                                float* sp, int* s_keep, int nv, int row) {
+  const int tid = threadIdx.x;
+  if (nv <= 64) {
+    // one wave, entry j in lane j: softmax weights, their running sum by a
+    // lane scan, the top-p and min-p cuts by ballots (the scores are sorted,
+    // so each cut keeps a prefix), and the renormalisation
+    if (tid < 64) {
+      const int j = tid;
+      const float y0 = key_value(s[0]);
+      const float yj = j < nv ? key_value(s[j]) : 0.f;
+      const float pj = j < nv ? expf(yj - y0) : 0.f;
+      float c = pj;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(c, o, 64);
+        if (j >= o) c += t;
+      }
+      const float tot = __shfl(c, nv - 1, 64);
+      int keep = nv;
+      if (a.top_p < 1.0f) {
+        const unsigned long long hit = __ballot(j < nv && c >= a.top_p * tot);
+        if (hit) keep = __ffsll(static_cast<long long>(hit));   // first j reaching the mass, plus one
+      }
+      if (a.min_p > 0.0f) {
+        const int m = __popcll(__ballot(j < keep && (yj - y0) >= a.ln_min_p));
+        keep = m < keep ? m : keep;
+      }
+      const float z = __shfl(c, keep - 1, 64);
+      const float inv = 1.0f / z;
+      if (j < keep) sp[j] = pj * inv;
+      if (j == 0) *s_keep = keep;
+    }
+  } else if (tid == 0) {
+    const float y0 = key_value(s[0]);
+    float tot = 0.f;
+    for (int j = 0; j < nv; ++j) {
+      sp[j] = expf(key_value(s[j]) - y0);
+      tot += sp[j];
+    }
+    int keep = nv;
+    if (a.top_p < 1.0f) {
+      const float target = a.top_p * tot;
+      float c = 0.f;
+      for (int j = 0; j < nv; ++j) {
+        c += sp[j];
+        if (c >= target) { keep = j + 1; break; }
+      }
+    }
+    if (a.min_p > 0.0f) {
+      int m = 0;
+      while (m < keep && (key_value(s[m]) - y0) >= a.ln_min_p) ++m;
+      keep = m < keep ? m : keep;
+    }
+    float z = 0.f;
+    for (int j = 0; j < keep; ++j) z += sp[j];
+    const float inv = 1.0f / z;
+    for (int j = 0; j < keep; ++j) sp[j] *= inv;
+    *s_keep = keep;
+  }
+  __syncthreads();
+  const int keep = *s_keep;
+  // re-key the kept entries by token id (ascending) with their probability bits
+  int k3 = 1;
+  while (k3 < keep) k3 <<= 1;
+  unsigned long long mine = ~0ull;                       // sorts after every real entry
+  if (tid < k3 && tid < keep) {
+    const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s[tid]);
+    mine = (static_cast<unsigned long long>(id) << 32) | __float_as_uint(sp[tid]);
+  }
+  __syncthreads();
+  if (tid < k3) s[tid] = ~mine;                          // descending of ~v = ascending of v
+  __syncthreads();
+  sort_small(s, k3);
+  for (int j = tid; j < keep; j += kVThreads) {
+    const unsigned long long vv = ~s[j];
+    sc.ids[static_cast<size_t>(row) * kSMaxTopK + j] = static_cast<int>(vv >> 32);
+    sc.probs[static_cast<size_t>(row) * kSMaxTopK + j] = __uint_as_float(static_cast<uint32_t>(vv));
+  }
+  if (tid == 0) sc.cnt[row] = keep;
+}
 
 __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledScratch sc, int nb, int kk,
                                                          int topk) {
@@ -403,6 +522,37 @@ __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledS
   const int row = blockIdx.x;
   const int ncand = nb * kk;
   const unsigned long long* cand = sc.cand + static_cast<size_t>(row) * ncand;
+  if (kk <= 64 && topk <= 64) {
+    // The chunks' candidate lists are sorted: wave w folds lists w, w + 4, ...
+    // into a running top 64 (a list per merge, eight lists' loads in flight),
+    // then wave 0 folds the four waves' lists.  The row's top-k is a prefix.
+    __shared__ unsigned long long s_acc[kVThreads / 64][64];
+    const int lane = tid & 63, wave = tid >> 6;
+    unsigned long long acc = 0ull;
+    for (int c0 = wave; c0 < nb; c0 += 8 * (kVThreads / 64)) {
+      unsigned long long l[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = c0 + q * (kVThreads / 64);
+        const int e = 63 - lane;                        // the list reversed: ascending
+        l[q] = (c < nb && e < kk) ? cand[static_cast<size_t>(c) * kk + e] : 0ull;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc = merge_top64(acc, l[q], lane);
+    }
+    s_acc[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 1; w < kVThreads / 64; ++w) acc = merge_top64(acc, s_acc[w][63 - lane], lane);
+      s[lane] = acc;
+      const int nreal = __popcll(__ballot(acc != 0ull));
+      if (lane == 0) s_cnt = nreal;
+    }
+    __syncthreads();
+    sample_row_tail(a, sc, s, sp, &s_keep, min(topk, s_cnt), row);
+    return;
+  }
   unsigned long long key[kSRowPer];
   int nreal = 0;
 #pragma unroll
@@ -433,83 +583,7 @@ __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledS
     }
   __syncthreads();
   sort_small(s, k2);                                     // the top-k by (value desc, id asc)
-  if (nv <= 64) {
-    // one wave, entry j in lane j: softmax weights, their running sum by a
-    // lane scan, the top-p and min-p cuts by ballots (the scores are sorted,
-    // so each cut keeps a prefix), and the renormalisation
-    if (tid < 64) {
-      const int j = tid;
-      const float y0 = key_value(s[0]);
-      const float yj = j < nv ? key_value(s[j]) : 0.f;
-      const float pj = j < nv ? expf(yj - y0) : 0.f;
-      float c = pj;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float t = __shfl_up(c, o, 64);
-        if (j >= o) c += t;
-      }
-      const float tot = __shfl(c, nv - 1, 64);
-      int keep = nv;
-      if (a.top_p < 1.0f) {
-        const unsigned long long hit = __ballot(j < nv && c >= a.top_p * tot);
-        if (hit) keep = __ffsll(static_cast<long long>(hit));   // first j reaching the mass, plus one
-      }
-      if (a.min_p > 0.0f) {
-        const int m = __popcll(__ballot(j < keep && (yj - y0) >= a.ln_min_p));
-        keep = m < keep ? m : keep;
-      }
-      const float z = __shfl(c, keep - 1, 64);
-      const float inv = 1.0f / z;
-      if (j < keep) sp[j] = pj * inv;
-      if (j == 0) s_keep = keep;
-    }
-  } else if (tid == 0) {
-    const float y0 = key_value(s[0]);
-    float tot = 0.f;
-    for (int j = 0; j < nv; ++j) {
-      sp[j] = expf(key_value(s[j]) - y0);
-      tot += sp[j];
-    }
-    int keep = nv;
-    if (a.top_p < 1.0f) {
-      const float target = a.top_p * tot;
-      float c = 0.f;
-      for (int j = 0; j < nv; ++j) {
-        c += sp[j];
-        if (c >= target) { keep = j + 1; break; }
-      }
-    }
-    if (a.min_p > 0.0f) {
-      int m = 0;
-      while (m < keep && (key_value(s[m]) - y0) >= a.ln_min_p) ++m;
-      keep = m < keep ? m : keep;
-    }
-    float z = 0.f;
-    for (int j = 0; j < keep; ++j) z += sp[j];
-    const float inv = 1.0f / z;
-    for (int j = 0; j < keep; ++j) sp[j] *= inv;
-    s_keep = keep;
-  }
-  __syncthreads();
-  const int keep = s_keep;
-  // re-key the kept entries by token id (ascending) with their probability bits
-  int k3 = 1;
-  while (k3 < keep) k3 <<= 1;
-  unsigned long long mine = ~0ull;                       // sorts after every real entry
-  if (tid < k3 && tid < keep) {
-    const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s[tid]);
-    mine = (static_cast<unsigned long long>(id) << 32) | __float_as_uint(sp[tid]);
-  }
-  __syncthreads();
-  if (tid < k3) s[tid] = ~mine;                          // descending of ~v = ascending of v
-  __syncthreads();
-  sort_small(s, k3);
-  for (int j = tid; j < keep; j += kVThreads) {
-    const unsigned long long vv = ~s[j];
-    sc.ids[static_cast<size_t>(row) * kSMaxTopK + j] = static_cast<int>(vv >> 32);
-    sc.probs[static_cast<size_t>(row) * kSMaxTopK + j] = __uint_as_float(static_cast<uint32_t>(vv));
-  }
-  if (tid == 0) sc.cnt[row] = keep;
+  sample_row_tail(a, sc, s, sp, &s_keep, nv, row);
 }
 
 __device__ float prob_in(const SampledScratch& sc, int row, int tok) {
