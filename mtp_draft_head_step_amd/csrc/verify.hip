@@ -299,6 +299,34 @@ __device__ void bitonic_small(unsigned long long* s, int n) {
     }
 }
 
+// One key per lane of a wave (lane i: element i), sorted descending by a
+// bitonic network of lane exchanges.
+__device__ __forceinline__ unsigned long long sort64_desc(unsigned long long v, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const unsigned long long o = xor_lane_u64(v, stride, lane);
+      const bool desc = (lane & size) == 0;
+      const bool lower = (lane & stride) == 0;
+      v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  return v;
+}
+
+// The 64 largest of a descending 64-key list a and an ascending one rb, one
+// key per lane (lane i: element i): their elementwise maximum is bitonic and
+// holds them; half-cleaners at strides 32..1 sort it descending.
+__device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long rb, int lane) {
+  unsigned long long m = a > rb ? a : rb;
+#pragma unroll
+  for (int st = 32; st > 0; st >>= 1) {
+    const unsigned long long o = xor_lane_u64(m, st, lane);
+    m = (lane & st) ? (m < o ? m : o) : (m > o ? m : o);
+  }
+  return m;
+}
+
 // Descending sort of n (a power of two) nonzero keys in LDS.  Up to 64 keys one
 // wave sorts them in registers (the same bitonic network over 64 lanes, the
 // slots past n holding 0, which sorts last): no workgroup barrier per stage.
@@ -337,6 +365,8 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
   __shared__ int sh[4];
   __shared__ int s_cnt;
   __shared__ unsigned long long s_sel[64];
+  __shared__ unsigned long long s_acc[kVThreads / 64][64];
+  __shared__ unsigned long long s_floor;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int n = a.n_draft;
@@ -378,8 +408,43 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
     }
   }
   const int take = min(kk, hi - lo);
-  const unsigned long long thr = kth_largest<kSPer>(key, take, hist, sh);
   unsigned long long* out = sc.cand + (static_cast<size_t>(row) * nb + blockIdx.x) * kk;
+  if (kk <= 64) {
+    // A floor under the take-th largest key: the take-th largest of the 256
+    // threads' maxima (at least take keys reach it).  The keys at or above it
+    // are usually few: when they fit one wave they are sorted there and the
+    // radix select is skipped.
+    const int lane = tid & 63, wave = tid >> 6;
+    unsigned long long mx = key[0];
+#pragma unroll
+    for (int u = 1; u < kSPer; ++u) mx = key[u] > mx ? key[u] : mx;
+    s_acc[wave][lane] = sort64_desc(mx, lane);
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    if (wave == 0) {
+      unsigned long long acc = s_acc[0][lane];
+#pragma unroll
+      for (int w = 1; w < kVThreads / 64; ++w) acc = merge_top64(acc, s_acc[w][63 - lane], lane);
+      if (lane == take - 1) s_floor = acc;
+      s_sel[lane] = 0ull;
+    }
+    __syncthreads();
+    const unsigned long long fl = s_floor;
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u)
+      if (key[u] != 0ull && key[u] >= fl) {
+        const int pos = atomicAdd(&s_cnt, 1);
+        if (pos < 64) s_sel[pos] = key[u];
+      }
+    __syncthreads();
+    if (s_cnt <= 64) {
+      sort_small(s_sel, 64);                             // the first `take` are the chunk's top
+      if (tid < kk) out[tid] = tid < take ? s_sel[tid] : 0ull;
+      return;
+    }
+    __syncthreads();
+  }
+  const unsigned long long thr = kth_largest<kSPer>(key, take, hist, sh);
   if (kk <= 64) {
     // the chunk's keys sorted (value desc, id asc; zeros after), so the row
     // kernel merges sorted lists
@@ -409,19 +474,6 @@ __global__ __launch_bounds__(kVThreads) void k_sample_chunk(VerifyArgs a, Sample
 }
 
 constexpr int kSRowPer = kSMaxCand / kVThreads;   // merge keys per thread
-
-// The 64 largest of a descending 64-key list a and an ascending one rb, one
-// key per lane (lane i: element i): their elementwise maximum is bitonic and
-// holds them; half-cleaners at strides 32..1 sort it descending.
-__device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long rb, int lane) {
-  unsigned long long m = a > rb ? a : rb;
-#pragma unroll
-  for (int st = 32; st > 0; st >>= 1) {
-    const unsigned long long o = xor_lane_u64(m, st, lane);
-    m = (lane & st) ? (m < o ? m : o) : (m > o ? m : o);
-  }
-  return m;
-}
 
 // The row's top-k (s[0..nv), value desc, id asc) to its support: softmax
 // weights, the top-p and min-p prefixes, renormalised, written by token id.
