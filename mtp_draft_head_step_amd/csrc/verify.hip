@@ -576,21 +576,23 @@ __global__ __launch_bounds__(kVThreads) void k_sample_row(VerifyArgs a, SampledS
   const unsigned long long* cand = sc.cand + static_cast<size_t>(row) * ncand;
   if (kk <= 64 && topk <= 64) {
     // The chunks' candidate lists are sorted: wave w folds lists w, w + 4, ...
-    // into a running top 64 (a list per merge, eight lists' loads in flight),
+    // into a running top 64 (a list per merge, sixteen lists' loads in flight),
     // then wave 0 folds the four waves' lists.  The row's top-k is a prefix.
     __shared__ unsigned long long s_acc[kVThreads / 64][64];
     const int lane = tid & 63, wave = tid >> 6;
     unsigned long long acc = 0ull;
-    for (int c0 = wave; c0 < nb; c0 += 8 * (kVThreads / 64)) {
-      unsigned long long l[8];
+    constexpr int kL = 16;                              // lists per wave per round trip
+    for (int c0 = wave; c0 < nb; c0 += kL * (kVThreads / 64)) {
+      unsigned long long l[kL];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kL; ++q) {
         const int c = c0 + q * (kVThreads / 64);
         const int e = 63 - lane;                        // the list reversed: ascending
         l[q] = (c < nb && e < kk) ? cand[static_cast<size_t>(c) * kk + e] : 0ull;
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc = merge_top64(acc, l[q], lane);
+      for (int q = 0; q < kL; ++q)
+        if (c0 + q * (kVThreads / 64) < nb) acc = merge_top64(acc, l[q], lane);
     }
     s_acc[wave][lane] = acc;
     __syncthreads();
