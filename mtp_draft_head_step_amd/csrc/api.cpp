@@ -326,10 +326,16 @@ GemvArgs unembed_args(const mtp_head* h, const mtp_kv* kv, const Layout& L, int 
 // The head forward for n rows (n_max host bound, n_dev device count; a device
 // count below n_min sets MTP_DEV_COUNT).  mode: KV_ONLY / LAST / ALL.
 // hidden_out: [1 or n, H] in act dtype (nullable).
+// fold_in (nullable): the previous step's argmax merge and append commit, run
+// by this call's fc pass when that pass is a one-row GEMV, else launched first.
+// defer_out (nullable): this call's own merge is returned instead of launched,
+// for a following call to fold (the argmax keys it reads sit in the workspace
+// after the rows a one-row call writes before its fc pass ends).
 int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, const void* hiddens,
                  int n_max, const int32_t* n_dev, int mode, int set_base, void* hidden_out,
                  float* logits, int32_t* argmax, void* ws, hipStream_t s, int n_min = 0,
-                 const Sessions& ss = kOneSession) {
+                 const Sessions& ss = kOneSession, const FinishArgs* fold_in = nullptr,
+                 FinishArgs* defer_out = nullptr) {
   const mtp_head_config& c = h->cfg;
   const int rows_total = ss.multi() ? ss.batch * n_max : n_max;   // workspace rows
   const int slots = slots_of(ss);
@@ -368,6 +374,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   }
   // 1. x = W_fc [RMSNorm(E[t]) | RMSNorm(h)]
   bool normed_qkv = false, normed_mlp = false;
+  const bool have_fold = fold_in && fold_in->state;
+  const bool fold = have_fold && fold_in->parts && !mfma && !ss.multi() && rows_total == 1;
+  if (have_fold && !fold) MTP_TRY(launch_finish(*fold_in, s));
   if (mfma) {
     PrepArgs p = base_prep(h, kv, n_max, n_dev, xa, ss);
     p.in_mode = IN_EMBED; p.K = 2 * H; p.ld_out = 2 * H;
@@ -391,6 +400,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a.embed = h->w.embed; a.embed_bf16 = h->wt == W_BF16;
   a.hid = hiddens; a.hid_bf16 = c.act_dtype == MTP_BF16; a.ld_hid = H;
   a.out_mode = OUT_F32; a.y = x; a.ldy = H;
+  if (fold) {
+    a.fin_parts = fold_in->parts; a.fin_nparts = fold_in->nparts; a.fin_amax = fold_in->amax_out;
+    a.fin_ndev = fold_in->n_dev; a.fin_nmax = fold_in->n_max; a.fin_set_base = fold_in->set_base;
+    a.fin_state = fold_in->state;
+  }
   if (!mfma) MTP_TRY(run_gemv(a, h->wt, rows_total, ROWS_RANGE, s));
 
   // 2. q, k, v = W_{q,k,v} RMSNorm(x; w_in)
@@ -433,6 +447,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   f.state = kv->state; f.n_max = n_max; f.n_dev = n_dev; f.set_base = set_base;
   f.batch = ss.batch; f.out_sb = ss.out_sb; f.ndev_sb = ss.ndev_sb;
   if (mode == MTP_FLUSH_KV_ONLY) {
+    if (defer_out) std::memset(defer_out, 0, sizeof(*defer_out));   // nothing left to fold
     MTP_TRY(launch_finish(f, s));
     return MTP_OK;
   }
@@ -532,6 +547,10 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   time_mark(TIME_UNEMBED, false, s, &tslot);
   // 9. argmax of the partial keys, commit the append (len, round base)
   f.parts = a.amax_part; f.nparts = grid; f.amax_out = argmax;
+  if (defer_out) {
+    *defer_out = f;
+    return MTP_OK;
+  }
   MTP_TRY(launch_finish(f, s));
   return MTP_OK;
 }
@@ -701,16 +720,24 @@ int mtp_draft_chain(const mtp_head* head, const mtp_kv* kv, const int32_t* pend_
   char* hout = static_cast<char*>(hiddens_out_dev);
   // the flush of the pending pairs gives d_0 and g_0
   // (a pending count of 0 is a device error here: a round always has a pending pair)
+  // each step's argmax merge and append commit run inside the next step's fc
+  // pass (the token it embeds); the last step's run on their own
+  FinishArgs pend;
+  std::memset(&pend, 0, sizeof(pend));
   st = head_forward(head, kv, pend_tokens_dev, pend_hiddens_dev, n_max, n_dev, MTP_FLUSH_LAST, 1, hout,
-                    draft_logits_dev, drafts_dev, ws, stream, 1);
+                    draft_logits_dev, drafts_dev, ws, stream, 1, kOneSession, nullptr,
+                    n_draft > 1 ? &pend : nullptr);
   if (st != MTP_OK) return st;
   // chained steps: (d_{i-1}, g_{i-1}) -> d_i, g_i
   for (int i = 1; i < n_draft; ++i) {
+    FinishArgs next;
+    std::memset(&next, 0, sizeof(next));
     st = head_forward(head, kv, drafts_dev + (i - 1), hout + (i - 1) * row_bytes, 1, nullptr, MTP_FLUSH_LAST, 0,
                       hout + i * row_bytes, draft_logits_dev ? draft_logits_dev + static_cast<size_t>(i) * c.vocab
                                                              : nullptr,
-                      drafts_dev + i, ws, stream);
+                      drafts_dev + i, ws, stream, 0, kOneSession, &pend, i + 1 < n_draft ? &next : nullptr);
     if (st != MTP_OK) return st;
+    pend = next;
   }
   return MTP_OK;
 }

@@ -371,6 +371,29 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   if (a.batch <= 1 && a.kv_state && a.kv_state[3] != 0) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
 
+  // the previous step's argmax merge, in every workgroup; its stores (the
+  // token and the append commit, workgroup 0) wait for the kernel's end, since
+  // a store this early would keep the compiler from loading the launch's
+  // uniform inputs through the scalar cache
+  int ftok = -1, flen = 0, fn = 0;
+  if (TWO && NR == 1 && a.fin_parts) {
+    flen = a.fin_state[0];
+    const int nd0 = a.fin_ndev ? *a.fin_ndev : a.fin_nmax;
+    unsigned long long b = block_max_u64_first(a.fin_parts, a.fin_nparts);
+    b = block_max_u64_rest(a.fin_parts, a.fin_nparts, b);
+    fn = min(max(nd0, 0), a.fin_nmax);
+    // the same in every lane: read out as a scalar so the staging branches and
+    // the embedding row address stay uniform
+    if (fn > 0) ftok = __builtin_amdgcn_readfirstlane(argmax_index(b));
+  }
+  auto fin_commit = [&]() {
+    if (TWO && NR == 1 && a.fin_parts && blockIdx.x == 0 && tid == 0) {
+      if (fn > 0 && a.fin_amax) *a.fin_amax = ftok;
+      a.fin_state[0] = flen + fn;
+      if (a.fin_set_base) a.fin_state[1] = flen + fn;
+    }
+  };
+
   // ---- activation rows handled by this launch.  Slot r (of NR) reads
   // workspace row jr[r], token tr[r] and hidden row hr[r]; ROW_LAST outputs of
   // the hidden copy and the logits go to row orw[r]; vr[r] tells whether the
@@ -415,6 +438,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   }
   if (!any) {
     if (a.out_mode == OUT_LOGITS && threadIdx.x < NR) a.amax_part[threadIdx.x * gridDim.x + blockIdx.x] = 0ull;
+    fin_commit();
     return;
   }
   const int K = a.K;
@@ -478,10 +502,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
               if (WT == W_F32 || !stage_wide<XB>(dst, A, B, 0, a.nw_bf16, k0, se, sh))
                 stage_range<XB>(dst, a.x, static_cast<long long>(jr[r]) * a.ldx, 0,
                             (a.in_mode == IN_RMS) ? a.nw : nullptr, 0, a.nw_bf16, k0, k0 + klen, k0, se);
-            } else if (WT != W_F32 && a.embed_bf16 == a.hid_bf16 && a.tok[tr[r]] >= 0 &&
-                       a.tok[tr[r]] < a.vocab_tok) {
+            } else if (WT != W_F32 && a.embed_bf16 == a.hid_bf16 && (ftok >= 0 ? ftok : a.tok[tr[r]]) >= 0 &&
+                       (ftok >= 0 ? ftok : a.tok[tr[r]]) < a.vocab_tok) {
               // both halves in one pass (the embedding and hidden rows share a type)
-              const int tk = a.tok[tr[r]];
+              const int tk = ftok >= 0 ? ftok : a.tok[tr[r]];
               const int ea = k0, eb = min(k0 + klen, half), ha = max(k0, half), hb = k0 + klen;
               const StageSeg A{a.embed, static_cast<long long>(tk) * half, a.nw, 0, ea, ea < eb ? eb : ea};
               const StageSeg B{a.hid, static_cast<long long>(hr[r]) * a.ld_hid - half, a.nw2,
@@ -496,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
               }
             } else {
               const int ea = k0, eb = min(k0 + klen, half);
-              const int tk = a.tok[tr[r]];
+              const int tk = ftok >= 0 ? ftok : a.tok[tr[r]];
               if (tk >= 0 && tk < a.vocab_tok) {
                 if (ea < eb)
                   stage_range<XB>(dst, a.embed, static_cast<long long>(tk) * half, a.embed_bf16, a.nw, 0,
@@ -663,6 +687,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       a.amax_part[tid * gridDim.x + blockIdx.x] = b;
     }
   }
+  fin_commit();
 }
 
 // Launch shape.  Single-phase launches are persistent: the grid is sized by

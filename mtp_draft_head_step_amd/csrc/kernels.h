@@ -69,6 +69,19 @@ struct GemvArgs {
   // and logits go to row b * out_sb of y2 and logits ([rows, vocab]).
   int batch;
   int tok_sb, hid_sb, out_sb, ndev_sb;
+  // IN_EMBED with one session and one row: the previous step's argmax merge
+  // and append commit folded into this launch (fin_parts nullable).  The token
+  // is the argmax of fin_parts[0, fin_nparts) when that step had rows (fin_n =
+  // clamp(*fin_ndev or fin_nmax, 0, fin_nmax) > 0), else tok[0]; workgroup 0
+  // stores it at fin_amax and commits fin_state[0] += fin_n (fin_state[1] = the
+  // new length when fin_set_base).  Nothing in this launch reads those words.
+  const unsigned long long* fin_parts;
+  int fin_nparts;
+  int32_t* fin_amax;
+  const int32_t* fin_ndev;
+  int fin_nmax;
+  int fin_set_base;
+  int32_t* fin_state;
 };
 
 // *grid_out (nullable) receives the number of workgroups launched.
