@@ -29,6 +29,8 @@ Other workloads (one JSON line each, same keys):
                         depth --depth (1..8), lm_head bf16 or int8-g128 (--lm),
                         planted acceptance p_i = 0.8 * 0.85^i, policy A or B,
                         --sessions independent sessions rotated (cold KV)
+  launch_floor          back-to-back launches of the one-workgroup KV rollback:
+                        the GPU time of one dependent launch (eager and graph)
 
 Each line carries ``roofline`` for the workload's dominant kernel (algorithmic
 bytes or flops per launch / its average duration from HIP events recorded
@@ -405,6 +407,64 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False)
         "cpu_baseline": with_host(cpu),
     })
     return out
+
+
+def run_launch_floor(args):
+    """Back-to-back launches of the library's smallest kernel (the one-workgroup
+    KV rollback, which loads the state words and stores the length): the GPU
+    time one dependent launch costs on its stream, eagerly and replayed from a
+    HIP graph.  Every small kernel of a round pays about this much."""
+    import torch
+
+    from mtp_draft_head_step_amd import abi
+    from mtp_draft_head_step_amd import inputs as I
+
+    shape = I.TINY_BF16
+    kp, vp = I.prefix_kv(shape, I.WL_TINY, 16, 64)
+    kv = abi.DraftKV(shape, 64, kp, vp, 16)
+    stream = torch.cuda.current_stream()
+    per = 256                                          # launches per timed batch
+
+    def batch():
+        st = torch.cuda.current_stream()            # the capture stream inside the graph block
+        for _ in range(per):
+            abi.kv_rollback(kv, 16, None, 0, st)      # to the current length: a no-op
+
+    for _ in range(args.warmup):
+        batch()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap_stream = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap_stream):
+        batch()
+    torch.cuda.synchronize()
+    eager, graph = [], []
+    for _ in range(args.repeats):
+        for mode, out in (("eager", eager), ("graph", graph)):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for _ in range(args.steps):
+                if mode == "eager":
+                    batch()
+                else:
+                    g.replay()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            out.append(ev[0].elapsed_time(ev[1]) * 1e3 / (args.steps * per))
+    if int(kv.state[3].item()) != 0 or int(kv.state[0].item()) != 16:
+        raise RuntimeError("device error word set by the launch-floor kernels")
+    e_med = sorted(eager)[len(eager) // 2]
+    g_med = sorted(graph)[len(graph) // 2]
+    line = base_line(args, round(1e6 / g_med, 1), "launches/s", round(g_med * 1e-3, 6), "int32",
+                     "synthetic (a 64-slot tiny-head draft KV; the launches change nothing)",
+                     {"workload": "launch_floor_one_workgroup", "kernel": "KV rollback to the current length",
+                      "launches_per_batch": per})
+    line["us_per_launch"] = {"graph": spread(graph), "eager": spread(eager)}
+    line["higher_is_better"] = True
+    line["roofline"] = None
+    line["cpu_baseline"] = None
+    return line
 
 
 def cpu_rounds(shape, storage, kp, vp, cap, ctx, N, pool_logits, pool_hid, first_tok, first_hid, ring0,
@@ -1285,7 +1345,7 @@ def main():
     ap.add_argument("--workload", default="qwen35_27b_round",
                     choices=["qwen35_27b_round", "tiny_round", "flush256_prefix8192", "flush256_qwen35_27b",
                              "verify_sampled", "depth_ctx32768", "flush_scaling_qwen35_27b",
-                             "depth_auto_ctx32768"])
+                             "depth_auto_ctx32768", "launch_floor"])
     ap.add_argument("--depth", default="4", help="depth_ctx32768: drafts per round (comma list: one line each)")
     ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"],
                     help="qwen35_27b_round, depth_ctx32768: lm_head storage (int8 per (row, 128-column group) "
@@ -1315,7 +1375,8 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     default_steps = {"qwen35_27b_round": 40, "tiny_round": 64, "flush256_prefix8192": 50, "flush256_qwen35_27b": 16,
-                     "verify_sampled": 10000, "depth_ctx32768": 256, "flush_scaling_qwen35_27b": 16, "depth_auto_ctx32768": 600}
+                     "verify_sampled": 10000, "depth_ctx32768": 256, "flush_scaling_qwen35_27b": 16, "depth_auto_ctx32768": 600,
+                     "launch_floor": 8}
     if args.steps is None:
         args.steps = default_steps[args.workload]
 
@@ -1344,6 +1405,8 @@ def main():
         lines = [run_flush_scaling(args)]
     elif args.workload == "depth_auto_ctx32768":
         lines = [run_depth_auto(args)]
+    elif args.workload == "launch_floor":
+        lines = [run_launch_floor(args)]
     else:
         lines = [run_depth(args, int(d), args.lm) for d in str(args.depth).split(",")]
     for line in lines:

@@ -181,8 +181,11 @@ __device__ __forceinline__ void norm_rope_head(const float* src, const void* nw,
   }
 }
 
-template <bool KVB, int D, int G, bool FUSE>
-__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+// NW waves per workgroup (8 for heavy one-row decode launches: two waves per
+// SIMD hide part of the latency of the per-key reductions)
+template <bool KVB, int D, int G, bool FUSE, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
+  constexpr int kAttnWaves = NW, kAttnThreads = NW * 64;
   constexpr int EPL = KVB ? 8 : 4;   // elements per lane (16 bytes)
   constexpr int LPK = D / EPL;       // lanes per key row
   constexpr int KPI = 64 / LPK;      // keys per wave instruction
@@ -543,20 +546,35 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   else a.o[oi] = out;
 }
 
-template <bool KVB, int D, bool FUSE>
-static hipError_t attn_dg(const AttnArgs& a, dim3 grid, hipStream_t s) {
+template <bool KVB, int D, bool FUSE, int NW>
+static hipError_t attn_dgw(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int g = a.hq / a.hkv;
   (void)hipGetLastError();
   switch (g) {
-    case 1: hipLaunchKernelGGL((k_attn<KVB, D, 1, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attn<KVB, D, 2, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_attn<KVB, D, 3, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attn<KVB, D, 4, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_attn<KVB, D, 6, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_attn<KVB, D, 8, FUSE>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_attn<KVB, D, 1, FUSE, NW>), grid, dim3(NW * 64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attn<KVB, D, 2, FUSE, NW>), grid, dim3(NW * 64), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_attn<KVB, D, 3, FUSE, NW>), grid, dim3(NW * 64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attn<KVB, D, 4, FUSE, NW>), grid, dim3(NW * 64), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_attn<KVB, D, 6, FUSE, NW>), grid, dim3(NW * 64), 0, s, a); break;
+    case 8:
+      if constexpr (NW == 4) hipLaunchKernelGGL((k_attn<KVB, D, 8, FUSE, NW>), grid, dim3(NW * 64), 0, s, a);
+      else return hipErrorInvalidValue;   // eight heads a group keep four waves (register room)
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <bool KVB, int D, bool FUSE>
+static hipError_t attn_dg(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  // one-row launches over bf16 K/V with many products per key (grouped heads x
+  // head_dim >= 1024, up to six heads a group): eight waves per workgroup (on
+  // the 27B shape 1 us less per launch; the tiny head's two grouped heads of 64
+  // measured 0.2 us slower)
+  const int g = a.hq / a.hkv;
+  if (KVB && a.row_sel == ROW_LAST && g <= 6 && g * D >= 1024)
+    return attn_dgw<KVB, D, FUSE, KVB ? 8 : 4>(a, grid, s);
+  return attn_dgw<KVB, D, FUSE, 4>(a, grid, s);
 }
 
 template <bool KVB, int D>
