@@ -850,7 +850,7 @@ def run_verify(args):
         "roofline": roofline("hbm", chunk_bytes / avg / 1e9, HBM_PEAK_GBS, "GB/s", None,
                              kernel=("whole-vocabulary transform pass over the 9 rows (penalty, temperature, "
                                      "row maxima; transformed rows written back)" if full else
-                                     "per-chunk top-k pass over the 9 rows (penalty, temperature, radix select)"),
+                                     "per-chunk top-k pass over the 9 rows (penalty, temperature, top-k above a floor, sorted)"),
                              bytes_per_launch=chunk_bytes, avg_us=round(avg * 1e6, 2), launches=nl),
         "cpu_baseline": with_host(cpu),
     })
