@@ -337,6 +337,15 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
                  const Sessions& ss = kOneSession, const FinishArgs* fold_in = nullptr,
                  FinishArgs* defer_out = nullptr) {
   const mtp_head_config& c = h->cfg;
+  // a folded merge not yet enqueued when this call returns (an error before its
+  // fc pass) is launched on the way out, so the previous step still commits
+  struct FoldGuard {
+    const FinishArgs* f;
+    hipStream_t s;
+    ~FoldGuard() {
+      if (f) (void)launch_finish(*f, s);
+    }
+  } guard{fold_in && fold_in->state ? fold_in : nullptr, s};
   const int rows_total = ss.multi() ? ss.batch * n_max : n_max;   // workspace rows
   const int slots = slots_of(ss);
   const Layout L = layout(c, rows_total, kv->capacity, slots);
@@ -376,7 +385,10 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   bool normed_qkv = false, normed_mlp = false;
   const bool have_fold = fold_in && fold_in->state;
   const bool fold = have_fold && fold_in->parts && !mfma && !ss.multi() && rows_total == 1;
-  if (have_fold && !fold) MTP_TRY(launch_finish(*fold_in, s));
+  if (have_fold && !fold) {
+    guard.f = nullptr;
+    MTP_TRY(launch_finish(*fold_in, s));
+  }
   if (mfma) {
     PrepArgs p = base_prep(h, kv, n_max, n_dev, xa, ss);
     p.in_mode = IN_EMBED; p.K = 2 * H; p.ld_out = 2 * H;
@@ -404,6 +416,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     a.fin_parts = fold_in->parts; a.fin_nparts = fold_in->nparts; a.fin_amax = fold_in->amax_out;
     a.fin_ndev = fold_in->n_dev; a.fin_nmax = fold_in->n_max; a.fin_set_base = fold_in->set_base;
     a.fin_state = fold_in->state;
+    guard.f = nullptr;   // the fc pass below carries it
   }
   if (!mfma) MTP_TRY(run_gemv(a, h->wt, rows_total, ROWS_RANGE, s));
 
