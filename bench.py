@@ -241,6 +241,73 @@ def calibrate_copy(args):
 
 
 # ---------------------------------------------------------------------------
+# the round's results on the host
+# ---------------------------------------------------------------------------
+class HostRows:
+    """`rows` x `cols` int32 rows in host-coherent pinned memory, filled by
+    device-to-host copies on the round's stream, with one completion event per
+    row.  The GPU writes coherent host memory uncached, so a finished copy is
+    visible to the host without a system-scope cache write-back: the events
+    are created without that fence (an event with it writes back and
+    invalidates the GPU's L2 between every two rounds).  The HIP calls go to
+    the runtime libmtp is bound to (symbol lookup through its handle)."""
+    COHERENT, D2H = 0x40000000, 2                                   # hipHostMallocCoherent, hipMemcpyDeviceToHost
+    EV_FLAGS = 0x2 | 0x20000000                                     # DisableTiming | DisableSystemFence
+
+    def __init__(self, rows, cols):
+        import ctypes as C
+        from mtp_draft_head_step_amd import abi
+        import numpy as np
+        self.C, hip = C, C.CDLL(abi.LIB_PATH)
+        vp = C.c_void_p
+        hip.hipHostMalloc.argtypes = [C.POINTER(vp), C.c_size_t, C.c_uint]
+        hip.hipHostFree.argtypes = [vp]
+        hip.hipMemcpyAsync.argtypes = [vp, vp, C.c_size_t, C.c_int, vp]
+        hip.hipEventCreateWithFlags.argtypes = [C.POINTER(vp), C.c_uint]
+        hip.hipEventRecord.argtypes = [vp, vp]
+        hip.hipEventSynchronize.argtypes = [vp]
+        hip.hipEventDestroy.argtypes = [vp]
+        self.hip, self.rows, self.cols = hip, rows, cols
+        self.ptr = vp()
+        self._ok(hip.hipHostMalloc(C.byref(self.ptr), rows * cols * 4, self.COHERENT), "hipHostMalloc")
+        self.view = np.ctypeslib.as_array((C.c_int32 * (rows * cols)).from_address(self.ptr.value)).reshape(rows, cols)
+        self.view[:] = 0
+        self.ev = []
+        for _ in range(rows):
+            e = vp()
+            self._ok(hip.hipEventCreateWithFlags(C.byref(e), self.EV_FLAGS), "hipEventCreateWithFlags")
+            self.ev.append(e)
+
+    @staticmethod
+    def _ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def copy(self, i, dev, stream):
+        """Enqueue the copy of device int32 tensor `dev` into row i (also inside a
+        graph capture, where it becomes a copy node)."""
+        assert dev.numel() == self.cols and dev.dtype.itemsize == 4 and dev.is_contiguous()
+        self._ok(self.hip.hipMemcpyAsync(self.ptr.value + i * self.cols * 4, dev.data_ptr(), self.cols * 4,
+                                         self.D2H, stream.cuda_stream), "hipMemcpyAsync")
+
+    def record(self, i, stream):
+        self._ok(self.hip.hipEventRecord(self.ev[i], stream.cuda_stream), "hipEventRecord")
+
+    def wait(self, i):
+        self._ok(self.hip.hipEventSynchronize(self.ev[i]), "hipEventSynchronize")
+        return self.view[i]
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+        if self.ptr.value:
+            self.hip.hipHostFree(self.ptr)
+            self.ptr = self.C.c_void_p()
+            self.view = None
+
+
+# ---------------------------------------------------------------------------
 # greedy rounds (the 27B-shaped head; the tiny fp32 head)
 # ---------------------------------------------------------------------------
 def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False):
@@ -287,8 +354,9 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False)
     io[1] = 1
     io[2:] = abi.to_device(first_tok)
     t_hid[POOL - 1].copy_(abi.to_device(first_hid))
-    host = torch.zeros((POOL, iost.numel()), dtype=torch.int32).pin_memory()
+    host = HostRows(POOL, iost.numel())
     totals = {"committed": 0, "accepted": 0, "rounds": 0}
+    last = {}
 
     def enqueue_round(r, st):
         prev = (r - 1) % POOL
@@ -297,12 +365,17 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False)
         abi.spec_verify(sp, N, V, t_logits[r % POOL], None, d_buf, ring, ring_st, None, io[2:], io[0:2], vws, st)
         abi.kv_rollback(kv, abi.TO_ROUND_BASE, None, N, st)
         # the round's results for the host: the KV state words, k, k+1, tokens
-        host[r % POOL].copy_(iost, non_blocking=True)
+        host.copy(r % POOL, iost, st)
 
     def consume(r):
-        row = host[r % POOL]
+        row = host.view[r % POOL]
         if int(row[3]) != 0:
             raise RuntimeError(f"device error word {int(row[3])} in round {r}")
+        # each round flushes the previous round's committed pairs and rolls back
+        # to that base: a stale row would break this chain
+        if last and int(row[0]) != last["len"] + last["committed"]:
+            raise RuntimeError(f"round {r}: KV length {int(row[0])}, expected {last['len'] + last['committed']}")
+        last.update(len=int(row[0]), committed=int(row[5]))
         totals["committed"] += int(row[5])
         totals["accepted"] += int(row[4])
         totals["rounds"] += 1
@@ -318,7 +391,6 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False)
         returns its elapsed seconds."""
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        done = [torch.cuda.Event(), torch.cuda.Event()]
         prev = None
         for r in range(first, first + args.steps):
             if graphs is not None:
@@ -328,12 +400,12 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False)
                     abi.mtp_timing_pause(False)
                 enqueue_round(r, stream)
                 abi.mtp_timing_pause(True)
-            done[r % 2].record(stream)
+            host.record(r % POOL, stream)
             if prev is not None:                          # the one host sync per round,
-                done[prev % 2].synchronize()              # overlapped with the next round
+                host.wait(prev % POOL)                    # overlapped with the next round
                 consume(prev)
             prev = r
-        done[prev % 2].synchronize()
+        host.wait(prev % POOL)
         consume(prev)
         torch.cuda.synchronize()
         return time.perf_counter() - t_start
@@ -366,6 +438,7 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False)
             graph_el.append(repeat(graphs, r0))
             r0 += args.steps
     host1 = host_info()
+    host.close()
     els = graph_el if graph_el else eager_el
     elapsed = sorted(els)[len(els) // 2]                 # the median repeat
     log(f"timed {args.repeats} x {args.steps} rounds; median {elapsed * 1e3:.1f} ms; unembedding {lm_n} launches")
@@ -1012,17 +1085,17 @@ def run_depth(args, N, lm):
     # timed replay: the same device work, host sync per round overlapped
     reset()
     prev_round.clear()
-    host = torch.zeros((POOL, 4 + 2 + N + 1), dtype=torch.int32).pin_memory()
+    host = HostRows(POOL, 4 + 2 + N + 1)
     got = [None] * R
 
     def enqueue(r):
         s = r % S
         draft(s, stream)
         verify_and_rollback(s, r, stream)
-        host[r % POOL].copy_(sessions[s]["iost"], non_blocking=True)   # one copy per round
+        host.copy(r % POOL, sessions[s]["iost"], stream)   # one copy per round
 
     def consume(r):
-        row = host[r % POOL]
+        row = host.view[r % POOL]
         if int(row[3]) != 0:
             raise RuntimeError(f"device error word in round {r}")
         got[r] = row[6: 6 + int(row[5])].tolist()
@@ -1033,21 +1106,21 @@ def run_depth(args, N, lm):
         consume(r)
     abi.mtp_timing_begin(abi.TIME_ATTENTION, args.steps * N + 4)
     torch.cuda.synchronize()
-    done = [torch.cuda.Event(), torch.cuda.Event()]
     t = time.perf_counter()
     prev = None
     for r in range(args.warmup, R):
         abi.mtp_timing_pause(not (r % TIME_EVERY == 0 or r == args.warmup))
         enqueue(r)
-        done[r % 2].record(stream)
+        host.record(r % POOL, stream)
         if prev is not None:
-            done[prev % 2].synchronize()
+            host.wait(prev % POOL)
             consume(prev)
         prev = r
-    done[prev % 2].synchronize()
+    host.wait(prev % POOL)
     consume(prev)
     torch.cuda.synchronize()
     el = time.perf_counter() - t
+    host.close()
     att_ms, att_n = abi.mtp_timing_end()
     if got != committed:
         raise RuntimeError("the timed replay committed a different stream than the recording pass")

@@ -939,7 +939,11 @@ int mtp_timing_begin(int32_t kind, int32_t max_launches) {
   g_timer.start.assign(max_launches, nullptr);
   g_timer.stop.assign(max_launches, nullptr);
   for (int i = 0; i < max_launches; ++i) {
-    if (hipEventCreate(&g_timer.start[i]) != hipSuccess || hipEventCreate(&g_timer.stop[i]) != hipSuccess) {
+    // Timing only: no system-scope fence (no cache write-back between the
+    // bracketed launch and its neighbours).
+    const unsigned fl = hipEventDisableSystemFence;
+    if (hipEventCreateWithFlags(&g_timer.start[i], fl) != hipSuccess ||
+        hipEventCreateWithFlags(&g_timer.stop[i], fl) != hipSuccess) {
       g_last_hip = hipErrorOutOfMemory;
       g_timer.on = false;
       return MTP_E_HIP;
