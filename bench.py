@@ -244,14 +244,14 @@ def calibrate_copy(args):
 # the round's results on the host
 # ---------------------------------------------------------------------------
 class HostRows:
-    """`rows` x `cols` int32 rows in host-coherent pinned memory, filled by
-    device-to-host copies on the round's stream, with one completion event per
-    row.  The GPU writes coherent host memory uncached, so a finished copy is
-    visible to the host without a system-scope cache write-back: the events
-    are created without that fence (an event with it writes back and
-    invalidates the GPU's L2 between every two rounds).  The HIP calls go to
-    the runtime libmtp is bound to (symbol lookup through its handle)."""
-    COHERENT, D2H = 0x40000000, 2                                   # hipHostMallocCoherent, hipMemcpyDeviceToHost
+    """`rows` x `cols` int32 rows in host-coherent pinned memory, each written
+    by a round's final verify kernel (system-scope stores, no copy launch), with
+    one completion event per row.  Those stores reach host memory uncached, so
+    the events are created without the system-scope fence (an event with it
+    writes back and invalidates the GPU's L2 between every two rounds).  The
+    HIP calls go to the runtime libmtp is bound to (symbol lookup through its
+    handle)."""
+    COHERENT = 0x40000000                                           # hipHostMallocCoherent
     EV_FLAGS = 0x2 | 0x20000000                                     # DisableTiming | DisableSystemFence
 
     def __init__(self, rows, cols):
@@ -262,7 +262,6 @@ class HostRows:
         vp = C.c_void_p
         hip.hipHostMalloc.argtypes = [C.POINTER(vp), C.c_size_t, C.c_uint]
         hip.hipHostFree.argtypes = [vp]
-        hip.hipMemcpyAsync.argtypes = [vp, vp, C.c_size_t, C.c_int, vp]
         hip.hipEventCreateWithFlags.argtypes = [C.POINTER(vp), C.c_uint]
         hip.hipEventRecord.argtypes = [vp, vp]
         hip.hipEventSynchronize.argtypes = [vp]
@@ -283,12 +282,10 @@ class HostRows:
         if rc != 0:
             raise RuntimeError(f"{what} failed with HIP error {rc}")
 
-    def copy(self, i, dev, stream):
-        """Enqueue the copy of device int32 tensor `dev` into row i (also inside a
-        graph capture, where it becomes a copy node)."""
-        assert dev.numel() == self.cols and dev.dtype.itemsize == 4 and dev.is_contiguous()
-        self._ok(self.hip.hipMemcpyAsync(self.ptr.value + i * self.cols * 4, dev.data_ptr(), self.cols * 4,
-                                         self.D2H, stream.cuda_stream), "hipMemcpyAsync")
+    def addr(self, i):
+        """Host address of row i: the report row the round's final verify
+        kernel writes (spec_verify_rollback)."""
+        return self.ptr.value + i * self.cols * 4
 
     def record(self, i, stream):
         self._ok(self.hip.hipEventRecord(self.ev[i], stream.cuda_stream), "hipEventRecord")
@@ -362,10 +359,10 @@ def run_greedy_rounds(args, shape, wl, ctx, N, workload, data, use_graphs=False)
         prev = (r - 1) % POOL
         # flush of the pending pairs + N - 1 chained steps, one call
         abi.mtp_draft_chain(head, kv, io[2:], t_hid[prev], N + 1, io[1:2], N, d_buf, g_buf, None, ws, st)
-        abi.spec_verify(sp, N, V, t_logits[r % POOL], None, d_buf, ring, ring_st, None, io[2:], io[0:2], vws, st)
-        abi.kv_rollback(kv, abi.TO_ROUND_BASE, None, N, st)
-        # the round's results for the host: the KV state words, k, k+1, tokens
-        host.copy(r % POOL, iost, st)
+        # verify, the rollback to the round base (policy A) and the round's
+        # results for the host (KV state words, k, k+1, tokens) in one call
+        abi.spec_verify_rollback(sp, N, V, t_logits[r % POOL], None, d_buf, ring, ring_st, None, io[2:], io[0:2],
+                                 vws, kv, abi.TO_ROUND_BASE, False, host.addr(r % POOL), st)
 
     def consume(r):
         row = host.view[r % POOL]
@@ -1049,11 +1046,11 @@ def run_depth(args, N, lm):
         toks, hid, cnt = pending_of(s)
         abi.mtp_draft_chain(head, ss["kv"], toks, hid, N + 1, cnt, N, ss["d"], ss["g"], None, ws, st)
 
-    def verify_and_rollback(s, r, st):
+    def verify_and_rollback(s, r, st, report=None):
         ss = sessions[s]
-        abi.spec_verify(sp, N, V, planted[r], None, ss["d"], ss["ring"], ss["ring_st"], None, ss["io"][2:],
-                        ss["io"][0:2], vws, st)
-        abi.kv_rollback(ss["kv"], abi.TO_ROUND_BASE, ss["io"][0:1] if policy == "B" else None, N, st)
+        abi.spec_verify_rollback(sp, N, V, planted[r], None, ss["d"], ss["ring"], ss["ring_st"], None,
+                                 ss["io"][2:], ss["io"][0:2], vws, ss["kv"], abi.TO_ROUND_BASE, policy == "B",
+                                 report, st)
         if policy == "B":
             abi.mtp_repair_pending(ss["io"][2:], ss["io"][0:2], pool_hid[r % POOL], H, abi.MTP_BF16, N,
                                    ss["pend_t"], ss["pend_h"], ss["n_dev"], st)
@@ -1091,8 +1088,7 @@ def run_depth(args, N, lm):
     def enqueue(r):
         s = r % S
         draft(s, stream)
-        verify_and_rollback(s, r, stream)
-        host.copy(r % POOL, sessions[s]["iost"], stream)   # one copy per round
+        verify_and_rollback(s, r, stream, host.addr(r % POOL))   # the round's results to the host
 
     def consume(r):
         row = host.view[r % POOL]

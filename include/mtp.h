@@ -330,6 +330,25 @@ int spec_verify(const spec_sampling *sp, int32_t n_draft, int32_t vocab,
 int kv_rollback(const mtp_kv *kv, int32_t to_len, const int32_t *n_accepted_dev,
                 int32_t n_draft, hipStream_t stream);
 
+/* A round's tail in one call: spec_verify (same arguments, same outputs), then
+ * in its final kernel the draft-KV rollback kv_rollback(kv, to_len,
+ * keep_accepted ? &out_counts_dev[0] : NULL, n_draft) would make (the #1174
+ * comment: trim attention KV by the rejected count; keep_accepted 0 or 1, 1
+ * only with MTP_TO_ROUND_BASE), with no launch of its own.  report_dev
+ * (nullable) receives int32 [6 + n_draft + 1] = {the KV state words after the
+ * rollback, k, k + 1, the first k + 1 committed tokens; later entries
+ * untouched} through system-scope stores, so it may be host-coherent pinned
+ * memory the host reads once the stream has passed this call.  The KV
+ * arguments are checked as kv_rollback checks them, before anything is
+ * enqueued. */
+int spec_verify_rollback(const spec_sampling *sp, int32_t n_draft, int32_t vocab,
+                         const float *target_logits_dev, const float *draft_logits_dev,
+                         const int32_t *draft_tokens_dev, int32_t *history_dev,
+                         int32_t *history_state_dev, const float *uniforms_dev,
+                         int32_t *out_tokens_dev, int32_t *out_counts_dev, void *ws,
+                         size_t ws_bytes, const mtp_kv *kv, int32_t to_len,
+                         int32_t keep_accepted, int32_t *report_dev, hipStream_t stream);
+
 /* Benchmark timing of one kernel class.  After mtp_timing_begin(kind, n) the
  * next n launches of that class (any stream, eager or being captured into a
  * graph) are each bracketed by a pair of HIP events recorded on their stream,

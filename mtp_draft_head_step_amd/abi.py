@@ -32,7 +32,7 @@ WEIGHT_FIELDS = ("embed", "lm_head", "lm_head_scales", "pre_fc_norm_embedding",
 
 EXPORTS = ("mtp_status_string", "mtp_last_error", "mtp_head_create", "mtp_head_destroy", "mtp_workspace_bytes",
            "mtp_workspace_init", "mtp_draft_step", "mtp_draft_step_static", "mtp_flush_pairs", "mtp_draft_chain", "mtp_repair_pending",
-           "spec_verify_workspace_bytes", "spec_verify", "kv_rollback", "mtp_timing_begin",
+           "spec_verify_workspace_bytes", "spec_verify", "spec_verify_rollback", "kv_rollback", "mtp_timing_begin",
            "mtp_timing_pause", "mtp_timing_elapsed", "mtp_timing_end", "mtp_depth_ctl_create",
            "mtp_batch_workspace_bytes", "mtp_draft_chain_batch", "spec_verify_batch", "kv_rollback_batch",
            "mtp_repair_pending_batch",
@@ -99,6 +99,9 @@ def _load():
     lib.mtp_draft_chain_batch.restype = C.c_int
     lib.mtp_draft_chain_batch.argtypes = [vp, C.POINTER(mtp_kv), i32, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp,
                                           sz, vp]
+    lib.spec_verify_rollback.restype = C.c_int
+    lib.spec_verify_rollback.argtypes = [C.POINTER(spec_sampling), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         C.POINTER(mtp_kv), i32, i32, vp, vp]
     lib.spec_verify_batch.restype = C.c_int
     lib.spec_verify_batch.argtypes = [C.POINTER(spec_sampling), i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       sz, vp]
@@ -238,6 +241,17 @@ def spec_verify(sp: spec_sampling, n_draft, vocab, target_logits, draft_logits, 
                          _ptr(draft_tokens), _ptr(history), _ptr(history_state), _ptr(uniforms),
                          _ptr(out_tokens), _ptr(out_counts), _ptr(ws), ws.nbytes, _stream(stream))
     _check(st, "spec_verify")
+
+
+def spec_verify_rollback(sp: spec_sampling, n_draft, vocab, target_logits, draft_logits, draft_tokens,
+                         history, history_state, uniforms, out_tokens, out_counts, ws, kv, to_len,
+                         keep_accepted=False, report=None, stream=None):
+    """`report`: a device tensor, a raw address (host-coherent pinned memory) or None."""
+    st = lib.spec_verify_rollback(C.byref(sp), int(n_draft), int(vocab), _ptr(target_logits), _ptr(draft_logits),
+                                  _ptr(draft_tokens), _ptr(history), _ptr(history_state), _ptr(uniforms),
+                                  _ptr(out_tokens), _ptr(out_counts), _ptr(ws), ws.nbytes, C.byref(kv.desc),
+                                  int(to_len), int(bool(keep_accepted)), _ptr(report), _stream(stream))
+    _check(st, "spec_verify_rollback")
 
 
 def kv_rollback(kv, to_len, n_accepted=None, n_draft=0, stream=None):

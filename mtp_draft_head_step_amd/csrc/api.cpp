@@ -869,7 +869,8 @@ int verify_sessions(const spec_sampling* sp, int32_t batch, int32_t n_draft, int
                     const float* target_logits_dev, const float* draft_logits_dev,
                     const int32_t* draft_tokens_dev, int32_t* history_dev, int32_t* history_state_dev,
                     const float* uniforms_dev, int32_t* out_tokens_dev, int32_t* out_counts_dev,
-                    void* ws, size_t ws_bytes, hipStream_t stream) {
+                    void* ws, size_t ws_bytes, hipStream_t stream, int32_t* kv_state = nullptr,
+                    int32_t kv_to_len = 0, int32_t kv_keep = 0, int32_t* report = nullptr) {
   if (!sp || !target_logits_dev || !history_dev || !history_state_dev || !out_tokens_dev ||
       !out_counts_dev || !ws)
     return MTP_E_INVALID_ARG;
@@ -902,6 +903,10 @@ int verify_sessions(const spec_sampling* sp, int32_t batch, int32_t n_draft, int
   a.scratch = wsp(ws, kHeadBytes + align_up((n_draft + 1) * nb * 8));
   a.batch = batch;
   a.sess_bytes = per;
+  a.kv_state = kv_state;
+  a.kv_to_len = kv_to_len;
+  a.kv_keep = kv_keep;
+  a.report = report;
   const hipError_t e = greedy ? launch_verify_greedy(a, stream) : launch_verify_sampled(a, stream);
   if (e == hipErrorNotSupported) return MTP_E_UNSUPPORTED;
   MTP_TRY(e);
@@ -918,6 +923,23 @@ int spec_verify(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
                 void* ws, size_t ws_bytes, hipStream_t stream) {
   return verify_sessions(sp, 1, n_draft, vocab, target_logits_dev, draft_logits_dev, draft_tokens_dev, history_dev,
                          history_state_dev, uniforms_dev, out_tokens_dev, out_counts_dev, ws, ws_bytes, stream);
+}
+
+int spec_verify_rollback(const spec_sampling* sp, int32_t n_draft, int32_t vocab,
+                         const float* target_logits_dev, const float* draft_logits_dev,
+                         const int32_t* draft_tokens_dev, int32_t* history_dev, int32_t* history_state_dev,
+                         const float* uniforms_dev, int32_t* out_tokens_dev, int32_t* out_counts_dev,
+                         void* ws, size_t ws_bytes, const mtp_kv* kv, int32_t to_len, int32_t keep_accepted,
+                         int32_t* report_dev, hipStream_t stream) {
+  // the rollback's own argument rules (kv_rollback), checked before anything is enqueued
+  if (!kv || !kv->state || kv->capacity <= 0) return MTP_E_INVALID_ARG;
+  if (to_len < MTP_TO_ROUND_BASE) return MTP_E_INVALID_ARG;
+  if (to_len > kv->capacity) return MTP_E_CAPACITY;
+  if (keep_accepted != 0 && keep_accepted != 1) return MTP_E_INVALID_ARG;
+  if (keep_accepted && to_len != MTP_TO_ROUND_BASE) return MTP_E_INVALID_ARG;
+  return verify_sessions(sp, 1, n_draft, vocab, target_logits_dev, draft_logits_dev, draft_tokens_dev, history_dev,
+                         history_state_dev, uniforms_dev, out_tokens_dev, out_counts_dev, ws, ws_bytes, stream,
+                         kv->state, to_len, keep_accepted, report_dev);
 }
 
 int spec_verify_batch(const spec_sampling* sp, int32_t batch, int32_t n_draft, int32_t vocab,

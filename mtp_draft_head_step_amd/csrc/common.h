@@ -200,4 +200,21 @@ __device__ __forceinline__ unsigned long long block_max_u64(const unsigned long 
   return b;
 }
 
+// Draft-KV rollback of one session's state words {length, round base, -,
+// error}: the new length (to_len >= 0, else the round base, plus min(k,
+// n_draft - 1) accepted chained entries when `keep`), or -1 when that passes
+// the current length (the caller then stores error 2).
+__device__ __forceinline__ int rollback_length(int to_len, int len, int base, int k, bool keep, int n_draft) {
+  int to = to_len;
+  if (to_len < 0) {
+    to = base;
+    if (keep) {
+      const int keep_max = n_draft > 0 ? n_draft - 1 : 0;
+      const int kk = k < 0 ? 0 : k;
+      to += kk < keep_max ? kk : keep_max;
+    }
+  }
+  return (to < 0 || to > len) ? -1 : to;
+}
+
 }  // namespace mtp

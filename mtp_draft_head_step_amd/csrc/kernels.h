@@ -271,6 +271,13 @@ struct VerifyArgs {
   // uniforms, outputs) and parts / scratch by b * sess_bytes
   int batch;
   size_t sess_bytes;
+  // The round's tail in the final kernel (one session): when kv_state is set,
+  // the draft KV's state words roll back as kv_rollback(kv_to_len, kv_keep ?
+  // &k : NULL) would; then, when report is set, the row {state words, k, k + 1,
+  // committed run} is written there (system-scope stores).
+  int32_t* kv_state;
+  int kv_to_len, kv_keep;
+  int32_t* report;
 };
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s);

@@ -17,16 +17,8 @@ __global__ void k_rollback(int32_t* st0, int to_len, const int32_t* n_acc0, int 
   const int err0 = st[3], len0 = st[0], base0 = st[1];
   const int k0 = n_acc ? *n_acc : 0;
   if (err0 != 0) return;
-  int to = to_len;
-  if (to_len < 0) {
-    to = base0;
-    if (n_acc) {
-      const int keep_max = n_draft > 0 ? n_draft - 1 : 0;
-      const int k = k0 < 0 ? 0 : k0;
-      to += k < keep_max ? k : keep_max;
-    }
-  }
-  if (to < 0 || to > len0) {
+  const int to = rollback_length(to_len, len0, base0, k0, n_acc != nullptr, n_draft);
+  if (to < 0) {
     st[3] = 2;
     return;
   }

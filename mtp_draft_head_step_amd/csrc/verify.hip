@@ -57,6 +57,68 @@ __device__ __forceinline__ VerifyArgs at_session(VerifyArgs a) {
   return a;
 }
 
+// The draft KV's state words {length, round base, word 2, error}, loaded with
+// the final kernel's other inputs (zeros without a fused rollback).
+struct KvWords {
+  int len, base, w2, err;
+};
+__device__ __forceinline__ KvWords load_kv_words(const VerifyArgs& a) {
+  KvWords w{0, 0, 0, 0};
+  if (a.kv_state) {
+    w.len = a.kv_state[0];
+    w.base = a.kv_state[1];
+    w.w2 = a.kv_state[2];
+    w.err = a.kv_state[3];
+  }
+  return w;
+}
+
+// Stores the host may read once the kernel is done (host-coherent memory):
+// system scope, so no cache level keeps them.
+__device__ __forceinline__ void store_sys(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// One thread commits a verified round: the run dr[0..k-1], tok goes to
+// out_tokens and into the history ring, the counts {k, k + 1} and the ring's
+// state words are stored; then the fused tail (see VerifyArgs): the draft-KV
+// rollback with this k and the report row.
+__device__ void commit_round(const VerifyArgs& a, const int32_t* dr, int k, int tok, KvWords w) {
+  int h = ring_head(a), c = ring_count(a);
+  int32_t* rep = a.report;
+  for (int r = 0; r <= k; ++r) {
+    const int t = r < k ? dr[r] : tok;
+    a.out_tokens[r] = t;
+    a.ring[h] = t;
+    if (rep) store_sys(rep + 6 + r, t);
+    h = (h + 1) % a.window;
+    c = c + 1 < a.window ? c + 1 : a.window;
+  }
+  a.out_counts[0] = k;
+  a.out_counts[1] = k + 1;
+  a.ring_state[0] = h;
+  a.ring_state[1] = c;
+  if (!a.kv_state) return;
+  if (w.err == 0) {
+    const int to = rollback_length(a.kv_to_len, w.len, w.base, k, a.kv_keep != 0, a.n_draft);
+    if (to < 0) {
+      w.err = 2;
+      a.kv_state[3] = 2;
+    } else {
+      w.len = to;
+      a.kv_state[0] = to;
+    }
+  }
+  if (rep) {
+    store_sys(rep + 0, w.len);
+    store_sys(rep + 1, w.base);
+    store_sys(rep + 2, w.w2);
+    store_sys(rep + 3, w.err);
+    store_sys(rep + 4, k);
+    store_sys(rep + 5, k + 1);
+  }
+}
+
 __global__ __launch_bounds__(kVThreads) void k_verify_greedy(VerifyArgs a) {
   a = at_session(a);
   __shared__ uint32_t bits[kVMaxChunk / 32];
@@ -126,7 +188,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a
     v[u] = e < tot ? a.parts[e] : 0ull;
   }
   const int dr = tid < n ? a.drafts[tid] : 0;
-  const int h0 = ring_head(a), c0 = ring_count(a);
+  const KvWords w = tid == 0 ? load_kv_words(a) : KvWords{0, 0, 0, 0};
   if (tid <= n) s_row[tid] = 0ull;
   if (tid < n) s_dr[tid] = dr;
   __syncthreads();
@@ -142,18 +204,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify_greedy_finish(VerifyArgs a
   for (int r = 0; r < n; ++r) {
     if (s_dr[r] != argmax_index(s_row[r])) { k = r; break; }
   }
-  int h = h0, c = c0;
-  for (int r = 0; r <= k; ++r) {
-    const int t = r < k ? s_dr[r] : argmax_index(s_row[k]);
-    a.out_tokens[r] = t;
-    a.ring[h] = t;
-    h = (h + 1) % a.window;
-    c = c + 1 < a.window ? c + 1 : a.window;
-  }
-  a.out_counts[0] = k;
-  a.out_counts[1] = k + 1;
-  a.ring_state[0] = h;
-  a.ring_state[1] = c;
+  commit_round(a, s_dr, k, argmax_index(s_row[k]), w);
 }
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
@@ -688,6 +739,7 @@ __global__ void k_sample_decide(VerifyArgs a, SampledScratch sc) {
     sc = sampled_scratch(a.scratch, a.n_draft, a.vocab);
   }
   if (threadIdx.x != 0) return;
+  const KvWords w = load_kv_words(a);
   const int n = a.n_draft;
   int k = n, tok = -1;
   for (int i = 0; i < n; ++i) {
@@ -701,18 +753,7 @@ __global__ void k_sample_decide(VerifyArgs a, SampledScratch sc) {
     break;
   }
   if (k == n) tok = draw(sc, n, -1, a.uniforms[n]);
-  int h = ring_head(a), c = ring_count(a);
-  for (int r = 0; r <= k; ++r) {
-    const int t = r < k ? a.drafts[r] : tok;
-    a.out_tokens[r] = t;
-    a.ring[h] = t;
-    h = (h + 1) % a.window;
-    c = c + 1 < a.window ? c + 1 : a.window;
-  }
-  a.out_counts[0] = k;
-  a.out_counts[1] = k + 1;
-  a.ring_state[0] = h;
-  a.ring_state[1] = c;
+  commit_round(a, a.drafts, k, tok, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1070,6 +1111,7 @@ __global__ __launch_bounds__(kFThreads) void k_full_decide(VerifyArgs a, FullScr
   __shared__ DrawShared ds;
   __shared__ int s_k;
   const int n = a.n_draft;
+  const KvWords w = threadIdx.x == 0 ? load_kv_words(a) : KvWords{0, 0, 0, 0};
   if (threadIdx.x == 0) {
     int k = n;
     for (int i = 0; i < n; ++i) {
@@ -1092,18 +1134,7 @@ __global__ __launch_bounds__(kFThreads) void k_full_decide(VerifyArgs a, FullScr
     tok = full_draw(a, fs, n, -1, a.uniforms[n], ds);
   }
   if (threadIdx.x != 0) return;
-  int h = ring_head(a), c = ring_count(a);
-  for (int r = 0; r <= k; ++r) {
-    const int t = r < k ? a.drafts[r] : tok;
-    a.out_tokens[r] = t;
-    a.ring[h] = t;
-    h = (h + 1) % a.window;
-    c = c + 1 < a.window ? c + 1 : a.window;
-  }
-  a.out_counts[0] = k;
-  a.out_counts[1] = k + 1;
-  a.ring_state[0] = h;
-  a.ring_state[1] = c;
+  commit_round(a, a.drafts, k, tok, w);
 }
 
 // the per-chunk candidate path holds the top_k keys of every chunk

@@ -126,6 +126,27 @@ def test_verify_fails_closed():
     assert call(bad_win, 2, 100, draft=None) == abi.MTP_E_INVALID_ARG
 
 
+def test_verify_rollback_fails_closed():
+    """The fused verify + rollback checks the rollback's arguments as kv_rollback
+    does and the verification's as spec_verify does, before any launch."""
+    v = abi.lib.spec_verify_rollback
+    greedy = abi.sampling()
+    kv = abi.mtp_kv(0x1000, 0x2000, 128, 0x3000)
+    no_state = abi.mtp_kv(0x1000, 0x2000, 128, 0)
+    def call(kvd, to_len, keep, n=2, wsb=1 << 30, draft=None):
+        return v(C.byref(greedy), n, 100, 0x10, draft, 0x30, 0x40, 0x50, None, 0x70, 0x80, 0x90, wsb,
+                 C.byref(kvd) if kvd is not None else None, to_len, keep, 0xa0, None)
+    assert call(kv, 129, 0) == abi.MTP_E_CAPACITY
+    assert call(kv, -2, 0) == abi.MTP_E_INVALID_ARG
+    assert call(kv, 5, 1) == abi.MTP_E_INVALID_ARG           # keep_accepted only with the round base
+    assert call(kv, abi.TO_ROUND_BASE, 2) == abi.MTP_E_INVALID_ARG
+    assert call(no_state, abi.TO_ROUND_BASE, 0) == abi.MTP_E_INVALID_ARG
+    assert call(None, abi.TO_ROUND_BASE, 0) == abi.MTP_E_INVALID_ARG
+    assert call(kv, abi.TO_ROUND_BASE, 0, n=17) == abi.MTP_E_INVALID_ARG
+    assert call(kv, abi.TO_ROUND_BASE, 0, wsb=8) == abi.MTP_E_WORKSPACE
+    assert call(kv, abi.TO_ROUND_BASE, 0, draft=0x20) == abi.MTP_E_INVALID_ARG
+
+
 def test_static_step_rejects_oversized_scratch_on_host():
     """The no-workspace draft step refuses, before any HIP call, a step whose
     scratch would not fit the library's static array (4 MiB per device)."""
