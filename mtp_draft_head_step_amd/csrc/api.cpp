@@ -268,10 +268,11 @@ hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t
   return hipSuccess;
 }
 
-hipError_t timed_gemm(const GemmArgs& g, hipStream_t s, const RowNorm* rn = nullptr, bool* normed = nullptr) {
+hipError_t timed_gemm(const GemmArgs& g, hipStream_t s, const RowNorm* rn = nullptr, bool* normed = nullptr,
+                      int* split_left = nullptr) {
   int slot = -1;
   time_mark(TIME_PROJECTION, true, s, &slot);
-  const hipError_t e = launch_gemm(g, s, rn, normed);
+  const hipError_t e = launch_gemm(g, s, rn, normed, split_left);
   time_mark(TIME_PROJECTION, false, s, &slot);
   return e;
 }
@@ -420,6 +421,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   }
   if (!mfma) MTP_TRY(run_gemv(a, h->wt, rows_total, ROWS_RANGE, s));
 
+  // LAST mode: the norm/RoPE/append runs inside the attention kernel, which
+  // also sums the q/k/v product's split-K partials (one session)
+  const bool fuse_rope = mode == MTP_FLUSH_LAST;
+  int qkv_split = 1;
+
   // 2. q, k, v = W_{q,k,v} RMSNorm(x; w_in)
   if (mfma) {
     if (!normed_qkv) {
@@ -432,7 +438,8 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     m2.w[1] = static_cast<const uint16_t*>(h->w.k_proj); m2.m[1] = hkv * D;
     m2.w[2] = static_cast<const uint16_t*>(h->w.v_proj); m2.m[2] = hkv * D;
     m2.M = qkv_rows; m2.K = H; m2.a = xa; m2.lda = H; m2.out_mode = OUT_F32; m2.y = qkv; m2.ldy = qkv_rows;
-    MTP_TRY(timed_gemm(m2, s));
+    const bool defer = fuse_rope && !ss.multi() && D >= kSplitMinHeadDim;
+    MTP_TRY(timed_gemm(m2, s, nullptr, nullptr, defer ? &qkv_split : nullptr));
   }
   a = base_gemv(h, kv, ss);
   a.w[0] = h->w.q_proj; a.m[0] = hq * D;
@@ -452,8 +459,6 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   r.eps = c.rms_eps; r.theta = c.rope_theta; r.hq = hq; r.hkv = hkv; r.d = D;
   r.kc = kv->k; r.vc = kv->v; r.kv_bf16 = c.kv_dtype == MTP_BF16; r.capacity = kv->capacity;
   r.state = kv->state; r.n_max = n_max; r.n_dev = n_dev; r.n_min = n_min;
-  // LAST mode: the norm/RoPE/append runs inside the attention kernel
-  const bool fuse_rope = mode == MTP_FLUSH_LAST;
   if (!fuse_rope) MTP_TRY(launch_rope_append(r, s));
   FinishArgs f;
   std::memset(&f, 0, sizeof(f));
@@ -477,6 +482,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   t.batch = ss.batch; t.kv_sb = ss.kv_sb; t.ndev_sb = ss.ndev_sb;
   if (fuse_rope) {
     t.fuse_rope = 1; t.qkv = qkv; t.ld_qkv = qkv_rows; t.q_norm = h->w.q_norm; t.k_norm = h->w.k_norm;
+    t.qkv_nsp = qkv_split;
+    if (qkv_split > 1) {   // partials [split, n_max, qkv_rows]
+      t.qkv = gpart;
+      t.qkv_pstride = n_max * qkv_rows;   // n_max <= 256 rows of at most 24 * 256 columns
+    }
     t.nw_bf16 = h->wt == W_BF16; t.eps = c.rms_eps; t.theta = c.rope_theta;
   }
   if (mfma_out && c.kv_dtype == MTP_BF16) {

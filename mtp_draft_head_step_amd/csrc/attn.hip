@@ -122,18 +122,50 @@ __device__ __forceinline__ void unpack16(const uint4& v, float (&f)[KVB ? 8 : 4]
 // RMSNorm over head_dim of one head (src, D fp32 values) times the norm weight,
 // then rotate-half RoPE at `pos` (one wave): put(d, value) for every d < D, each
 // value by the lane that computed it.
+// Element d of a projection row held as nsp split-K partials ps floats apart,
+// summed in split order (nsp <= 1: the row itself).  The first kSplitLoads
+// partials are loaded together (one memory round trip); offsets are 32-bit
+// element indices from one base, so every split shares one scalar address.
+// Compiled for head_dim >= kSplitMinHeadDim only (SPLIT; the host defers no
+// reduce below it).
+constexpr int kSplitLoads = 4;
+template <int NE, bool SPLIT>
+__device__ __forceinline__ void load_split_row(const float* src, int ps, int nsp, int lane, float (&x)[NE]) {
+  if (!SPLIT || nsp <= 1) {
+#pragma unroll
+    for (int k = 0; k < NE; ++k) x[k] = src[lane + 64 * k];
+    return;
+  }
+  float y[kSplitLoads][NE];
+#pragma unroll
+  for (int q = 0; q < kSplitLoads; ++q)
+    if (q == 0 || q < nsp)
+#pragma unroll
+      for (int k = 0; k < NE; ++k) y[q][k] = src[q * ps + lane + 64 * k];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) x[k] = y[0][k];
+#pragma unroll
+  for (int q = 1; q < kSplitLoads; ++q)
+    if (q < nsp)
+#pragma unroll
+      for (int k = 0; k < NE; ++k) x[k] += y[q][k];
+  for (int q = kSplitLoads; q < nsp; ++q)
+#pragma unroll
+    for (int k = 0; k < NE; ++k) x[k] += src[q * ps + lane + 64 * k];
+}
+
 template <int D, typename Put>
 __device__ __forceinline__ void norm_rope_head(const float* src, const void* nw, int nw_bf16, float eps,
                                                int pos, double l2t, int lane, Put put,
-                                               const float2* cs = nullptr) {
-  // cs: (cos, sin) of every rotation pair at `pos`, if the caller has them
+                                               const float2* cs = nullptr, int ps = 0, int nsp = 1) {
+  // cs: (cos, sin) of every rotation pair at `pos`, if the caller has them;
+  // ps, nsp: the row as split-K partials (load_split_row)
   // every load first (one memory round trip), then the arithmetic in the same
   // per-lane order as an element-at-a-time loop: lane holds d = lane + 64 k
   constexpr int NE = D / 64;                 // elements per lane (D >= 64)
   constexpr int NP = (D / 2 + 63) / 64;      // rotation pairs per lane
   float x[NE];
-#pragma unroll
-  for (int k = 0; k < NE; ++k) x[k] = src[lane + 64 * k];
+  load_split_row<NE, (D >= kSplitMinHeadDim)>(src, ps, nsp, lane, x);
   // weights as raw bits (bf16 in the high half once converted); the
   // conversion waits until after both load forms join
   uint32_t b1[NP], b2[NP];
@@ -290,11 +322,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
       norm_rope_head<D>(row + (a.hq + h) * D, a.k_norm, a.nw_bf16, a.eps, sl, l2t, lane, [&](int d, float v) {
         if constexpr (KVB) static_cast<uint16_t*>(kcs)[o + d] = f32_to_bf16(v);
         else static_cast<float*>(kcs)[o + d] = v;
-      });
+      }, nullptr, a.qkv_pstride, a.qkv_nsp);
       const float* vsrc = row + (a.hq + a.hkv + h) * D;
       float vv[D / 64];
-#pragma unroll
-      for (int k = 0; k < D / 64; ++k) vv[k] = vsrc[lane + 64 * k];
+      load_split_row<D / 64, (D >= kSplitMinHeadDim)>(vsrc, a.qkv_pstride, a.qkv_nsp, lane, vv);
 #pragma unroll
       for (int k = 0; k < D / 64; ++k) {
         if constexpr (KVB) static_cast<uint16_t*>(vcs)[o + lane + 64 * k] = f32_to_bf16(vv[k]);
@@ -307,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
     for (int g = wave; g < G; g += kAttnWaves) {
       float* qd = s_q[g];
       norm_rope_head<D>(qrow + (h * G + g) * D, a.q_norm, a.nw_bf16, a.eps, off + j, l2t, lane,
-                        [&](int d, float v) { qd[d] = v; }, s_cs);
+                        [&](int d, float v) { qd[d] = v; }, s_cs, a.qkv_pstride, a.qkv_nsp);
     }
     __syncthreads();   // the appended rows and the queries are visible to the whole workgroup
 #pragma unroll

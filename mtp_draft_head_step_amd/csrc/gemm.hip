@@ -868,8 +868,9 @@ bool gemm_supported(int M, int K, const int* m, int nmat) {
   return true;
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn, bool* normed) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn, bool* normed, int* split_left) {
   if (normed) *normed = false;
+  if (split_left) *split_left = 1;
   if (a.n_max <= 0) return hipSuccess;
   const bool swiglu = a.out_mode == OUT_SWIGLU;
   (void)hipGetLastError();
@@ -898,7 +899,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn, bool
       if (nt == 8) MTP_STREAM(false, 8); else if (nt == 4) MTP_STREAM(false, 4); else MTP_STREAM(false, 2);
     }
 #undef MTP_STREAM
-    if (nsp > 1) {
+    if (nsp > 1 && split_left && !rn && a.out_mode == OUT_F32) {
+      *split_left = nsp;                       // the caller's next kernel reduces
+    } else if (nsp > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (rn && a.out_mode != OUT_SWIGLU && a.M <= kNormThreads * 4 * kNormPer && a.M % 4 == 0 &&

@@ -160,7 +160,12 @@ struct RowNorm {
 };
 // rn (nullable): also write RMSNorm(y) rows when the product reduces split-K
 // partials; *normed (nullable) tells whether it did (else the caller preps).
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn = nullptr, bool* normed = nullptr);
+// split_left (nullable): a plain split-K product (no rn) leaves its partials
+// in a.part ([split, n_max, M]) unreduced and stores the split count there (1
+// when the product ran unsplit, or reduced them itself): the caller's next
+// kernel sums them.
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowNorm* rn = nullptr, bool* normed = nullptr,
+                       int* split_left = nullptr);
 bool gemm_supported(int M, int K, const int* m, int nmat);
 // fp32 elements of the partial-sum workspace a product of `rows` rows needs
 // (0 when it runs unsplit)
@@ -216,10 +221,14 @@ struct AttnArgs {
   int o_bf16;
   // ROW_LAST with fuse_rope: the q/k RMSNorm + RoPE and the K/V append of the
   // rows j < n run inside the attention kernel (no separate append launch); the
-  // q/k/v projections of the rows are read from qkv.
+  // q/k/v projections of the rows are read from qkv, or, with qkv_nsp > 1, are
+  // the sums in split order of the product's split-K partials qkv + q *
+  // qkv_pstride, q < qkv_nsp (the reduce the product would have launched).
   int fuse_rope;
   const float* qkv;        // [rows, (Hq + 2 Hkv) * D]
   int ld_qkv;
+  int qkv_pstride;
+  int qkv_nsp;
   const void* q_norm;
   const void* k_norm;
   int nw_bf16;
@@ -227,6 +236,8 @@ struct AttnArgs {
   float theta;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// smallest head_dim whose fused prologue sums split partials (qkv_nsp > 1)
+constexpr int kSplitMinHeadDim = 128;
 // the matrix-core flush attention and its merge (chunks at most kFlushMaxChunks)
 constexpr int kFlushMaxChunks = 128;
 hipError_t launch_attention_flush(const AttnArgs& a, hipStream_t s);
