@@ -313,6 +313,28 @@ __device__ __forceinline__ void gemv_fma(float (&acc)[RPW][NR], float (&acc2)[RP
   }
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at dst + 16 l (dst wave-uniform).
+__device__ __forceinline__ void lds_direct16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// The prefetched chunks j .. j + pf - 1 of every row slot, read back from this
+// wave's LDS region (slot (s, u) at byte 1024 (s pf + u), each lane its own 16
+// bytes), in the same accumulation order as the streamed path.
+template <int WT, int NR, int RPW, bool TWO, bool XB>
+__device__ __forceinline__ void gemv_fma_lds(float (&acc)[RPW][NR], float (&acc2)[RPW][NR], const char* pfw,
+                                             int pf, int lane, int j, int lpr, const void* __restrict__ xl, int kp,
+                                             const uint16_t* const (&srow)[RPW], int g0, int split) {
+  for (int u = 0; u < pf; ++u) {
+    uint4 w[RPW][1];
+#pragma unroll
+    for (int s = 0; s < RPW; ++s)
+      w[s][0] = *reinterpret_cast<const uint4*>(pfw + (s * pf + u) * 1024 + lane * 16);
+    gemv_fma<WT, NR, RPW, 1, TWO, XB>(acc, acc2, w, j + u, lpr, xl, kp, srow, g0, split);
+  }
+}
+
 template <int WT, int NR, int RPW, int U, bool TWO, bool XB>
 __device__ __forceinline__ void gemv_body(float (&acc)[RPW][NR], float (&acc2)[RPW][NR],
                                           const char* const (&lane_row)[RPW], int j, int lpr,
@@ -359,7 +381,7 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int blk, int rows_p
 template <int WT, int NR, int RPW, bool TWO, bool XB, bool WSK>
 __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
   // staged inputs [NR][kp]: fp32, or bf16 when XB (few-row flushes with bf16 weights)
-  extern __shared__ float xs_f[];
+  extern __shared__ __attribute__((aligned(16))) float xs_f[];
   using XT = typename std::conditional<XB, uint16_t, float>::type;
   XT* xs = reinterpret_cast<XT*>(xs_f);
   __shared__ float s_red[kWaves][2 * NR];
@@ -490,6 +512,21 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       // stages once, a multi-phase loop restages per phase
       if (blk == static_cast<int>(blockIdx.x) || nphase > 1) {
         __syncthreads();
+        if constexpr (NR == 1) {
+          // the first chunks of this wave's rows go to LDS while the input is staged
+          if (a.pf > 0 && blk == static_cast<int>(blockIdx.x) && nphase == 1) {
+            const int cpl0 = (K / EPC) / lpr;
+            const int jb = WSK ? wave * cpl0 / kWaves : 0;
+            const size_t stride = static_cast<size_t>(lpr) * 16;
+            char* pfw = reinterpret_cast<char*>(xs_f) + a.pf_off + wave * (RPW * a.pf * 1024);
+#pragma unroll
+            for (int s = 0; s < RPW; ++s) {
+              const char* lr = rowp[s] + static_cast<size_t>(li) * 16;
+              for (int u = 0; u < a.pf; ++u)
+                lds_direct16(lr + static_cast<size_t>(jb + u) * stride, pfw + (s * a.pf + u) * 1024);
+            }
+          }
+        }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           XT* dst = xs + r * a.kp;
@@ -557,6 +594,23 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       // few-row passes keep twice the loads in flight (their staged rows cap
       // the workgroups per CU)
       constexpr int kU = NR > 1 ? 2 * kUnroll : kUnroll;
+      if constexpr (NR == 1) {
+        if (a.pf > 0 && blk == static_cast<int>(blockIdx.x) && nphase == 1) {
+          // the prefetched chunks; the next batch's loads go out first
+          const char* pfw = reinterpret_cast<const char*>(xs_f) + a.pf_off + wave * (RPW * a.pf * 1024);
+          const int jp = j + a.pf;
+          if (jp + kU <= je) {
+            uint4 wn[RPW][kU];
+            gemv_load<RPW, kU>(wn, lane_row, jp, lpr);
+            gemv_fma_lds<WT, NR, RPW, TWO, XB>(acc, acc2, pfw, a.pf, lane, j, lpr, xl, a.kp, srow, g0, split_chunk);
+            gemv_fma<WT, NR, RPW, kU, TWO, XB>(acc, acc2, wn, jp, lpr, xl, a.kp, srow, g0, split_chunk);
+            j = jp + kU;
+          } else {
+            gemv_fma_lds<WT, NR, RPW, TWO, XB>(acc, acc2, pfw, a.pf, lane, j, lpr, xl, a.kp, srow, g0, split_chunk);
+            j = jp;
+          }
+        }
+      }
       for (; j + kU <= je; j += kU)
         gemv_body<WT, NR, RPW, kU, TWO, XB>(acc, acc2, lane_row, j, lpr, xl, a.kp, srow, g0, split_chunk);
       if constexpr (kU > kUnroll)
@@ -722,19 +776,41 @@ hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int max_pe
   const int rps = kWave / a.lpr;
   const int rows_per_wg = (WSK ? 1 : kWaves) * ((a.out_mode == OUT_SWIGLU) ? RPW / 2 : RPW) * rps;
   const int nblocks = (a.M + rows_per_wg - 1) / rows_per_wg;
-  const size_t lds = static_cast<size_t>(NR) * a.kp * (XB ? 2 : 4);
+  size_t lds = static_cast<size_t>(NR) * a.kp * (XB ? 2 : 4);
   int grid = nblocks;
   const void* fn = reinterpret_cast<const void*>(&k_gemv<WT, NR, RPW, TWO, XB, WSK>);
+  a.pf = 0;
+  a.pf_off = 0;
   if (a.grid_stride) {
     // workgroups per CU: the kernel's real occupancy (registers and LDS) at this
     // LDS size, capped by the tuning
     int occ = 1, cus = 1;
-    const hipError_t e = occupancy_of(fn, lds, &occ, &cus);
+    hipError_t e = occupancy_of(fn, lds, &occ, &cus);
     if (e != hipSuccess) return e;
     occ = occ < 1 ? 1 : (occ > max_per_cu ? max_per_cu : occ);
     const int cap = cus * occ;
     const int per = (nblocks + cap - 1) / cap;          // row blocks per workgroup
     grid = (nblocks + per - 1) / per;
+    if (NR == 1 && a.kp >= a.K) {
+      // the first-chunk prefetch: as many chunks per lane (up to one streamed
+      // batch) as fit beside the staged row without lowering the occupancy
+      const int cpl = (a.K / WTraits<WT>::EPC) / a.lpr;
+      const int per_wave = WSK ? cpl / kWaves : cpl;
+      const size_t off = (lds + 15) & ~static_cast<size_t>(15);
+      for (int pf = per_wave < kUnroll ? per_wave : kUnroll; pf >= 1; --pf) {
+        const size_t tot = off + static_cast<size_t>(kWaves) * RPW * pf * 1024;
+        if (tot > kMaxLds) continue;
+        int occ1 = 1, cus1 = 1;
+        e = occupancy_of(fn, tot, &occ1, &cus1);
+        if (e != hipSuccess) return e;
+        if ((occ1 > max_per_cu ? max_per_cu : occ1) >= occ) {
+          a.pf = pf;
+          a.pf_off = static_cast<int>(off);
+          lds = tot;
+          break;
+        }
+      }
+    }
   }
   if (grid_out) *grid_out = grid;
   if (a.dry_run) return hipSuccess;
