@@ -768,9 +768,12 @@ constexpr GemvTuning kGemvTuning{};
 hipError_t occupancy_of(const void* fn, size_t lds, int* per_cu, int* cus);
 hipError_t raise_lds_limit(const void* fn);
 
-template <int WT, int NR, int RPW, bool TWO, bool WSK = false>
+// XB1: stage one bf16 row (the long-K projection: half the LDS, which leaves
+// room for the first-chunk prefetch; the input rounded to bf16 as the matrix-core
+// products round theirs)
+template <int WT, int NR, int RPW, bool TWO, bool WSK = false, bool XB1 = false>
 hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int max_per_cu) {
-  constexpr bool XB = NR > 1 && WT == W_BF16;
+  constexpr bool XB = (NR > 1 || XB1) && WT == W_BF16;
   GemvArgs a = a0;
   if (a.out_mode == OUT_SWIGLU && RPW < 2) return hipErrorInvalidValue;
   const int rps = kWave / a.lpr;
@@ -860,7 +863,9 @@ hipError_t launch_r(const GemvArgs& a, hipStream_t s, int* g) {
         switch (rpw) {
           case 1: return launch_t<WT, NR, 1, false, true>(a, s, g, per_cu);
           case 2: return launch_t<WT, NR, 2, false, true>(a, s, g, per_cu);
-          default: return launch_t<WT, NR, 4, false, true>(a, s, g, per_cu);
+          default:
+            if (a.K >= t.long_k && a.in_mode == IN_F32) return launch_t<WT, NR, 4, false, true, true>(a, s, g, per_cu);
+            return launch_t<WT, NR, 4, false, true>(a, s, g, per_cu);
         }
       }
     }
