@@ -749,12 +749,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
 // gets the same number of row blocks (+-1); each stages its input once.
 struct GemvTuning {
   // measured on MI355X (rows per slot, workgroups per CU, waves splitting each
-  // row) for the 27B-shaped head
-  int rpw_large = 4, wg_per_cu_large = 2, wsk_large = 0;    // unembedding (>= large_rows rows)
+  // row) for the 27B-shaped head, with the first-chunk prefetch
+  int rpw_large = 2, wg_per_cu_large = 2, wsk_large = 0;    // unembedding (>= large_rows rows)
   int rpw_swiglu = 2, wg_per_cu_swiglu = 2, wsk_swiglu = 0; // gate/up pairs
-  int rpw_small = 4, wg_per_cu_small = 3, wsk_small = 0;    // 6K..64K-row projections
+  int rpw_small = 2, wg_per_cu_small = 3, wsk_small = 0;    // 6K..64K-row projections
   int rpw_few = 2, wg_per_cu_few = 8, wsk_few = 0;          // projections of < few_rows rows
-  int rpw_long = 4, wg_per_cu_long = 2, wsk_long = 1;       // the same with rows of >= long_k columns
+  int rpw_long = 2, wg_per_cu_long = 2, wsk_long = 1;       // the same with rows of >= long_k columns
   int rpw_embed = 2, wg_per_cu_embed = 6, wsk_embed = 0;    // the fc projection
   int wg_per_cu_rows = 6, wsk_rows = 0, rpw_rows = 2;       // few-row (NR > 1) flush passes
   long large_rows = 65536;
@@ -862,7 +862,9 @@ hipError_t launch_r(const GemvArgs& a, hipStream_t s, int* g) {
       if (wsk) {
         switch (rpw) {
           case 1: return launch_t<WT, NR, 1, false, true>(a, s, g, per_cu);
-          case 2: return launch_t<WT, NR, 2, false, true>(a, s, g, per_cu);
+          case 2:
+            if (a.K >= t.long_k && a.in_mode == IN_F32) return launch_t<WT, NR, 2, false, true, true>(a, s, g, per_cu);
+            return launch_t<WT, NR, 2, false, true>(a, s, g, per_cu);
           default:
             if (a.K >= t.long_k && a.in_mode == IN_F32) return launch_t<WT, NR, 4, false, true, true>(a, s, g, per_cu);
             return launch_t<WT, NR, 4, false, true>(a, s, g, per_cu);
