@@ -31,6 +31,9 @@ Other workloads (one JSON line each, same keys):
                         --sessions independent sessions rotated (cold KV)
   launch_floor          back-to-back launches of the one-workgroup KV rollback:
                         the GPU time of one dependent launch (eager and graph)
+  batch_qwen35_27b      --batch (default 4) independent sessions of the 27B-shaped
+                        head, 4096-slot prefixes, 2 drafts, greedy, in batched calls
+                        (each weight streamed once for every session's rows)
 
 Each line carries ``roofline`` for the workload's dominant kernel (algorithmic
 bytes or flops per launch / its average duration from HIP events recorded
@@ -535,6 +538,147 @@ def run_launch_floor(args):
     line["roofline"] = None
     line["cpu_baseline"] = None
     return line
+
+
+# ---------------------------------------------------------------------------
+# B sessions per round (the 27B-shaped head): one weight pass for every session
+# ---------------------------------------------------------------------------
+def run_batch_rounds(args):
+    """Greedy rounds of --batch independent sessions of the 27B-shaped head,
+    each at a 4096-slot prefix, launched as batched calls: mtp_draft_chain_batch
+    (the pending pairs of every session flushed, then the chained step, each
+    weight streamed once for all sessions' rows), spec_verify_batch,
+    kv_rollback_batch (policy A); one host sync per round (the sessions' state
+    words and counts), overlapped with the next round."""
+    import numpy as np
+    import torch
+
+    from mtp_draft_head_step_amd import abi
+    from mtp_draft_head_step_amd import inputs as I
+
+    B, N, ctx = int(args.batch), 2, 4096
+    if not 1 <= B <= 16:
+        raise SystemExit("--batch takes 1..16 sessions")
+    shape, wl = I.QWEN35_27B, I.WL_QWEN
+    V, H = shape.vocab, shape.hidden
+    t0 = time.time()
+    storage = I.head_weights(shape, wl)
+    head = abi.Head(shape, storage)
+    cap = ctx + 1 + (args.warmup + args.repeats * args.steps + POOL + 4) * (N + 1) + 64
+    kps, vps = zip(*[I.prefix_kv(shape, wl + 100 * b, ctx, cap) for b in range(B)])
+    kv = abi.BatchKV(shape, B, cap, np.stack(kps), np.stack(vps), [ctx] * B)
+    del kps, vps
+    pool_logits = np.stack([np.stack([I.logits_rows(wl, 5, (r, b), N + 1, V, 3.0)[0] for b in range(B)])
+                            for r in range(POOL)])
+    pool_hid = np.stack([np.stack([I.target_hiddens(shape, wl, (r, b), N + 1) for b in range(B)])
+                         for r in range(POOL)])
+    t_logits, t_hid = abi.to_device(pool_logits), abi.to_device(pool_hid)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    rings = [I.history_ring(wl, b, 64, V) for b in range(B)]
+    ring = abi.to_device(np.stack([r for r, _ in rings]))
+    ring_st = abi.to_device(np.stack([st for _, st in rings]))
+    # pending pairs live in fixed places: tokens = out_t (the previous verify's
+    # committed tokens), count = out_c[:, 1], hiddens = the previous round's
+    # target hiddens; round 0 starts from one pending pair per session
+    out_t = abi.to_device(np.stack([I.tokens_uniform(wl, (0, b), N + 1, V) for b in range(B)]).astype(np.int32))
+    out_c = torch.zeros((B, 2), **i32)
+    out_c[:, 1] = 1
+    t_hid[POOL - 1].copy_(abi.to_device(np.stack([I.target_hiddens(shape, wl, (1000, b), N + 1)
+                                                  for b in range(B)])))
+    d_buf = torch.zeros((B, N), **i32)
+    g_buf = torch.zeros((B, N, H), dtype=torch.bfloat16, device="cuda")
+    ws = abi.Workspace(abi.mtp_batch_workspace_bytes(head.cfg, B, N + 1, cap))
+    vws = abi.Workspace(B * abi.spec_verify_workspace_bytes(N, V))
+    sp = abi.sampling(window=64)
+    host_st = torch.zeros((POOL, B, 4), dtype=torch.int32).pin_memory()
+    host_c = torch.zeros((POOL, B, 2), dtype=torch.int32).pin_memory()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"{B} sessions resident ({time.time() - t0:.1f}s); capacity {cap}")
+    totals = {"committed": 0, "rounds": 0}
+    last = {}
+
+    def enqueue_round(r, st):
+        prev = (r - 1) % POOL
+        abi.mtp_draft_chain_batch(head, kv, B, out_t, t_hid[prev], N + 1, out_c[:, 1:], 2, N, d_buf, g_buf, None,
+                                  ws, st)
+        abi.spec_verify_batch(sp, B, N, V, t_logits[r % POOL], None, d_buf, ring, ring_st, None, out_t, out_c,
+                              vws, st)
+        abi.kv_rollback_batch(kv, B, abi.TO_ROUND_BASE, None, N, st)
+        host_st[r % POOL].copy_(kv.state, non_blocking=True)
+        host_c[r % POOL].copy_(out_c, non_blocking=True)
+
+    def consume(r):
+        sw, cw = host_st[r % POOL], host_c[r % POOL]
+        if int(sw[:, 3].abs().sum()) != 0:
+            raise RuntimeError(f"device error words {sw[:, 3].tolist()} in round {r}")
+        lens, comm = sw[:, 0].tolist(), cw[:, 1].tolist()
+        if last and [a + c for a, c in zip(last["len"], last["comm"])] != lens:
+            raise RuntimeError(f"round {r}: KV lengths {lens} do not follow the previous round")
+        last.update(len=lens, comm=comm)
+        totals["committed"] += sum(comm)
+        totals["rounds"] += 1
+
+    for r in range(args.warmup):
+        enqueue_round(r, stream)
+        stream.synchronize()
+        consume(r)
+    els = []
+    r0 = args.warmup
+    abi.mtp_timing_begin(abi.TIME_UNEMBED, args.repeats * args.steps * N + 4)
+    for _ in range(args.repeats):
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        done = [torch.cuda.Event(), torch.cuda.Event()]
+        prev = None
+        for r in range(r0, r0 + args.steps):
+            abi.mtp_timing_pause(not (r % TIME_EVERY == 0 or r == r0))
+            enqueue_round(r, stream)
+            abi.mtp_timing_pause(True)
+            done[r % 2].record(stream)
+            if prev is not None:
+                done[prev % 2].synchronize()
+                consume(prev)
+            prev = r
+        done[prev % 2].synchronize()
+        consume(prev)
+        torch.cuda.synchronize()
+        els.append(time.perf_counter() - t_start)
+        r0 += args.steps
+    lm_ms, lm_n = abi.mtp_timing_end()
+    elapsed = sorted(els)[len(els) // 2]
+    rounds_s = args.steps / elapsed
+    ub = unembed_bytes(shape)
+    lm_avg_s = lm_ms / lm_n / 1e3 if lm_n else None
+    cpu = None
+    if args.cpu_seconds > 0:
+        # the oracle runs sessions one after another: session 0's rounds give its rate
+        kp0, vp0 = I.prefix_kv(shape, wl, ctx, cap)
+        cpu = cpu_rounds(shape, storage, kp0, vp0, cap, ctx, N, pool_logits[:, 0], pool_hid[:, 0],
+                         I.tokens_uniform(wl, (0, 0), N + 1, V), I.target_hiddens(shape, wl, (1000, 0), N + 1),
+                         rings[0][0], rings[0][1], args.cpu_seconds, args.steps + args.warmup, single=False)
+        cpu["sample"] = ("session 0 of the batch: " + cpu["sample"] +
+                         "; the oracle runs the sessions one after another, so its rate does not depend on B")
+    out = base_line(args, round(B * N * rounds_s, 2), "draft tokens/s", elapsed / args.steps * 1e3, "bf16",
+                    "synthetic (seeded N(0,0.02) weights of the Qwen3.5-27B MTP head shape; per session a "
+                    "4096-slot N(0,1) prefix, N(0,3) target logits, N(0,1) target hiddens)",
+                    {"workload": "qwen35_27b_mtp_head_round_batch", "sessions": B, "hidden": H,
+                     "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv", "head_dim": shape.head_dim,
+                     "intermediate": shape.intermediate, "vocab": V, "draft_kv_context": ctx,
+                     "drafts_per_round": N, "temperature": 0.0, "policy": "A", "lm_head": shape.lm_head_dtype})
+    out.update({
+        "rounds_per_s": round(rounds_s, 2),
+        "draft_tokens_per_s_per_session": round(N * rounds_s, 2),
+        "repeats": {"draft_tokens_per_s": spread([B * N * args.steps / e for e in els], 2),
+                    "ms_per_round": spread([e / args.steps * 1e3 for e in els], 4)},
+        "committed_per_round": round(totals["committed"] / max(1, totals["rounds"]), 4),
+        "launch": "eager, batched calls, host sync per round overlapped with the next round",
+        "roofline": roofline("hbm", ub / lm_avg_s / 1e9 if lm_avg_s else None, HBM_PEAK_GBS, "GB/s", None,
+                             kernel=f"unembedding GEMV ({B} rows, lm_head {V}x{H} bf16)", bytes_per_launch=ub,
+                             avg_us=round(lm_avg_s * 1e6, 2) if lm_avg_s else None, launches=lm_n),
+        "cpu_baseline": with_host(cpu),
+    })
+    return out
 
 
 def cpu_rounds(shape, storage, kp, vp, cap, ctx, N, pool_logits, pool_hid, first_tok, first_hid, ring0,
@@ -1414,7 +1558,8 @@ def main():
     ap.add_argument("--workload", default="qwen35_27b_round",
                     choices=["qwen35_27b_round", "tiny_round", "flush256_prefix8192", "flush256_qwen35_27b",
                              "verify_sampled", "depth_ctx32768", "flush_scaling_qwen35_27b",
-                             "depth_auto_ctx32768", "launch_floor"])
+                             "depth_auto_ctx32768", "launch_floor", "batch_qwen35_27b"])
+    ap.add_argument("--batch", type=int, default=4, help="batch_qwen35_27b: sessions per batched call (1..16)")
     ap.add_argument("--depth", default="4", help="depth_ctx32768: drafts per round (comma list: one line each)")
     ap.add_argument("--lm", default="bf16", choices=["bf16", "i8g128"],
                     help="qwen35_27b_round, depth_ctx32768: lm_head storage (int8 per (row, 128-column group) "
@@ -1445,7 +1590,7 @@ def main():
         sys.exit(2)
     default_steps = {"qwen35_27b_round": 40, "tiny_round": 64, "flush256_prefix8192": 50, "flush256_qwen35_27b": 16,
                      "verify_sampled": 10000, "depth_ctx32768": 256, "flush_scaling_qwen35_27b": 16, "depth_auto_ctx32768": 600,
-                     "launch_floor": 8}
+                     "launch_floor": 8, "batch_qwen35_27b": 40}
     if args.steps is None:
         args.steps = default_steps[args.workload]
 
@@ -1476,6 +1621,8 @@ def main():
         lines = [run_depth_auto(args)]
     elif args.workload == "launch_floor":
         lines = [run_launch_floor(args)]
+    elif args.workload == "batch_qwen35_27b":
+        lines = [run_batch_rounds(args)]
     else:
         lines = [run_depth(args, int(d), args.lm) for d in str(args.depth).split(",")]
     for line in lines:
