@@ -224,6 +224,13 @@ const Sessions kOneSession{};
 
 // unembedding rows per launch (one per session; the GEMV row counts are 1, 2, 3, 4, 8, 16)
 int slots_of(const Sessions& ss) { return ss.multi() ? nr_for(ss.batch) : 1; }
+// Past four sessions the one-row-per-session GEMVs (the unembedding, and o_proj
+// and the MLP after a LAST-mode flush) run as launches of four sessions each:
+// the few-row GEMV's staged-input reads from LDS grow with its row count and
+// bound it past four rows (the 27B unembedding: 8 rows 752 us against 2 x 289
+// us for two launches of four; 16 rows 5.5 ms against 4 x 289 us).
+constexpr int kLastRowGroup = 4;
+int last_row_nr(int slots) { return slots > kLastRowGroup ? kLastRowGroup : slots; }
 
 GemvArgs base_gemv(const mtp_head* h, const mtp_kv* kv, const Sessions& ss = kOneSession) {
   GemvArgs a;
@@ -251,11 +258,15 @@ hipError_t run_gemv(GemvArgs a, int wt, int rows_total, int row_sel, hipStream_t
   // ROW_LAST: the last row of each session (one slot per session)
   a.row_sel = row_sel;
   if (row_sel == ROW_LAST) {
-    const int nr = a.batch > 1 ? nr_for(a.batch) : 1;
-    a.row_base = 0;
+    const int nr = last_row_nr(a.batch > 1 ? nr_for(a.batch) : 1);
     a.kp = kp_for(a.K, wt, nr);
     a.grid_stride = a.kp == a.K;
-    return timed_gemv(a, wt, nr, s, grid_out, kind);
+    for (int b = 0; b < (a.batch > 1 ? a.batch : 1); b += nr) {   // sessions b .. b + nr - 1
+      a.row_base = b;
+      hipError_t e = timed_gemv(a, wt, nr, s, b == 0 ? grid_out : nullptr, kind);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   const int nr = nr_for(rows_total);
   a.kp = kp_for(a.K, wt, nr);
@@ -319,7 +330,7 @@ GemvArgs unembed_args(const mtp_head* h, const mtp_kv* kv, const Layout& L, int 
   a.amax_part = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax));
   a.row_sel = ROW_LAST;
   a.row_base = 0;
-  a.kp = kp_for(a.K, h->lmt, slots_of(ss));
+  a.kp = kp_for(a.K, h->lmt, last_row_nr(slots_of(ss)));   // rows per launch (launches of four past four)
   a.grid_stride = a.kp == a.K;
   return a;
 }
@@ -358,7 +369,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     GemvArgs u = unembed_args(h, kv, L, n_max, n_dev, nullptr, nullptr, ws, ss);
     u.dry_run = 1;
     int grid = 0;
-    MTP_TRY(launch_gemv(u, h->lmt, slots, s, &grid));
+    MTP_TRY(launch_gemv(u, h->lmt, last_row_nr(slots), s, &grid));
     if (grid < 1 || static_cast<size_t>(grid) > amax_parts(c)) return MTP_E_UNSUPPORTED;
   }
   const int H = c.hidden, D = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, I = c.intermediate;
@@ -566,7 +577,16 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   a = unembed_args(h, kv, L, n_max, n_dev, g, logits, ws, ss);
   int tslot = -1, grid = 0;
   time_mark(TIME_UNEMBED, true, s, &tslot);
-  MTP_TRY(launch_gemv(a, h->lmt, slots, s, &grid));
+  const int unr = last_row_nr(slots);
+  MTP_TRY(launch_gemv(a, h->lmt, unr, s, &grid));
+  for (int g0 = unr; g0 < (ss.multi() ? ss.batch : 1); g0 += unr) {
+    // sessions g0 .. g0 + unr - 1; their keys continue the [session][grid] layout
+    // (every launch of the same row count has the same grid)
+    GemvArgs u = a;
+    u.row_base = a.row_base + g0;
+    u.amax_part = a.amax_part + static_cast<size_t>(g0) * grid;
+    MTP_TRY(launch_gemv(u, h->lmt, unr, s, nullptr));
+  }
   time_mark(TIME_UNEMBED, false, s, &tslot);
   // 9. argmax of the partial keys, commit the append (len, round base)
   f.parts = a.amax_part; f.nparts = grid; f.amax_out = argmax;

@@ -161,6 +161,8 @@ CASES = {
     "tiny_f32_b4_B": (I.TINY_F32, [128, 40, 300, 7], 2, "B"),
     "tiny_bf16_b3_A": (I.TINY_BF16, [64, 65, 500], 3, "A"),
     "tiny_bf16_b6_A": (I.TINY_BF16, [10, 20, 30, 40, 50, 60], 3, "A"),
+    # nine sessions: the unembedding in launches of four, four and one
+    "tiny_f32_b9_A": (I.TINY_F32, [128, 40, 300, 7, 90, 11, 64, 200, 33], 2, "A"),
     "h2048_b2_B": (H2048, [333, 77], 2, "B"),
 }
 
