@@ -490,6 +490,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   t.q = qr; t.kc = kv->k; t.vc = kv->v; t.kv_bf16 = c.kv_dtype == MTP_BF16; t.capacity = kv->capacity;
   t.state = kv->state; t.hq = hq; t.hkv = hkv; t.d = D; t.n_max = n_max; t.n_dev = n_dev; t.n_min = n_min;
   t.row_sel = rsel; t.nchunk = L.nchunk;
+  // several sessions' last rows: about the same ~256 workgroups in all (a
+  // decode-attention workgroup fills its CU's wave slots, so more would queue)
+  if (ss.multi() && rsel == ROW_LAST) t.nchunk = (L.nchunk + ss.batch - 1) / ss.batch;
   t.batch = ss.batch; t.kv_sb = ss.kv_sb; t.ndev_sb = ss.ndev_sb;
   if (fuse_rope) {
     t.fuse_rope = 1; t.qkv = qkv; t.ld_qkv = qkv_rows; t.q_norm = h->w.q_norm; t.k_norm = h->w.k_norm;
