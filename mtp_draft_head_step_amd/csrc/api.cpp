@@ -99,8 +99,10 @@ int nr_for(int rows) {
 }
 
 int kp_for(int K, int t, int nr) {
-  // 128 KB of staged inputs in LDS: fp32, or bf16 for few-row flushes with bf16 weights
-  const int budget = (nr > 1 && t == W_BF16 ? 65536 : 32768) / nr;
+  // staged inputs in LDS: 128 KB of fp32, or 144 KB of bf16 for few-row passes
+  // with bf16 weights (four rows of 17408, the 27B-shaped down projection's
+  // input, in one phase)
+  const int budget = (nr > 1 && t == W_BF16 ? 73728 : 32768) / nr;
   if (K <= budget) return K;
   const int q = lpr_for(K, t) * epc_of(t);
   int kp = budget / q * q;
