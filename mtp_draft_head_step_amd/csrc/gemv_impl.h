@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       // stages once, a multi-phase loop restages per phase
       if (blk == static_cast<int>(blockIdx.x) || nphase > 1) {
         __syncthreads();
-        if constexpr (NR == 1) {
+        if constexpr (NR <= 4) {
           // the first chunks of this wave's rows go to LDS while the input is staged
           if (a.pf > 0 && blk == static_cast<int>(blockIdx.x) && nphase == 1) {
             const int cpl0 = (K / EPC) / lpr;
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvArgs a) {
       // few-row passes keep twice the loads in flight (their staged rows cap
       // the workgroups per CU)
       constexpr int kU = NR > 1 ? 2 * kUnroll : kUnroll;
-      if constexpr (NR == 1) {
+      if constexpr (NR <= 4) {
         if (a.pf > 0 && blk == static_cast<int>(blockIdx.x) && nphase == 1) {
           // the prefetched chunks; the next batch's loads go out first
           const char* pfw = reinterpret_cast<const char*>(xs_f) + a.pf_off + wave * (RPW * a.pf * 1024);
@@ -794,9 +794,13 @@ hipError_t launch_t(const GemvArgs& a0, hipStream_t s, int* grid_out, int max_pe
     const int cap = cus * occ;
     const int per = (nblocks + cap - 1) / cap;          // row blocks per workgroup
     grid = (nblocks + per - 1) / per;
-    if (NR == 1 && a.kp >= a.K) {
+    // few-row passes (2-4 rows) over small matrices skip it: those stay
+    // cache-resident between launches, so the prefetch only adds an LDS pass
+    constexpr size_t kWBytes = WT == W_F32 ? 4 : (WT == W_BF16 ? 2 : 1);
+    const bool big = static_cast<size_t>(a.M) * a.K * kWBytes >= (static_cast<size_t>(4) << 20);
+    if ((NR == 1 || (NR <= 4 && big)) && a.kp >= a.K) {
       // the first-chunk prefetch: as many chunks per lane (up to one streamed
-      // batch) as fit beside the staged row without lowering the occupancy
+      // batch) as fit beside the staged row(s) without lowering the occupancy
       const int cpl = (a.K / WTraits<WT>::EPC) / a.lpr;
       const int per_wave = WSK ? cpl / kWaves : cpl;
       const size_t off = (lds + 15) & ~static_cast<size_t>(15);

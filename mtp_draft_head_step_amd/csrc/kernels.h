@@ -82,7 +82,8 @@ struct GemvArgs {
   int fin_nmax;
   int fin_set_base;
   int32_t* fin_state;
-  // One activation row, single phase (set by the launcher): each wave's first
+  // Up to four activation rows, single phase (set by the launcher; more than
+  // one row only over large matrices): each wave's first
   // pf chunks per lane of every row slot of its first row block are loaded
   // straight into LDS at byte offset pf_off of the dynamic LDS before the input
   // staging (their memory latency overlaps it; no registers are held).
