@@ -119,7 +119,7 @@ int nchunk_for(const mtp_head_config& c, int capacity) {
 }
 
 struct Layout {
-  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, xa, gpart, total;
+  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, xa, gpart, uxa, ulog, total;
   int nchunk;
 };
 
@@ -136,6 +136,15 @@ constexpr int kLargeHidden = 2048;
 
 int gemv_max_rows(const mtp_head_config& c) {
   return c.hidden >= kLargeHidden ? kGemvMaxRowsLarge : kGemvMaxRows;
+}
+
+// More than four sessions: their unembedding runs as one matrix-core product
+// over the sessions' normalised last rows (the lm_head streamed once for every
+// session) instead of GEMV launches of four sessions each.  bf16 lm_head.
+constexpr int kUnembedProductSlots = 5;
+bool unembed_product(const mtp_head_config& c, int slots) {
+  const int mv[1] = {c.vocab};
+  return slots >= kUnembedProductSlots && c.lm_head_dtype == MTP_BF16 && gemm_supported(c.vocab, c.hidden, mv, 1);
 }
 
 // upper bound on the unembedding GEMV's workgroup count (one argmax key each)
@@ -173,7 +182,14 @@ Layout layout(const mtp_head_config& c, int rows, int capacity, int slots = 1) {
                      gemm_part_floats(rows, I, H, mi, 2, true),
                      gemm_part_floats(rows, H, I, mh, 1, false)});
   }
+  const bool up = unembed_product(c, slots);
+  if (up) {
+    const int mv[1] = {c.vocab};
+    part = std::max(part, gemm_part_floats(slots, c.vocab, static_cast<int>(H), mv, 1, false));
+  }
   L.gpart = part ? take(part * 4) : off;
+  L.uxa = up ? take(static_cast<size_t>(slots) * H * 2) : off;             // normalised last rows, bf16
+  L.ulog = up ? take(static_cast<size_t>(slots) * c.vocab * 4) : off;      // their logits
   L.total = off;
   return L;
 }
@@ -579,6 +595,40 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   }
 
   // 8. logits = W_lm RMSNorm(g; w_norm) of the last row, with its argmax
+  if (ss.multi() && unembed_product(c, slots)) {
+    // the sessions' last rows normalised, one product over them, the chunk keys
+    LastRowsArgs lr;
+    std::memset(&lr, 0, sizeof(lr));
+    lr.x = g; lr.K = H; lr.n_max = n_max; lr.n_dev = n_dev; lr.ndev_sb = ss.ndev_sb; lr.state = kv->state;
+    lr.batch = ss.batch; lr.nw = h->w.norm; lr.nw_bf16 = h->wt == W_BF16; lr.eps = c.rms_eps;
+    lr.out = reinterpret_cast<uint16_t*>(wsp(ws, L.uxa)); lr.rows = slots;
+    MTP_TRY(launch_last_rows_norm(lr, s));
+    GemmArgs mu;
+    std::memset(&mu, 0, sizeof(mu));
+    mu.w[0] = static_cast<const uint16_t*>(h->w.lm_head); mu.m[0] = c.vocab; mu.M = c.vocab; mu.K = H;
+    mu.n_max = slots; mu.part = gpart;
+    mu.a = lr.out; mu.lda = H; mu.out_mode = OUT_F32;
+    mu.y = reinterpret_cast<float*>(wsp(ws, L.ulog)); mu.ldy = c.vocab;
+    int tslot = -1;
+    time_mark(TIME_UNEMBED, true, s, &tslot);
+    const hipError_t eu = launch_gemm(mu, s);
+    time_mark(TIME_UNEMBED, false, s, &tslot);
+    MTP_TRY(eu);
+    ArgmaxRowsArgs am;
+    std::memset(&am, 0, sizeof(am));
+    am.logits = mu.y; am.V = c.vocab; am.ld = c.vocab; am.n_dev = n_dev; am.ndev_sb = ss.ndev_sb;
+    am.n_max = n_max; am.state = kv->state; am.batch = ss.batch;
+    am.parts = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax)); am.nparts = argmax_rows_parts(c.vocab);
+    am.logits_out = logits; am.out_sb = ss.out_sb;
+    MTP_TRY(launch_argmax_rows(am, s));
+    f.parts = am.parts; f.nparts = am.nparts; f.amax_out = argmax;
+    if (defer_out) {
+      *defer_out = f;
+      return MTP_OK;
+    }
+    MTP_TRY(launch_finish(f, s));
+    return MTP_OK;
+  }
   a = unembed_args(h, kv, L, n_max, n_dev, g, logits, ws, ss);
   int tslot = -1, grid = 0;
   time_mark(TIME_UNEMBED, true, s, &tslot);

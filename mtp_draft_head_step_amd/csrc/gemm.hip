@@ -185,6 +185,82 @@ __global__ __launch_bounds__(kPrepThreads) void k_rows_prep(PrepArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The unembedding of several sessions' last rows as one matrix-core product:
+// k_last_rows_norm writes row b = bf16(x * w * inv) of session b's last row
+// (zeros for a session with no row or a set error word), the product writes
+// the logits rows, and k_argmax_rows turns each 4096-logit chunk of a row into
+// one argmax key (the finishing kernel merges them as it merges the GEMV's).
+__device__ __forceinline__ int last_row_of(const int32_t* state, const int32_t* n_dev, int ndev_sb, int n_max,
+                                           int batch, int b) {
+  if (b >= batch || state[4 * b + 3] != 0) return -1;
+  const int n = n_dev ? min(max(n_dev[b * ndev_sb], 0), n_max) : n_max;
+  return n > 0 ? n - 1 : -1;
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_last_rows_norm(LastRowsArgs a) {
+  __shared__ float red[kPrepThreads / kWave];
+  const int b = blockIdx.x;
+  const int j = last_row_of(a.state, a.n_dev, a.ndev_sb, a.n_max, a.batch, b);
+  uint16_t* out = a.out + static_cast<size_t>(b) * a.K;
+  if (j < 0) {
+    for (int k = threadIdx.x; k < a.K; k += kPrepThreads) out[k] = 0;
+    return;
+  }
+  const float* x = a.x + (static_cast<size_t>(b) * a.n_max + j) * a.K;
+  float se = 0.f;
+  for (int k = threadIdx.x; k < a.K; k += kPrepThreads) se += x[k] * x[k];
+  const float inv = 1.0f / sqrtf(block_sum(se, red) / static_cast<float>(a.K) + a.eps);
+  for (int k = threadIdx.x; k < a.K; k += kPrepThreads) {
+    const float w = a.nw_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.nw)[k]) : static_cast<const float*>(a.nw)[k];
+    out[k] = f32_to_bf16(x[k] * w * inv);
+  }
+}
+
+hipError_t launch_last_rows_norm(const LastRowsArgs& a, hipStream_t s) {
+  if (a.rows < 1 || a.K < 1) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_last_rows_norm, dim3(a.rows), dim3(kPrepThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+constexpr int kArgmaxChunk = 4096;
+
+__global__ __launch_bounds__(256) void k_argmax_rows(ArgmaxRowsArgs a) {
+  __shared__ unsigned long long s_best[4];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int lo = c * kArgmaxChunk, hi = min(a.V, lo + kArgmaxChunk);
+  const bool valid = last_row_of(a.state, a.n_dev, a.ndev_sb, a.n_max, a.batch, b) >= 0;
+  const float* row = a.logits + static_cast<size_t>(b) * a.ld;
+  float* out = (valid && a.logits_out) ? a.logits_out + static_cast<size_t>(b) * a.out_sb * a.V : nullptr;
+  unsigned long long best = 0ull;
+  if (valid) {
+    for (int i = lo + threadIdx.x; i < hi; i += 256) {
+      const float v = row[i];
+      const unsigned long long key = argmax_key(v, static_cast<uint32_t>(i));
+      best = key > best ? key : best;
+      if (out) out[i] = v;
+    }
+  }
+  best = wave_max_u64(best);
+  if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long m = s_best[0];
+    for (int w = 1; w < 4; ++w) m = s_best[w] > m ? s_best[w] : m;
+    a.parts[static_cast<size_t>(b) * a.nparts + c] = m;
+  }
+}
+
+int argmax_rows_parts(int V) { return (V + kArgmaxChunk - 1) / kArgmaxChunk; }
+
+hipError_t launch_argmax_rows(const ArgmaxRowsArgs& a, hipStream_t s) {
+  if (a.batch < 1 || a.nparts != argmax_rows_parts(a.V)) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_argmax_rows, dim3(a.nparts, a.batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_rows_prep(const PrepArgs& a, hipStream_t s) {
   if (a.n_max <= 0) return hipSuccess;
   const int rows = a.batch > 1 ? a.batch * a.n_max : a.n_max;

@@ -129,6 +129,46 @@ struct PrepArgs {
 };
 hipError_t launch_rows_prep(const PrepArgs& a, hipStream_t s);
 
+// Several sessions' last rows normalised into bf16 rows (the batched
+// unembedding's product input): out row b = bf16(x * nw * inv_rms) of session
+// b's last row x (flattened rows b * n_max + j), zeros past the batch, for a
+// session with no row or with its error word set.  One workgroup per row.
+struct LastRowsArgs {
+  const float* x;            // [batch * n_max, K]
+  int K;
+  int n_max;
+  const int32_t* n_dev;      // session b's count n_dev[b * ndev_sb] (null: n_max)
+  int ndev_sb;
+  const int32_t* state;      // session b's state words state + 4 b
+  int batch;
+  const void* nw;
+  int nw_bf16;
+  float eps;
+  uint16_t* out;             // [rows, K] bf16
+  int rows;                  // >= batch
+};
+hipError_t launch_last_rows_norm(const LastRowsArgs& a, hipStream_t s);
+
+// The argmax key of every 4096-logit chunk of each session's logits row
+// (parts[b * nparts + c]; 0 for a session without a row), the row copied to
+// logits_out + b * out_sb * V when that is set and the session has a row.
+struct ArgmaxRowsArgs {
+  const float* logits;       // [batch, ld]
+  int V;
+  int ld;
+  const int32_t* n_dev;
+  int ndev_sb;
+  int n_max;
+  const int32_t* state;
+  int batch;
+  unsigned long long* parts;
+  int nparts;                // argmax_rows_parts(V)
+  float* logits_out;         // nullable
+  int out_sb;
+};
+int argmax_rows_parts(int V);
+hipError_t launch_argmax_rows(const ArgmaxRowsArgs& a, hipStream_t s);
+
 // Y[j, c] = sum_k A[j, k] W[c, k] over activation rows j < n on bf16 MFMA tiles
 // (64 rows x 64 columns per workgroup).  W: up to three stacked bf16 matrices
 // (OUT_SWIGLU: w[0] gate and w[1] up, M rows each).  A: bf16 rows, or fp32 rows

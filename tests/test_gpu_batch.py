@@ -164,6 +164,8 @@ CASES = {
     # nine sessions: the unembedding in launches of four, four and one
     "tiny_f32_b9_A": (I.TINY_F32, [128, 40, 300, 7, 90, 11, 64, 200, 33], 2, "A"),
     "h2048_b2_B": (H2048, [333, 77], 2, "B"),
+    # six sessions of a large-vocabulary head: the unembedding as one product
+    "h2048_b6_A": (H2048, [333, 77, 120, 9, 250, 64], 2, "A"),
 }
 
 
