@@ -138,10 +138,12 @@ int gemv_max_rows(const mtp_head_config& c) {
   return c.hidden >= kLargeHidden ? kGemvMaxRowsLarge : kGemvMaxRows;
 }
 
-// More than four sessions: their unembedding runs as one matrix-core product
+// Three sessions and more: their unembedding runs as one matrix-core product
 // over the sessions' normalised last rows (the lm_head streamed once for every
-// session) instead of GEMV launches of four sessions each.  bf16 lm_head.
-constexpr int kUnembedProductSlots = 5;
+// session) instead of few-row GEMV launches (27B shape, rounds of B sessions:
+// B=2 4397 vs 4311 draft tokens/s for the GEMV, B=3 5957 vs 6057, B=4 7460 vs
+// 7867).  bf16 lm_head.
+constexpr int kUnembedProductSlots = 3;
 bool unembed_product(const mtp_head_config& c, int slots) {
   const int mv[1] = {c.vocab};
   return slots >= kUnembedProductSlots && c.lm_head_dtype == MTP_BF16 && gemm_supported(c.vocab, c.hidden, mv, 1);
