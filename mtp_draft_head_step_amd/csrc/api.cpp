@@ -119,7 +119,7 @@ int nchunk_for(const mtp_head_config& c, int capacity) {
 }
 
 struct Layout {
-  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, xa, gpart, uxa, ulog, total;
+  size_t x, qkv, qr, part_o, part_ml, o, x1, m, g, amax, xa, gpart, uxa, ulog, lo, lx, lb, total;
   int nchunk;
 };
 
@@ -147,6 +147,17 @@ constexpr int kUnembedProductSlots = 3;
 bool unembed_product(const mtp_head_config& c, int slots) {
   const int mv[1] = {c.vocab};
   return slots >= kUnembedProductSlots && c.lm_head_dtype == MTP_BF16 && gemm_supported(c.vocab, c.hidden, mv, 1);
+}
+
+// With the unembedding as a product (bf16 weights too), o_proj and the MLP run
+// as products over the sessions' gathered last rows as well: each weight
+// streamed once for every session rather than once per launch of four.
+bool last_rows_product(const mtp_head_config& c, int slots) {
+  if (!unembed_product(c, slots) || c.weight_dtype != MTP_BF16) return false;
+  const int H = c.hidden, I = c.intermediate;
+  const int mh[1] = {H}, mi[1] = {I};
+  return gemm_supported(H, c.n_q_heads * c.head_dim, mh, 1) && gemm_supported(I, H, mi, 1) &&
+         gemm_supported(H, I, mh, 1);
 }
 
 // upper bound on the unembedding GEMV's workgroup count (one argmax key each)
@@ -189,9 +200,19 @@ Layout layout(const mtp_head_config& c, int rows, int capacity, int slots = 1) {
     const int mv[1] = {c.vocab};
     part = std::max(part, gemm_part_floats(slots, c.vocab, static_cast<int>(H), mv, 1, false));
   }
+  const bool lp = last_rows_product(c, slots);
+  if (lp) {
+    const int mh[1] = {static_cast<int>(H)};
+    const int mi[2] = {static_cast<int>(I), static_cast<int>(I)};
+    part = std::max({part, gemm_part_floats(slots, H, hq * D, mh, 1, false),
+                     gemm_part_floats(slots, I, H, mi, 2, true), gemm_part_floats(slots, H, I, mh, 1, false)});
+  }
   L.gpart = part ? take(part * 4) : off;
   L.uxa = up ? take(static_cast<size_t>(slots) * H * 2) : off;             // normalised last rows, bf16
   L.ulog = up ? take(static_cast<size_t>(slots) * c.vocab * 4) : off;      // their logits
+  L.lo = lp ? take(static_cast<size_t>(slots) * hq * D * 2) : off;         // gathered o rows, bf16
+  L.lx = lp ? take(static_cast<size_t>(slots) * H * 4) : off;              // gathered x rows
+  L.lb = lp ? take(static_cast<size_t>(slots) * H * 2) : off;              // MLP input rows, bf16
   L.total = off;
   return L;
 }
@@ -503,6 +524,22 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
 
   const int rsel = (mode == MTP_FLUSH_ALL) ? ROWS_RANGE : ROW_LAST;
   const bool mfma_out = mfma && rsel == ROWS_RANGE;   // o, MLP over every row
+  // several sessions' last rows: o, the MLP and the unembedding as products
+  // over the gathered rows [batch, .] (outputs kept compact until the hidden copy)
+  const bool lprod = ss.multi() && rsel == ROW_LAST && last_rows_product(c, slots);
+  LastRowsArgs gr;
+  std::memset(&gr, 0, sizeof(gr));
+  gr.n_max = n_max; gr.n_dev = n_dev; gr.ndev_sb = ss.ndev_sb; gr.state = kv->state; gr.batch = ss.batch;
+  gr.nw_bf16 = h->wt == W_BF16; gr.eps = c.rms_eps; gr.rows = ss.batch;
+  auto last_gemm = [&](const void* a_rows, int lda) {
+    GemmArgs g;
+    std::memset(&g, 0, sizeof(g));
+    g.n_max = ss.batch; g.part = gpart; g.a = a_rows; g.lda = lda;
+    return g;
+  };
+  uint16_t* lo = reinterpret_cast<uint16_t*>(wsp(ws, L.lo));
+  float* lx = reinterpret_cast<float*>(wsp(ws, L.lx));
+  uint16_t* lb = reinterpret_cast<uint16_t*>(wsp(ws, L.lb));
 
   // 4. attention over the draft KV
   AttnArgs t;
@@ -552,6 +589,18 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     // a split-K reduce also writes the MLP input rows, RMSNorm(x1; w_post)
     const RowNorm rn{h->w.post_attention_layernorm, h->wt == W_BF16, c.rms_eps, xa, H};
     MTP_TRY(timed_gemm(m5, s, &rn, &normed_mlp));
+  } else if (lprod) {
+    LastRowsArgs go = gr;                       // o rows, bf16
+    go.x = o; go.K = hq * D; go.out = lo;
+    MTP_TRY(launch_last_rows_norm(go, s));
+    LastRowsArgs gx = gr;                       // residual rows, fp32
+    gx.x = x; gx.K = H; gx.out_f32 = lx;
+    MTP_TRY(launch_last_rows_norm(gx, s));
+    GemmArgs m5 = last_gemm(lo, hq * D);
+    m5.w[0] = static_cast<const uint16_t*>(h->w.o_proj); m5.m[0] = H; m5.M = H; m5.K = hq * D;
+    m5.out_mode = OUT_RESID; m5.res = lx; m5.ldres = H; m5.y = x1; m5.ldy = H;
+    const RowNorm rn{h->w.post_attention_layernorm, h->wt == W_BF16, c.rms_eps, lb, H};
+    MTP_TRY(timed_gemm(m5, s, &rn, &normed_mlp));
   } else {
     MTP_TRY(run_gemv(a, h->wt, rows_total, rsel, s));
   }
@@ -574,6 +623,17 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     m6.w[1] = static_cast<const uint16_t*>(h->w.up_proj); m6.m[1] = I;
     m6.M = I; m6.K = H; m6.a = xa; m6.lda = H; m6.out_mode = OUT_SWIGLU; m6.y = m; m6.ldy = I; m6.y_bf16 = 1;
     MTP_TRY(timed_gemm(m6, s));
+  } else if (lprod) {
+    if (!normed_mlp) {
+      LastRowsArgs gb = gr;
+      gb.x = x1; gb.compact_in = 1; gb.K = H; gb.nw = h->w.post_attention_layernorm; gb.out = lb;
+      MTP_TRY(launch_last_rows_norm(gb, s));
+    }
+    GemmArgs m6 = last_gemm(lb, H);
+    m6.w[0] = static_cast<const uint16_t*>(h->w.gate_proj); m6.m[0] = I;
+    m6.w[1] = static_cast<const uint16_t*>(h->w.up_proj); m6.m[1] = I;
+    m6.M = I; m6.K = H; m6.out_mode = OUT_SWIGLU; m6.y = m; m6.ldy = I; m6.y_bf16 = 1;
+    MTP_TRY(timed_gemm(m6, s));
   } else {
     MTP_TRY(run_gemv(a, h->wt, rows_total, rsel, s));
   }
@@ -592,6 +652,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     m7.out_mode = OUT_RESID; m7.res = x1; m7.ldres = H; m7.y = g; m7.ldy = H;
     m7.y2 = hidden_out; m7.y2_bf16 = c.act_dtype == MTP_BF16; m7.ldy2 = H;
     MTP_TRY(timed_gemm(m7, s));
+  } else if (lprod) {   // g rows compact; the hidden copy is written with the unembedding's input
+    GemmArgs m7 = last_gemm(m, I);
+    m7.w[0] = static_cast<const uint16_t*>(h->w.down_proj); m7.m[0] = H; m7.M = H; m7.K = I;
+    m7.out_mode = OUT_RESID; m7.res = x1; m7.ldres = H; m7.y = g; m7.ldy = H;
+    MTP_TRY(timed_gemm(m7, s));
   } else {
     MTP_TRY(run_gemv(a, h->wt, rows_total, rsel, s));
   }
@@ -604,6 +669,11 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     lr.x = g; lr.K = H; lr.n_max = n_max; lr.n_dev = n_dev; lr.ndev_sb = ss.ndev_sb; lr.state = kv->state;
     lr.batch = ss.batch; lr.nw = h->w.norm; lr.nw_bf16 = h->wt == W_BF16; lr.eps = c.rms_eps;
     lr.out = reinterpret_cast<uint16_t*>(wsp(ws, L.uxa)); lr.rows = slots;
+    if (lprod) {   // g gathered already; each valid session's row also goes to hidden_out
+      lr.compact_in = 1;
+      lr.copy = hidden_out; lr.copy_bf16 = c.act_dtype == MTP_BF16;
+      lr.copy_ld = static_cast<long long>(ss.out_sb) * H;
+    }
     MTP_TRY(launch_last_rows_norm(lr, s));
     GemmArgs mu;
     std::memset(&mu, 0, sizeof(mu));

@@ -134,18 +134,23 @@ hipError_t launch_rows_prep(const PrepArgs& a, hipStream_t s);
 // b's last row x (flattened rows b * n_max + j), zeros past the batch, for a
 // session with no row or with its error word set.  One workgroup per row.
 struct LastRowsArgs {
-  const float* x;            // [batch * n_max, K]
+  const float* x;            // [batch * n_max, K], or [batch, K] when compact_in
   int K;
   int n_max;
   const int32_t* n_dev;      // session b's count n_dev[b * ndev_sb] (null: n_max)
   int ndev_sb;
   const int32_t* state;      // session b's state words state + 4 b
   int batch;
-  const void* nw;
+  const void* nw;            // null: no normalisation (the row itself in bf16)
   int nw_bf16;
   float eps;
-  uint16_t* out;             // [rows, K] bf16
+  uint16_t* out;             // [rows, K] bf16 (nullable)
   int rows;                  // >= batch
+  int compact_in;            // session b's row is x + b K (already gathered)
+  float* out_f32;            // nullable: [rows, K] the row itself, fp32
+  void* copy;                // nullable: the row itself of each valid session at copy + b copy_ld
+  int copy_bf16;
+  long long copy_ld;
 };
 hipError_t launch_last_rows_norm(const LastRowsArgs& a, hipStream_t s);
 
