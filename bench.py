@@ -648,8 +648,14 @@ def run_batch_rounds(args):
     lm_ms, lm_n = abi.mtp_timing_end()
     elapsed = sorted(els)[len(els) // 2]
     rounds_s = args.steps / elapsed
-    groups = (B + 3) // 4                       # the unembedding runs in launches of four sessions
+    # three sessions and more with a bf16 lm_head: one matrix-core product over
+    # the sessions' last rows (the lm_head read once); else GEMV launches of four
+    product = B >= 3 and shape.lm_head_dtype == I.BF16
+    groups = 1 if product else (B + 3) // 4
     ub = unembed_bytes(shape) * groups
+    ukind = (f"unembedding product over the {B} sessions' last rows (one matrix-core launch, lm_head {V}x{H} "
+             f"bf16)" if product else
+             f"unembedding GEMV ({B} rows in {groups} launch(es) of up to four, lm_head {V}x{H} bf16)")
     lm_avg_s = lm_ms / lm_n / 1e3 if lm_n else None
     cpu = None
     if args.cpu_seconds > 0:
@@ -675,8 +681,7 @@ def run_batch_rounds(args):
         "committed_per_round": round(totals["committed"] / max(1, totals["rounds"]), 4),
         "launch": "eager, batched calls, host sync per round overlapped with the next round",
         "roofline": roofline("hbm", ub / lm_avg_s / 1e9 if lm_avg_s else None, HBM_PEAK_GBS, "GB/s", None,
-                             kernel=f"unembedding GEMV ({B} rows in {groups} launch(es) of up to four, "
-                                    f"lm_head {V}x{H} bf16)", bytes_per_launch=ub,
+                             kernel=ukind, bytes_per_launch=ub,
                              avg_us=round(lm_avg_s * 1e6, 2) if lm_avg_s else None, launches=lm_n),
         "cpu_baseline": with_host(cpu),
     })

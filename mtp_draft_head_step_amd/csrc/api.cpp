@@ -573,6 +573,10 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   t.part_ml = reinterpret_cast<float*>(wsp(ws, L.part_ml));
   t.o = o;
   t.o_bf16 = mfma_out;   // the many-row o product reads bf16 rows
+  if (lprod) {           // the o product's rows, gathered by the merge
+    t.o = reinterpret_cast<float*>(lo); t.o_bf16 = 1; t.o_compact = 1;
+    t.xg = x; t.xg_out = lx; t.ld_xg = H;
+  }
   MTP_TRY(launch_attention(t, s));
 
   // 5. x1 = x + W_o o
@@ -590,12 +594,6 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     const RowNorm rn{h->w.post_attention_layernorm, h->wt == W_BF16, c.rms_eps, xa, H};
     MTP_TRY(timed_gemm(m5, s, &rn, &normed_mlp));
   } else if (lprod) {
-    LastRowsArgs go = gr;                       // o rows, bf16
-    go.x = o; go.K = hq * D; go.out = lo;
-    MTP_TRY(launch_last_rows_norm(go, s));
-    LastRowsArgs gx = gr;                       // residual rows, fp32
-    gx.x = x; gx.K = H; gx.out_f32 = lx;
-    MTP_TRY(launch_last_rows_norm(gx, s));
     GemmArgs m5 = last_gemm(lo, hq * D);
     m5.w[0] = static_cast<const uint16_t*>(h->w.o_proj); m5.m[0] = H; m5.M = H; m5.K = hq * D;
     m5.out_mode = OUT_RESID; m5.res = lx; m5.ldres = H; m5.y = x1; m5.ldy = H;

@@ -497,10 +497,25 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int32_t* st = a.state + 4 * sess;
   const int err0 = st[3];
   const int nd0 = a.n_dev ? a.n_dev[multi ? sess * a.ndev_sb : 0] : a.n_max;
-  if (err0 != 0) return;
   const int n = min(max(nd0, 0), a.n_max);
   const int jl = (a.row_sel == ROW_LAST) ? n - 1 : static_cast<int>(blockIdx.y);
-  if (jl < 0 || jl >= n) return;
+  const bool valid = err0 == 0 && jl >= 0 && jl < n;
+  if (a.o_compact) {
+    // gathered rows for products over the sessions' last rows: o at row sess
+    // (bf16) and, from head 0's block, the residual row; zeros for a session
+    // without a row
+    if (blockIdx.x == 0 && a.xg_out) {
+      float* xo = a.xg_out + static_cast<size_t>(sess) * a.ld_xg;
+      const float* xs = valid ? a.xg + (static_cast<size_t>(sess) * a.n_max + jl) * a.ld_xg : nullptr;
+      for (int k = threadIdx.x; k < a.ld_xg; k += 256) xo[k] = valid ? xs[k] : 0.f;
+    }
+    if (!valid) {
+      if (static_cast<int>(threadIdx.x) < a.d)
+        reinterpret_cast<uint16_t*>(a.o)[(static_cast<size_t>(sess) * a.hq + blockIdx.x) * a.d + threadIdx.x] = 0;
+      return;
+    }
+  }
+  if (!valid) return;
   const int j = sess * a.n_max + jl;   // workspace row
   const int hq = blockIdx.x;
   const int D = a.d;
@@ -572,7 +587,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     }
   }
   const float out = ((num0 + num1) + (num2 + num3)) * inv;
-  const size_t oi = static_cast<size_t>(j) * a.hq * D + hq * D + d;
+  const size_t oi = static_cast<size_t>(a.o_compact ? sess : j) * a.hq * D + hq * D + d;
   if (a.o_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(out);
   else a.o[oi] = out;
 }

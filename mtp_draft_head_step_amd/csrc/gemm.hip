@@ -187,11 +187,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_rows_prep(PrepArgs a) {
 
 // ---------------------------------------------------------------------------
 // Several sessions' last rows as matrix-core products (o_proj, the MLP and the
-// unembedding): k_last_rows_norm gathers row b = bf16(x * w * inv) of session
-// b's last row, or the row itself when no norm weight is given (zeros for a
-// session with no row or a set error word), the products run over the gathered
-// rows, and k_argmax_rows turns each 4096-logit chunk of a logits row into one
-// argmax key (the finishing kernel merges them as it merges the GEMV's).
+// unembedding): k_last_rows_norm writes row b = bf16(x * w * inv) of session
+// b's last row (zeros for a session with no row or a set error word), the
+// products run over those rows, and k_argmax_rows turns each 4096-logit chunk
+// of a logits row into one argmax key (the finishing kernel merges them as it
+// merges the GEMV's).
 __device__ __forceinline__ int last_row_of(const int32_t* state, const int32_t* n_dev, int ndev_sb, int n_max,
                                            int batch, int b) {
   if (b >= batch || state[4 * b + 3] != 0) return -1;
@@ -203,36 +203,24 @@ __global__ __launch_bounds__(kPrepThreads) void k_last_rows_norm(LastRowsArgs a)
   __shared__ float red[kPrepThreads / kWave];
   const int b = blockIdx.x;
   const int j = last_row_of(a.state, a.n_dev, a.ndev_sb, a.n_max, a.batch, b);
-  uint16_t* out = a.out ? a.out + static_cast<size_t>(b) * a.K : nullptr;
-  float* of = a.out_f32 ? a.out_f32 + static_cast<size_t>(b) * a.K : nullptr;
+  uint16_t* out = a.out + static_cast<size_t>(b) * a.K;
   if (j < 0) {
-    for (int k = threadIdx.x; k < a.K; k += kPrepThreads) {
-      if (out) out[k] = 0;
-      if (of) of[k] = 0.f;
-    }
+    for (int k = threadIdx.x; k < a.K; k += kPrepThreads) out[k] = 0;
     return;
   }
   const float* x = a.x + (a.compact_in ? static_cast<size_t>(b) : static_cast<size_t>(b) * a.n_max + j) * a.K;
-  float inv = 1.f;
-  if (a.nw) {   // uniform over the block
-    float se = 0.f;
-    for (int k = threadIdx.x; k < a.K; k += kPrepThreads) se += x[k] * x[k];
-    inv = 1.0f / sqrtf(block_sum(se, red) / static_cast<float>(a.K) + a.eps);
-  }
+  float se = 0.f;
+  for (int k = threadIdx.x; k < a.K; k += kPrepThreads) se += x[k] * x[k];
+  const float inv = 1.0f / sqrtf(block_sum(se, red) / static_cast<float>(a.K) + a.eps);
   for (int k = threadIdx.x; k < a.K; k += kPrepThreads) {
     const float v = x[k];
-    if (of) of[k] = v;
     if (a.copy) {
       const size_t o = static_cast<size_t>(b) * a.copy_ld + k;
       if (a.copy_bf16) static_cast<uint16_t*>(a.copy)[o] = f32_to_bf16(v);
       else static_cast<float*>(a.copy)[o] = v;
     }
-    if (out) {
-      const float w = !a.nw ? 1.f
-                            : (a.nw_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.nw)[k])
-                                         : static_cast<const float*>(a.nw)[k]);
-      out[k] = f32_to_bf16(a.nw ? v * w * inv : v);
-    }
+    const float w = a.nw_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.nw)[k]) : static_cast<const float*>(a.nw)[k];
+    out[k] = f32_to_bf16(v * w * inv);
   }
 }
 

@@ -141,13 +141,12 @@ struct LastRowsArgs {
   int ndev_sb;
   const int32_t* state;      // session b's state words state + 4 b
   int batch;
-  const void* nw;            // null: no normalisation (the row itself in bf16)
+  const void* nw;
   int nw_bf16;
   float eps;
-  uint16_t* out;             // [rows, K] bf16 (nullable)
+  uint16_t* out;             // [rows, K] bf16
   int rows;                  // >= batch
   int compact_in;            // session b's row is x + b K (already gathered)
-  float* out_f32;            // nullable: [rows, K] the row itself, fp32
   void* copy;                // nullable: the row itself of each valid session at copy + b copy_ld
   int copy_bf16;
   long long copy_ld;
@@ -271,6 +270,13 @@ struct AttnArgs {
   float* part_ml;          // [rows, Hq, nchunk, 2]
   float* o;                // [rows, Hq * D] (bf16 when o_bf16)
   int o_bf16;
+  // several sessions, ROW_LAST: the merge writes session b's o row at row b
+  // (bf16, o_bf16 set) and copies its residual row xg[b * n_max + n - 1] to
+  // xg_out[b] (ld_xg floats), zeros for a session without a row
+  int o_compact;
+  const float* xg;
+  float* xg_out;
+  int ld_xg;
   // ROW_LAST with fuse_rope: the q/k RMSNorm + RoPE and the K/V append of the
   // rows j < n run inside the attention kernel (no separate append launch); the
   // q/k/v projections of the rows are read from qkv, or, with qkv_nsp > 1, are
