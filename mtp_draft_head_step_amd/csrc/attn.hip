@@ -502,12 +502,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const bool valid = err0 == 0 && jl >= 0 && jl < n;
   if (a.o_compact) {
     // gathered rows for products over the sessions' last rows: o at row sess
-    // (bf16) and, from head 0's block, the residual row; zeros for a session
-    // without a row
-    if (blockIdx.x == 0 && a.xg_out) {
+    // (bf16) and the residual row, spread over the session's head blocks;
+    // zeros for a session without a row
+    if (a.xg_out) {
       float* xo = a.xg_out + static_cast<size_t>(sess) * a.ld_xg;
       const float* xs = valid ? a.xg + (static_cast<size_t>(sess) * a.n_max + jl) * a.ld_xg : nullptr;
-      for (int k = threadIdx.x; k < a.ld_xg; k += 256) xo[k] = valid ? xs[k] : 0.f;
+      for (int k = blockIdx.x * 256 + threadIdx.x; k < a.ld_xg; k += gridDim.x * 256) xo[k] = valid ? xs[k] : 0.f;
     }
     if (!valid) {
       if (static_cast<int>(threadIdx.x) < a.d)
