@@ -474,7 +474,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
   if (!mfma) MTP_TRY(run_gemv(a, h->wt, rows_total, ROWS_RANGE, s));
 
   // LAST mode: the norm/RoPE/append runs inside the attention kernel, which
-  // also sums the q/k/v product's split-K partials (one session)
+  // also sums the q/k/v product's split-K partials
   const bool fuse_rope = mode == MTP_FLUSH_LAST;
   int qkv_split = 1;
 
@@ -490,7 +490,9 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     m2.w[1] = static_cast<const uint16_t*>(h->w.k_proj); m2.m[1] = hkv * D;
     m2.w[2] = static_cast<const uint16_t*>(h->w.v_proj); m2.m[2] = hkv * D;
     m2.M = qkv_rows; m2.K = H; m2.a = xa; m2.lda = H; m2.out_mode = OUT_F32; m2.y = qkv; m2.ldy = qkv_rows;
-    const bool defer = fuse_rope && !ss.multi() && D >= kSplitMinHeadDim;
+    // the attention's split sums take 32-bit offsets into the partials
+    const bool defer = fuse_rope && D >= kSplitMinHeadDim &&
+                       gemm_part_floats(rows_total, qkv_rows, H, m2.m, 3, false) * 4 < (size_t{1} << 31);
     MTP_TRY(timed_gemm(m2, s, nullptr, nullptr, defer ? &qkv_split : nullptr));
   }
   a = base_gemv(h, kv, ss);
@@ -556,7 +558,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     t.qkv_nsp = qkv_split;
     if (qkv_split > 1) {   // partials [split, n_max, qkv_rows]
       t.qkv = gpart;
-      t.qkv_pstride = n_max * qkv_rows;   // n_max <= 256 rows of at most 24 * 256 columns
+      t.qkv_pstride = rows_total * qkv_rows;   // every session's rows, b * n_max + j
     }
     t.nw_bf16 = h->wt == W_BF16; t.eps = c.rms_eps; t.theta = c.rope_theta;
   }
