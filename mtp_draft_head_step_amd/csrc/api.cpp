@@ -435,7 +435,7 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
       return MTP_E_UNSUPPORTED;
   }
   // 1. x = W_fc [RMSNorm(E[t]) | RMSNorm(h)]
-  bool normed_qkv = false, normed_mlp = false;
+  bool normed_qkv = false, normed_mlp = false, normed_g = false;
   const bool have_fold = fold_in && fold_in->state;
   const bool fold = have_fold && fold_in->parts && !mfma && !ss.multi() && rows_total == 1;
   if (have_fold && !fold) {
@@ -652,11 +652,12 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     m7.out_mode = OUT_RESID; m7.res = x1; m7.ldres = H; m7.y = g; m7.ldy = H;
     m7.y2 = hidden_out; m7.y2_bf16 = c.act_dtype == MTP_BF16; m7.ldy2 = H;
     MTP_TRY(timed_gemm(m7, s));
-  } else if (lprod) {   // g rows compact; the hidden copy is written with the unembedding's input
+  } else if (lprod) {   // g rows compact; a split-K reduce also writes the unembedding's input rows
     GemmArgs m7 = last_gemm(m, I);
     m7.w[0] = static_cast<const uint16_t*>(h->w.down_proj); m7.m[0] = H; m7.M = H; m7.K = I;
     m7.out_mode = OUT_RESID; m7.res = x1; m7.ldres = H; m7.y = g; m7.ldy = H;
-    MTP_TRY(timed_gemm(m7, s));
+    const RowNorm rn{h->w.norm, h->wt == W_BF16, c.rms_eps, reinterpret_cast<uint16_t*>(wsp(ws, L.uxa)), H};
+    MTP_TRY(timed_gemm(m7, s, &rn, &normed_g));
   } else {
     MTP_TRY(run_gemv(a, h->wt, rows_total, rsel, s));
   }
@@ -668,17 +669,17 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     std::memset(&lr, 0, sizeof(lr));
     lr.x = g; lr.K = H; lr.n_max = n_max; lr.n_dev = n_dev; lr.ndev_sb = ss.ndev_sb; lr.state = kv->state;
     lr.batch = ss.batch; lr.nw = h->w.norm; lr.nw_bf16 = h->wt == W_BF16; lr.eps = c.rms_eps;
-    lr.out = reinterpret_cast<uint16_t*>(wsp(ws, L.uxa)); lr.rows = slots;
+    lr.out = reinterpret_cast<uint16_t*>(wsp(ws, L.uxa)); lr.rows = ss.batch;
     if (lprod) {   // g gathered already; each valid session's row also goes to hidden_out
       lr.compact_in = 1;
       lr.copy = hidden_out; lr.copy_bf16 = c.act_dtype == MTP_BF16;
       lr.copy_ld = static_cast<long long>(ss.out_sb) * H;
     }
-    MTP_TRY(launch_last_rows_norm(lr, s));
+    if (!normed_g) MTP_TRY(launch_last_rows_norm(lr, s));
     GemmArgs mu;
     std::memset(&mu, 0, sizeof(mu));
     mu.w[0] = static_cast<const uint16_t*>(h->w.lm_head); mu.m[0] = c.vocab; mu.M = c.vocab; mu.K = H;
-    mu.n_max = slots; mu.part = gpart;
+    mu.n_max = ss.batch; mu.part = gpart;
     mu.a = lr.out; mu.lda = H; mu.out_mode = OUT_F32;
     mu.y = reinterpret_cast<float*>(wsp(ws, L.ulog)); mu.ldy = c.vocab;
     int tslot = -1;
@@ -692,6 +693,10 @@ int head_forward(const mtp_head* h, const mtp_kv* kv, const int32_t* tokens, con
     am.n_max = n_max; am.state = kv->state; am.batch = ss.batch;
     am.parts = reinterpret_cast<unsigned long long*>(wsp(ws, L.amax)); am.nparts = argmax_rows_parts(c.vocab);
     am.logits_out = logits; am.out_sb = ss.out_sb;
+    if (normed_g) {   // the hidden copy of each valid session, with the chunk keys
+      am.copy_src = g; am.K = H; am.copy = hidden_out; am.copy_bf16 = c.act_dtype == MTP_BF16;
+      am.copy_ld = static_cast<long long>(ss.out_sb) * H;
+    }
     MTP_TRY(launch_argmax_rows(am, s));
     f.parts = am.parts; f.nparts = am.nparts; f.amax_out = argmax;
     if (defer_out) {

@@ -241,6 +241,16 @@ __global__ __launch_bounds__(256) void k_argmax_rows(ArgmaxRowsArgs a) {
   const float* row = a.logits + static_cast<size_t>(b) * a.ld;
   float* out = (valid && a.logits_out) ? a.logits_out + static_cast<size_t>(b) * a.out_sb * a.V : nullptr;
   unsigned long long best = 0ull;
+  if (valid && a.copy) {
+    const int per = (a.K + gridDim.x - 1) / gridDim.x;
+    const int k1 = min(a.K, (c + 1) * per);
+    const float* src = a.copy_src + static_cast<size_t>(b) * a.K;
+    for (int k = c * per + threadIdx.x; k < k1; k += 256) {
+      const size_t o = static_cast<size_t>(b) * a.copy_ld + k;
+      if (a.copy_bf16) static_cast<uint16_t*>(a.copy)[o] = f32_to_bf16(src[k]);
+      else static_cast<float*>(a.copy)[o] = src[k];
+    }
+  }
   if (valid) {
     for (int i = lo + threadIdx.x; i < hi; i += 256) {
       const float v = row[i];

@@ -169,6 +169,13 @@ struct ArgmaxRowsArgs {
   int nparts;                // argmax_rows_parts(V)
   float* logits_out;         // nullable
   int out_sb;
+  // nullable: each valid session's row copy_src + b K also goes to copy + b
+  // copy_ld (the hidden copy), spread over the row's chunk blocks
+  const float* copy_src;
+  int K;
+  void* copy;
+  int copy_bf16;
+  long long copy_ld;
 };
 int argmax_rows_parts(int V);
 hipError_t launch_argmax_rows(const ArgmaxRowsArgs& a, hipStream_t s);
