@@ -161,6 +161,10 @@ CASES = {
     "tiny_f32_b4_B": (I.TINY_F32, [128, 40, 300, 7], 2, "B"),
     "tiny_bf16_b3_A": (I.TINY_BF16, [64, 65, 500], 3, "A"),
     "tiny_bf16_b6_A": (I.TINY_BF16, [10, 20, 30, 40, 50, 60], 3, "A"),
+    # the last-row products at the largest batch, and with per-session pending
+    # counts (policy B: each session's last row at its own index)
+    "tiny_bf16_b16_A": (I.TINY_BF16, [5 + 19 * i for i in range(16)], 2, "A"),
+    "tiny_bf16_b5_B": (I.TINY_BF16, [64, 7, 200, 33, 120], 3, "B"),
     # nine sessions: the unembedding in launches of four, four and one
     "tiny_f32_b9_A": (I.TINY_F32, [128, 40, 300, 7, 90, 11, 64, 200, 33], 2, "A"),
     "h2048_b2_B": (H2048, [333, 77], 2, "B"),
